@@ -1,0 +1,98 @@
+"""Seeded synthetic inputs for C = A.B (shared by the GPU tests, the bench and
+the oracle's tests; it holds no GEMM arithmetic).
+
+Every generator returns row-major ``uint16`` bit patterns of fp16 or bf16
+values.  Samples come from ``numpy.random.Generator(PCG64(seed))``.  They are
+rounded to the half format by a library conversion: numpy's correctly rounded
+float64 -> float16 cast for fp16, torch's float32 -> bfloat16 cast (round to
+nearest, ties to even) for bf16.
+
+Workload recipes (the shapes and value laws of the GEMM configurations):
+
+* ``uniform``  i.i.d. U[-1, 1)  (fp16 workloads; a sample may round to +1.0)
+* ``normal``   i.i.d. N(0, 1)   (bf16 workloads)
+* ``ints``     i.i.d. integers in {lo..hi} (bit-exact fixture: every partial sum
+  of an fp32 accumulation is an integer far below 2^24, hence exact)
+* ``quarter``  i.i.d. multiples of 0.25 in [-2, 2] (exact in fp16 and bf16;
+  every product is a multiple of 1/16, so fp32 partial sums stay exact while
+  their magnitude is below 2^19)
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F16, BF16 = "f16", "bf16"
+
+
+def _rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(int(seed)))
+
+
+def _to_bits(x: np.ndarray, fmt: str) -> np.ndarray:
+    if fmt == F16:
+        return np.ascontiguousarray(x.astype(np.float16)).view(np.uint16)
+    if fmt == BF16:
+        import torch
+        t = torch.from_numpy(np.ascontiguousarray(x.astype(np.float32)))
+        return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    raise ValueError("unknown format %r" % (fmt,))
+
+
+def uniform(shape, seed: int, fmt: str = F16, lo: float = -1.0, hi: float = 1.0) -> np.ndarray:
+    return _to_bits(_rng(seed).uniform(lo, hi, size=shape), fmt)
+
+
+def normal(shape, seed: int, fmt: str = BF16) -> np.ndarray:
+    if fmt == BF16:
+        x = _rng(seed).standard_normal(size=shape, dtype=np.float32)
+    else:
+        x = _rng(seed).standard_normal(size=shape)
+    return _to_bits(x, fmt)
+
+
+def ints(shape, seed: int, fmt: str = F16, lo: int = -2, hi: int = 2) -> np.ndarray:
+    return _to_bits(_rng(seed).integers(lo, hi + 1, size=shape).astype(np.float64), fmt)
+
+
+def quarter(shape, seed: int, fmt: str = F16) -> np.ndarray:
+    return _to_bits(_rng(seed).integers(-8, 9, size=shape).astype(np.float64) * 0.25, fmt)
+
+
+def from_values(values, fmt: str) -> np.ndarray:
+    """Exactly representable values (fixtures) -> bit patterns."""
+    x = np.asarray(values, dtype=np.float64)
+    bits = _to_bits(x, fmt)
+    return bits
+
+
+def padded(bits: np.ndarray, ld: int, fill: int = 0x7E00) -> np.ndarray:
+    """Copy a rows x cols matrix into a rows x ld buffer (ld >= cols); the
+    padding columns hold ``fill`` (a NaN pattern by default, so any read of
+    them shows up in the result).  Returns the full rows x ld array."""
+    rows, cols = bits.shape
+    if ld < cols:
+        raise ValueError("ld < cols")
+    out = np.full((rows, ld), fill, dtype=np.uint16)
+    out[:, :cols] = bits
+    return out
+
+
+# Seeds per workload: A = 100*c + 1, B = 100*c + 2, integer fixture +10.
+WORKLOADS = {
+    "f16_256": dict(M=256, N=256, K=256, fmt=F16, out="f32", law="uniform", c=1),
+    "f16_256_int": dict(M=256, N=256, K=256, fmt=F16, out="f32", law="ints", c=1),
+    "f16_2048": dict(M=2048, N=2048, K=2048, fmt=F16, out="f32", law="uniform", c=2),
+    "bf16_4096": dict(M=4096, N=4096, K=4096, fmt=BF16, out="bf16", law="normal", c=3),
+    "bf16_8192": dict(M=8192, N=8192, K=8192, fmt=BF16, out="bf16", law="normal", c=4),
+    "f16_ragged": dict(M=3000, N=5000, K=4099, fmt=F16, out="f16", law="uniform", c=5),
+}
+
+
+def workload_inputs(name: str):
+    """(A_bits, B_bits, spec) for a named workload."""
+    w = WORKLOADS[name]
+    law = {"uniform": uniform, "normal": normal, "ints": ints, "quarter": quarter}[w["law"]]
+    off = 10 if w["law"] == "ints" else 0
+    A = law((w["M"], w["K"]), 100 * w["c"] + 1 + off, w["fmt"])
+    B = law((w["K"], w["N"]), 100 * w["c"] + 2 + off, w["fmt"])
+    return A, B, w

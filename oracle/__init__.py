@@ -1,0 +1,222 @@
+"""TEST INFRASTRUCTURE ONLY: the CPU fp64 oracle for C = A.B.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The GPU library never imports, links or
+calls it, and this package imports nothing from the GPU library.
+
+The arithmetic lives in ``oracle.c`` (plain C, built with gcc into
+``liboracle.so`` next to this file).  This module is argument marshalling plus
+the comparison rule that decides parity:
+
+* ``gemm_f64`` / ``gemm_rows_f64``: C[i][j] = sum_k A[i][k]*B[k][j] in fp64, k
+  ascending, on exactly decoded fp16/bf16 inputs (the "arithmetic correctness
+  reference" of "GEMM From Naive CUDA to Tensor Cores", section "The
+  two-reference testing protocol").
+* ``round_to`` / ``ulp``: IEEE round-to-nearest-even to fp32/fp16/bf16 and the
+  spacing of those formats (same page, section "What FP32 accumulation
+  preserves, and what it can't recover").
+* ``bound``: the acceptance bound for a GPU result y against the fp64 result r:
+  |y - r| <= K * 2^-20 for fp32 output, and ulp_fmt(r) + K * 2^-20 for fp16 or
+  bf16 output.  Bit-exact fixtures instead require y == round_to(fmt, r).
+* ``flops``: the 2MNK count (same page, "Compute one output before launching a
+  warp": one multiply and one add per inner step).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+IN_F16, IN_BF16 = 0, 1
+OUT_F32, OUT_F16, OUT_BF16 = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c with gcc into liboracle.so (plain -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH) or (
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC",
+                               "-shared", _SRC, "-o", tmp, "-lm", "-lpthread"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        lib = ctypes.CDLL(build())
+        i64, u16p, f64p, i64p = (ctypes.c_int64, ctypes.POINTER(ctypes.c_uint16),
+                                 ctypes.POINTER(ctypes.c_double),
+                                 ctypes.POINTER(ctypes.c_int64))
+        lib.oracle_gemm_f64.argtypes = [i64, i64, i64, ctypes.c_int, u16p, i64, u16p, i64,
+                                        f64p, i64, ctypes.c_int]
+        lib.oracle_gemm_f64.restype = ctypes.c_int
+        lib.oracle_gemm_rows_f64.argtypes = [i64, i64p, i64, i64, ctypes.c_int, u16p, i64,
+                                             u16p, i64, f64p, i64, ctypes.c_int]
+        lib.oracle_gemm_rows_f64.restype = ctypes.c_int
+        lib.oracle_decode_array.argtypes = [ctypes.c_int, u16p, f64p, i64]
+        lib.oracle_decode_array.restype = None
+        lib.oracle_round_to.argtypes = [ctypes.c_int, ctypes.c_double]
+        lib.oracle_round_to.restype = ctypes.c_double
+        lib.oracle_ulp.argtypes = [ctypes.c_int, ctypes.c_double]
+        lib.oracle_ulp.restype = ctypes.c_double
+        lib.oracle_decode_f16.argtypes = [ctypes.c_uint16]
+        lib.oracle_decode_f16.restype = ctypes.c_double
+        lib.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
+        lib.oracle_decode_bf16.restype = ctypes.c_double
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _fmt_in(in_fmt) -> int:
+    if in_fmt in ("f16", "fp16", "float16", IN_F16):
+        return IN_F16
+    if in_fmt in ("bf16", "bfloat16", IN_BF16):
+        return IN_BF16
+    raise ValueError("unknown input format %r" % (in_fmt,))
+
+
+def _fmt_out(out_fmt) -> int:
+    if out_fmt in ("f32", "fp32", "float32", OUT_F32):
+        return OUT_F32
+    if out_fmt in ("f16", "fp16", "float16", OUT_F16):
+        return OUT_F16
+    if out_fmt in ("bf16", "bfloat16", OUT_BF16):
+        return OUT_BF16
+    raise ValueError("unknown output format %r" % (out_fmt,))
+
+
+def _as_bits_2d(x: np.ndarray) -> np.ndarray:
+    x = np.asarray(x)
+    if x.dtype != np.uint16:
+        raise TypeError("oracle inputs are uint16 bit patterns, got %s" % x.dtype)
+    if x.ndim != 2:
+        raise ValueError("oracle inputs are 2-D")
+    if x.strides[1] != 2:
+        x = np.ascontiguousarray(x)
+    return x
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def gemm_f64(A_bits, B_bits, in_fmt, threads: int | None = None) -> np.ndarray:
+    """Full C = A.B in fp64 from fp16/bf16 bit patterns (row-major, any row stride)."""
+    A = _as_bits_2d(A_bits)
+    B = _as_bits_2d(B_bits)
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ: %d vs %d" % (K, K2))
+    C = np.zeros((M, N), dtype=np.float64)
+    rc = _load().oracle_gemm_f64(M, N, K, _fmt_in(in_fmt), _ptr(A, ctypes.c_uint16),
+                                 A.strides[0] // 2, _ptr(B, ctypes.c_uint16), B.strides[0] // 2,
+                                 _ptr(C, ctypes.c_double), N, threads or default_threads())
+    if rc != 0:
+        raise MemoryError("oracle allocation failed")
+    return C
+
+
+def gemm_rows_f64(A_bits, B_bits, rows, in_fmt, threads: int | None = None) -> np.ndarray:
+    """Rows ``rows`` of C = A.B in fp64 (len(rows) x N)."""
+    A = _as_bits_2d(A_bits)
+    B = _as_bits_2d(B_bits)
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ: %d vs %d" % (K, K2))
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    if r.size and (r.min() < 0 or r.max() >= M):
+        raise IndexError("row index out of range")
+    C = np.zeros((r.size, N), dtype=np.float64)
+    rc = _load().oracle_gemm_rows_f64(r.size, _ptr(r, ctypes.c_int64), N, K, _fmt_in(in_fmt),
+                                      _ptr(A, ctypes.c_uint16), A.strides[0] // 2,
+                                      _ptr(B, ctypes.c_uint16), B.strides[0] // 2,
+                                      _ptr(C, ctypes.c_double), N, threads or default_threads())
+    if rc != 0:
+        raise MemoryError("oracle allocation failed")
+    return C
+
+
+def decode(bits, in_fmt) -> np.ndarray:
+    """fp16/bf16 bit patterns -> exact float64 values (oracle's own decoder)."""
+    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    out = np.empty(b.shape, dtype=np.float64)
+    _load().oracle_decode_array(_fmt_in(in_fmt), _ptr(b, ctypes.c_uint16),
+                                _ptr(out, ctypes.c_double), b.size)
+    return out
+
+
+def round_to(x, out_fmt) -> np.ndarray:
+    """IEEE round-to-nearest-even of float64 values to fp32/fp16/bf16 (as float64)."""
+    f = _fmt_out(out_fmt)
+    lib = _load()
+    xs = np.asarray(x, dtype=np.float64)
+    flat = xs.reshape(-1)
+    out = np.fromiter((lib.oracle_round_to(f, float(v)) for v in flat), dtype=np.float64,
+                      count=flat.size)
+    return out.reshape(xs.shape)
+
+
+def ulp(r, out_fmt) -> np.ndarray:
+    """Spacing of the output format at r (smallest subnormal at r == 0)."""
+    f = _fmt_out(out_fmt)
+    lib = _load()
+    rs = np.asarray(r, dtype=np.float64)
+    flat = rs.reshape(-1)
+    out = np.fromiter((lib.oracle_ulp(f, float(v)) for v in flat), dtype=np.float64,
+                      count=flat.size)
+    return out.reshape(rs.shape)
+
+
+def flops(M: int, N: int, K: int) -> int:
+    """2MNK: one multiply and one add per inner-loop step."""
+    return 2 * int(M) * int(N) * int(K)
+
+
+def bound(K: int, out_fmt, r) -> np.ndarray:
+    """Acceptance bound on |y - r| for a GPU output y against oracle value r."""
+    f = _fmt_out(out_fmt)
+    acc = float(K) * 2.0 ** -20
+    r = np.asarray(r, dtype=np.float64)
+    if f == OUT_F32:
+        return np.full(r.shape, acc)
+    return ulp(r, f) + acc
+
+
+def compare(y, r, K: int, out_fmt) -> dict:
+    """Check a GPU result y (float64 array of decoded outputs) against oracle r.
+
+    Returns max_abs, max_rel (over |r| > 0), the worst excess over the bound,
+    the number of elements outside the bound, and ``ok``.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    if y.shape != r.shape:
+        raise ValueError("shape mismatch %s vs %s" % (y.shape, r.shape))
+    if y.size == 0:
+        return {"ok": True, "max_abs": 0.0, "max_rel": 0.0, "n_bad": 0, "worst_ratio": 0.0}
+    err = np.abs(y - r)
+    err = np.where(np.isnan(err), np.inf, err)
+    b = bound(K, out_fmt, r)
+    nz = np.abs(r) > 0
+    max_rel = float(np.max(err[nz] / np.abs(r[nz]))) if nz.any() else 0.0
+    n_bad = int(np.count_nonzero(err > b))
+    return {"ok": n_bad == 0, "max_abs": float(err.max()), "max_rel": max_rel,
+            "n_bad": n_bad, "worst_ratio": float(np.max(err / b))}

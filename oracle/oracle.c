@@ -1,0 +1,222 @@
+/*
+ * oracle.c -- TEST INFRASTRUCTURE ONLY.  The plain CPU reference for C = A*B.
+ *
+ * Only the test-suite, the smoke check and the CPU-baseline leg of the
+ * benchmark may load this code.  The GPU library never links, includes or
+ * calls it, and it shares no source, header, table or helper with the GPU
+ * path.
+ *
+ * What it computes (the plain definition, nothing else):
+ *   For 0 <= i < M and 0 <= j < N,  C[i][j] = sum_{k=0}^{K-1} A[i][k] * B[k][j]
+ *   with A [M,K], B [K,N], C [M,N] all row-major, i.e. the alpha = 1, beta = 0
+ *   case of C <- alpha*A*B + beta*C whose old output is never read
+ *   ("GEMM From Naive CUDA to Tensor Cores", opening section and
+ *   "Compute one output before launching a warp").
+ *
+ * Precision contract: the inputs are fp16 or bf16 bit patterns.  Each one is
+ * decoded exactly to a double by the bit-level decoders below, and the dot
+ * product is accumulated in double, k ascending for every (i, j).  This is the
+ * "arithmetic correctness reference" of the two-reference protocol on the same
+ * page (section "The two-reference testing protocol": round the inputs to the
+ * half format, then accumulate in FP64).  Products of two fp16 (11-bit
+ * significand) or two bf16 (8-bit significand) values are exact in double, so
+ * the only rounding is the fp64 summation, bounded by (K-1) * 2^-53 * sum|a*b|.
+ *
+ * Output rounding: oracle_round_to() rounds a double to fp32, fp16 or bf16
+ * with IEEE round-to-nearest, ties to even (the mode the rounding demo in
+ * section "What FP32 accumulation preserves, and what it can't recover" of the
+ * same page relies on).  It is used to build the expected value of bit-exact
+ * fixtures whose exact result is not representable in the output format.
+ *
+ * Parity pins (tests/test_oracle_pins.py): the page's 2x3 . 3x2 worked example,
+ * exact rational brute force on tiny shapes, closed forms (all-ones,
+ * identity, permutation, rank-1), the two-reference example, the fp16 rounding
+ * table of the precision section, and numpy's IEEE float16 conversion.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORACLE_IN_F16 = 0, ORACLE_IN_BF16 = 1 };
+enum { ORACLE_OUT_F32 = 0, ORACLE_OUT_F16 = 1, ORACLE_OUT_BF16 = 2 };
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ * Normal:    (1024 + f) * 2^(e - 25)      Subnormal: f * 2^-24 */
+double oracle_decode_f16(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = (f != 0) ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);
+    return sign ? -v : v;
+}
+
+/* bfloat16: 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits.
+ * Normal:    (128 + f) * 2^(e - 134)      Subnormal: f * 2^-133 */
+double oracle_decode_bf16(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 7) & 0xff;
+    int f = h & 0x7f;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -133);
+    else if (e == 255)
+        v = (f != 0) ? NAN : INFINITY;
+    else
+        v = ldexp((double)(128 + f), e - 134);
+    return sign ? -v : v;
+}
+
+static double decode_one(int in_fmt, uint16_t h) {
+    return in_fmt == ORACLE_IN_BF16 ? oracle_decode_bf16(h) : oracle_decode_f16(h);
+}
+
+/* Round-to-nearest-even of a non-negative double q to an integer, written
+ * out: q < 2^53 here, so q - floor(q) is exact. */
+static double rne_integer(double q) {
+    double fl = floor(q);
+    double d = q - fl;
+    if (d > 0.5) return fl + 1.0;
+    if (d < 0.5) return fl;
+    return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;
+}
+
+/* Round x to a binary format with p significand bits (hidden bit included),
+ * minimum normal exponent emin and maximum exponent emax, IEEE RNE.
+ * Returns the rounded value as a double (+-inf on overflow, NaN kept). */
+static double round_generic(double x, int p, int emin, int emax) {
+    if (isnan(x)) return x;
+    if (x == 0.0 || isinf(x)) return x;
+    double a = fabs(x);
+    int E;                       /* a = m * 2^E, m in [0.5, 1) */
+    frexp(a, &E);
+    int e = E - 1;               /* a in [2^e, 2^(e+1)) */
+    if (e < emin) e = emin;      /* subnormal range: fixed quantum 2^(emin-p+1) */
+    double quantum = ldexp(1.0, e - p + 1);
+    double q = rne_integer(a / quantum);   /* exact scaling by a power of two */
+    double r = q * quantum;
+    /* overflow: anything that rounds to 2^(emax+1) or above is infinite */
+    if (r >= ldexp(1.0, emax + 1)) r = INFINITY;
+    return x < 0 ? -r : r;
+}
+
+double oracle_round_to(int out_fmt, double x) {
+    switch (out_fmt) {
+    case ORACLE_OUT_F16:  return round_generic(x, 11, -14, 15);
+    case ORACLE_OUT_BF16: return round_generic(x, 8, -126, 127);
+    default:              return round_generic(x, 24, -126, 127);
+    }
+}
+
+/* Spacing of the output format at r: 2^(floor(log2|r|) - p + 1), floored at
+ * the format's smallest subnormal (also the value used for r == 0). */
+double oracle_ulp(int out_fmt, double r) {
+    int p, emin;
+    switch (out_fmt) {
+    case ORACLE_OUT_F16:  p = 11; emin = -14;  break;
+    case ORACLE_OUT_BF16: p = 8;  emin = -126; break;
+    default:              p = 24; emin = -126; break;
+    }
+    double a = fabs(r);
+    int e = emin;
+    if (a != 0.0 && isfinite(a)) {
+        int E;
+        frexp(a, &E);
+        e = E - 1;
+        if (e < emin) e = emin;
+    }
+    return ldexp(1.0, e - p + 1);
+}
+
+void oracle_decode_array(int in_fmt, const uint16_t* src, double* dst, int64_t n) {
+    for (int64_t t = 0; t < n; ++t) dst[t] = decode_one(in_fmt, src[t]);
+}
+
+/* ------------------------------------------------------------------------
+ * The triple loop.  Row i of C (or of the selected rows) is
+ *   acc[j] = 0;  for k = 0..K-1: a = A[i][k]; for j: acc[j] += a * B[k][j]
+ * which is k ascending for every (i, j).  B is decoded once into doubles.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    const uint16_t* A; int64_t lda;
+    const double* Bd;              /* K x N decoded, row-major, stride N */
+    double* C; int64_t ldc;
+    const int64_t* rows;           /* NULL: rows r0..r1-1 of A; else rows[r] */
+    int64_t r0, r1;
+    int64_t N, K;
+    int in_fmt;
+} oracle_job_t;
+
+static void* oracle_worker(void* arg) {
+    oracle_job_t* jb = (oracle_job_t*)arg;
+    for (int64_t r = jb->r0; r < jb->r1; ++r) {
+        int64_t i = jb->rows ? jb->rows[r] : r;
+        double* c = jb->C + r * jb->ldc;
+        for (int64_t j = 0; j < jb->N; ++j) c[j] = 0.0;
+        const uint16_t* arow = jb->A + i * jb->lda;
+        for (int64_t k = 0; k < jb->K; ++k) {
+            double a = decode_one(jb->in_fmt, arow[k]);
+            const double* b = jb->Bd + k * jb->N;
+            for (int64_t j = 0; j < jb->N; ++j) c[j] += a * b[j];
+        }
+    }
+    return NULL;
+}
+
+static int run_rows(int in_fmt, int64_t nrows, const int64_t* rows, int64_t N, int64_t K,
+                    const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                    double* C, int64_t ldc, int nthreads) {
+    if (nrows <= 0 || N <= 0) return 0;
+    double* Bd = NULL;
+    if (K > 0) {
+        Bd = (double*)malloc((size_t)K * (size_t)N * sizeof(double));
+        if (!Bd) return -1;
+        for (int64_t k = 0; k < K; ++k)
+            oracle_decode_array(in_fmt, B + k * ldb, Bd + k * N, N);
+    }
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > nrows) nthreads = (int)nrows;
+    pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    oracle_job_t* jobs = (oracle_job_t*)malloc(sizeof(oracle_job_t) * (size_t)nthreads);
+    char* spawned = (char*)calloc((size_t)nthreads, 1);
+    if (!th || !jobs || !spawned) { free(Bd); free(th); free(jobs); free(spawned); return -1; }
+    int64_t per = (nrows + nthreads - 1) / nthreads;
+    for (int t = 0; t < nthreads; ++t) {
+        oracle_job_t* jb = &jobs[t];
+        jb->A = A; jb->lda = lda; jb->Bd = Bd; jb->C = C; jb->ldc = ldc;
+        jb->rows = rows; jb->N = N; jb->K = K; jb->in_fmt = in_fmt;
+        jb->r0 = t * per;
+        jb->r1 = (t + 1) * per < nrows ? (t + 1) * per : nrows;
+        if (jb->r0 >= jb->r1) continue;
+        if (nthreads > 1 && pthread_create(&th[t], NULL, oracle_worker, jb) == 0)
+            spawned[t] = 1;
+        else
+            oracle_worker(jb);          /* single thread, or could not spawn */
+    }
+    for (int t = 0; t < nthreads; ++t)
+        if (spawned[t]) pthread_join(th[t], NULL);
+    free(Bd); free(th); free(jobs); free(spawned);
+    return 0;
+}
+
+/* Full product: C (M x N doubles, stride ldc) = A (M x K, stride lda) *
+ * B (K x N, stride ldb).  Returns 0, or -1 on allocation failure. */
+int oracle_gemm_f64(int64_t M, int64_t N, int64_t K, int in_fmt,
+                    const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                    double* C, int64_t ldc, int nthreads) {
+    return run_rows(in_fmt, M, NULL, N, K, A, lda, B, ldb, C, ldc, nthreads);
+}
+
+/* Selected rows only: C is nrows x N (stride ldc); output row r is row rows[r]. */
+int oracle_gemm_rows_f64(int64_t nrows, const int64_t* rows, int64_t N, int64_t K, int in_fmt,
+                         const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                         double* C, int64_t ldc, int nthreads) {
+    return run_rows(in_fmt, nrows, rows, N, K, A, lda, B, ldb, C, ldc, nthreads);
+}

@@ -1,0 +1,121 @@
+"""Planted mistakes in a copy of the oracle (CPU only).
+
+Each mutant is oracle.c with one plausible slip (a dropped term, a wrong sign,
+a transposed operand, an ignored stride, a wrong exponent bias, a wrong tie
+rule).  It is compiled to a temporary library and run through a small battery
+of the pins; every mutant must fail at least one of them, and the unmutated
+copy must pass all of them.  This shows the pins have teeth.
+"""
+import ctypes
+import json
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+from dense_half_precision_tiled_amd import inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTANTS = {
+    "control": None,
+    "dropped_last_k": ("for (int64_t k = 0; k < jb->K; ++k) {", "for (int64_t k = 0; k + 1 < jb->K; ++k) {"),
+    "sign_dropped_f16": ("    return sign ? -v : v;\n}\n\n/* bfloat16", "    (void)sign; return v;\n}\n\n/* bfloat16"),
+    "transposed_B": ("c[j] += a * b[j];", "c[j] += a * jb->Bd[(j % jb->K) * jb->N + (k % jb->N)]; (void)b;"),
+    "ignores_lda": ("const uint16_t* arow = jb->A + i * jb->lda;", "const uint16_t* arow = jb->A + i * jb->K;"),
+    "subnormal_scale": ("v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);"),
+    "bf16_bias": ("v = ldexp((double)(128 + f), e - 134);", "v = ldexp((double)(128 + f), e - 133);"),
+    "ties_away": ("return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;", "return fl + 1.0;"),
+    "accumulate_in_float": ("c[j] += a * b[j];", "c[j] = (float)(c[j] + a * b[j]);"),
+}
+
+
+def _build(tmp_path, name, mutation):
+    src = open(SRC).read()
+    if mutation is not None:
+        old, new = mutation
+        assert src.count(old) >= 1, "mutation anchor not found: %s" % name
+        src = src.replace(old, new, 1)
+    c = tmp_path / ("%s.c" % name)
+    so = tmp_path / ("lib%s.so" % name)
+    c.write_text(src)
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", str(c), "-o", str(so),
+                           "-lm", "-lpthread"])
+    lib = ctypes.CDLL(str(so))
+    i64, u16p, f64p = ctypes.c_int64, ctypes.POINTER(ctypes.c_uint16), ctypes.POINTER(ctypes.c_double)
+    lib.oracle_gemm_f64.argtypes = [i64, i64, i64, ctypes.c_int, u16p, i64, u16p, i64, f64p, i64,
+                                    ctypes.c_int]
+    lib.oracle_decode_array.argtypes = [ctypes.c_int, u16p, f64p, i64]
+    lib.oracle_round_to.argtypes = [ctypes.c_int, ctypes.c_double]
+    lib.oracle_round_to.restype = ctypes.c_double
+    return lib
+
+
+def _gemm(lib, A, B, fmt):
+    M, K = A.shape
+    N = B.shape[1]
+    C = np.zeros((M, N))
+    lib.oracle_gemm_f64(M, N, K, 0 if fmt == "f16" else 1,
+                        A.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)), A.strides[0] // 2,
+                        B.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)), B.strides[0] // 2,
+                        C.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), N, 2)
+    return C
+
+
+def _battery(lib):
+    """Names of the pins this library fails."""
+    failed = []
+    with open(os.path.join(ROOT, "tests", "golden", "worked_example_2x3x2.json")) as f:
+        g = json.load(f)
+    for fmt in ("f16", "bf16"):
+        C = _gemm(lib, inputs.from_values(g["A"], fmt), inputs.from_values(g["B"], fmt), fmt)
+        if C.tolist() != g["C"]:
+            failed.append("worked_example_" + fmt)
+    # integer fixture with padded leading dimensions, against an int64 matmul
+    A = inputs.padded(inputs.ints((19, 37), 5, "f16"), 48)[:, :37]
+    B = inputs.padded(inputs.ints((37, 23), 6, "f16"), 32)[:, :23]
+    exact = (A.view(np.float16).astype(np.int64) @ B.view(np.float16).astype(np.int64))
+    if not np.array_equal(_gemm(lib, A, B, "f16"), exact.astype(np.float64)):
+        failed.append("int_fixture_ld")
+    # brute force against exact scaled-integer arithmetic on a random case
+    A = inputs.uniform((9, 300), 7, "f16")
+    B = inputs.uniform((300, 11), 8, "f16")
+    Ai = (A.view(np.float16).astype(np.float64) * 2.0 ** 24).astype(np.int64)
+    Bi = (B.view(np.float16).astype(np.float64) * 2.0 ** 24).astype(np.int64)
+    exact = np.array([[float(int(v)) for v in r] for r in Ai @ Bi]) * 2.0 ** -48
+    absdot = np.abs(Ai).astype(float) @ np.abs(Bi).astype(float) * 2.0 ** -48
+    if not np.all(np.abs(_gemm(lib, A, B, "f16") - exact) <= 300 * 2.0 ** -52 * absdot):
+        failed.append("exact_random")
+    # decoders against numpy / float32 widening
+    bits = np.arange(65536, dtype=np.uint16)
+    with np.errstate(invalid="ignore"):
+        bf16_ref = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for fmt, ref in (("f16", bits.view(np.float16).astype(np.float64)),
+                     ("bf16", bf16_ref)):
+        out = np.empty(65536)
+        lib.oracle_decode_array(0 if fmt == "f16" else 1,
+                                bits.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)),
+                                out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), 65536)
+        fin = np.isfinite(ref)
+        if not np.array_equal(out[fin], ref[fin]):
+            failed.append("decode_" + fmt)
+    # rounding ties against numpy's IEEE float16 cast
+    ties = 1.0 + (np.arange(0, 1000) + 0.5) * 2.0 ** -10   # halfway between fp16 neighbours in [1, 2)
+    got = np.array([lib.oracle_round_to(1, float(t)) for t in ties])
+    if not np.array_equal(got, ties.astype(np.float16).astype(np.float64)):
+        failed.append("round_ties_f16")
+    return failed
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, name):
+    lib = _build(tmp_path, name, MUTANTS[name])
+    failed = _battery(lib)
+    if name == "control":
+        assert failed == []
+    else:
+        assert failed, "planted mistake %s passed every pin" % name
