@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Throughput of C = A.B on one MI355X through the C ABI (gemm_run).
+
+One step = one gemm_run over the whole workload (default: bf16 8192^3 with
+bf16 output, A and B i.i.d. N(0,1)).  Inputs are generated on the host from
+fixed seeds and are resident in HBM before timing starts; the timed region is
+K back-to-back launches on one stream between two HIP events, after W
+untimed warmups.  TFLOP/s counts 2MNK per step.
+
+Printed: one JSON line with the contract fields plus
+  roofline      the GEMM kernel against the dense bf16/fp16 MFMA peak;
+  cpu_baseline  the CPU fp64 oracle timed on a bounded sample of output rows
+                of the same workload on this host (and those rows checked
+                against the GPU result);
+  secondary     the same measurement on bf16 4096^3.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOP/s (2MNK/t) at 4096³ and 8192³ bf16/fp16; % of MFMA peak"
+PEAK_TFLOPS = 2500.0        # MI355X published dense fp16/bf16 MFMA peak
+HBM_GBPS = 8000.0           # MI355X published HBM3E bandwidth
+CODES = {("f16", "f32"): 0, ("f16", "f16"): 1, ("bf16", "f32"): 2, ("bf16", "bf16"): 3}
+KERNEL_SOURCES = ["dense_half_precision_tiled_amd/csrc/gemm_kernels.hip",
+                  "dense_half_precision_tiled_amd/csrc/gemm_internal.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def describe(w) -> str:
+    return "%s GEMM C=A.B M=%d N=%d K=%d row-major, %s inputs, fp32 accumulate, %s output" % (
+        w["fmt"], w["M"], w["N"], w["K"],
+        "U[-1,1)" if w["law"] == "uniform" else "N(0,1)", w["out"])
+
+
+def upload(bits, torch):
+    import numpy as np
+    return torch.from_numpy(bits.view(np.int16)).cuda()
+
+
+def measure(G, torch, name, steps, warmup, instance=None):
+    """Upload a workload, run one correctness launch into a poisoned C, then
+    time `steps` launches.  Returns a dict with the timing and the buffers."""
+    import numpy as np
+    from dense_half_precision_tiled_amd import inputs
+    A, B, w = inputs.workload_inputs(name)
+    M, N, K = w["M"], w["N"], w["K"]
+    code = CODES[(w["fmt"], w["out"])]
+    tA, tB = upload(A, torch), upload(B, torch)
+    odt = torch.float32 if w["out"] == "f32" else torch.int16
+    tC = torch.full((M, N), -1, dtype=torch.int32 if odt == torch.float32 else torch.int16,
+                    device="cuda")                      # all-ones bits: NaN poison
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+    args = (M, N, K, code, tA.data_ptr(), K, tB.data_ptr(), N, tC.data_ptr(), N, s)
+
+    def launch():
+        st = G.gemm_run(*args) if instance is None else G.gemm_run_instance(instance, *args)
+        if st != 0:
+            raise RuntimeError("gemm_run failed: %s" % G.gemm_strerror(st))
+
+    launch()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        launch()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / steps
+    flops = 2.0 * M * N * K
+    inst = G.gemm_select_instance(M, N, K, code, tA.data_ptr(), K, tB.data_ptr(), N,
+                                  tC.data_ptr(), N) if instance is None else instance
+    return {"name": name, "w": w, "A": A, "B": B, "C": tC, "ms": ms, "wall_s": wall,
+            "tflops": flops / (ms * 1e-3) / 1e12, "instance": G.gemm_instance_name(inst),
+            "alg_bytes": 2 * (M * K + K * N) + (4 if w["out"] == "f32" else 2) * M * N}
+
+
+def traffic_from_profiles(name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when that summary is missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    entry = d.get("workloads", {}).get(name)
+    return None if entry is None else entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(res, budget_s: float):
+    """Time the CPU oracle on a sample of output rows of the same workload and
+    check those rows of the GPU result against it."""
+    import numpy as np
+    import torch
+    import oracle
+    w = res["w"]
+    M, N, K = w["M"], w["N"], w["K"]
+    threads = oracle.default_threads()
+    rng = np.random.Generator(np.random.PCG64(1234))
+    probe_rows = np.array(sorted({0, M - 1} | set(rng.integers(0, M, 2).tolist())), dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.gemm_rows_f64(res["A"], res["B"], probe_rows, w["fmt"], threads)
+    t_probe = time.perf_counter() - t0
+    per_row = t_probe / probe_rows.size
+    nrows = int(max(probe_rows.size, min(M, budget_s / max(per_row, 1e-6))))
+    rows = np.array(sorted(set(rng.integers(0, M, nrows).tolist()) | {0, M - 1}), dtype=np.int64)
+    t0 = time.perf_counter()
+    r = oracle.gemm_rows_f64(res["A"], res["B"], rows, w["fmt"], threads)
+    t = time.perf_counter() - t0
+    raw = res["C"].cpu().numpy()
+    if w["out"] == "f32":
+        y = raw.view(np.float32).astype(np.float64)[rows]
+    elif w["out"] == "f16":
+        y = raw.view(np.float16).astype(np.float64)[rows]
+    else:
+        y = (raw.view(np.uint16)[rows].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    check = oracle.compare(y, r, K, w["out"])
+    flops = 2.0 * rows.size * N * K
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d output rows (all %d columns, full K=%d), fp64 triple loop, %.1f s"
+                      % (rows.size, M, N, K, t),
+            "seconds": round(t, 3),
+            "parity_on_sample": {"ok": check["ok"], "max_abs": check["max_abs"],
+                                 "max_rel": check["max_rel"], "n_bad": check["n_bad"]}}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="bf16_8192")
+    ap.add_argument("--secondary", default="bf16_4096", help="'' to skip")
+    ap.add_argument("--instance", type=int, default=None, help="force a kernel instance id")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for cpu_baseline (0 to skip)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    from dense_half_precision_tiled_amd import gemm as G
+    G.load()
+
+    main_res = measure(G, torch, args.workload, args.steps, args.warmup, args.instance)
+    sec = None
+    if args.secondary:
+        r2 = measure(G, torch, args.secondary, max(args.steps, 50), args.warmup, args.instance)
+        sec = {"workload": describe(r2["w"]), "value": round(r2["tflops"], 2), "unit": "TFLOP/s",
+               "ms_per_step": round(r2["ms"], 5), "frac_of_peak": round(r2["tflops"] / PEAK_TFLOPS, 4),
+               "kernel": r2["instance"]}
+        del r2
+
+    w = main_res["w"]
+    traffic = traffic_from_profiles(args.workload)
+    line = {
+        "metric": METRIC,
+        "value": round(main_res["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w["fmt"],
+        "data": "synthetic",
+        "config": {"workload": describe(w), "M": w["M"], "N": w["N"], "K": w["K"],
+                   "in": w["fmt"], "out": w["out"], "kernel": main_res["instance"],
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(main_res["tflops"], 2), "peak": PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(main_res["tflops"] / PEAK_TFLOPS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes": main_res["alg_bytes"],
+                     "hbm_gbps_algorithmic": round(main_res["alg_bytes"] / (main_res["ms"] * 1e-3) / 1e9, 1)},
+    }
+    if sec is not None:
+        line["secondary"] = sec
+    if args.cpu_budget > 0:
+        line["cpu_baseline"] = cpu_baseline(main_res, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,51 @@
+"""Build libdhpt_gemm.so in-tree with hipcc for gfx950 (no GPU needed)."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libdhpt_gemm.so")
+ARCH = "gfx950"
+
+SOURCES = ["gemm_api.cpp", "gemm_kernels.hip"]
+
+# Packed-fp32 VALU ops stay disabled in every HIP translation unit.
+HIP_FLAGS = ["-x", "hip", "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
+             "-Wall", "-Wno-unused-command-line-argument",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-I" + INCLUDE, "-I" + CSRC]
+
+
+def hipcc() -> str:
+    return os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    """Compile every source and link the shared library.  Always recompiles."""
+    build_dir = os.path.join(PKG, "_build")
+    os.makedirs(build_dir, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+        cmd = [hipcc()] + HIP_FLAGS + list(extra_flags or []) + ["-c", os.path.join(CSRC, src),
+                                                                  "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True, stderr=None if verbose else subprocess.PIPE)
+        objs.append(obj)
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,176 @@
+// gemm_api.cpp -- the C ABI declared in include/gemm.h: argument validation,
+// instance selection and the launch on the caller's stream.  No allocation,
+// no host synchronisation, no state.
+#include "gemm.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_internal.h"
+
+namespace {
+
+using dhpt::Problem;
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxLd = int64_t(1) << 40;
+constexpr int64_t kMaxExtent = int64_t(1) << 47;   // elements spanned by one operand
+
+int out_elem_size(int dtype) { return (dtype == GEMM_F16_F32 || dtype == GEMM_BF16_F32) ? 4 : 2; }
+
+bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; }
+
+// Byte extent [begin, end) of a rows x cols row-major matrix with leading dim ld.
+void extent(const void* p, int64_t rows, int64_t cols, int64_t ld, int esz, uintptr_t* b, uintptr_t* e) {
+    *b = reinterpret_cast<uintptr_t>(p);
+    *e = *b + (uintptr_t)(((rows - 1) * ld + cols) * esz);
+}
+
+// Validate; on success fill `p` and return GEMM_OK (and *noop for empty output).
+int validate(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
+             const void* B, int64_t ldb, const void* C, int64_t ldc, Problem* p, bool* noop) {
+    *noop = false;
+    if (dtype < GEMM_F16_F32 || dtype > GEMM_BF16_BF16) return GEMM_ERR_DTYPE;
+    if (M < 0 || N < 0 || K < 0) return GEMM_ERR_DIM;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return GEMM_ERR_RANGE;
+    if (lda < 0 || ldb < 0 || ldc < 0) return GEMM_ERR_LD;
+    if (lda > kMaxLd || ldb > kMaxLd || ldc > kMaxLd) return GEMM_ERR_RANGE;
+    if (lda < K || ldb < N || ldc < N) return GEMM_ERR_LD;
+    // byte extents stay far below 2^63, and the tile grid fits a 32-bit launch
+    if ((M > 1 && lda > kMaxExtent / (M - 1)) || (K > 1 && ldb > kMaxExtent / (K - 1)) ||
+        (M > 1 && ldc > kMaxExtent / (M - 1)))
+        return GEMM_ERR_RANGE;
+    if (((M + 127) / 128) * ((N + 127) / 128) > kMaxDim) return GEMM_ERR_RANGE;
+    if (M == 0 || N == 0) { *noop = true; return GEMM_OK; }
+    if (C == nullptr) return GEMM_ERR_NULL;
+    if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_ERR_NULL;
+    const int osz = out_elem_size(dtype);
+    if (reinterpret_cast<uintptr_t>(C) % osz != 0) return GEMM_ERR_ALIGN;
+    if (K > 0 && (reinterpret_cast<uintptr_t>(A) % 2 != 0 || reinterpret_cast<uintptr_t>(B) % 2 != 0))
+        return GEMM_ERR_ALIGN;
+    if (K > 0) {
+        uintptr_t c0, c1, a0, a1, b0, b1;
+        extent(C, M, N, ldc, osz, &c0, &c1);
+        extent(A, M, K, lda, 2, &a0, &a1);
+        extent(B, K, N, ldb, 2, &b0, &b1);
+        if (overlaps(c0, c1, a0, a1) || overlaps(c0, c1, b0, b1)) return GEMM_ERR_ALIAS;
+    }
+    p->M = (int)M; p->N = (int)N; p->K = (int)K; p->dtype = dtype;
+    p->A = static_cast<const uint16_t*>(A); p->lda = lda;
+    p->B = static_cast<const uint16_t*>(B); p->ldb = ldb;
+    p->C = const_cast<void*>(C); p->ldc = ldc;
+    p->vecA = (reinterpret_cast<uintptr_t>(A) % 16 == 0) && (lda % 8 == 0);
+    p->vecB = (reinterpret_cast<uintptr_t>(B) % 16 == 0) && (ldb % 8 == 0);
+    return GEMM_OK;
+}
+
+int64_t tiles_for(int id, int64_t M, int64_t N) {
+    const dhpt::InstanceInfo& in = dhpt::kInstances[id];
+    return ((M + in.bm - 1) / in.bm) * ((N + in.bn - 1) / in.bn);
+}
+
+// Large tiles when they still give at least half a wave over the 256 CUs;
+// otherwise 128x128 tiles (more workgroups for mid-size shapes).
+int choose_instance(const Problem& p) {
+    const bool big = tiles_for(0, p.M, p.N) >= 128;
+    const int order[2][2] = {{0, 2}, {1, 3}};      // [tile][edge]
+    const int tile = big ? 0 : 1;
+    if (dhpt::instance_supports(order[tile][0], p)) return order[tile][0];
+    return order[tile][1];
+}
+
+int enqueue(int id, const Problem& p, hipStream_t s) {
+    hipError_t err = hipGetLastError();   // clear a stale error so it is not blamed on this launch
+    (void)err;
+    err = dhpt::launch_instance(id, p, s);
+    return err == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_run(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
+             const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
+    Problem p;
+    bool noop;
+    int st = validate(M, N, K, dtype, A, lda, B, ldb, C, ldc, &p, &noop);
+    if (st != GEMM_OK || noop) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (K == 0) {
+        (void)hipGetLastError();
+        return dhpt::launch_zero_fill(p, s) == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+    }
+    return enqueue(choose_instance(p), p, s);
+}
+
+int gemm_run_instance(int instance, int64_t M, int64_t N, int64_t K, int dtype, const void* A,
+                      int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
+    if (instance < 0 || instance >= dhpt::kNumInstances) return GEMM_ERR_INSTANCE;
+    Problem p;
+    bool noop;
+    int st = validate(M, N, K, dtype, A, lda, B, ldb, C, ldc, &p, &noop);
+    if (st != GEMM_OK || noop) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (K == 0) {
+        (void)hipGetLastError();
+        return dhpt::launch_zero_fill(p, s) == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+    }
+    if (!dhpt::instance_supports(instance, p)) return GEMM_ERR_INSTANCE;
+    return enqueue(instance, p, s);
+}
+
+int gemm_select_instance(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
+                         const void* B, int64_t ldb, const void* C, int64_t ldc) {
+    Problem p;
+    bool noop;
+    int st = validate(M, N, K, dtype, A, lda, B, ldb, C, ldc, &p, &noop);
+    if (st != GEMM_OK) return st;
+    if (noop || K == 0) return GEMM_OK;
+    return choose_instance(p);
+}
+
+int gemm_num_instances(void) { return dhpt::kNumInstances; }
+
+const char* gemm_instance_name(int instance) {
+    if (instance < 0 || instance >= dhpt::kNumInstances) return "?";
+    return dhpt::kInstances[instance].name;
+}
+
+int64_t gemm_tile_order(int instance, int64_t M, int64_t N, int32_t* tm, int32_t* tn, int64_t count) {
+    if (instance < 0 || instance >= dhpt::kNumInstances) return GEMM_ERR_INSTANCE;
+    if (M < 0 || N < 0) return GEMM_ERR_DIM;
+    if (M > kMaxDim || N > kMaxDim) return GEMM_ERR_RANGE;
+    const dhpt::InstanceInfo& in = dhpt::kInstances[instance];
+    const int64_t tilesM = (M + in.bm - 1) / in.bm, tilesN = (N + in.bn - 1) / in.bn;
+    const int64_t T = tilesM * tilesN;
+    if (T > kMaxDim) return GEMM_ERR_RANGE;
+    if (tm != nullptr && tn != nullptr) {
+        const int64_t n = count < T ? count : T;
+        for (int64_t w = 0; w < n; ++w) {
+            int a, b;
+            dhpt::tile_coords((int)w, (int)tilesM, (int)tilesN, in.group_m, &a, &b);
+            tm[w] = a;
+            tn[w] = b;
+        }
+    }
+    return T;
+}
+
+const char* gemm_strerror(int status) {
+    switch (status) {
+    case GEMM_OK: return "success";
+    case GEMM_ERR_DIM: return "negative dimension";
+    case GEMM_ERR_LD: return "leading dimension smaller than the row length (lda < K, ldb < N or ldc < N)";
+    case GEMM_ERR_NULL: return "null pointer for a non-empty operand";
+    case GEMM_ERR_DTYPE: return "unknown dtype";
+    case GEMM_ERR_ALIAS: return "C overlaps A or B";
+    case GEMM_ERR_RANGE: return "dimension or leading dimension out of the supported range";
+    case GEMM_ERR_LAUNCH: return "kernel launch failed";
+    case GEMM_ERR_ALIGN: return "pointer not aligned to its element size";
+    case GEMM_ERR_INSTANCE: return "unknown instance, or instance cannot run this shape";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,138 @@
+/*
+ * gemm.h -- C ABI of the MI355X (gfx950) dense half-precision GEMM library
+ * (libdhpt_gemm.so).  Plain C types only; no allocation, no host
+ * synchronisation, no state kept between calls.
+ *
+ * The operation (gemm_run) is the alpha = 1, beta = 0 case of
+ * C <- alpha*A*B + beta*C in which the old C is never read, on row-major
+ * A [M,K], B [K,N] and C [M,N] ("GEMM From Naive CUDA to Tensor Cores",
+ * opening section; its section "Layout is part of the type" lists what the
+ * contract must pin down: logical shapes, storage order, leading dimensions,
+ * alignment and the input/accumulator/output types):
+ *
+ *     C[i*ldc + j] = sum_{k=0}^{K-1} A[i*lda + k] * B[k*ldb + j]
+ *                    for 0 <= i < M, 0 <= j < N.
+ *
+ * The products of the half-precision inputs are accumulated in fp32 (the FP16
+ * input, FP32 accumulate contract of the Ada tensor-core GEMM write-up, section
+ * "D = A . B"), then converted once to the output type (fp32 as is; fp16 and
+ * bf16 by IEEE round-to-nearest-even).
+ */
+#ifndef DHPT_GEMM_H
+#define DHPT_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Input/output type pair.  A and B always share the input type. */
+typedef enum {
+    GEMM_F16_F32 = 0,   /* fp16 A, B -> fp32 C */
+    GEMM_F16_F16 = 1,   /* fp16 A, B -> fp16 C */
+    GEMM_BF16_F32 = 2,  /* bf16 A, B -> fp32 C */
+    GEMM_BF16_BF16 = 3  /* bf16 A, B -> bf16 C */
+} gemm_dtype_t;
+
+/* Status codes.  Every error is returned before anything is enqueued. */
+enum {
+    GEMM_OK = 0,
+    GEMM_ERR_DIM = -1,      /* M, N or K negative */
+    GEMM_ERR_LD = -2,       /* lda < K, ldb < N or ldc < N (or a negative ld) */
+    GEMM_ERR_NULL = -3,     /* C null with M*N > 0, or A/B null with M*N*K > 0 */
+    GEMM_ERR_DTYPE = -4,    /* dtype not one of gemm_dtype_t */
+    GEMM_ERR_ALIAS = -5,    /* C's byte range overlaps A's or B's */
+    GEMM_ERR_RANGE = -6,    /* a dimension >= 2^31, a leading dimension > 2^40, an
+                               operand spanning more than 2^47 elements, or more
+                               than 2^31-1 output tiles */
+    GEMM_ERR_LAUNCH = -7,   /* the HIP runtime rejected the kernel launch */
+    GEMM_ERR_ALIGN = -8,    /* a pointer not aligned to its element size */
+    GEMM_ERR_INSTANCE = -9  /* gemm_run_instance: unknown id, or the instance
+                               cannot handle this shape/alignment */
+};
+
+/*
+ * gemm_run -- enqueue C = A.B on `stream`.
+ *
+ *   M, N, K    logical sizes (A is M x K, B is K x N, C is M x N).
+ *   dtype      a gemm_dtype_t value.
+ *   A, lda     device pointer to row-major A; element (i,k) at A[i*lda + k]
+ *              (16-bit elements), lda >= K.
+ *   B, ldb     device pointer to row-major B; element (k,j) at B[k*ldb + j],
+ *              ldb >= N.
+ *   C, ldc     device pointer to row-major C; element (i,j) at C[i*ldc + j]
+ *              (4-byte elements for fp32 output, 2-byte otherwise), ldc >= N.
+ *   stream     a hipStream_t cast to void*; NULL means the null stream.
+ *
+ * Ownership: the caller allocates A, B and C on the current HIP device and
+ * keeps them alive until the enqueued work completes.  The library allocates
+ * nothing and reads A and B only.  It writes exactly the M x N elements of C;
+ * the padding columns j >= N of each C row (and everything else) are never
+ * touched, and the old contents of C are never read.
+ *
+ * Sizes: M == 0 or N == 0 is a successful no-op.  K == 0 writes zeros to the
+ * M x N region (the product of an M x 0 and a 0 x N matrix).
+ *
+ * Alignment: only natural element alignment is required.  Leading dimensions
+ * and base pointers that are multiples of 16 bytes select the vector-load
+ * kernels; anything else runs on the element-masked edge kernels.
+ *
+ * Returns GEMM_OK once the kernel is enqueued (asynchronous: device faults
+ * surface at the caller's next synchronisation), or a GEMM_ERR_* code.
+ */
+int gemm_run(int64_t M, int64_t N, int64_t K, int dtype,
+             const void* A, int64_t lda, const void* B, int64_t ldb,
+             void* C, int64_t ldc, void* stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* gemm_strerror(int status);
+
+/*
+ * Kernel instances.  Each instance is one compiled tile geometry; all compute
+ * the same function.  gemm_run picks one from the shape, the alignment and the
+ * number of output tiles.
+ *
+ * gemm_select_instance returns the id gemm_run would use for these arguments
+ * (pointers are only inspected for alignment, never dereferenced; no GPU call
+ * is made), or a negative GEMM_ERR_* code for arguments gemm_run rejects.
+ * For no-op sizes (M == 0, N == 0 or K == 0) it returns GEMM_OK.
+ */
+int gemm_select_instance(int64_t M, int64_t N, int64_t K, int dtype,
+                         const void* A, int64_t lda, const void* B, int64_t ldb,
+                         const void* C, int64_t ldc);
+
+/* Number of instance ids (0 .. gemm_num_instances()-1). */
+int gemm_num_instances(void);
+
+/* Static name of an instance id ("?" for an unknown id). */
+const char* gemm_instance_name(int instance);
+
+/*
+ * gemm_run_instance -- gemm_run with the instance forced (for sweeps and for
+ * the tests that require instances differing only in data movement or tile
+ * order to agree bit for bit).  Same arguments, ownership and status codes as
+ * gemm_run, plus GEMM_ERR_INSTANCE when `instance` is unknown or cannot
+ * handle the shape or alignment.
+ */
+int gemm_run_instance(int instance, int64_t M, int64_t N, int64_t K, int dtype,
+                      const void* A, int64_t lda, const void* B, int64_t ldb,
+                      void* C, int64_t ldc, void* stream);
+
+/*
+ * gemm_tile_order -- host evaluation of an instance's workgroup-to-tile map
+ * (the L2-aware visit order of the Ada write-up, section "grouped CTA
+ * rasterization", applied per XCD).  For workgroup ids 0 .. count-1 of a launch
+ * on an M x N output it writes the output tile row tm[w] and column tn[w].
+ * Returns the number of workgroups of that launch, or a negative GEMM_ERR_*
+ * code.  With tm == NULL or tn == NULL nothing is written.  No GPU call is
+ * made.
+ */
+int64_t gemm_tile_order(int instance, int64_t M, int64_t N,
+                        int32_t* tm, int32_t* tn, int64_t count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DHPT_GEMM_H */

@@ -1,0 +1,147 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/gemm.h declares, rejects bad arguments before touching the device,
+and its instance choice and tile visit order are what they claim."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from dense_half_precision_tiled_amd import gemm as G
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm.h")
+
+# Fake, never dereferenced device addresses for validation-only calls.
+PA, PB, PC = 0x10000000, 0x20000000, 0x30000000
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(G.LIB_PATH):
+        from dense_half_precision_tiled_amd import build
+        build.build()
+    return G.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) == set(G.EXPORTED)
+    raw = ctypes.CDLL(G.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_strerror_covers_every_status(lib):
+    for st in range(0, -10, -1):
+        s = G.gemm_strerror(st)
+        assert s and s != "unknown status"
+    assert G.gemm_strerror(12345) == "unknown status"
+
+
+@pytest.mark.parametrize("args,want", [
+    ((-1, 4, 4, 0, PA, 4, PB, 4, PC, 4), G.GEMM_ERR_DIM),
+    ((4, -1, 4, 0, PA, 4, PB, 4, PC, 4), G.GEMM_ERR_DIM),
+    ((4, 4, -1, 0, PA, 4, PB, 4, PC, 4), G.GEMM_ERR_DIM),
+    ((4, 4, 4, 7, PA, 4, PB, 4, PC, 4), G.GEMM_ERR_DTYPE),
+    ((4, 4, 4, -1, PA, 4, PB, 4, PC, 4), G.GEMM_ERR_DTYPE),
+    ((4, 4, 8, 0, PA, 7, PB, 4, PC, 4), G.GEMM_ERR_LD),
+    ((4, 4, 8, 0, PA, 8, PB, 3, PC, 4), G.GEMM_ERR_LD),
+    ((4, 4, 8, 0, PA, 8, PB, 4, PC, 3), G.GEMM_ERR_LD),
+    ((4, 4, 8, 0, PA, -8, PB, 4, PC, 4), G.GEMM_ERR_LD),
+    ((4, 4, 8, 0, PA, 8, PB, 4, 0, 4), G.GEMM_ERR_NULL),
+    ((4, 4, 8, 0, 0, 8, PB, 4, PC, 4), G.GEMM_ERR_NULL),
+    ((4, 4, 8, 0, PA, 8, 0, 4, PC, 4), G.GEMM_ERR_NULL),
+    ((4, 4, 8, 0, PA + 1, 8, PB, 4, PC, 4), G.GEMM_ERR_ALIGN),
+    ((4, 4, 8, 0, PA, 8, PB, 4, PC + 2, 4), G.GEMM_ERR_ALIGN),     # fp32 C needs 4 B
+    ((1 << 31, 4, 8, 0, PA, 8, PB, 4, PC, 4), G.GEMM_ERR_RANGE),
+    ((4, 4, 8, 0, PA, (1 << 40) + 8, PB, 4, PC, 4), G.GEMM_ERR_RANGE),
+    ((1 << 20, 4, 8, 0, PA, 1 << 30, PB, 4, PC, 4), G.GEMM_ERR_RANGE),
+    # C overlapping A, then B
+    ((4, 4, 8, 0, PA, 8, PB, 4, PA + 16, 4), G.GEMM_ERR_ALIAS),
+    ((4, 4, 8, 3, PA, 8, PB, 4, PB + 8, 4), G.GEMM_ERR_ALIAS),
+])
+def test_invalid_arguments_rejected_before_launch(lib, args, want):
+    assert G.gemm_run(*args, None) == want
+    assert G.gemm_select_instance(*args) == want
+    for inst in range(G.gemm_num_instances()):
+        assert G.gemm_run_instance(inst, *args, None) == want
+
+
+def test_empty_output_is_a_noop_without_launch(lib):
+    # M == 0 or N == 0: success, nothing enqueued, pointers may be null
+    assert G.gemm_run(0, 5, 7, 0, 0, 7, 0, 5, 0, 5, None) == G.GEMM_OK
+    assert G.gemm_run(5, 0, 7, 0, 0, 7, 0, 0, 0, 0, None) == G.GEMM_OK
+    assert G.gemm_select_instance(5, 0, 7, 0, 0, 7, 0, 0, 0, 0) == G.GEMM_OK
+
+
+def test_adjacent_buffers_are_not_aliases(lib):
+    # C starts exactly where A ends: allowed (only overlap is rejected)
+    M, N, K = 4, 4, 8
+    a_end = PA + ((M - 1) * K + K) * 2
+    assert G.gemm_select_instance(M, N, K, 0, PA, K, PB, N, a_end, N) >= 0
+
+
+def test_unknown_instance(lib):
+    n = G.gemm_num_instances()
+    assert n >= 2
+    assert G.gemm_run_instance(n, 4, 4, 4, 0, PA, 4, PB, 4, PC, 4, None) == G.GEMM_ERR_INSTANCE
+    assert G.gemm_instance_name(n) == "?"
+    for i in range(n):
+        assert G.gemm_instance_name(i).startswith("mfma_")
+
+
+def _pick(M, N, K, dtype=3, lda=None, ldb=None, ldc=None, pa=PA, pb=PB):
+    return G.gemm_instance_name(G.gemm_select_instance(
+        M, N, K, dtype, pa, lda or K, pb, ldb or N, 0x7000000000, ldc or N))
+
+
+def test_instance_choice(lib):
+    assert _pick(8192, 8192, 8192) == "mfma_256x256x64"
+    assert _pick(4096, 4096, 4096) == "mfma_256x256x64"
+    assert _pick(2048, 2048, 2048, 0) == "mfma_128x128x64"
+    assert _pick(256, 256, 256, 0) == "mfma_128x128x64"
+    # ragged shape with a 2-byte-aligned lda: edge kernel
+    assert _pick(3000, 5000, 4099, 1).endswith("_edge")
+    # aligned shape but a misaligned base pointer: edge kernel
+    assert _pick(4096, 4096, 4096, pa=PA + 2).endswith("_edge")
+    # K not a multiple of 64: edge kernel
+    assert _pick(4096, 4096, 4000).endswith("_edge")
+
+
+@pytest.mark.parametrize("shape", [(8192, 8192), (4096, 4096), (2048, 2048), (3000, 5000),
+                                   (256, 256), (2, 2), (257, 263), (100000, 128), (128, 70000)])
+def test_tile_order_is_a_bijection(lib, shape):
+    M, N = shape
+    for inst in range(G.gemm_num_instances()):
+        tm, tn = G.gemm_tile_order(inst, M, N)
+        name = G.gemm_instance_name(inst)
+        bm = int(name.split("_")[1].split("x")[0])
+        bn = int(name.split("_")[1].split("x")[1])
+        tilesM, tilesN = -(-M // bm), -(-N // bn)
+        assert tm.size == tilesM * tilesN
+        assert tm.min() >= 0 and tm.max() < tilesM and tn.min() >= 0 and tn.max() < tilesN
+        flat = tm.astype(np.int64) * tilesN + tn
+        assert np.unique(flat).size == flat.size
+
+
+@pytest.mark.parametrize("n", [4096, 8192])
+def test_tile_order_keeps_each_xcd_compact(lib, n):
+    """The first 32 workgroups dealt to one XCD (w = x, x+8, x+16, ... under
+    round-robin dispatch) share that XCD's L2.  With the remap they cover a
+    4x8 or 8x4 block of tiles: at most 12 distinct A row-panels plus B
+    column-panels, never more than plain row-major order needs."""
+    tm, tn = G.gemm_tile_order(0, n, n)
+    tiles_n = n // 256
+    for x in range(8):
+        sel = np.arange(x, 256, 8)
+        panels = np.unique(tm[sel]).size + np.unique(tn[sel]).size
+        row_major = np.unique(sel // tiles_n).size + np.unique(sel % tiles_n).size
+        assert panels <= 12 and panels <= row_major, (x, panels, row_major)

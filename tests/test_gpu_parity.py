@@ -1,0 +1,325 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars (written in each test):
+* exact fixtures (small integers, multiples of 0.25, unique-valued identity
+  products): every element equals round_to(out_fmt, oracle), bit for bit
+  (+0 and -0 compare equal);
+* random inputs: |y - r| <= K * 2^-20 (fp32 output) or
+  ulp_fmt(r) + K * 2^-20 (fp16/bf16 output) for every checked element;
+* full-size shapes: oracle rows sampled (first, last, tile edges, the last
+  partial tile) plus a Freivalds check of the whole matrix;
+* memory outside the M x N region of C (row padding and guard bands) is
+  never written.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from dense_half_precision_tiled_amd import inputs
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DTYPES = {0: ("f16", "f32"), 1: ("f16", "f16"), 2: ("bf16", "f32"), 3: ("bf16", "bf16")}
+POISON16 = 0x7E11      # a quiet-NaN pattern in both fp16 and bf16
+POISON32 = 0x7FC01234  # a quiet NaN in fp32
+GUARD = 64             # guard elements before and after C
+
+
+@pytest.fixture(scope="module")
+def G():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from dense_half_precision_tiled_amd import gemm
+    gemm.load()      # raises if the library is missing: no fallback
+    return gemm
+
+
+def _dev(bits, ld=None, offset=0):
+    """Upload a rows x cols bit matrix into a buffer with row stride ld,
+    starting `offset` elements into the allocation; padding is poisoned."""
+    rows, cols = bits.shape
+    ld = ld or cols
+    buf = np.full(offset + max(rows * ld, 1) + 8, POISON16, dtype=np.uint16)
+    if rows and cols:
+        buf[offset:offset + rows * ld].reshape(rows, ld)[:, :cols] = bits
+    t = torch.from_numpy(buf.view(np.int16)).cuda()
+    return t, t.data_ptr() + 2 * offset, ld
+
+
+def _decode_out(raw, out_fmt):
+    if out_fmt == "f32":
+        return raw.view(np.float32).astype(np.float64)
+    if out_fmt == "f16":
+        return raw.view(np.float16).astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        return (raw.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def run(G, A, B, code, lda=None, ldb=None, ldc=None, a_off=0, instance=None, stream=None,
+        expect=0):
+    """C = A.B on the GPU; returns the decoded M x N result.  Checks that the
+    row padding of C and guard bands around it keep their poison."""
+    M, K = A.shape
+    N = B.shape[1]
+    out_fmt = DTYPES[code][1]
+    tA, pA, lda = _dev(A, lda, a_off)
+    tB, pB, ldb = _dev(B, ldb)
+    ldc = ldc or N
+    if out_fmt == "f32":
+        cbuf = np.full(2 * GUARD + max(M * ldc, 1), POISON32, dtype=np.uint32)
+        tC = torch.from_numpy(cbuf.view(np.int32)).cuda()
+        esz = 4
+    else:
+        cbuf = np.full(2 * GUARD + max(M * ldc, 1), POISON16, dtype=np.uint16)
+        tC = torch.from_numpy(cbuf.view(np.int16)).cuda()
+        esz = 2
+    pC = tC.data_ptr() + esz * GUARD
+    s = stream.cuda_stream if stream is not None else torch.cuda.current_stream().cuda_stream
+    if instance is None:
+        st = G.gemm_run(M, N, K, code, pA, lda, pB, ldb, pC, ldc, s)
+    else:
+        st = G.gemm_run_instance(instance, M, N, K, code, pA, lda, pB, ldb, pC, ldc, s)
+    assert st == expect, G.gemm_strerror(st)
+    torch.cuda.synchronize()
+    raw = tC.cpu().numpy().view(np.uint32 if esz == 4 else np.uint16)
+    assert np.all(raw[:GUARD] == cbuf[:GUARD]) and np.all(raw[-GUARD:] == cbuf[-GUARD:]), \
+        "guard band written"
+    body = raw[GUARD:GUARD + M * ldc].reshape(M, ldc) if M else raw[:0].reshape(0, ldc)
+    if ldc > N:
+        assert np.all(body[:, N:] == cbuf[GUARD]), "row padding of C written"
+    return _decode_out(np.ascontiguousarray(body[:, :N]), out_fmt)
+
+
+def assert_bound(y, r, K, out_fmt, what=""):
+    res = oracle.compare(y, r, K, out_fmt)
+    assert res["ok"], "%s: %d elements outside the bound; max_abs %.3g, worst/bound %.3g" % (
+        what, res["n_bad"], res["max_abs"], res["worst_ratio"])
+    return res
+
+
+def assert_exact(y, r, out_fmt, what=""):
+    want = oracle.round_to(r, out_fmt)
+    bad = ~((y == want) | (np.isnan(y) & np.isnan(want)))
+    assert not bad.any(), "%s: %d elements differ, first at %s: %r vs %r" % (
+        what, bad.sum(), np.argwhere(bad)[0], y[bad][0], want[bad][0])
+
+
+def law_for(fmt):
+    return inputs.uniform if fmt == "f16" else inputs.normal
+
+
+# ------------------------------------------------------------ exact fixtures
+@pytest.mark.parametrize("code", [0, 1, 2, 3])
+def test_worked_example(G, code):
+    import json
+    with open(os.path.join(os.path.dirname(__file__), "golden", "worked_example_2x3x2.json")) as f:
+        g = json.load(f)
+    fmt, out = DTYPES[code]
+    y = run(G, inputs.from_values(g["A"], fmt), inputs.from_values(g["B"], fmt), code)
+    assert y.tolist() == g["C"]
+
+
+def test_integer_fixture_256_bit_exact(G):
+    """fp16 integers in {-2..2}, 256^3, fp32 output: |C| <= 1024, exact."""
+    A, B, w = inputs.workload_inputs("f16_256_int")
+    y = run(G, A, B, 0)
+    r = oracle.gemm_f64(A, B, "f16")
+    assert np.array_equal(y, r)
+
+
+@pytest.mark.parametrize("code", [0, 1, 2, 3])
+@pytest.mark.parametrize("shape", [(512, 512, 512), (257, 263, 251), (1024, 768, 640),
+                                   (64, 1000, 2048)])
+def test_quarter_grid_bit_exact(G, code, shape):
+    M, N, K = shape
+    fmt, out = DTYPES[code]
+    A = inputs.quarter((M, K), 71, fmt)
+    B = inputs.quarter((K, N), 72, fmt)
+    y = run(G, A, B, code)
+    assert_exact(y, oracle.gemm_f64(A, B, fmt), out, "quarter %s" % (shape,))
+
+
+@pytest.mark.parametrize("code", [0, 3])
+def test_unique_value_ownership(G, code):
+    """Identity times a matrix of distinct integers returns that matrix: every
+    output element lands where it belongs (fragment and accumulator maps)."""
+    fmt, out = DTYPES[code]
+    n = 256
+    U = (np.arange(n * n) % 251 - 125).reshape(n, n).astype(np.float64)    # distinct per row
+    U[:, ::7] += 0.5
+    I = np.eye(n)
+    y = run(G, inputs.from_values(I, fmt), inputs.from_values(U, fmt), code)
+    assert np.array_equal(y, U)
+    y = run(G, inputs.from_values(U, fmt), inputs.from_values(I, fmt), code)
+    assert np.array_equal(y, U)
+    P = np.eye(n)[np.random.Generator(np.random.PCG64(3)).permutation(n)]
+    y = run(G, inputs.from_values(P, fmt), inputs.from_values(U, fmt), code)
+    assert np.array_equal(y, P @ U)
+
+
+# ------------------------------------------------------------ random, small
+SMALL = [(1, 1, 1), (2, 2, 3), (3, 5, 7), (8, 8, 8), (1, 300, 17), (300, 1, 17), (17, 65, 19),
+         (31, 29, 37), (73, 61, 67), (129, 131, 65), (64, 64, 1), (255, 257, 129)]
+
+
+@pytest.mark.parametrize("code", [0, 1, 2, 3])
+def test_random_small_shapes(G, code):
+    fmt, out = DTYPES[code]
+    for i, (M, N, K) in enumerate(SMALL):
+        A = law_for(fmt)((M, K), 1000 + i, fmt)
+        B = law_for(fmt)((K, N), 2000 + i, fmt)
+        y = run(G, A, B, code)
+        assert_bound(y, oracle.gemm_f64(A, B, fmt), K, out, "shape %s" % ((M, N, K),))
+
+
+def test_config_256_uniform(G):
+    A, B, w = inputs.workload_inputs("f16_256")
+    y = run(G, A, B, 0)
+    assert_bound(y, oracle.gemm_f64(A, B, "f16"), w["K"], "f32", "256^3")
+
+
+@pytest.mark.parametrize("code", [0, 3])
+def test_padded_leading_dimensions(G, code):
+    fmt, out = DTYPES[code]
+    M, N, K = 300, 260, 200
+    A = law_for(fmt)((M, K), 81, fmt)
+    B = law_for(fmt)((K, N), 82, fmt)
+    r = oracle.gemm_f64(A, B, fmt)
+    y = run(G, A, B, code, lda=K + 8, ldb=N + 24, ldc=N + 40)
+    assert_bound(y, r, K, out, "padded ld")
+    # 2-byte aligned rows and base pointer: the element-masked path
+    y2 = run(G, A, B, code, lda=K + 1, ldb=N + 3, ldc=N + 1, a_off=1)
+    assert_bound(y2, r, K, out, "misaligned")
+    assert np.array_equal(y, y2)
+
+
+@pytest.mark.parametrize("code", [0, 3])
+def test_aligned_tile_multiples_with_padding(G, code):
+    """Tile-multiple shapes with 16-byte-aligned padded strides (vector path)."""
+    fmt, out = DTYPES[code]
+    M, N, K = 512, 256, 320
+    A = law_for(fmt)((M, K), 91, fmt)
+    B = law_for(fmt)((K, N), 92, fmt)
+    r = oracle.gemm_f64(A, B, fmt)
+    y = run(G, A, B, code, lda=K + 64, ldb=N + 8, ldc=N + 16)
+    assert_bound(y, r, K, out, "aligned padded")
+
+
+def test_zero_K_writes_zeros(G):
+    for code in (0, 1, 3):
+        A = np.zeros((5, 0), dtype=np.uint16)
+        B = np.zeros((0, 7), dtype=np.uint16)
+        y = run(G, A, B, code, lda=1, ldc=9)
+        assert np.all(y == 0) and y.shape == (5, 7)
+
+
+def test_empty_output_leaves_C_untouched(G):
+    A = inputs.uniform((0, 5), 1, "f16")
+    B = inputs.uniform((5, 4), 2, "f16")
+    y = run(G, A, B, 0)
+    assert y.shape == (0, 4)
+
+
+def test_instances_agree_bitwise(G):
+    """Instances that differ only in tile size, edge masking or visit order do
+    the same per-element arithmetic in the same order: identical bits."""
+    n = G.gemm_num_instances()
+    for code in (0, 3):
+        fmt, out = DTYPES[code]
+        A = law_for(fmt)((512, 512), 101, fmt)
+        B = law_for(fmt)((512, 512), 102, fmt)
+        ys = [run(G, A, B, code, instance=i) for i in range(n)]
+        for i in range(1, n):
+            assert np.array_equal(ys[0], ys[i]), G.gemm_instance_name(i)
+        assert_bound(ys[0], oracle.gemm_f64(A, B, fmt), 512, out, "instances")
+
+
+def test_edge_instances_on_ragged_shapes(G):
+    n = G.gemm_num_instances()
+    for (M, N, K) in [(129, 131, 67), (300, 260, 130), (1, 513, 65)]:
+        A = inputs.uniform((M, K), M + N, "f16")
+        B = inputs.uniform((K, N), M + K, "f16")
+        r = oracle.gemm_f64(A, B, "f16")
+        for i in range(n):
+            if not G.gemm_instance_name(i).endswith("_edge"):
+                continue
+            y = run(G, A, B, 1, instance=i)
+            assert_bound(y, r, K, "f16", "%s %s" % (G.gemm_instance_name(i), (M, N, K)))
+
+
+def test_non_edge_instance_rejects_ragged_shape(G):
+    A = inputs.uniform((129, 64), 1, "f16")
+    B = inputs.uniform((64, 128), 2, "f16")
+    run(G, A, B, 0, instance=0, expect=G.GEMM_ERR_INSTANCE)
+
+
+def test_runs_on_the_given_stream(G):
+    s = torch.cuda.Stream()
+    A = inputs.normal((384, 256), 5, "bf16")
+    B = inputs.normal((256, 512), 6, "bf16")
+    y = run(G, A, B, 3, stream=s)
+    assert_bound(y, oracle.gemm_f64(A, B, "bf16"), 256, "bf16", "stream")
+
+
+def test_torch_convenience_form(G):
+    A = torch.randn(200, 96, dtype=torch.bfloat16, device="cuda")
+    B = torch.randn(96, 150, dtype=torch.bfloat16, device="cuda")
+    C = G.gemm(A, B, torch.float32)
+    Ab = A.cpu().view(torch.int16).numpy().view(np.uint16)
+    Bb = B.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert_bound(C.cpu().double().numpy(), oracle.gemm_f64(Ab, Bb, "bf16"), 96, "f32", "torch")
+
+
+# ------------------------------------------------------------ full-size workloads
+def _sample_rows(M, bm=256, n=24, seed=0):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    last_tile = (M // bm) * bm if M % bm else M - bm
+    rows = {0, 1, M - 1, min(bm, M - 1), min(bm - 1, M - 1), last_tile, min(last_tile + 1, M - 1)}
+    rows |= set(rng.integers(0, M, n).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def _freivalds(y, A, B, fmt, out, K, trials=2):
+    """C x == A (B x) for random x in {-1, 1}^N, within sum|x| * per-element bound."""
+    Ad = oracle.decode(A, fmt)
+    Bd = oracle.decode(B, fmt)
+    rng = np.random.Generator(np.random.PCG64(99))
+    for _ in range(trials):
+        x = rng.choice(np.array([-1.0, 1.0]), size=y.shape[1])
+        lhs = y @ x
+        rhs = Ad @ (Bd @ x)
+        per = oracle.bound(K, out, np.abs(y).max(axis=1, keepdims=True) * 2.0)[:, 0]
+        assert np.all(np.abs(lhs - rhs) <= y.shape[1] * per), "Freivalds check failed"
+
+
+@pytest.mark.parametrize("name", ["f16_2048", "bf16_4096", "bf16_8192", "f16_ragged"])
+def test_full_size_workloads(G, name):
+    A, B, w = inputs.workload_inputs(name)
+    code = {("f16", "f32"): 0, ("f16", "f16"): 1, ("bf16", "f32"): 2,
+            ("bf16", "bf16"): 3}[(w["fmt"], w["out"])]
+    print("full-size workload", name, flush=True)
+    y = run(G, A, B, code)
+    rows = _sample_rows(w["M"], n=12 if w["M"] >= 8192 else 24)
+    r = oracle.gemm_rows_f64(A, B, rows, w["fmt"])
+    res = assert_bound(y[rows], r, w["K"], w["out"], name)
+    print(name, "sampled rows", rows.size, "max_abs %.3g max_rel %.3g" % (res["max_abs"], res["max_rel"]),
+          flush=True)
+    _freivalds(y, A, B, w["fmt"], w["out"], w["K"])
+
+
+def test_quarter_grid_full_size_bit_exact(G):
+    """4096^3 bf16 -> fp32 on 0.25-grid inputs: every partial sum exact."""
+    n = 4096
+    A = inputs.quarter((n, n), 201, "bf16")
+    B = inputs.quarter((n, n), 202, "bf16")
+    y = run(G, A, B, 2)
+    rows = _sample_rows(n, n=8, seed=5)
+    assert np.array_equal(y[rows], oracle.gemm_rows_f64(A, B, rows, "bf16"))
+    # exact Freivalds: all values are multiples of 1/16 below 2^24 in magnitude
+    Ad = oracle.decode(A, "bf16")
+    Bd = oracle.decode(B, "bf16")
+    x = np.random.Generator(np.random.PCG64(7)).integers(-2, 3, n).astype(np.float64)
+    assert np.array_equal(y @ x, Ad @ (Bd @ x))
