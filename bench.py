@@ -123,12 +123,17 @@ def cpu_baseline(res, budget_s: float):
     M, N, K = w["M"], w["N"], w["K"]
     threads = oracle.default_threads()
     rng = np.random.Generator(np.random.PCG64(1234))
-    probe_rows = np.array(sorted({0, M - 1} | set(rng.integers(0, M, 2).tolist())), dtype=np.int64)
-    t0 = time.perf_counter()
-    oracle.gemm_rows_f64(res["A"], res["B"], probe_rows, w["fmt"], threads)
-    t_probe = time.perf_counter() - t0
-    per_row = t_probe / probe_rows.size
-    nrows = int(max(probe_rows.size, min(M, budget_s / max(per_row, 1e-6))))
+    # Each call pays a fixed cost (decoding B) plus a cost per row: time 1 and
+    # 5 rows to separate them, then size the sample to the budget.
+    times = []
+    for n in (1, 5):
+        rows = rng.integers(0, M, n).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.gemm_rows_f64(res["A"], res["B"], rows, w["fmt"], threads)
+        times.append(time.perf_counter() - t0)
+    per_row = max((times[1] - times[0]) / 4.0, 1e-6)
+    fixed = max(times[0] - per_row, 0.0)
+    nrows = int(min(M, max(8, (budget_s - fixed) / per_row)))
     rows = np.array(sorted(set(rng.integers(0, M, nrows).tolist()) | {0, M - 1}), dtype=np.int64)
     t0 = time.perf_counter()
     r = oracle.gemm_rows_f64(res["A"], res["B"], rows, w["fmt"], threads)
