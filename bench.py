@@ -155,16 +155,39 @@ def cpu_baseline(res, budget_s: float):
                                  "max_rel": check["max_rel"], "n_bad": check["n_bad"]}}
 
 
+def copy_calibration(torch, nbytes: int, steps: int, warmup: int) -> int:
+    """Plain device-to-device copy of nbytes: reads nbytes and writes nbytes
+    per launch.  Its FETCH_SIZE / WRITE_SIZE readings calibrate the counters."""
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / max(steps, 1)
+    print(json.dumps({"copy_bytes": nbytes, "launches": steps + warmup, "ms_per_copy": round(ms, 5),
+                      "gbps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="bf16_8192")
-    ap.add_argument("--secondary", default="bf16_4096", help="'' to skip")
+    ap.add_argument("--secondary", default="bf16_4096", help="'none' to skip")
     ap.add_argument("--instance", type=int, default=None, help="force a kernel instance id")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for cpu_baseline (0 to skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="instead of the GEMM, time a plain device copy of BYTES bytes "
+                         "(the reference kernel for scaling HBM byte counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -176,12 +199,15 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 1
+    if args.copy_calibration > 0:
+        return copy_calibration(torch, args.copy_calibration, args.steps, args.warmup)
+
     from dense_half_precision_tiled_amd import gemm as G
     G.load()
 
     main_res = measure(G, torch, args.workload, args.steps, args.warmup, args.instance)
     sec = None
-    if args.secondary:
+    if args.secondary and args.secondary != "none":
         r2 = measure(G, torch, args.secondary, max(args.steps, 50), args.warmup, args.instance)
         sec = {"workload": describe(r2["w"]), "value": round(r2["tflops"], 2), "unit": "TFLOP/s",
                "ms_per_step": round(r2["ms"], 5), "frac_of_peak": round(r2["tflops"] / PEAK_TFLOPS, 4),

@@ -1,0 +1,147 @@
+// probes.hip -- small gfx950 kernels that record how an instruction
+// distributes data over the 64 lanes of a wave, so the tests can pin the
+// lane layouts the GEMM kernels rely on (the unique-value ownership probe of
+// "mma.sync and ldmatrix", section "Two probes and one matmul": fill the
+// tiles with one distinct value per cell and let the host name the
+// coordinate every lane received).
+//
+// Every probe runs one wave (64 lanes), keeps all accesses inside its own
+// buffers (addresses are masked in-kernel as well as checked on the host),
+// and synchronises before returning.  Test infrastructure only.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: LDS holds 1024 16-bit values equal to their index.
+// Lane l reads at byte address addr[l] (8-byte aligned, < 2048); out[4l+j]
+// receives element j of the lane's result.
+__global__ void probe_tr16_kernel(const int32_t* addr, int16_t* out) {
+    __shared__ short lds[1024];
+    const int l = threadIdx.x;
+    for (int i = l; i < 1024; i += 64) lds[i] = (short)i;
+    __syncthreads();
+    const int a = addr[l] & 2040;                 // in range and 8-byte aligned
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) char*)lds + a));
+    for (int j = 0; j < 4; ++j) out[4 * l + j] = v[j];
+}
+
+// global_load_lds_dwordx4: LDS (4096 bytes) is cleared, then every lane
+// loads the 16 bytes src[4*src_chunk[l] .. +3] (src holds 64 chunks) into
+// LDS through the instruction with LDS base `base` (bytes, 16-aligned,
+// <= 3072).  out receives the whole LDS image (1024 dwords).
+__global__ void probe_load_lds_kernel(const uint32_t* src, const int32_t* src_chunk, int base,
+                                      uint32_t* out) {
+    __shared__ uint32_t lds[1024];
+    const int l = threadIdx.x;
+    for (int i = l; i < 1024; i += 64) lds[i] = 0xFFFFFFFFu;
+    __syncthreads();
+    const int c = src_chunk[l] & 63;
+    const int b = base & 3056;
+    __builtin_amdgcn_global_load_lds(src + 4 * c, lds + b / 4, 16, 0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int i = l; i < 1024; i += 64) out[i] = lds[i];
+}
+
+// v_mfma_f32_32x32x16_{f16,bf16} and v_mfma_f32_16x16x32_{f16,bf16} with
+// operands taken straight from lane registers: a[8l+j], b[8l+j] are lane l's
+// operand elements (bit patterns); d receives the accumulator registers,
+// d[16l+i] (32x32) or d[4l+i] (16x16).
+template <bool BF16, bool BIG>
+__global__ void probe_mfma_kernel(const uint16_t* a, const uint16_t* b, float* d) {
+    const int l = threadIdx.x;
+    u32x4 av, bv;
+    for (int j = 0; j < 4; ++j) {
+        av[j] = (uint32_t)a[8 * l + 2 * j] | ((uint32_t)a[8 * l + 2 * j + 1] << 16);
+        bv[j] = (uint32_t)b[8 * l + 2 * j] | ((uint32_t)b[8 * l + 2 * j + 1] << 16);
+    }
+    if constexpr (BIG) {
+        f32x16 acc = {};
+        if constexpr (BF16)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                          __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+        else
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, av),
+                                                         __builtin_bit_cast(f16x8, bv), acc, 0, 0, 0);
+        for (int i = 0; i < 16; ++i) d[16 * l + i] = acc[i];
+    } else {
+        f32x4 acc = {};
+        if constexpr (BF16)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                          __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+        else
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av),
+                                                         __builtin_bit_cast(f16x8, bv), acc, 0, 0, 0);
+        for (int i = 0; i < 4; ++i) d[4 * l + i] = acc[i];
+    }
+}
+
+// Back-to-back independent MFMAs on register-resident operands, timed with
+// the shader clock (s_memtime) by lane 0 of every wave: cycles[w] for
+// `iters` x 8 MFMAs of one wave.  Launch with any number of 256-lane blocks.
+template <bool BF16>
+__global__ __launch_bounds__(256) void probe_mfma_rate_kernel(int iters, uint64_t* cycles, float* sink) {
+    u32x4 av = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};
+    u32x4 bv = av;
+    f32x16 acc[8];
+    for (int i = 0; i < 8; ++i) acc[i] = (f32x16){};
+    __syncthreads();
+    const uint64_t t0 = __builtin_readcyclecounter();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if constexpr (BF16)
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                                 __builtin_bit_cast(bf16x8, bv), acc[i], 0, 0, 0);
+            else
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, av),
+                                                                __builtin_bit_cast(f16x8, bv), acc[i], 0, 0, 0);
+        }
+    }
+    float s = 0.0f;
+    for (int i = 0; i < 8; ++i) s += acc[i][0];
+    const uint64_t t1 = __builtin_readcyclecounter();
+    const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    if ((threadIdx.x & 63) == 0) cycles[wave] = t1 - t0;
+    if (s == 12345.0f) sink[0] = s;
+}
+
+extern "C" {
+
+int probe_tr16(const int32_t* addr, int16_t* out) {
+    hipLaunchKernelGGL(probe_tr16_kernel, dim3(1), dim3(64), 0, 0, addr, out);
+    return (int)hipDeviceSynchronize();
+}
+
+int probe_load_lds(const uint32_t* src, const int32_t* src_chunk, int base, uint32_t* out) {
+    hipLaunchKernelGGL(probe_load_lds_kernel, dim3(1), dim3(64), 0, 0, src, src_chunk, base, out);
+    return (int)hipDeviceSynchronize();
+}
+
+// kind: 0 f16 32x32x16, 1 bf16 32x32x16, 2 f16 16x16x32, 3 bf16 16x16x32
+int probe_mfma(int kind, const uint16_t* a, const uint16_t* b, float* d) {
+    switch (kind) {
+    case 0: hipLaunchKernelGGL((probe_mfma_kernel<false, true>), dim3(1), dim3(64), 0, 0, a, b, d); break;
+    case 1: hipLaunchKernelGGL((probe_mfma_kernel<true, true>), dim3(1), dim3(64), 0, 0, a, b, d); break;
+    case 2: hipLaunchKernelGGL((probe_mfma_kernel<false, false>), dim3(1), dim3(64), 0, 0, a, b, d); break;
+    default: hipLaunchKernelGGL((probe_mfma_kernel<true, false>), dim3(1), dim3(64), 0, 0, a, b, d); break;
+    }
+    return (int)hipDeviceSynchronize();
+}
+
+int probe_mfma_rate(int bf16, int blocks, int iters, uint64_t* cycles, float* sink) {
+    if (bf16)
+        hipLaunchKernelGGL(probe_mfma_rate_kernel<true>, dim3(blocks), dim3(256), 0, 0, iters, cycles, sink);
+    else
+        hipLaunchKernelGGL(probe_mfma_rate_kernel<false>, dim3(blocks), dim3(256), 0, 0, iters, cycles, sink);
+    return (int)hipDeviceSynchronize();
+}
+
+}  // extern "C"

@@ -1,0 +1,127 @@
+"""Lane-layout pins for the gfx950 instructions the GEMM kernels rely on, and
+the MFMA issue-rate measurement (the register-resident rate probe of the Ada
+tensor-core GEMM write-up, "If you benchmark Tensor Cores on a GeForce part":
+FLOP per clock per compute unit from an in-kernel clock, independent of the
+clock frequency).
+
+Every probe runs one wave on buffers it owns; addresses are checked here and
+masked in the kernel."""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "tests", "probes", "libdhpt_probes.so")
+
+
+@pytest.fixture(scope="module")
+def P():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    if not os.path.exists(LIB):
+        import __graft_entry__
+        __graft_entry__.build_probes()
+    lib = ctypes.CDLL(LIB)
+    vp = ctypes.c_void_p
+    lib.probe_tr16.argtypes = [vp, vp]
+    lib.probe_load_lds.argtypes = [vp, vp, ctypes.c_int, vp]
+    lib.probe_mfma.argtypes = [ctypes.c_int, vp, vp, vp]
+    lib.probe_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
+    return lib
+
+
+@pytest.mark.parametrize("pattern", ["linear", "perm5", "rows32"])
+def test_ds_read_tr16_b64_layout(P, pattern):
+    """Within each group of 16 lanes, lane i receives element i % 4 of the
+    8-byte rows addressed by lanes 4j + i/4 of its group, j = 0..3: one read
+    hands every lane a column of a 4 x 16 block of 16-bit values."""
+    addr = {"linear": [8 * l for l in range(64)],
+            "perm5": [8 * ((5 * l) % 64) for l in range(64)],
+            "rows32": [32 * (l % 16) + 8 * (l // 16) + 512 for l in range(64)]}[pattern]
+    assert all(a % 8 == 0 and 0 <= a <= 2040 for a in addr)
+    a = torch.tensor(addr, dtype=torch.int32, device="cuda")
+    o = torch.zeros(256, dtype=torch.int16, device="cuda")
+    assert P.probe_tr16(a.data_ptr(), o.data_ptr()) == 0
+    got = o.cpu().numpy().reshape(64, 4).astype(np.int64)
+    for l in range(64):
+        g, i = l // 16, l % 16
+        for j in range(4):
+            src_lane = 16 * g + 4 * j + i // 4
+            assert got[l, j] == addr[src_lane] // 2 + i % 4, (l, j)
+
+
+def test_global_load_lds_dwordx4_layout(P):
+    """Lane l's 16 bytes land at LDS base + 16*l; nothing else is written."""
+    src = torch.arange(256, dtype=torch.int32, device="cuda")
+    chunks = [(7 * l) % 64 for l in range(64)]
+    ch = torch.tensor(chunks, dtype=torch.int32, device="cuda")
+    out = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    base = 256
+    assert P.probe_load_lds(src.data_ptr(), ch.data_ptr(), base, out.data_ptr()) == 0
+    lds = out.cpu().numpy().astype(np.int64)
+    for l in range(64):
+        assert lds[base // 4 + 4 * l: base // 4 + 4 * l + 4].tolist() == list(range(4 * chunks[l], 4 * chunks[l] + 4))
+    rest = np.concatenate([lds[:base // 4], lds[base // 4 + 256:]])
+    assert np.all(rest == -1)
+
+
+@pytest.mark.parametrize("kind", [0, 1, 2, 3])
+def test_mfma_operand_and_accumulator_maps(P, kind):
+    """32x32x16: A row l%32, B column l%32, 8 values of k = 8(l/32)+j; D
+    element i of lane l is row 8(i/4) + 4(l/32) + i%4, column l%32.
+    16x16x32: A row l%16, B column l%16, k = 8(l/16)+j; D element i is row
+    4(l/16) + i, column l%16."""
+    rng = np.random.Generator(np.random.PCG64(10 + kind))
+    a = rng.integers(-3, 4, 512).astype(np.float32)
+    b = rng.integers(-3, 4, 512).astype(np.float32)
+    dt = torch.bfloat16 if kind in (1, 3) else torch.float16
+    ta = torch.from_numpy(a).to(dt).cuda().view(torch.int16)
+    tb = torch.from_numpy(b).to(dt).cuda().view(torch.int16)
+    td = torch.zeros(1024, dtype=torch.float32, device="cuda")
+    assert P.probe_mfma(kind, ta.data_ptr(), tb.data_ptr(), td.data_ptr()) == 0
+    d = td.cpu().numpy().astype(np.float64)
+    a = a.reshape(64, 8)
+    b = b.reshape(64, 8)
+    if kind in (0, 1):
+        A = np.zeros((32, 16)); B = np.zeros((16, 32)); got = np.zeros((32, 32))
+        for l in range(64):
+            A[l % 32, 8 * (l // 32):8 * (l // 32) + 8] = a[l]
+            B[8 * (l // 32):8 * (l // 32) + 8, l % 32] = b[l]
+            for i in range(16):
+                got[8 * (i // 4) + 4 * (l // 32) + i % 4, l % 32] = d[16 * l + i]
+    else:
+        A = np.zeros((16, 32)); B = np.zeros((32, 16)); got = np.zeros((16, 16))
+        for l in range(64):
+            A[l % 16, 8 * (l // 16):8 * (l // 16) + 8] = a[l]
+            B[8 * (l // 16):8 * (l // 16) + 8, l % 16] = b[l]
+            for i in range(4):
+                got[4 * (l // 16) + i, l % 16] = d[4 * l + i]
+    assert np.array_equal(got, A @ B)
+
+
+def test_mfma_issue_rate(P):
+    """Eight independent v_mfma_f32_32x32x16 per wave, one wave per SIMD on
+    every CU: FLOP per shader clock per CU should be the 4096 of the CDNA4
+    design (32768 FLOP every 32 cycles on each of 4 SIMDs)."""
+    blocks, iters = 256, 4000
+    cyc = torch.zeros(blocks * 4, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    for bf16 in (0, 1):
+        P.probe_mfma_rate(bf16, blocks, 100, cyc.data_ptr(), sink.data_ptr())     # warm
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        assert P.probe_mfma_rate(bf16, blocks, iters, cyc.data_ptr(), sink.data_ptr()) == 0
+        e1.record()
+        torch.cuda.synchronize()
+        cycles = float(cyc.cpu().numpy().mean())
+        flop_per_clk_cu = 4 * iters * 8 * 32768.0 / cycles
+        ms = e0.elapsed_time(e1)
+        clock_ghz = cycles / (ms * 1e-3) / 1e9
+        print("mfma %s: %.0f FLOP/clk/CU, shader clock under load ~%.2f GHz, %.0f TFLOP/s" % (
+            "bf16" if bf16 else "f16", flop_per_clk_cu, clock_ghz, blocks * 4 * iters * 8 * 32768 / ms / 1e9))
+        assert 3500 < flop_per_clk_cu <= 4096 * 1.01
