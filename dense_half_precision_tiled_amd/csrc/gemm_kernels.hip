@@ -37,6 +37,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gemm_internal.h"
 
 namespace dhpt {
@@ -252,12 +254,223 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(void* C, int64_t ldc, in
     }
 }
 
+// ----------------------------------------------------------------------------
+// Direct-to-LDS kernel (aligned shapes: M % 256 == N % 256 == K % 64 == 0,
+// 16-byte aligned operands).
+//
+// Global -> LDS with global_load_lds_dwordx4: each lane hands 16 bytes of
+// global memory to LDS address base + 16 * lane, so a wave fills 1 KiB of LDS
+// per instruction without touching VGPRs; the copy is asynchronous and
+// completes against vmcnt, the gfx950 counterpart of the cp.async stages of
+// the Ada write-up.  Two stages: the loads of slice kt+1 are issued right
+// after the barrier that opens slice kt and land while slice kt is multiplied.
+//
+// LDS layouts (16-byte chunk granularity):
+//   A stage: 256 rows x 128 B.  Logical chunk c of row r sits at physical
+//     chunk c ^ (r & 7) ^ ((r >> 3) & 1).  The fragment reads (one row per
+//     lane, same logical chunk) then cover every 16-byte bank group once per 8
+//     rows and once per 16 rows, whether LDS serves 128 or 256 bytes per
+//     clock.
+//   B stage: 64 rows (k) x 512 B (256 n), row-major as in global memory.
+//     Logical chunk c of row k sits at physical chunk c ^ g(k & 3) with
+//     g = {0, 4, 10, 14}: the four rows read together by a transposing read
+//     land in four different 64-byte bank blocks.
+// The swizzle is applied on the global side: the lane that writes physical
+// chunk p of row r fetches logical chunk p ^ swizzle(r).
+//
+// LDS -> VGPR: A fragments with ds_read_b128 (8 consecutive k of one row);
+// B fragments with two ds_read_b64_tr_b16 each.  Within a 16-lane group that
+// instruction gives lane i the 4 values of column i of the 4 x 16 block whose
+// rows are addressed by lanes 4j + i/4, so lane l ends up holding
+// B[k0 .. k0+7][n0 + l % 32] -- the MFMA B operand -- straight from the
+// row-major tile (the ldmatrix .trans idea of "mma.sync and ldmatrix", in
+// its gfx950 form).
+// ----------------------------------------------------------------------------
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ __forceinline__ int swz_a(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz_b(int k) { return 4 * (k & 1) + 10 * ((k >> 1) & 1); }
+
+// One global_load_lds_dwordx4: this lane's 16 bytes at `src` go to LDS byte
+// address lds_base + 16 * lane.  Issued through inline assembly so that the
+// compiler does not track it: it would otherwise make every later LDS read
+// wait for the copy (vmcnt(0)), serialising the next slice's copy with the
+// current slice's math.  Completion is awaited explicitly (vmcnt) before the
+// barrier that publishes the stage.  M0 has no other user in these kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(lds_base) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Keep the scheduler from moving anything across this point: the source order
+// below is the issue order.
+#define DHPT_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+template <int IN, int OUT>
+__global__ __launch_bounds__(256, 1) void gemm_lds_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
+    void* __restrict__ C, int64_t ldc, int M, int N, int K, int tilesM, int tilesN, int group_m) {
+    constexpr int BM = 256, BN = 256, BK = 64;
+    constexpr int A_BYTES = BM * BK * 2, STAGE_BYTES = 2 * A_BYTES;   // 32 KiB A + 32 KiB B
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
+    const uint32_t smem_base = (uint32_t)(size_t)(lds_char*)smem;
+
+    const int l = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = w >> 1, wn = w & 1;
+
+    int tm, tn;
+    tile_coords(blockIdx.x, tilesM, tilesN, group_m, &tm, &tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    // Global sources of this lane's 16 copies per slice (8 for A, 8 for B).
+    // A: copy i of wave w fills rows 64w + 8i + l/8, physical chunk l%8.
+    // B: copy i of wave w fills rows 16w + 2i + l/32, physical chunk l%32.
+    const uint16_t* a_src[8];
+    const uint16_t* b_src[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = 64 * w + 8 * i + (l >> 3);
+        const int c = (l & 7) ^ swz_a(r);
+        a_src[i] = A + (int64_t)(m0 + r) * lda + 8 * c;
+        const int kr = 16 * w + 2 * i + (l >> 5);
+        const int cb = (l & 31) ^ swz_b(kr);
+        b_src[i] = B + (int64_t)kr * ldb + n0 + 8 * cb;
+    }
+    const int64_t b_step = (int64_t)BK * ldb;
+    const uint32_t dma_a = smem_base + (64 * w) * 128;              // + stage + 1024 i
+    const uint32_t dma_b = smem_base + A_BYTES + (16 * w) * 512;    // + stage + 1024 i
+
+    // Fragment addresses (bytes within a stage).
+    // A: row wm*128 + 32i + (l & 31), logical chunk 2s + (l >> 5).
+    const int a_sw = (l & 7) ^ ((l >> 3) & 1);             // swz_a of every row this lane reads
+    const int a_off0 = (wm * 128 + (l & 31)) * 128;
+    // B: k = 16s + 8(g>>1) + 4r + (i'>>2), n = wn*128 + 32j + 16(g&1) + 4(i'&3)
+    const int g = l >> 4, ip = l & 15;
+    const int b_sw = swz_b(ip >> 2);                        // (k & 3) == (i' >> 2) for every read
+    int b_off[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int n = wn * 128 + 32 * j + 16 * (g & 1) + 4 * (ip & 3);
+        b_off[j] = A_BYTES + (8 * (g >> 1) + (ip >> 2)) * 512 + (((n >> 3) ^ b_sw) * 16) + (n & 7) * 2;
+    }
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    u32x4 fa[2][4], fb[2][4];      // two fragment buffers: k-steps alternate between them
+
+    auto read_frags = [&](int stage, int s, int buf) {
+        const char* st = smem + stage * STAGE_BYTES;
+        const int achunk = (2 * s + (l >> 5)) ^ a_sw;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            fa[buf][i] = *reinterpret_cast<const u32x4*>(st + a_off0 + i * 32 * 128 + achunk * 16);
+        const lds_char* sb = (const lds_char*)st;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int off = b_off[j] + 16 * s * 512;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(sb + off));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(sb + off + 4 * 512));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            fb[buf][j] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+        }
+    };
+    auto issue_copy = [&](int stage, int i) {          // copy i of 16 for the next slice
+        if (i < 8) {
+            lds_dma16(a_src[i], dma_a + stage * STAGE_BYTES + 1024 * i);
+            a_src[i] += BK;
+        } else {
+            lds_dma16(b_src[i - 8], dma_b + stage * STAGE_BYTES + 1024 * (i - 8));
+            b_src[i - 8] += b_step;
+        }
+    };
+    auto mfma4 = [&](int buf, int i) {                 // one A fragment against the 4 B fragments
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16<IN>(fa[buf][i], fb[buf][j], acc[i][j]);
+    };
+
+    // One slice: barrier, then k-step 3 of the previous slice (its fragments
+    // are already in buffer 1) with the copies of the next slice tucked between
+    // its MFMAs, then k-steps 0..2 of this slice, each behind the fragment
+    // reads of the following k-step.  Running the previous slice's last k-step
+    // after the barrier hides the latency of this slice's first reads.
+    auto slice = [&](int kt, auto has_prev, auto has_next) {
+        const int stage = kt & 1;
+        wait_dma_all();                 // this wave's copies of slice kt have landed
+        __syncthreads();                // ... and everyone's; slice kt-1 is fully read
+        DHPT_FENCE();
+        read_frags(stage, 0, 0);
+        DHPT_FENCE();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (decltype(has_prev)::value) mfma4(1, i);
+            if constexpr (decltype(has_next)::value) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) issue_copy(stage ^ 1, 4 * i + q);
+            }
+            DHPT_FENCE();
+        }
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+            read_frags(stage, s + 1, (s + 1) & 1);
+            DHPT_FENCE();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mfma4(s & 1, i);
+            DHPT_FENCE();
+        }
+    };
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
+
+    const int nk = K / BK;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) issue_copy(0, i);
+    if (nk > 1) {
+        slice(0, no{}, yes{});
+        for (int kt = 1; kt < nk - 1; ++kt) slice(kt, yes{}, yes{});
+        slice(nk - 1, yes{}, no{});
+    } else {
+        slice(0, no{}, no{});
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mfma4(1, i);          // k-step 3 of the last slice
+
+    const int gl = l >> 5;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int col = n0 + wn * 128 + 32 * j + (l & 31);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = m0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * gl + (e & 3);
+                store_out<OUT>(C, (int64_t)row * ldc + col, acc[i][j][e]);
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- instances
 const InstanceInfo kInstances[] = {
-    {"mfma_256x256x64", 256, 256, 64, false, 8},
+    {"mfma_256x256x64_lds", 256, 256, 64, false, 8},
     {"mfma_128x128x64", 128, 128, 64, false, 8},
     {"mfma_256x256x64_edge", 256, 256, 64, true, 8},
     {"mfma_128x128x64_edge", 128, 128, 64, true, 8},
+    {"mfma_256x256x64", 256, 256, 64, false, 8},
 };
 const int kNumInstances = sizeof(kInstances) / sizeof(kInstances[0]);
 
@@ -286,10 +499,28 @@ static hipError_t launch_tile(const Problem& p, int group_m, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int IN, int OUT>
+static void launch_lds_typed(const Problem& p, int group_m, hipStream_t s) {
+    const int tilesM = p.M / 256, tilesN = p.N / 256;
+    hipLaunchKernelGGL((gemm_lds_kernel<IN, OUT>), dim3((unsigned)(tilesM * tilesN)), dim3(256), 0, s,
+                       p.A, p.lda, p.B, p.ldb, p.C, p.ldc, p.M, p.N, p.K, tilesM, tilesN, group_m);
+}
+
+static hipError_t launch_lds(const Problem& p, int group_m, hipStream_t s) {
+    switch (p.dtype) {
+    case 0: launch_lds_typed<IN_F16, OUT_F32>(p, group_m, s); break;
+    case 1: launch_lds_typed<IN_F16, OUT_F16>(p, group_m, s); break;
+    case 2: launch_lds_typed<IN_BF16, OUT_F32>(p, group_m, s); break;
+    default: launch_lds_typed<IN_BF16, OUT_BF16>(p, group_m, s); break;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_instance(int id, const Problem& p, hipStream_t s) {
     const int gm = kInstances[id].group_m;
     switch (id) {
-    case 0: return launch_tile<256, 256, false>(p, gm, s);
+    case 0: return launch_lds(p, gm, s);
+    case 4: return launch_tile<256, 256, false>(p, gm, s);
     case 1: return launch_tile<128, 128, false>(p, gm, s);
     case 2: return launch_tile<256, 256, true>(p, gm, s);
     default: return launch_tile<128, 128, true>(p, gm, s);
