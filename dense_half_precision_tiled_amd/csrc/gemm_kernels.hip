@@ -269,12 +269,13 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(void* C, int64_t ldc, in
 //   A stage: 256 rows x 128 B.  Logical chunk c of row r sits at physical
 //     chunk c ^ (r & 7) ^ ((r >> 3) & 1).  The fragment reads (one row per
 //     lane, same logical chunk) then cover every 16-byte bank group once per 8
-//     rows and once per 16 rows, whether LDS serves 128 or 256 bytes per
-//     clock.
+//     rows; measured, they run at ~8.6 clocks per 1 KiB instruction per CU
+//     (the LDS's 128 bytes per clock), against 24 without the swizzle.
 //   B stage: 64 rows (k) x 512 B (256 n), row-major as in global memory.
-//     Logical chunk c of row k sits at physical chunk c ^ g(k & 3) with
-//     g = {0, 4, 10, 14}: the four rows read together by a transposing read
-//     land in four different 64-byte bank blocks.
+//     Logical chunk c of row k sits at physical chunk c ^ 2(k & 3).  Measured
+//     on gfx950 (LDS-rate probe, 4 waves per CU), the transposing reads then
+//     run at their floor of ~8.3 clocks per instruction per CU; unswizzled
+//     rows take 9.0 and a 64-byte-block rotation 10.1.
 // The swizzle is applied on the global side: the lane that writes physical
 // chunk p of row r fetches logical chunk p ^ swizzle(r).
 //
@@ -290,7 +291,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
 __device__ __forceinline__ int swz_a(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-__device__ __forceinline__ int swz_b(int k) { return 4 * (k & 1) + 10 * ((k >> 1) & 1); }
+__device__ __forceinline__ int swz_b(int k) { return 2 * (k & 3); }
 
 // One global_load_lds_dwordx4: this lane's 16 bytes at `src` go to LDS byte
 // address lds_base + 16 * lane.  Issued through inline assembly so that the
@@ -312,13 +313,33 @@ __device__ __forceinline__ void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0
 // below is the issue order.
 #define DHPT_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-template <int IN, int OUT>
+template <int N>
+__device__ __forceinline__ void wait_dma_le() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
+
+// 256x256 output tile, BK-deep slices (64 or 32), STAGES LDS stages: the
+// copies of slice kt + STAGES - 1 are issued while slice kt is multiplied.
+// FD = fragment prefetch distance in k-steps (1 or 2): the LDS reads of
+// k-step s + FD are issued while the MFMAs of k-step s run.
+template <int IN, int OUT, int BK, int STAGES, int FD = 1>
 __global__ __launch_bounds__(256, 1) void gemm_lds_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
     void* __restrict__ C, int64_t ldc, int M, int N, int K, int tilesM, int tilesN, int group_m) {
-    constexpr int BM = 256, BN = 256, BK = 64;
-    constexpr int A_BYTES = BM * BK * 2, STAGE_BYTES = 2 * A_BYTES;   // 32 KiB A + 32 KiB B
-    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
+    static_assert(BK == 64 || BK == 32, "slice depth");
+    constexpr int BM = 256, BN = 256;
+    constexpr int ROWB = BK * 2;                          // bytes per A row in LDS
+    constexpr int A_BYTES = BM * ROWB, B_BYTES = BK * BN * 2;
+    constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    constexpr int KSTEPS = BK / 16;
+    constexpr int CPW = BK / 8;                           // copies per wave per slice, for A and for B
+    constexpr int COPIES = 2 * CPW;
+    constexpr int A_ROWS_PER_COPY = 1024 / ROWB;          // 8 (BK 64) or 16 (BK 32)
+    constexpr int A_CHUNKS = ROWB / 16;                   // 8 or 4
+    constexpr int B_ROWS_PER_WAVE = BK / 4;
+    constexpr int D = STAGES - 1;                         // prefetch distance in slices
+    constexpr int NB = (FD == 1) ? 2 : KSTEPS;            // fragment buffers
+    static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS");
+    static_assert(FD == 1 || (FD == 2 && KSTEPS == 4), "fragment distance");
+    __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
     const uint32_t smem_base = (uint32_t)(size_t)(lds_char*)smem;
 
     const int l = threadIdx.x & 63;
@@ -329,29 +350,31 @@ __global__ __launch_bounds__(256, 1) void gemm_lds_kernel(
     tile_coords(blockIdx.x, tilesM, tilesN, group_m, &tm, &tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
-    // Global sources of this lane's 16 copies per slice (8 for A, 8 for B).
-    // A: copy i of wave w fills rows 64w + 8i + l/8, physical chunk l%8.
-    // B: copy i of wave w fills rows 16w + 2i + l/32, physical chunk l%32.
-    const uint16_t* a_src[8];
-    const uint16_t* b_src[8];
+    // A swizzle (physical 16-byte chunk = logical chunk ^ swa(row)):
+    // 128-byte rows: (r & 7) ^ ((r >> 3) & 1); 64-byte rows: (r >> 1) & 3.
+    auto swa = [](int r) { return BK == 64 ? ((r & 7) ^ ((r >> 3) & 1)) : ((r >> 1) & 3); };
+
+    // Global sources of this lane's copies.  A copy i of wave w fills rows
+    // 64w + A_ROWS_PER_COPY*i + l / A_CHUNKS, physical chunk l % A_CHUNKS;
+    // B copy i fills rows B_ROWS_PER_WAVE*w + 2i + l/32, physical chunk l%32.
+    const uint16_t* a_src[CPW];
+    const uint16_t* b_src[CPW];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = 64 * w + 8 * i + (l >> 3);
-        const int c = (l & 7) ^ swz_a(r);
+    for (int i = 0; i < CPW; ++i) {
+        const int r = 64 * w + A_ROWS_PER_COPY * i + l / A_CHUNKS;
+        const int c = (l % A_CHUNKS) ^ swa(r);
         a_src[i] = A + (int64_t)(m0 + r) * lda + 8 * c;
-        const int kr = 16 * w + 2 * i + (l >> 5);
+        const int kr = B_ROWS_PER_WAVE * w + 2 * i + (l >> 5);
         const int cb = (l & 31) ^ swz_b(kr);
         b_src[i] = B + (int64_t)kr * ldb + n0 + 8 * cb;
     }
     const int64_t b_step = (int64_t)BK * ldb;
-    const uint32_t dma_a = smem_base + (64 * w) * 128;              // + stage + 1024 i
-    const uint32_t dma_b = smem_base + A_BYTES + (16 * w) * 512;    // + stage + 1024 i
+    const uint32_t dma_a = smem_base + (64 * w) * ROWB;
+    const uint32_t dma_b = smem_base + A_BYTES + (B_ROWS_PER_WAVE * w) * 512;
 
     // Fragment addresses (bytes within a stage).
-    // A: row wm*128 + 32i + (l & 31), logical chunk 2s + (l >> 5).
-    const int a_sw = (l & 7) ^ ((l >> 3) & 1);             // swz_a of every row this lane reads
-    const int a_off0 = (wm * 128 + (l & 31)) * 128;
-    // B: k = 16s + 8(g>>1) + 4r + (i'>>2), n = wn*128 + 32j + 16(g&1) + 4(i'&3)
+    const int a_off0 = (wm * 128 + (l & 31)) * ROWB;
+    const int a_sw = swa(l & 31);                           // swa of every row this lane reads
     const int g = l >> 4, ip = l & 15;
     const int b_sw = swz_b(ip >> 2);                        // (k & 3) == (i' >> 2) for every read
     int b_off[4];
@@ -369,76 +392,276 @@ __global__ __launch_bounds__(256, 1) void gemm_lds_kernel(
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    u32x4 fa[2][4], fb[2][4];      // two fragment buffers: k-steps alternate between them
+    u32x4 fa[NB][4];               // fragment buffers: k-step s uses buffer s % NB
+    s16x4 fbh[NB][4][2];           // the two transposing reads behind each B fragment
 
-    auto read_frags = [&](int stage, int s, int buf) {
+    // The 12 LDS reads of one k-step, in the order the next k-step's MFMAs
+    // consume them: A0, B0 (two halves), B1, B2, B3, A1, A2, A3.
+    auto read_piece = [&](int stage, int s, int buf, int q) {
         const char* st = smem + stage * STAGE_BYTES;
-        const int achunk = (2 * s + (l >> 5)) ^ a_sw;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            fa[buf][i] = *reinterpret_cast<const u32x4*>(st + a_off0 + i * 32 * 128 + achunk * 16);
-        const lds_char* sb = (const lds_char*)st;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int off = b_off[j] + 16 * s * 512;
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(sb + off));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(sb + off + 4 * 512));
-            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-            fb[buf][j] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+        if (q == 0 || q >= 9) {
+            const int i = (q == 0) ? 0 : q - 8;
+            const int achunk = (2 * s + (l >> 5)) ^ a_sw;
+            fa[buf][i] = *reinterpret_cast<const u32x4*>(st + a_off0 + i * 32 * ROWB + achunk * 16);
+        } else {
+            const int j = (q - 1) >> 1, h = (q - 1) & 1;
+            const int off = b_off[j] + 16 * s * 512 + h * 4 * 512;
+            fbh[buf][j][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)((const lds_char*)st + off));
         }
     };
-    auto issue_copy = [&](int stage, int i) {          // copy i of 16 for the next slice
-        if (i < 8) {
+    auto issue_copy = [&](int stage, int i) {          // copy i of COPIES for one slice
+        if (i < CPW) {
             lds_dma16(a_src[i], dma_a + stage * STAGE_BYTES + 1024 * i);
             a_src[i] += BK;
         } else {
-            lds_dma16(b_src[i - 8], dma_b + stage * STAGE_BYTES + 1024 * (i - 8));
-            b_src[i - 8] += b_step;
+            lds_dma16(b_src[i - CPW], dma_b + stage * STAGE_BYTES + 1024 * (i - CPW));
+            b_src[i - CPW] += b_step;
         }
     };
-    auto mfma4 = [&](int buf, int i) {                 // one A fragment against the 4 B fragments
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16<IN>(fa[buf][i], fb[buf][j], acc[i][j]);
+    auto mfma1 = [&](int buf, int q) {                 // MFMA q of a k-step: A frag q/4, B frag q%4
+        const int i = q >> 2, j = q & 3;
+        const u32x2 l2 = __builtin_bit_cast(u32x2, fbh[buf][j][0]);
+        const u32x2 h2 = __builtin_bit_cast(u32x2, fbh[buf][j][1]);
+        acc[i][j] = mfma_32x32x16<IN>(fa[buf][i], u32x4{l2[0], l2[1], h2[0], h2[1]}, acc[i][j]);
     };
 
-    // One slice: barrier, then k-step 3 of the previous slice (its fragments
-    // are already in buffer 1) with the copies of the next slice tucked between
-    // its MFMAs, then k-steps 0..2 of this slice, each behind the fragment
-    // reads of the following k-step.  Running the previous slice's last k-step
-    // after the barrier hides the latency of this slice's first reads.
-    auto slice = [&](int kt, auto has_prev, auto has_next) {
-        const int stage = kt & 1;
-        wait_dma_all();                 // this wave's copies of slice kt have landed
-        __syncthreads();                // ... and everyone's; slice kt-1 is fully read
-        DHPT_FENCE();
-        read_frags(stage, 0, 0);
-        DHPT_FENCE();
+    // 16 issue slots: MFMA q of the k-step held in `buf` (if any), then at most
+    // one LDS read of the next k-step and at most one copy of a later slice,
+    // so the single wave on each SIMD never stalls behind a burst of LDS or
+    // copy instructions while its MFMA pipe runs dry.
+    auto units = [&](auto do_mfma, int buf, int rstage, int rs, int rbuf, auto do_copy, int cstage) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if constexpr (decltype(has_prev)::value) mfma4(1, i);
-            if constexpr (decltype(has_next)::value) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) issue_copy(stage ^ 1, 4 * i + q);
+        for (int q = 0; q < 16; ++q) {
+            if constexpr (decltype(do_mfma)::value) mfma1(buf, q);
+            if (q < 12) read_piece(rstage, rs, rbuf, q);
+            if constexpr (decltype(do_copy)::value) {
+                if (q % (16 / COPIES) == 0) issue_copy(cstage, q / (16 / COPIES));
             }
-            DHPT_FENCE();
-        }
-#pragma unroll
-        for (int s = 0; s < 3; ++s) {
-            read_frags(stage, s + 1, (s + 1) & 1);
-            DHPT_FENCE();
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mfma4(s & 1, i);
             DHPT_FENCE();
         }
     };
     using yes = std::integral_constant<bool, true>;
     using no = std::integral_constant<bool, false>;
 
-    const int nk = K / BK;
+    // The copies of slice kt landed for every wave (this wave's: vmcnt; the
+    // others': the barrier), and slice kt-1 has been read by everyone.
+    // `later` = slices after kt whose copies are already in flight.
+    auto open_slice = [&](int later) {
+        if (later >= 3) wait_dma_le<3 * COPIES>();
+        else if (later == 2) wait_dma_le<2 * COPIES>();
+        else if (later == 1) wait_dma_le<COPIES>();
+        else wait_dma_le<0>();
+        __syncthreads();
+        DHPT_FENCE();
+    };
+
+    // One slice: the previous slice's last FD k-steps (fragments already in
+    // registers) interleaved with this slice's first FD k-steps of reads and
+    // the copies of slice kt + D; then k-steps 0 .. KSTEPS-FD-1, each
+    // interleaved with the reads of k-step s + FD.  Running the previous
+    // slice's last k-steps after the barrier hides the latency of this
+    // slice's first reads.
+    auto slice = [&](int kt, auto has_prev, auto has_next) {
+        const int stage = kt % STAGES;
+        const int cstage = (kt + D) % STAGES;
+        if constexpr (FD == 1) {
+            units(has_prev, 1, stage, 0, 0, has_next, cstage);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) issue_copy(0, i);
+            for (int s = 0; s < KSTEPS - 1; ++s) units(yes{}, s & 1, stage, s + 1, (s + 1) & 1, no{}, 0);
+        } else {
+            // 32 slots: MFMAs of the previous slice's k-steps 2 and 3, reads of
+            // this slice's k-steps 0 and 1, one copy every other slot.
+#pragma unroll
+            for (int q = 0; q < 32; ++q) {
+                if constexpr (decltype(has_prev)::value) mfma1(2 + (q >> 4), q & 15);
+                if ((q & 15) < 12) read_piece(stage, q >> 4, q >> 4, q & 15);
+                if constexpr (decltype(has_next)::value) {
+                    if ((q & 1) == 0) issue_copy(cstage, q >> 1);
+                }
+                DHPT_FENCE();
+            }
+            units(yes{}, 0, stage, 2, 2, no{}, 0);
+            units(yes{}, 1, stage, 3, 3, no{}, 0);
+        }
+    };
+
+    const int nk = K / BK;
+    for (int t = 0; t < D && t < nk; ++t)
+#pragma unroll
+        for (int i = 0; i < COPIES; ++i) issue_copy(t, i);
+    // slice 0
+    open_slice(nk - 1 < D - 1 ? nk - 1 : D - 1);
+    if (D < nk) slice(0, no{}, yes{}); else slice(0, no{}, no{});
+    // steady state: copies of slice kt + D are issued
+    for (int kt = 1; kt < nk - D; ++kt) {
+        open_slice(D - 1);
+        slice(kt, yes{}, yes{});
+    }
+    // last D slices (or fewer): no more copies
+    for (int kt = (nk - D > 1 ? nk - D : 1); kt < nk; ++kt) {
+        open_slice(nk - 1 - kt);
+        slice(kt, yes{}, no{});
+    }
+    if constexpr (FD == 2) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) mfma1(2, q);     // last two k-steps of the last slice
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) mfma1(FD == 2 ? 3 : 1, q);
+
+    const int gl = l >> 5;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int col = n0 + wn * 128 + 32 * j + (l & 31);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = m0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * gl + (e & 3);
+                store_out<OUT>(C, (int64_t)row * ldc + col, acc[i][j][e]);
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Variant with B transposed on its way into LDS.  A is copied global -> LDS
+// as above; B goes global -> VGPR (one 8 x 8 block of 16-bit values per lane,
+// eight 16-byte loads of consecutive rows), is transposed with byte
+// permutes, and is written k-contiguous ([n][k], the same swizzled 128-byte
+// rows as A).  Both MFMA operands are then read with ds_read_b128, whose LDS
+// cost per byte is half that of the transposing read.
+// ----------------------------------------------------------------------------
+template <int IN, int OUT>
+__global__ __launch_bounds__(256, 1) void gemm_ldsbt_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
+    void* __restrict__ C, int64_t ldc, int M, int N, int K, int tilesM, int tilesN, int group_m) {
+    constexpr int BM = 256, BN = 256, BK = 64, ROWB = 128;
+    constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
+    constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
+    const uint32_t smem_base = (uint32_t)(size_t)(lds_char*)smem;
+
+    const int l = threadIdx.x & 63;
+    const int t = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = w >> 1, wn = w & 1;
+
+    int tm, tn;
+    tile_coords(blockIdx.x, tilesM, tilesN, group_m, &tm, &tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    // A copies: copy i of wave w fills rows 64w + 8i + l/8, physical chunk l%8.
+    const uint16_t* a_src[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = 64 * w + 8 * i + (l >> 3);
+        a_src[i] = A + (int64_t)(m0 + r) * lda + 8 * ((l & 7) ^ swz_a(r));
+    }
+    const uint32_t dma_a = smem_base + (64 * w) * ROWB;
+    // B block of this lane: rows 8*kb .. 8*kb+7 of the slice, columns 8*nc .. +7.
+    const int kb = t & 7, nc = t >> 3;
+    const uint16_t* b_src = B + (int64_t)(8 * kb) * ldb + n0 + 8 * nc;
+    const int64_t b_step = (int64_t)BK * ldb;
+    int b_dst[8];                                   // byte offsets of the 8 transposed chunks
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int n = 8 * nc + j;
+        b_dst[j] = A_BYTES + n * ROWB + 16 * (kb ^ swz_a(n));
+    }
+
+    const int a_off0 = (wm * 128 + (l & 31)) * ROWB;
+    const int b_off0 = A_BYTES + (wn * 128 + (l & 31)) * ROWB;
+    const int f_sw = swz_a(l & 31);                 // swizzle of every fragment row this lane reads
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    u32x4 fa[2][4], fb[2][4];
+    u32x4 rb[8];
+
+    // The 8 LDS reads of one k-step in consumption order: A0, B0..B3, A1..A3.
+    auto read_piece = [&](int stage, int s, int buf, int q) {
+        const char* st = smem + stage * STAGE_BYTES;
+        const int chunk16 = ((2 * s + (l >> 5)) ^ f_sw) * 16;
+        if (q == 0 || q >= 5) {
+            const int i = (q == 0) ? 0 : q - 4;
+            fa[buf][i] = *reinterpret_cast<const u32x4*>(st + a_off0 + i * 32 * ROWB + chunk16);
+        } else {
+            const int j = q - 1;
+            fb[buf][j] = *reinterpret_cast<const u32x4*>(st + b_off0 + j * 32 * ROWB + chunk16);
+        }
+    };
+    auto issue_a_copy = [&](int stage, int i) {
+        lds_dma16(a_src[i], dma_a + stage * STAGE_BYTES + 1024 * i);
+        a_src[i] += BK;
+    };
+    auto load_b_row = [&](int r) {
+        rb[r] = *reinterpret_cast<const u32x4*>(b_src + (int64_t)r * ldb);
+        if (r == 7) b_src += b_step;
+    };
+    auto write_b_col = [&](int stage, int j) {       // column j of the 8x8 block, k contiguous
+        u32x4 v;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) v[d] = pack_col(rb[2 * d], rb[2 * d + 1], j);
+        *reinterpret_cast<u32x4*>(smem + stage * STAGE_BYTES + b_dst[j]) = v;
+    };
+    auto mfma1 = [&](int buf, int q) {
+        const int i = q >> 2, j = q & 3;
+        acc[i][j] = mfma_32x32x16<IN>(fa[buf][i], fb[buf][j], acc[i][j]);
+    };
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
+
+    // Slots of one k-step: MFMA q, then (slots 0..7) one read of the next
+    // k-step; the prefetch of the next slice rides in the first k-step (A
+    // copy and B row load per slot), its transposed B writes in the last.
+    auto units = [&](auto do_mfma, int buf, int rstage, int rs, int rbuf, auto do_fetch, auto do_bwrite,
+                     int nstage) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            if constexpr (decltype(do_mfma)::value) mfma1(buf, q);
+            if (q < 8) read_piece(rstage, rs, rbuf, q);
+            if constexpr (decltype(do_fetch)::value) {
+                if (q < 8) issue_a_copy(nstage, q);
+                else load_b_row(q - 8);
+            }
+            if constexpr (decltype(do_bwrite)::value) {
+                if (q >= 8) write_b_col(nstage, q - 8);
+            }
+            DHPT_FENCE();
+        }
+    };
+
+    // Slice kt: barrier (A copies and B writes of slice kt visible, slice
+    // kt-1 fully read); the previous slice's last k-step with this slice's
+    // first reads and the fetch of slice kt+1; k-steps 0..2 with the reads of
+    // the following k-step; slice kt+1's B block is written during k-step 2.
+    auto slice = [&](int kt, auto has_prev, auto has_next) {
+        const int stage = kt & 1, nstage = stage ^ 1;
+        wait_dma_all();
+        __syncthreads();
+        DHPT_FENCE();
+        units(has_prev, 1, stage, 0, 0, has_next, no{}, nstage);
+        units(yes{}, 0, stage, 1, 1, no{}, no{}, nstage);
+        units(yes{}, 1, stage, 2, 0, no{}, no{}, nstage);
+        units(yes{}, 0, stage, 3, 1, no{}, has_next, nstage);
+    };
+
+    const int nk = K / BK;
+    // prologue: slice 0 in stage 0
+#pragma unroll
+    for (int i = 0; i < 8; ++i) issue_a_copy(0, i);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) load_b_row(r);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) write_b_col(0, j);
     if (nk > 1) {
         slice(0, no{}, yes{});
         for (int kt = 1; kt < nk - 1; ++kt) slice(kt, yes{}, yes{});
@@ -447,7 +670,7 @@ __global__ __launch_bounds__(256, 1) void gemm_lds_kernel(
         slice(0, no{}, no{});
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) mfma4(1, i);          // k-step 3 of the last slice
+    for (int q = 0; q < 16; ++q) mfma1(1, q);
 
     const int gl = l >> 5;
 #pragma unroll
@@ -466,11 +689,15 @@ __global__ __launch_bounds__(256, 1) void gemm_lds_kernel(
 
 // ---------------------------------------------------------------- instances
 const InstanceInfo kInstances[] = {
-    {"mfma_256x256x64_lds", 256, 256, 64, false, 8},
+    {"mfma_256x256x64_lds2", 256, 256, 64, false, 8},
     {"mfma_128x128x64", 128, 128, 64, false, 8},
     {"mfma_256x256x64_edge", 256, 256, 64, true, 8},
     {"mfma_128x128x64_edge", 128, 128, 64, true, 8},
     {"mfma_256x256x64", 256, 256, 64, false, 8},
+    {"mfma_256x256x32_lds4", 256, 256, 32, false, 8},
+    {"mfma_256x256x32_lds5", 256, 256, 32, false, 8},
+    {"mfma_256x256x64_ldsbt", 256, 256, 64, false, 8},
+    {"mfma_256x256x64_lds2_fd2", 256, 256, 64, false, 8},
 };
 const int kNumInstances = sizeof(kInstances) / sizeof(kInstances[0]);
 
@@ -499,19 +726,38 @@ static hipError_t launch_tile(const Problem& p, int group_m, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int IN, int OUT>
+template <int IN, int OUT, int BK, int STAGES, int FD>
 static void launch_lds_typed(const Problem& p, int group_m, hipStream_t s) {
     const int tilesM = p.M / 256, tilesN = p.N / 256;
-    hipLaunchKernelGGL((gemm_lds_kernel<IN, OUT>), dim3((unsigned)(tilesM * tilesN)), dim3(256), 0, s,
+    hipLaunchKernelGGL((gemm_lds_kernel<IN, OUT, BK, STAGES, FD>), dim3((unsigned)(tilesM * tilesN)),
+                       dim3(256), 0, s, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, p.M, p.N, p.K, tilesM, tilesN,
+                       group_m);
+}
+
+template <int IN, int OUT>
+static void launch_ldsbt_typed(const Problem& p, int group_m, hipStream_t s) {
+    const int tilesM = p.M / 256, tilesN = p.N / 256;
+    hipLaunchKernelGGL((gemm_ldsbt_kernel<IN, OUT>), dim3((unsigned)(tilesM * tilesN)), dim3(256), 0, s,
                        p.A, p.lda, p.B, p.ldb, p.C, p.ldc, p.M, p.N, p.K, tilesM, tilesN, group_m);
 }
 
+static hipError_t launch_ldsbt(const Problem& p, int group_m, hipStream_t s) {
+    switch (p.dtype) {
+    case 0: launch_ldsbt_typed<IN_F16, OUT_F32>(p, group_m, s); break;
+    case 1: launch_ldsbt_typed<IN_F16, OUT_F16>(p, group_m, s); break;
+    case 2: launch_ldsbt_typed<IN_BF16, OUT_F32>(p, group_m, s); break;
+    default: launch_ldsbt_typed<IN_BF16, OUT_BF16>(p, group_m, s); break;
+    }
+    return hipGetLastError();
+}
+
+template <int BK, int STAGES, int FD = 1>
 static hipError_t launch_lds(const Problem& p, int group_m, hipStream_t s) {
     switch (p.dtype) {
-    case 0: launch_lds_typed<IN_F16, OUT_F32>(p, group_m, s); break;
-    case 1: launch_lds_typed<IN_F16, OUT_F16>(p, group_m, s); break;
-    case 2: launch_lds_typed<IN_BF16, OUT_F32>(p, group_m, s); break;
-    default: launch_lds_typed<IN_BF16, OUT_BF16>(p, group_m, s); break;
+    case 0: launch_lds_typed<IN_F16, OUT_F32, BK, STAGES, FD>(p, group_m, s); break;
+    case 1: launch_lds_typed<IN_F16, OUT_F16, BK, STAGES, FD>(p, group_m, s); break;
+    case 2: launch_lds_typed<IN_BF16, OUT_F32, BK, STAGES, FD>(p, group_m, s); break;
+    default: launch_lds_typed<IN_BF16, OUT_BF16, BK, STAGES, FD>(p, group_m, s); break;
     }
     return hipGetLastError();
 }
@@ -519,7 +765,11 @@ static hipError_t launch_lds(const Problem& p, int group_m, hipStream_t s) {
 hipError_t launch_instance(int id, const Problem& p, hipStream_t s) {
     const int gm = kInstances[id].group_m;
     switch (id) {
-    case 0: return launch_lds(p, gm, s);
+    case 0: return launch_lds<64, 2>(p, gm, s);
+    case 5: return launch_lds<32, 4>(p, gm, s);
+    case 6: return launch_lds<32, 5>(p, gm, s);
+    case 7: return launch_ldsbt(p, gm, s);
+    case 8: return launch_lds<64, 2, 2>(p, gm, s);
     case 4: return launch_tile<256, 256, false>(p, gm, s);
     case 1: return launch_tile<128, 128, false>(p, gm, s);
     case 2: return launch_tile<256, 256, true>(p, gm, s);

@@ -17,6 +17,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ds_read_b64_tr_b16: LDS holds 1024 16-bit values equal to their index.
 // Lane l reads at byte address addr[l] (8-byte aligned, < 2048); out[4l+j]
@@ -113,7 +114,102 @@ __global__ __launch_bounds__(256) void probe_mfma_rate_kernel(int iters, uint64_
     if (s == 12345.0f) sink[0] = s;
 }
 
+// LDS throughput: every wave of 4 per block issues `iters` x 8 LDS
+// instructions of one kind and lane 0 records the shader cycles.  Lane l of
+// wave w uses byte address addr[64 w + l] (masked to the 64 KiB buffer and
+// to the access size), moved by (it & 3) << 14 each iteration so nothing can
+// be hoisted, and by u * 8192 for the 8 unrolled instructions.
+//   kind 0: ds_read_b128   1: ds_read_b64   2: ds_read_b64_tr_b16
+//   kind 3: ds_write_b128
+template <int KIND>
+__global__ __launch_bounds__(256) void probe_lds_rate_kernel(int iters, const int32_t* addr_table,
+                                                             uint64_t* cycles, uint32_t* sink) {
+    __shared__ __attribute__((aligned(1024))) char lds[65536];
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    for (int i = threadIdx.x; i < 65536 / 4; i += 256) reinterpret_cast<uint32_t*>(lds)[i] = i;
+    const int align = (KIND == 0 || KIND == 3) ? 16 : 8;
+    const int addr = addr_table[threadIdx.x] & 65535 & ~(align - 1);
+    uint32_t x = 0;
+    u32x4 wv = {(uint32_t)l, 1u, 2u, 3u};
+    __syncthreads();
+    const uint64_t t0 = __builtin_readcyclecounter();
+    for (int it = 0; it < iters; ++it) {
+        const int base = addr + ((it & 3) << 14);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int a = (base + u * 8192) & 65535;
+            if constexpr (KIND == 0) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(lds + a);
+                x ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+            } else if constexpr (KIND == 1) {
+                const uint64_t v = *reinterpret_cast<const uint64_t*>(lds + a);
+                x ^= (uint32_t)v ^ (uint32_t)(v >> 32);
+            } else if constexpr (KIND == 3) {
+                wv[1] ^= (uint32_t)it;
+                *reinterpret_cast<u32x4*>(lds + a) = wv;
+            } else {
+                const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) char*)lds + a));
+                const u32x2 v2 = __builtin_bit_cast(u32x2, v);
+                x ^= v2[0] ^ v2[1];
+            }
+        }
+    }
+    const uint64_t t1 = __builtin_readcyclecounter();
+    if (l == 0) cycles[blockIdx.x * 4 + w] = t1 - t0;
+    if (KIND == 3) x = reinterpret_cast<const uint32_t*>(lds)[threadIdx.x];
+    if (x == 0x12345678u) sink[0] = x;
+}
+
+// Global -> LDS copy throughput: every wave of 4 per block issues `iters` x 8
+// global_load_lds_dwordx4 (1 KiB each) from a source of `src_bytes` bytes
+// (a power of two, at least 8 KiB; small enough to stay in L2) into its own
+// 8 KiB of LDS, waits for all of them, and lane 0 records the shader cycles.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__global__ __launch_bounds__(256) void probe_dma_rate_kernel(int iters, const char* src, int src_bytes,
+                                                             uint64_t* cycles, uint32_t* sink) {
+    __shared__ __attribute__((aligned(1024))) char lds[32768];
+    const int l = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t base = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)lds + w * 8192;
+    const int mask = src_bytes - 1;
+    __syncthreads();
+    const uint64_t t0 = __builtin_readcyclecounter();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const char* p = src + (((it * 8 + u) * 1024 + w * 65536 + blockIdx.x * 4096 + l * 16) & mask);
+            asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                         :: "v"(p), "s"(base + u * 1024) : "memory", "m0");
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const uint64_t t1 = __builtin_readcyclecounter();
+    if (l == 0) cycles[blockIdx.x * 4 + w] = t1 - t0;
+    __syncthreads();
+    if (reinterpret_cast<const uint32_t*>(lds)[threadIdx.x] == 0x12345678u) sink[0] = 1;
+}
+#pragma clang diagnostic pop
+
 extern "C" {
+
+int probe_dma_rate(int blocks, int iters, const char* src, int src_bytes, uint64_t* cycles, uint32_t* sink) {
+    if (src_bytes < 8192 || (src_bytes & (src_bytes - 1)) != 0) return -1;
+    hipLaunchKernelGGL(probe_dma_rate_kernel, dim3(blocks), dim3(256), 0, 0, iters, src, src_bytes, cycles, sink);
+    return (int)hipDeviceSynchronize();
+}
+
+int probe_lds_rate(int kind, int blocks, int iters, const int32_t* addr_table, uint64_t* cycles,
+                   uint32_t* sink) {
+    switch (kind) {
+    case 0: hipLaunchKernelGGL(probe_lds_rate_kernel<0>, dim3(blocks), dim3(256), 0, 0, iters, addr_table, cycles, sink); break;
+    case 1: hipLaunchKernelGGL(probe_lds_rate_kernel<1>, dim3(blocks), dim3(256), 0, 0, iters, addr_table, cycles, sink); break;
+    case 2: hipLaunchKernelGGL(probe_lds_rate_kernel<2>, dim3(blocks), dim3(256), 0, 0, iters, addr_table, cycles, sink); break;
+    default: hipLaunchKernelGGL(probe_lds_rate_kernel<3>, dim3(blocks), dim3(256), 0, 0, iters, addr_table, cycles, sink); break;
+    }
+    return (int)hipDeviceSynchronize();
+}
 
 int probe_tr16(const int32_t* addr, int16_t* out) {
     hipLaunchKernelGGL(probe_tr16_kernel, dim3(1), dim3(64), 0, 0, addr, out);

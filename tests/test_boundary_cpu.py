@@ -104,8 +104,8 @@ def _pick(M, N, K, dtype=3, lda=None, ldb=None, ldc=None, pa=PA, pb=PB):
 
 
 def test_instance_choice(lib):
-    assert _pick(8192, 8192, 8192) == "mfma_256x256x64_lds"
-    assert _pick(4096, 4096, 4096) == "mfma_256x256x64_lds"
+    assert _pick(8192, 8192, 8192) == "mfma_256x256x64_lds2_fd2"
+    assert _pick(4096, 4096, 4096) == "mfma_256x256x64_lds2_fd2"
     assert _pick(2048, 2048, 2048, 0) == "mfma_128x128x64"
     assert _pick(256, 256, 256, 0) == "mfma_128x128x64"
     # ragged shape with a 2-byte-aligned lda: edge kernel

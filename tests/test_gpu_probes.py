@@ -32,6 +32,11 @@ def P():
     lib.probe_load_lds.argtypes = [vp, vp, ctypes.c_int, vp]
     lib.probe_mfma.argtypes = [ctypes.c_int, vp, vp, vp]
     lib.probe_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
+    lib.probe_lds_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp]
+    lib.probe_dma_rate.argtypes = [ctypes.c_int, ctypes.c_int, vp, ctypes.c_int, vp, vp]
+    for f in (lib.probe_tr16, lib.probe_load_lds, lib.probe_mfma, lib.probe_mfma_rate,
+              lib.probe_lds_rate, lib.probe_dma_rate):
+        f.restype = ctypes.c_int
     return lib
 
 
@@ -125,3 +130,81 @@ def test_mfma_issue_rate(P):
         print("mfma %s: %.0f FLOP/clk/CU, shader clock under load ~%.2f GHz, %.0f TFLOP/s" % (
             "bf16" if bf16 else "f16", flop_per_clk_cu, clock_ghz, blocks * 4 * iters * 8 * 32768 / ms / 1e9))
         assert 3500 < flop_per_clk_cu <= 4096 * 1.01
+
+
+def _a_fragment_addresses(row_bytes):
+    """The GEMM's A-fragment reads: wave (wm, wn) = (w >> 1, w & 1), lane l reads
+    row wm*128 + (l & 31), logical chunk l >> 5, XOR-swizzled as in the kernel."""
+    out = []
+    for w in range(4):
+        for l in range(64):
+            r = (w >> 1) * 128 + (l & 31)
+            c = l >> 5
+            out.append(r * row_bytes + 16 * (c ^ (r & 7) ^ ((r >> 3) & 1)))
+    return out
+
+
+def _b_fragment_addresses(swizzle):
+    """The GEMM's B-fragment transposing reads (512-byte rows of k)."""
+    out = []
+    for w in range(4):
+        for l in range(64):
+            g, ip = l >> 4, l & 15
+            k = 8 * (g >> 1) + (ip >> 2)
+            n = (w & 1) * 128 + 16 * (g & 1) + 4 * (ip & 3)
+            out.append(k * 512 + (((n >> 3) ^ swizzle(k)) * 16) + (n & 7) * 2)
+    return out
+
+
+def test_lds_read_rate(P):
+    """LDS cost of the fragment-read instructions in shader clocks per
+    instruction per CU (4 waves per CU).  Recorded, gated only for sanity;
+    the GEMM's swizzles are the ones that measured fastest here."""
+    blocks, iters = 256, 1500
+    cyc = torch.zeros(blocks * 4, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    cases = [
+        ("ds_read_b128 A fragments, swizzled", 0, 1024, _a_fragment_addresses(128)),
+        ("ds_read_b128 A fragments, unswizzled", 0, 1024,
+         [((w >> 1) * 128 + (l & 31)) * 128 + 16 * (l >> 5) for w in range(4) for l in range(64)]),
+        ("ds_read_b128 consecutive", 0, 1024, [w * 1024 + 16 * l for w in range(4) for l in range(64)]),
+        ("ds_read_b64 consecutive", 1, 512, [w * 512 + 8 * l for w in range(4) for l in range(64)]),
+        ("ds_read_b64_tr_b16 B fragments, c^2(k&3)", 2, 512, _b_fragment_addresses(lambda k: 2 * (k & 3))),
+        ("ds_read_b64_tr_b16 B fragments, unswizzled", 2, 512, _b_fragment_addresses(lambda k: 0)),
+        ("ds_write_b128 consecutive", 3, 1024, [w * 1024 + 16 * l for w in range(4) for l in range(64)]),
+    ]
+    res = {}
+    for name, kind, nbytes, addr in cases:
+        assert len(addr) == 256 and all(0 <= a < 65536 for a in addr)
+        t = torch.tensor(addr, dtype=torch.int32, device="cuda")
+        assert P.probe_lds_rate(kind, blocks, 20, t.data_ptr(), cyc.data_ptr(), sink.data_ptr()) == 0
+        assert P.probe_lds_rate(kind, blocks, iters, t.data_ptr(), cyc.data_ptr(), sink.data_ptr()) == 0
+        clk = float(cyc.cpu().numpy().mean()) / (4 * iters * 8)
+        res[name] = clk
+        print("%-44s %5.2f clk/instr/CU  %6.1f bytes/clk/CU" % (name, clk, nbytes / clk))
+        assert 0.5 < clk < 200
+    assert res["ds_read_b128 A fragments, swizzled"] < res["ds_read_b128 A fragments, unswizzled"]
+
+
+def test_dma_rate(P):
+    """global_load_lds_dwordx4 throughput into LDS (bytes per shader clock
+    per CU) from an L2-resident source of 4 MiB and from an HBM-sized one.
+    Recorded; gated only for sanity."""
+    blocks, iters = 256, 400
+    cyc = torch.zeros(blocks * 4, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for nbytes in (1 << 22, 1 << 30):
+        src = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        assert P.probe_dma_rate(blocks, 20, src.data_ptr(), nbytes, cyc.data_ptr(), sink.data_ptr()) == 0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        assert P.probe_dma_rate(blocks, iters, src.data_ptr(), nbytes, cyc.data_ptr(), sink.data_ptr()) == 0
+        e1.record()
+        torch.cuda.synchronize()
+        cycles = float(cyc.cpu().numpy().mean())
+        rate = 4 * iters * 8 * 1024 / cycles
+        gbs = blocks * 4 * iters * 8 * 1024 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        print("global_load_lds from %4d MiB: %.1f bytes/clk/CU, %.2f clk per 1 KiB copy per CU, %.0f GB/s total"
+              % (nbytes >> 20, rate, cycles / (4 * iters * 8), gbs))
+        assert 4 < rate < 1024
+        del src
