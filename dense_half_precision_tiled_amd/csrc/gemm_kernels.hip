@@ -411,6 +411,7 @@ __global__ __launch_bounds__(256, 1) void gemm_lds_kernel(
         }
     };
     auto issue_copy = [&](int stage, int i) {          // copy i of COPIES for one slice
+        if (i < 0 || i >= COPIES) return;              // never taken: every caller passes 0 .. COPIES-1
         if (i < CPW) {
             lds_dma16(a_src[i], dma_a + stage * STAGE_BYTES + 1024 * i);
             a_src[i] += BK;
@@ -427,16 +428,28 @@ __global__ __launch_bounds__(256, 1) void gemm_lds_kernel(
     };
 
     // 16 issue slots: MFMA q of the k-step held in `buf` (if any), then at most
-    // one LDS read of the next k-step and at most one copy of a later slice,
-    // so the single wave on each SIMD never stalls behind a burst of LDS or
-    // copy instructions while its MFMA pipe runs dry.
-    auto units = [&](auto do_mfma, int buf, int rstage, int rs, int rbuf, auto do_copy, int cstage) {
+    // one LDS read of the next k-step and at most one copy of a later slice.
+    // Copies are spread evenly over the slice's MFMA slots (slot_base numbers
+    // this group's first slot within the slice): the per-CU copy path takes
+    // about 58 bytes per clock, so a burst of copies would back up and stall
+    // the single wave on each SIMD, MFMA pipe and all.
+    // With two stages (D == 1) the copies must land within one slice, so they
+    // go out early (one per slot, or every other slot with FD == 2).
+    constexpr int SPACING = (D >= 2) ? (KSTEPS * 16) / COPIES : ((FD == 2) ? 2 : 16 / COPIES);
+    // Every slice issues copies 0 .. COPIES-1 exactly once: slot n of the
+    // slice (0 .. 16*KSTEPS-1) issues copy n / SPACING when n % SPACING == 0
+    // and n / SPACING < COPIES.
+    static_assert(SPACING >= 1 && (COPIES - 1) * SPACING < 16 * KSTEPS, "copy schedule must fit the slice");
+    auto copy_at = [](int slot) { return (slot % SPACING == 0 && slot / SPACING < COPIES) ? slot / SPACING : -1; };
+    auto units = [&](auto do_mfma, int buf, int rstage, int rs, int rbuf, auto do_copy, int cstage,
+                     int slot_base) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
             if constexpr (decltype(do_mfma)::value) mfma1(buf, q);
             if (q < 12) read_piece(rstage, rs, rbuf, q);
             if constexpr (decltype(do_copy)::value) {
-                if (q % (16 / COPIES) == 0) issue_copy(cstage, q / (16 / COPIES));
+                const int c = copy_at(slot_base + q);
+                if (c >= 0) issue_copy(cstage, c);
             }
             DHPT_FENCE();
         }
@@ -466,23 +479,25 @@ __global__ __launch_bounds__(256, 1) void gemm_lds_kernel(
         const int stage = kt % STAGES;
         const int cstage = (kt + D) % STAGES;
         if constexpr (FD == 1) {
-            units(has_prev, 1, stage, 0, 0, has_next, cstage);
+            units(has_prev, 1, stage, 0, 0, has_next, cstage, 0);
 #pragma unroll
-            for (int s = 0; s < KSTEPS - 1; ++s) units(yes{}, s & 1, stage, s + 1, (s + 1) & 1, no{}, 0);
+            for (int s = 0; s < KSTEPS - 1; ++s)
+                units(yes{}, s & 1, stage, s + 1, (s + 1) & 1, has_next, cstage, 16 * (s + 1));
         } else {
-            // 32 slots: MFMAs of the previous slice's k-steps 2 and 3, reads of
-            // this slice's k-steps 0 and 1, one copy every other slot.
+            // 32 slots: MFMAs of the previous slice's k-steps 2 and 3 with the
+            // reads of this slice's k-steps 0 and 1.
 #pragma unroll
             for (int q = 0; q < 32; ++q) {
                 if constexpr (decltype(has_prev)::value) mfma1(2 + (q >> 4), q & 15);
                 if ((q & 15) < 12) read_piece(stage, q >> 4, q >> 4, q & 15);
                 if constexpr (decltype(has_next)::value) {
-                    if ((q & 1) == 0) issue_copy(cstage, q >> 1);
+                    const int c = copy_at(q);
+                    if (c >= 0) issue_copy(cstage, c);
                 }
                 DHPT_FENCE();
             }
-            units(yes{}, 0, stage, 2, 2, no{}, 0);
-            units(yes{}, 1, stage, 3, 3, no{}, 0);
+            units(yes{}, 0, stage, 2, 2, has_next, cstage, 32);
+            units(yes{}, 1, stage, 3, 3, has_next, cstage, 48);
         }
     };
 
@@ -516,6 +531,182 @@ __global__ __launch_bounds__(256, 1) void gemm_lds_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int col = n0 + wn * 128 + 32 * j + (l & 31);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = m0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * gl + (e & 3);
+                store_out<OUT>(C, (int64_t)row * ldc + col, acc[i][j][e]);
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Eight-wave kernel: 512 lanes, two waves per SIMD, 2 x 4 grid of 128 x 64
+// wave tiles over the 256 x 256 output tile (128 fp32 accumulators per lane).
+// Same LDS stages, swizzles and copies as gemm_lds_kernel.  With a second
+// wave on every SIMD, one wave's MFMAs run while the other waits on LDS or
+// on the barrier, and twice as many fragment reads are in flight: measured on
+// gfx950, LDS throughput grows with the reads in flight (ds_read_b128 about
+// 100 / 187 / 263 bytes per clock per CU with 4 / 8 / 16 waves; the
+// transposing read 62 / 120 / 155).
+// ----------------------------------------------------------------------------
+template <int IN, int OUT, int FD>
+__global__ __launch_bounds__(512, 1) void gemm_lds8_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
+    void* __restrict__ C, int64_t ldc, int M, int N, int K, int tilesM, int tilesN, int group_m) {
+    constexpr int BM = 256, BN = 256, BK = 64, ROWB = 128;
+    constexpr int A_BYTES = BM * ROWB, B_BYTES = BK * BN * 2;
+    constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    constexpr int KSTEPS = 4;
+    constexpr int CPW = 4;                        // copies per wave per slice, for A and for B
+    constexpr int COPIES = 2 * CPW;
+    constexpr int NB = FD + 1;                    // fragment buffers (k-step s uses buffer s % NB)
+    static_assert(FD == 1 || FD == 2, "fragment distance");
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
+    const uint32_t smem_base = (uint32_t)(size_t)(lds_char*)smem;
+
+    const int l = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = w >> 2, wn = w & 3;
+
+    int tm, tn;
+    tile_coords(blockIdx.x, tilesM, tilesN, group_m, &tm, &tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    // Copies: A copy i of wave w fills rows 32w + 8i + l/8 (physical chunk l%8);
+    // B copy i fills rows 8w + 2i + l/32 (physical chunk l%32).
+    const uint16_t* a_src[CPW];
+    const uint16_t* b_src[CPW];
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+        const int r = 32 * w + 8 * i + (l >> 3);
+        a_src[i] = A + (int64_t)(m0 + r) * lda + 8 * ((l & 7) ^ swz_a(r));
+        const int kr = 8 * w + 2 * i + (l >> 5);
+        b_src[i] = B + (int64_t)kr * ldb + n0 + 8 * ((l & 31) ^ swz_b(kr));
+    }
+    const int64_t b_step = (int64_t)BK * ldb;
+    const uint32_t dma_a = smem_base + (32 * w) * ROWB;
+    const uint32_t dma_b = smem_base + A_BYTES + (8 * w) * 512;
+
+    const int a_off0 = (wm * 128 + (l & 31)) * ROWB;
+    const int a_sw = swz_a(l & 31);
+    const int g = l >> 4, ip = l & 15;
+    const int b_sw = swz_b(ip >> 2);
+    int b_off[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int n = wn * 64 + 32 * j + 16 * (g & 1) + 4 * (ip & 3);
+        b_off[j] = A_BYTES + (8 * (g >> 1) + (ip >> 2)) * 512 + (((n >> 3) ^ b_sw) * 16) + (n & 7) * 2;
+    }
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    u32x4 fa[NB][4];
+    s16x4 fbh[NB][2][2];
+
+    // The 8 LDS reads of one k-step in consumption order: A0, B0 lo/hi,
+    // B1 lo/hi, A1, A2, A3.
+    auto read_piece = [&](int stage, int s, int buf, int q) {
+        const char* st = smem + stage * STAGE_BYTES;
+        if (q == 0 || q >= 5) {
+            const int i = (q == 0) ? 0 : q - 4;
+            const int achunk = (2 * s + (l >> 5)) ^ a_sw;
+            fa[buf][i] = *reinterpret_cast<const u32x4*>(st + a_off0 + i * 32 * ROWB + achunk * 16);
+        } else {
+            const int j = (q - 1) >> 1, h = (q - 1) & 1;
+            const int off = b_off[j] + 16 * s * 512 + h * 4 * 512;
+            fbh[buf][j][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)((const lds_char*)st + off));
+        }
+    };
+    auto issue_copy = [&](int stage, int i) {
+        if (i < 0 || i >= COPIES) return;              // never taken: every caller passes 0 .. COPIES-1
+        if (i < CPW) {
+            lds_dma16(a_src[i], dma_a + stage * STAGE_BYTES + 1024 * i);
+            a_src[i] += BK;
+        } else {
+            lds_dma16(b_src[i - CPW], dma_b + stage * STAGE_BYTES + 1024 * (i - CPW));
+            b_src[i - CPW] += b_step;
+        }
+    };
+    auto mfma1 = [&](int buf, int q) {                 // MFMA q of a k-step: A frag q/2, B frag q%2
+        const int i = q >> 1, j = q & 1;
+        const u32x2 l2 = __builtin_bit_cast(u32x2, fbh[buf][j][0]);
+        const u32x2 h2 = __builtin_bit_cast(u32x2, fbh[buf][j][1]);
+        acc[i][j] = mfma_32x32x16<IN>(fa[buf][i], u32x4{l2[0], l2[1], h2[0], h2[1]}, acc[i][j]);
+    };
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
+
+    // 8 issue slots per k-step: MFMA q, one read of a later k-step, and (in
+    // the first k-step of the slice) one copy of the next slice.
+    auto units = [&](auto do_mfma, int buf, int rstage, int rs, int rbuf, auto do_copy, int cstage) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            if constexpr (decltype(do_mfma)::value) mfma1(buf, q);
+            read_piece(rstage, rs, rbuf, q);
+            if constexpr (decltype(do_copy)::value) issue_copy(cstage, q);
+            DHPT_FENCE();
+        }
+    };
+
+    // Slice kt (k-steps 0..3 of stage kt&1): the previous slice's last FD
+    // k-steps run right after the barrier, interleaved with this slice's
+    // first FD k-steps of reads and the next slice's copies.
+    auto slice = [&](int kt, auto has_prev, auto has_next) {
+        const int stage = kt & 1;
+        wait_dma_all();
+        __syncthreads();
+        DHPT_FENCE();
+        if constexpr (FD == 1) {
+            units(has_prev, 3 % NB, stage, 0, 0, has_next, stage ^ 1);
+#pragma unroll
+            for (int s = 0; s < KSTEPS - 1; ++s) units(yes{}, s % NB, stage, s + 1, (s + 1) % NB, no{}, 0);
+        } else {
+            // buffers: k-step s of slice kt uses (4kt + s) % 3; with four steps
+            // per slice that is (kt + s) % 3.
+            const int o = kt % 3;
+            units(has_prev, (o + 2) % 3, stage, 0, o, has_next, stage ^ 1);          // prev step 2
+            units(has_prev, (o + 0) % 3, stage, 1, (o + 1) % 3, no{}, 0);           // prev step 3
+#pragma unroll
+            for (int s = 0; s < KSTEPS - 2; ++s)
+                units(yes{}, (o + s) % 3, stage, s + 2, (o + s + 2) % 3, no{}, 0);
+        }
+    };
+
+    const int nk = K / BK;
+#pragma unroll
+    for (int i = 0; i < COPIES; ++i) issue_copy(0, i);
+    if (nk > 1) {
+        slice(0, no{}, yes{});
+        for (int kt = 1; kt < nk - 1; ++kt) slice(kt, yes{}, yes{});
+        slice(nk - 1, yes{}, no{});
+    } else {
+        slice(0, no{}, no{});
+    }
+    if constexpr (FD == 1) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) mfma1(3 % NB, q);
+    } else {
+        const int o = (nk - 1) % 3;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) mfma1((o + 2) % 3, q);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) mfma1(o, q);
+    }
+
+    const int gl = l >> 5;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = n0 + wn * 64 + 32 * j + (l & 31);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int row = m0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * gl + (e & 3);
@@ -698,6 +889,7 @@ const InstanceInfo kInstances[] = {
     {"mfma_256x256x32_lds5", 256, 256, 32, false, 8},
     {"mfma_256x256x64_ldsbt", 256, 256, 64, false, 8},
     {"mfma_256x256x64_lds2_fd2", 256, 256, 64, false, 8},
+    {"mfma_256x256x64_w8", 256, 256, 64, false, 8},
 };
 const int kNumInstances = sizeof(kInstances) / sizeof(kInstances[0]);
 
@@ -741,6 +933,24 @@ static void launch_ldsbt_typed(const Problem& p, int group_m, hipStream_t s) {
                        p.A, p.lda, p.B, p.ldb, p.C, p.ldc, p.M, p.N, p.K, tilesM, tilesN, group_m);
 }
 
+template <int IN, int OUT, int FD>
+static void launch_lds8_typed(const Problem& p, int group_m, hipStream_t s) {
+    const int tilesM = p.M / 256, tilesN = p.N / 256;
+    hipLaunchKernelGGL((gemm_lds8_kernel<IN, OUT, FD>), dim3((unsigned)(tilesM * tilesN)), dim3(512), 0, s,
+                       p.A, p.lda, p.B, p.ldb, p.C, p.ldc, p.M, p.N, p.K, tilesM, tilesN, group_m);
+}
+
+template <int FD>
+static hipError_t launch_lds8(const Problem& p, int group_m, hipStream_t s) {
+    switch (p.dtype) {
+    case 0: launch_lds8_typed<IN_F16, OUT_F32, FD>(p, group_m, s); break;
+    case 1: launch_lds8_typed<IN_F16, OUT_F16, FD>(p, group_m, s); break;
+    case 2: launch_lds8_typed<IN_BF16, OUT_F32, FD>(p, group_m, s); break;
+    default: launch_lds8_typed<IN_BF16, OUT_BF16, FD>(p, group_m, s); break;
+    }
+    return hipGetLastError();
+}
+
 static hipError_t launch_ldsbt(const Problem& p, int group_m, hipStream_t s) {
     switch (p.dtype) {
     case 0: launch_ldsbt_typed<IN_F16, OUT_F32>(p, group_m, s); break;
@@ -770,6 +980,7 @@ hipError_t launch_instance(int id, const Problem& p, hipStream_t s) {
     case 6: return launch_lds<32, 5>(p, gm, s);
     case 7: return launch_ldsbt(p, gm, s);
     case 8: return launch_lds<64, 2, 2>(p, gm, s);
+    case 9: return launch_lds8<1>(p, gm, s);
     case 4: return launch_tile<256, 256, false>(p, gm, s);
     case 1: return launch_tile<128, 128, false>(p, gm, s);
     case 2: return launch_tile<256, 256, true>(p, gm, s);

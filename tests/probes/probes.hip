@@ -192,7 +192,61 @@ __global__ __launch_bounds__(256) void probe_dma_rate_kernel(int iters, const ch
 }
 #pragma clang diagnostic pop
 
+// LDS read throughput against parallelism: blockDim.x / 64 waves per CU, each
+// issuing `iters` x UNROLL independent reads.  KIND 0: ds_read_b128 on
+// consecutive 16-byte chunks; 1: ds_read_b64_tr_b16 with the GEMM's
+// B-fragment addressing (rows of 512 bytes, chunk ^ 2(k&3)).  Addresses stay
+// inside the 64 KiB buffer.
+template <int KIND, int UNROLL>
+__global__ __launch_bounds__(1024) void probe_lds_par_kernel(int iters, uint64_t* cycles, uint32_t* sink) {
+    __shared__ __attribute__((aligned(1024))) char lds[65536];
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    for (int i = threadIdx.x; i < 65536 / 4; i += blockDim.x) reinterpret_cast<uint32_t*>(lds)[i] = i;
+    int addr;
+    if (KIND == 0) {
+        addr = (w * 1024 + l * 16) & 65535;
+    } else {
+        const int g = l >> 4, ip = l & 15;
+        const int k = 8 * (g >> 1) + (ip >> 2) + 16 * ((w >> 1) & 3);
+        const int n = 16 * (g & 1) + 4 * (ip & 3) + 128 * (w & 1);
+        addr = k * 512 + (((n >> 3) ^ (2 * (k & 3))) * 16) + (n & 7) * 2;
+    }
+    uint32_t x = 0;
+    __syncthreads();
+    const uint64_t t0 = __builtin_readcyclecounter();
+    for (int it = 0; it < iters; ++it) {
+        const int base = addr + ((it & 1) << 15);
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int a = (base + u * 2048) & 65535;
+            if constexpr (KIND == 0) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(lds + (a & ~15));
+                x ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+            } else {
+                const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) char*)lds + (a & ~7)));
+                const u32x2 v2 = __builtin_bit_cast(u32x2, v);
+                x ^= v2[0] ^ v2[1];
+            }
+        }
+    }
+    const uint64_t t1 = __builtin_readcyclecounter();
+    if (l == 0) cycles[blockIdx.x * 16 + w] = t1 - t0;
+    if (x == 0x12345678u) sink[0] = x;
+}
+
 extern "C" {
+
+// cycles must hold blocks * 16 entries; threads in {256, 512, 1024}.
+int probe_lds_par(int kind, int unroll16, int blocks, int threads, int iters, uint64_t* cycles, uint32_t* sink) {
+    if (threads != 256 && threads != 512 && threads != 1024) return -1;
+    const dim3 g(blocks), b(threads);
+    if (kind == 0 && !unroll16) hipLaunchKernelGGL((probe_lds_par_kernel<0, 8>), g, b, 0, 0, iters, cycles, sink);
+    else if (kind == 0) hipLaunchKernelGGL((probe_lds_par_kernel<0, 16>), g, b, 0, 0, iters, cycles, sink);
+    else if (!unroll16) hipLaunchKernelGGL((probe_lds_par_kernel<1, 8>), g, b, 0, 0, iters, cycles, sink);
+    else hipLaunchKernelGGL((probe_lds_par_kernel<1, 16>), g, b, 0, 0, iters, cycles, sink);
+    return (int)hipDeviceSynchronize();
+}
 
 int probe_dma_rate(int blocks, int iters, const char* src, int src_bytes, uint64_t* cycles, uint32_t* sink) {
     if (src_bytes < 8192 || (src_bytes & (src_bytes - 1)) != 0) return -1;
