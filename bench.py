@@ -32,6 +32,7 @@ PEAK_TFLOPS = 2500.0        # MI355X published dense fp16/bf16 MFMA peak
 HBM_GBPS = 8000.0           # MI355X published HBM3E bandwidth
 CODES = {("f16", "f32"): 0, ("f16", "f16"): 1, ("bf16", "f32"): 2, ("bf16", "bf16"): 3}
 KERNEL_SOURCES = ["dense_half_precision_tiled_amd/csrc/gemm_kernels.hip",
+                  "dense_half_precision_tiled_amd/csrc/gemm_dl.hip",
                   "dense_half_precision_tiled_amd/csrc/gemm_internal.h"]
 
 

@@ -12,7 +12,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdhpt_gemm.so")
 ARCH = "gfx950"
 
-SOURCES = ["gemm_api.cpp", "gemm_kernels.hip"]
+SOURCES = ["gemm_api.cpp", "gemm_kernels.hip", "gemm_dl.hip"]
 
 # Packed-fp32 VALU ops stay disabled in every HIP translation unit.
 HIP_FLAGS = ["-x", "hip", "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",

@@ -69,16 +69,19 @@ int64_t tiles_for(int id, int64_t M, int64_t N) {
     return ((M + in.bm - 1) / in.bm) * ((N + in.bn - 1) / in.bn);
 }
 
-// Large tiles when they still give at least half a wave over the 256 CUs;
-// otherwise 128x128 tiles (more workgroups for mid-size shapes).  For the
-// large aligned case the direct-to-LDS kernel with fragment prefetch
-// distance 2 (instance 8) measured fastest.
+// Large (256x256) tiles when they still give at least half a wave over the
+// 256 CUs, otherwise 128x128 tiles.  Within a size, the first instance that
+// supports the problem: the direct-to-LDS kernel for whole tiles, its
+// clamped-edge form for any M and K with N a multiple of 8, and the
+// element-masked kernel for everything else.
 int choose_instance(const Problem& p) {
+    static const int big_order[] = {10, 11, 2};
+    static const int mid_order[] = {14, 15, 3};
     const bool big = tiles_for(0, p.M, p.N) >= 128;
-    const int order[2][2] = {{8, 2}, {1, 3}};      // [tile][edge]
-    const int tile = big ? 0 : 1;
-    if (dhpt::instance_supports(order[tile][0], p)) return order[tile][0];
-    return order[tile][1];
+    const int* order = big ? big_order : mid_order;
+    for (int k = 0; k < 3; ++k)
+        if (dhpt::instance_supports(order[k], p)) return order[k];
+    return big ? 2 : 3;
 }
 
 int enqueue(int id, const Problem& p, hipStream_t s) {

@@ -17,12 +17,21 @@ struct Problem {
     bool vecA, vecB;           // 16-byte aligned base and leading dimension
 };
 
+// What an instance requires of the problem.
+enum Requirement {
+    REQ_ANY = 0,               // any shape, any alignment (element-masked edges)
+    REQ_TILE_VEC = 1,          // M % bm, N % bn, K % bk == 0 and 16-byte aligned A, B rows
+    REQ_TILE = 2,              // M % bm, N % bn, K % bk == 0 (any 2-byte alignment)
+    REQ_N8 = 3,                // N % 8 == 0 and N >= 8 (clamped edges, zero-filled K tail)
+};
+
 // One compiled tile geometry.  Every instance computes the same function.
 struct InstanceInfo {
     const char* name;
     int bm, bn, bk;            // workgroup tile
-    bool edge;                 // masked loads/stores: any shape, any alignment
+    bool edge;                 // handles partial tiles (masked stores)
     int group_m;               // tile-rows per group of the visit order
+    int req;                   // Requirement
 };
 
 extern const InstanceInfo kInstances[];
@@ -33,6 +42,10 @@ extern const int kNumInstances;
 bool instance_supports(int id, const Problem& p);
 
 hipError_t launch_instance(int id, const Problem& p, hipStream_t stream);
+
+// The direct-to-LDS family (gemm_dl.hip): tile 256 or 128, fragment prefetch
+// distance 1 or 2, edge handling on or off.
+hipError_t launch_dl(int tile, int fd, bool edge, const Problem& p, int group_m, hipStream_t stream);
 hipError_t launch_zero_fill(const Problem& p, hipStream_t stream);
 
 // Workgroup id -> output tile (tm, tn).

@@ -880,24 +880,38 @@ __global__ __launch_bounds__(256, 1) void gemm_ldsbt_kernel(
 
 // ---------------------------------------------------------------- instances
 const InstanceInfo kInstances[] = {
-    {"mfma_256x256x64_lds2", 256, 256, 64, false, 8},
-    {"mfma_128x128x64", 128, 128, 64, false, 8},
-    {"mfma_256x256x64_edge", 256, 256, 64, true, 8},
-    {"mfma_128x128x64_edge", 128, 128, 64, true, 8},
-    {"mfma_256x256x64", 256, 256, 64, false, 8},
-    {"mfma_256x256x32_lds4", 256, 256, 32, false, 8},
-    {"mfma_256x256x32_lds5", 256, 256, 32, false, 8},
-    {"mfma_256x256x64_ldsbt", 256, 256, 64, false, 8},
-    {"mfma_256x256x64_lds2_fd2", 256, 256, 64, false, 8},
-    {"mfma_256x256x64_w8", 256, 256, 64, false, 8},
+    {"mfma_256x256x64_lds2", 256, 256, 64, false, 8, REQ_TILE_VEC},
+    {"mfma_128x128x64", 128, 128, 64, false, 8, REQ_TILE_VEC},
+    {"mfma_256x256x64_edge", 256, 256, 64, true, 8, REQ_ANY},
+    {"mfma_128x128x64_edge", 128, 128, 64, true, 8, REQ_ANY},
+    {"mfma_256x256x64", 256, 256, 64, false, 8, REQ_TILE_VEC},
+    {"mfma_256x256x32_lds4", 256, 256, 32, false, 8, REQ_TILE_VEC},
+    {"mfma_256x256x32_lds5", 256, 256, 32, false, 8, REQ_TILE_VEC},
+    {"mfma_256x256x64_ldsbt", 256, 256, 64, false, 8, REQ_TILE_VEC},
+    {"mfma_256x256x64_lds2_fd2", 256, 256, 64, false, 8, REQ_TILE_VEC},
+    {"mfma_256x256x64_w8", 256, 256, 64, false, 8, REQ_TILE_VEC},
+    {"dl_256x256x64_fd2", 256, 256, 64, false, 8, REQ_TILE},
+    {"dl_256x256x64_fd2_edge", 256, 256, 64, true, 8, REQ_N8},
+    {"dl_128x128x64_fd1", 128, 128, 64, false, 8, REQ_TILE},
+    {"dl_128x128x64_fd1_edge", 128, 128, 64, true, 8, REQ_N8},
+    {"dl_128x128x64_fd2", 128, 128, 64, false, 8, REQ_TILE},
+    {"dl_128x128x64_fd2_edge", 128, 128, 64, true, 8, REQ_N8},
+    {"dl_256x256x64_fd1", 256, 256, 64, false, 8, REQ_TILE},
+    {"dl_256x256x64_fd1_edge", 256, 256, 64, true, 8, REQ_N8},
 };
 const int kNumInstances = sizeof(kInstances) / sizeof(kInstances[0]);
 
 bool instance_supports(int id, const Problem& p) {
     if (id < 0 || id >= kNumInstances) return false;
     const InstanceInfo& in = kInstances[id];
-    if (in.edge) return true;
-    return p.M % in.bm == 0 && p.N % in.bn == 0 && p.K % in.bk == 0 && p.vecA && p.vecB;
+    const bool tiled = p.M % in.bm == 0 && p.N % in.bn == 0 && p.K % in.bk == 0;
+    switch (in.req) {
+    case REQ_ANY: return true;
+    case REQ_TILE_VEC: return tiled && p.vecA && p.vecB;
+    case REQ_TILE: return tiled;
+    case REQ_N8: return p.N % 8 == 0 && p.N >= 8;
+    default: return false;
+    }
 }
 
 template <int BM, int BN, bool EDGE>
@@ -981,6 +995,14 @@ hipError_t launch_instance(int id, const Problem& p, hipStream_t s) {
     case 7: return launch_ldsbt(p, gm, s);
     case 8: return launch_lds<64, 2, 2>(p, gm, s);
     case 9: return launch_lds8<1>(p, gm, s);
+    case 10: return launch_dl(256, 2, false, p, gm, s);
+    case 11: return launch_dl(256, 2, true, p, gm, s);
+    case 12: return launch_dl(128, 1, false, p, gm, s);
+    case 13: return launch_dl(128, 1, true, p, gm, s);
+    case 14: return launch_dl(128, 2, false, p, gm, s);
+    case 15: return launch_dl(128, 2, true, p, gm, s);
+    case 16: return launch_dl(256, 1, false, p, gm, s);
+    case 17: return launch_dl(256, 1, true, p, gm, s);
     case 4: return launch_tile<256, 256, false>(p, gm, s);
     case 1: return launch_tile<128, 128, false>(p, gm, s);
     case 2: return launch_tile<256, 256, true>(p, gm, s);

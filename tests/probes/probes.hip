@@ -235,7 +235,38 @@ __global__ __launch_bounds__(1024) void probe_lds_par_kernel(int iters, uint64_t
     if (x == 0x12345678u) sink[0] = x;
 }
 
+// 16-byte global loads from addresses that are only 2-byte aligned: lane l
+// reads the 16 bytes at src + offset + 32 l with global_load_dwordx4 (into
+// out_vec[4l..4l+3]) and with global_load_lds_dwordx4 (LDS image copied to
+// out_lds[4l..4l+3]).  src must hold at least offset + 32*64 + 16 bytes; the
+// host checks it.  Either the bytes at the exact address come back, or (in
+// strict alignment mode) those of the aligned-down address: no fault either way.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__global__ void probe_unaligned_kernel(const char* src, int offset, uint32_t* out_vec, uint32_t* out_lds) {
+    __shared__ __attribute__((aligned(1024))) uint32_t lds[256];
+    const int l = threadIdx.x;
+    const char* p = src + offset + 32 * l;
+    u32x4 v;
+    asm volatile("global_load_dwordx4 %0, %1, off\n\ts_waitcnt vmcnt(0)" : "=v"(v) : "v"(p) : "memory");
+    for (int j = 0; j < 4; ++j) out_vec[4 * l + j] = v[j];
+    lds[l] = 0; lds[64 + l] = 0; lds[128 + l] = 0; lds[192 + l] = 0;
+    __syncthreads();
+    const uint32_t base = (uint32_t)(size_t)(__attribute__((address_space(3))) uint32_t*)lds;
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off\n\ts_waitcnt vmcnt(0)"
+                 :: "v"(p), "s"(base) : "memory", "m0");
+    __syncthreads();
+    for (int j = 0; j < 4; ++j) out_lds[4 * l + j] = lds[4 * l + j];
+}
+#pragma clang diagnostic pop
+
 extern "C" {
+
+int probe_unaligned(const char* src, int src_bytes, int offset, uint32_t* out_vec, uint32_t* out_lds) {
+    if (offset < 0 || offset + 32 * 64 + 16 > src_bytes) return -1;
+    hipLaunchKernelGGL(probe_unaligned_kernel, dim3(1), dim3(64), 0, 0, src, offset, out_vec, out_lds);
+    return (int)hipDeviceSynchronize();
+}
 
 // cycles must hold blocks * 16 entries; threads in {256, 512, 1024}.
 int probe_lds_par(int kind, int unroll16, int blocks, int threads, int iters, uint64_t* cycles, uint32_t* sink) {

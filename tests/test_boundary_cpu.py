@@ -95,7 +95,7 @@ def test_unknown_instance(lib):
     assert G.gemm_run_instance(n, 4, 4, 4, 0, PA, 4, PB, 4, PC, 4, None) == G.GEMM_ERR_INSTANCE
     assert G.gemm_instance_name(n) == "?"
     for i in range(n):
-        assert G.gemm_instance_name(i).startswith("mfma_")
+        assert G.gemm_instance_name(i).startswith(("mfma_", "dl_"))
 
 
 def _pick(M, N, K, dtype=3, lda=None, ldb=None, ldc=None, pa=PA, pb=PB):
@@ -104,16 +104,19 @@ def _pick(M, N, K, dtype=3, lda=None, ldb=None, ldc=None, pa=PA, pb=PB):
 
 
 def test_instance_choice(lib):
-    assert _pick(8192, 8192, 8192) == "mfma_256x256x64_lds2_fd2"
-    assert _pick(4096, 4096, 4096) == "mfma_256x256x64_lds2_fd2"
-    assert _pick(2048, 2048, 2048, 0) == "mfma_128x128x64"
-    assert _pick(256, 256, 256, 0) == "mfma_128x128x64"
-    # ragged shape with a 2-byte-aligned lda: edge kernel
-    assert _pick(3000, 5000, 4099, 1).endswith("_edge")
-    # aligned shape but a misaligned base pointer: edge kernel
-    assert _pick(4096, 4096, 4096, pa=PA + 2).endswith("_edge")
-    # K not a multiple of 64: edge kernel
-    assert _pick(4096, 4096, 4000).endswith("_edge")
+    assert _pick(8192, 8192, 8192) == "dl_256x256x64_fd2"
+    assert _pick(4096, 4096, 4096) == "dl_256x256x64_fd2"
+    assert _pick(2048, 2048, 2048, 0) == "dl_128x128x64_fd2"
+    assert _pick(256, 256, 256, 0) == "dl_128x128x64_fd2"
+    # ragged shape, 2-byte-aligned lda, N a multiple of 8: clamped-edge kernel
+    assert _pick(3000, 5000, 4099, 1) == "dl_256x256x64_fd2_edge"
+    # misaligned base pointer: unaligned 16-byte loads are fine, same kernel
+    assert _pick(4096, 4096, 4096, pa=PA + 2) == "dl_256x256x64_fd2"
+    # K not a multiple of 64: edge kernel with the zero-filled tail slice
+    assert _pick(4096, 4096, 4000) == "dl_256x256x64_fd2_edge"
+    # N not a multiple of 8: element-masked kernel
+    assert _pick(4096, 4100, 4096) == "mfma_256x256x64_edge"
+    assert _pick(100, 7, 33, 0).endswith("_edge")
 
 
 @pytest.mark.parametrize("shape", [(8192, 8192), (4096, 4096), (2048, 2048), (3000, 5000),

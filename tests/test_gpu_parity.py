@@ -231,23 +231,60 @@ def test_instances_agree_bitwise(G):
         fmt, out = DTYPES[code]
         A = law_for(fmt)((512, 512), 101, fmt)
         B = law_for(fmt)((512, 512), 102, fmt)
-        ys = [run(G, A, B, code, instance=i) for i in range(n)]
+        ys = []
+        for i in range(n):
+            print("instance", G.gemm_instance_name(i), code, flush=True)
+            ys.append(run(G, A, B, code, instance=i))
         for i in range(1, n):
             assert np.array_equal(ys[0], ys[i]), G.gemm_instance_name(i)
         assert_bound(ys[0], oracle.gemm_f64(A, B, fmt), 512, out, "instances")
 
 
-def test_edge_instances_on_ragged_shapes(G):
+RAGGED = [(129, 131, 67), (300, 260, 130), (1, 513, 65), (129, 136, 67), (300, 264, 130),
+          (1, 520, 65), (255, 8, 200), (8, 1032, 63), (257, 392, 1), (520, 512, 576)]
+
+
+def _edge_instances(G):
     n = G.gemm_num_instances()
-    for (M, N, K) in [(129, 131, 67), (300, 260, 130), (1, 513, 65)]:
+    return [i for i in range(n) if G.gemm_instance_name(i).endswith("_edge")]
+
+
+def _expect_for(G, i, N):
+    """dl_*_edge instances read B in 8-column chunks: they take N % 8 == 0
+    only and refuse other shapes with GEMM_ERR_INSTANCE."""
+    if G.gemm_instance_name(i).startswith("dl_") and N % 8 != 0:
+        return G.GEMM_ERR_INSTANCE
+    return 0
+
+
+def test_edge_instances_on_ragged_shapes(G):
+    for (M, N, K) in RAGGED:
         A = inputs.uniform((M, K), M + N, "f16")
         B = inputs.uniform((K, N), M + K, "f16")
         r = oracle.gemm_f64(A, B, "f16")
-        for i in range(n):
-            if not G.gemm_instance_name(i).endswith("_edge"):
-                continue
-            y = run(G, A, B, 1, instance=i)
-            assert_bound(y, r, K, "f16", "%s %s" % (G.gemm_instance_name(i), (M, N, K)))
+        for i in _edge_instances(G):
+            print("edge", G.gemm_instance_name(i), (M, N, K), flush=True)
+            expect = _expect_for(G, i, N)
+            y = run(G, A, B, 1, instance=i, expect=expect)
+            if expect == 0:
+                assert_bound(y, r, K, "f16", "%s %s" % (G.gemm_instance_name(i), (M, N, K)))
+
+
+@pytest.mark.parametrize("code", [0, 3])
+def test_edge_instances_misaligned_strides(G, code):
+    """2-byte-aligned base pointer and leading dimensions on every edge
+    instance: same bits as the packed, aligned call."""
+    fmt, out = DTYPES[code]
+    M, N, K = 300, 264, 200
+    A = law_for(fmt)((M, K), 111, fmt)
+    B = law_for(fmt)((K, N), 112, fmt)
+    r = oracle.gemm_f64(A, B, fmt)
+    for i in _edge_instances(G):
+        print("misaligned", G.gemm_instance_name(i), flush=True)
+        y = run(G, A, B, code, instance=i)
+        y2 = run(G, A, B, code, lda=K + 1, ldb=N + 3, ldc=N + 1, a_off=1, instance=i)
+        assert_bound(y2, r, K, out, "misaligned %s" % G.gemm_instance_name(i))
+        assert np.array_equal(y, y2)
 
 
 def test_non_edge_instance_rejects_ragged_shape(G):

@@ -208,3 +208,26 @@ def test_dma_rate(P):
               % (nbytes >> 20, rate, cycles / (4 * iters * 8), gbs))
         assert 4 < rate < 1024
         del src
+
+
+@pytest.mark.parametrize("offset", [0, 2, 6, 10, 14])
+def test_unaligned_16_byte_global_loads(P, offset):
+    """Record whether global_load_dwordx4 and global_load_lds_dwordx4 return
+    the 16 bytes at a 2-byte-aligned address (unaligned mode) or those of the
+    aligned-down address (strict mode).  The GEMM's misaligned-A path relies on
+    this: it is pinned here."""
+    P.probe_unaligned.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    P.probe_unaligned.restype = ctypes.c_int
+    nbytes = 4096
+    src = torch.arange(nbytes, dtype=torch.int32, device="cuda").to(torch.uint8)
+    ov = torch.zeros(256, dtype=torch.int32, device="cuda")
+    ol = torch.zeros(256, dtype=torch.int32, device="cuda")
+    assert P.probe_unaligned(src.data_ptr(), nbytes, offset, ov.data_ptr(), ol.data_ptr()) == 0
+    host = src.cpu().numpy()
+    vec = ov.cpu().numpy().view(np.uint8).reshape(64, 16)
+    lds = ol.cpu().numpy().view(np.uint8).reshape(64, 16)
+    exact = np.stack([host[offset + 32 * l: offset + 32 * l + 16] for l in range(64)])
+    down = np.stack([host[(offset + 32 * l) & ~15: ((offset + 32 * l) & ~15) + 16] for l in range(64)])
+    kind = lambda got: "exact" if np.array_equal(got, exact) else ("aligned-down" if np.array_equal(got, down) else "other")
+    print("offset %2d: global_load_dwordx4 -> %s, global_load_lds_dwordx4 -> %s" % (offset, kind(vec), kind(lds)))
+    assert kind(vec) != "other" and kind(lds) != "other"
