@@ -20,6 +20,11 @@ the comparison rule that decides parity:
   bf16 output.  Bit-exact fixtures instead require y == round_to(fmt, r).
 * ``flops``: the 2MNK count (same page, "Compute one output before launching a
   warp": one multiply and one add per inner step).
+* ``gemm_ex_f64`` / ``bound_ex`` / ``compare_ex``: the general form
+  act(alpha*A.B + beta*C_old + bias) with B row-major or column-major, for the
+  fused-epilogue entry point (alpha/beta: the general GEMM the same page opens
+  with; bias + ReLU: the fused epilogue of the Ada tensor-core GEMM write-up;
+  column-major B: that write-up's "TN" layout).
 """
 from __future__ import annotations
 
@@ -52,28 +57,35 @@ def build(force: bool = False) -> str:
 def _load():
     global _lib
     if _lib is None:
-        lib = ctypes.CDLL(build())
-        i64, u16p, f64p, i64p = (ctypes.c_int64, ctypes.POINTER(ctypes.c_uint16),
-                                 ctypes.POINTER(ctypes.c_double),
-                                 ctypes.POINTER(ctypes.c_int64))
-        lib.oracle_gemm_f64.argtypes = [i64, i64, i64, ctypes.c_int, u16p, i64, u16p, i64,
-                                        f64p, i64, ctypes.c_int]
-        lib.oracle_gemm_f64.restype = ctypes.c_int
-        lib.oracle_gemm_rows_f64.argtypes = [i64, i64p, i64, i64, ctypes.c_int, u16p, i64,
-                                             u16p, i64, f64p, i64, ctypes.c_int]
-        lib.oracle_gemm_rows_f64.restype = ctypes.c_int
-        lib.oracle_decode_array.argtypes = [ctypes.c_int, u16p, f64p, i64]
-        lib.oracle_decode_array.restype = None
-        lib.oracle_round_to.argtypes = [ctypes.c_int, ctypes.c_double]
-        lib.oracle_round_to.restype = ctypes.c_double
-        lib.oracle_ulp.argtypes = [ctypes.c_int, ctypes.c_double]
-        lib.oracle_ulp.restype = ctypes.c_double
-        lib.oracle_decode_f16.argtypes = [ctypes.c_uint16]
-        lib.oracle_decode_f16.restype = ctypes.c_double
-        lib.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
-        lib.oracle_decode_bf16.restype = ctypes.c_double
-        _lib = lib
+        _lib = _declare(ctypes.CDLL(build()))
     return _lib
+
+
+def _declare(lib):
+    """Set the argument and result types of the oracle's exported functions."""
+    i64, u16p, f64p, i64p = (ctypes.c_int64, ctypes.POINTER(ctypes.c_uint16),
+                             ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64))
+    lib.oracle_gemm_f64.argtypes = [i64, i64, i64, ctypes.c_int, u16p, i64, u16p, i64,
+                                    f64p, i64, ctypes.c_int]
+    lib.oracle_gemm_f64.restype = ctypes.c_int
+    lib.oracle_gemm_rows_f64.argtypes = [i64, i64p, i64, i64, ctypes.c_int, u16p, i64,
+                                         u16p, i64, f64p, i64, ctypes.c_int]
+    lib.oracle_gemm_rows_f64.restype = ctypes.c_int
+    lib.oracle_gemm_ex_f64.argtypes = [i64, i64p, i64, i64, ctypes.c_int, ctypes.c_int, u16p,
+                                       i64, u16p, i64, ctypes.c_double, ctypes.c_double, f64p,
+                                       i64, f64p, ctypes.c_int, f64p, i64, ctypes.c_int]
+    lib.oracle_gemm_ex_f64.restype = ctypes.c_int
+    lib.oracle_decode_array.argtypes = [ctypes.c_int, u16p, f64p, i64]
+    lib.oracle_decode_array.restype = None
+    lib.oracle_round_to.argtypes = [ctypes.c_int, ctypes.c_double]
+    lib.oracle_round_to.restype = ctypes.c_double
+    lib.oracle_ulp.argtypes = [ctypes.c_int, ctypes.c_double]
+    lib.oracle_ulp.restype = ctypes.c_double
+    lib.oracle_decode_f16.argtypes = [ctypes.c_uint16]
+    lib.oracle_decode_f16.restype = ctypes.c_double
+    lib.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
+    lib.oracle_decode_bf16.restype = ctypes.c_double
+    return lib
 
 
 def _ptr(a: np.ndarray, ctype):
@@ -220,3 +232,103 @@ def compare(y, r, K: int, out_fmt) -> dict:
     n_bad = int(np.count_nonzero(err > b))
     return {"ok": n_bad == 0, "max_abs": float(err.max()), "max_rel": max_rel,
             "n_bad": n_bad, "worst_ratio": float(np.max(err / b))}
+
+
+B_ROW_MAJOR, B_COL_MAJOR = 0, 1
+
+
+def _layout(b_layout) -> int:
+    if b_layout in ("row", "nn", B_ROW_MAJOR):
+        return B_ROW_MAJOR
+    if b_layout in ("col", "tn", B_COL_MAJOR):
+        return B_COL_MAJOR
+    raise ValueError("unknown B layout %r" % (b_layout,))
+
+
+def gemm_ex_f64(A_bits, B_bits, in_fmt, b_layout="row", alpha=1.0, beta=0.0, C_old=None,
+                bias=None, relu=False, rows=None, threads: int | None = None) -> np.ndarray:
+    """act(alpha * A.B + beta * C_old + bias) in fp64.
+
+    B_bits is K x N (b_layout "row") or its N x K transpose (b_layout "col").
+    C_old: float64 values of the old output (the selected rows when ``rows``
+    is given); ignored when beta == 0.  bias: N float64 values or None.
+    relu: apply max(x, 0) last.  rows: output rows to compute (None = all).
+    """
+    A = _as_bits_2d(A_bits)
+    B = _as_bits_2d(B_bits)
+    lay = _layout(b_layout)
+    M, K = A.shape
+    K2, N = B.shape if lay == B_ROW_MAJOR else B.shape[::-1]
+    if K != K2:
+        raise ValueError("inner dimensions differ: %d vs %d" % (K, K2))
+    if rows is None:
+        r = np.arange(M, dtype=np.int64)
+    else:
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        if r.size and (r.min() < 0 or r.max() >= M):
+            raise IndexError("row index out of range")
+    C = np.zeros((r.size, N), dtype=np.float64)
+    cold_p, ldcold = None, 0
+    if beta != 0.0:
+        if C_old is None:
+            raise ValueError("beta != 0 needs C_old")
+        cold = np.ascontiguousarray(np.asarray(C_old, dtype=np.float64))
+        if cold.shape != (r.size, N):
+            raise ValueError("C_old must be %d x %d" % (r.size, N))
+        cold_p, ldcold = _ptr(cold, ctypes.c_double), N
+    bias_p = None
+    if bias is not None:
+        bz = np.ascontiguousarray(np.asarray(bias, dtype=np.float64))
+        if bz.shape != (N,):
+            raise ValueError("bias must have N = %d values" % N)
+        bias_p = _ptr(bz, ctypes.c_double)
+    rc = _load().oracle_gemm_ex_f64(r.size, _ptr(r, ctypes.c_int64), N, K, _fmt_in(in_fmt), lay,
+                                    _ptr(A, ctypes.c_uint16), A.strides[0] // 2,
+                                    _ptr(B, ctypes.c_uint16), B.strides[0] // 2,
+                                    float(alpha), float(beta), cold_p, ldcold, bias_p,
+                                    1 if relu else 0, _ptr(C, ctypes.c_double), N,
+                                    threads or default_threads())
+    if rc != 0:
+        raise MemoryError("oracle allocation failed") if rc == -1 else ValueError("oracle rc %d" % rc)
+    return C
+
+
+def bound_ex(K: int, out_fmt, r, alpha=1.0, beta=0.0, C_old=None, bias=None, dot=None) -> np.ndarray:
+    """Acceptance bound for the general form.
+
+    The fp32 accumulation contributes |alpha| * K * 2^-20 (the plain bound
+    scaled by alpha); the fp32 epilogue (scale, add beta*C_old, add bias) and
+    an fp32 output rounding contribute at most four roundings of 2^-24 each
+    of the largest magnitude involved, bounded by
+    2^-22 * (|alpha * dot| + |beta * C_old| + |bias|); a half-precision
+    output adds one ulp of its format at r.  ReLU is 1-Lipschitz and adds
+    nothing.  ``dot`` is the fp64 A.B (defaults to r, exact when alpha = 1,
+    beta = 0, no bias and no ReLU clipping)."""
+    f = _fmt_out(out_fmt)
+    r = np.asarray(r, dtype=np.float64)
+    d = r if dot is None else np.asarray(dot, dtype=np.float64)
+    mag = np.abs(alpha * d)
+    if beta != 0.0:
+        mag = mag + np.abs(beta * np.asarray(C_old, dtype=np.float64))
+    if bias is not None:
+        mag = mag + np.abs(np.asarray(bias, dtype=np.float64))[None, :]
+    b = abs(alpha) * float(K) * 2.0 ** -20 + 2.0 ** -22 * mag
+    if f != OUT_F32:
+        b = b + ulp(r, f)
+    return b
+
+
+def compare_ex(y, r, K: int, out_fmt, **kw) -> dict:
+    """compare() with the bound of the general form (keyword args of bound_ex)."""
+    y = np.asarray(y, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    if y.shape != r.shape:
+        raise ValueError("shape mismatch %s vs %s" % (y.shape, r.shape))
+    if y.size == 0:
+        return {"ok": True, "max_abs": 0.0, "n_bad": 0, "worst_ratio": 0.0}
+    err = np.abs(y - r)
+    err = np.where(np.isnan(err), np.inf, err)
+    b = bound_ex(K, out_fmt, r, **kw)
+    n_bad = int(np.count_nonzero(err > b))
+    return {"ok": n_bad == 0, "max_abs": float(err.max()), "n_bad": n_bad,
+            "worst_ratio": float(np.max(err / b))}

@@ -28,6 +28,21 @@
  * same page relies on).  It is used to build the expected value of bit-exact
  * fixtures whose exact result is not representable in the output format.
  *
+ * General form (oracle_gemm_ex_f64), for the fused-epilogue entry point:
+ *   C[i][j] = act( alpha * sum_k A[i][k] * B(k, j) + beta * Cold[i][j] + bias[j] )
+ *   - alpha, beta: the general C <- alpha*A*B + beta*C the naive-to-tensor-core
+ *     page opens with; with beta == 0 the old output is not read at all, so
+ *     whatever it holds (even NaN) cannot leak into the result;
+ *   - bias: one value per output column, added before the activation, and
+ *     act = ReLU (max(x, 0)) or the identity: the bias + ReLU epilogue that
+ *     the Ada tensor-core GEMM write-up folds into the kernel (section on the
+ *     fused epilogue), applied once to the unrounded value;
+ *   - B(k, j) is B[k*ldb + j] for a row-major K x N operand, or B[j*ldb + k]
+ *     when B is stored column-major (its N x K transpose row-major), the "TN"
+ *     layout the same write-up chose ("A row-major, B column-major").
+ *   Everything after the dot product is done in double, once, without
+ *   intermediate rounding.
+ *
  * Parity pins (tests/test_oracle_pins.py): the page's 2x3 . 3x2 worked example,
  * exact rational brute force on tiny shapes, closed forms (all-ones,
  * identity, permutation, rank-1), the two-reference example, the fp16 rounding
@@ -41,6 +56,7 @@
 
 enum { ORACLE_IN_F16 = 0, ORACLE_IN_BF16 = 1 };
 enum { ORACLE_OUT_F32 = 0, ORACLE_OUT_F16 = 1, ORACLE_OUT_BF16 = 2 };
+enum { ORACLE_B_ROW_MAJOR = 0, ORACLE_B_COL_MAJOR = 1 };
 
 /* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
  * Normal:    (1024 + f) * 2^(e - 25)      Subnormal: f * 2^-24 */
@@ -170,16 +186,22 @@ static void* oracle_worker(void* arg) {
     return NULL;
 }
 
-static int run_rows(int in_fmt, int64_t nrows, const int64_t* rows, int64_t N, int64_t K,
-                    const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+static int run_rows(int in_fmt, int b_layout, int64_t nrows, const int64_t* rows, int64_t N,
+                    int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                     double* C, int64_t ldc, int nthreads) {
     if (nrows <= 0 || N <= 0) return 0;
     double* Bd = NULL;
     if (K > 0) {
         Bd = (double*)malloc((size_t)K * (size_t)N * sizeof(double));
         if (!Bd) return -1;
-        for (int64_t k = 0; k < K; ++k)
-            oracle_decode_array(in_fmt, B + k * ldb, Bd + k * N, N);
+        if (b_layout == ORACLE_B_COL_MAJOR) {
+            /* B(k, j) = B[j*ldb + k]: column j of the K x N operand is row j in memory */
+            for (int64_t j = 0; j < N; ++j)
+                for (int64_t k = 0; k < K; ++k) Bd[k * N + j] = decode_one(in_fmt, B[j * ldb + k]);
+        } else {
+            for (int64_t k = 0; k < K; ++k)
+                oracle_decode_array(in_fmt, B + k * ldb, Bd + k * N, N);
+        }
     }
     if (nthreads < 1) nthreads = 1;
     if (nthreads > nrows) nthreads = (int)nrows;
@@ -211,12 +233,38 @@ static int run_rows(int in_fmt, int64_t nrows, const int64_t* rows, int64_t N, i
 int oracle_gemm_f64(int64_t M, int64_t N, int64_t K, int in_fmt,
                     const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                     double* C, int64_t ldc, int nthreads) {
-    return run_rows(in_fmt, M, NULL, N, K, A, lda, B, ldb, C, ldc, nthreads);
+    return run_rows(in_fmt, ORACLE_B_ROW_MAJOR, M, NULL, N, K, A, lda, B, ldb, C, ldc, nthreads);
 }
 
 /* Selected rows only: C is nrows x N (stride ldc); output row r is row rows[r]. */
 int oracle_gemm_rows_f64(int64_t nrows, const int64_t* rows, int64_t N, int64_t K, int in_fmt,
                          const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                          double* C, int64_t ldc, int nthreads) {
-    return run_rows(in_fmt, nrows, rows, N, K, A, lda, B, ldb, C, ldc, nthreads);
+    return run_rows(in_fmt, ORACLE_B_ROW_MAJOR, nrows, rows, N, K, A, lda, B, ldb, C, ldc, nthreads);
+}
+
+/* The general form.  Output row r (0 <= r < nrows) is row i = rows[r] of the
+ * result (rows == NULL: i = r).  B is read as B(k, j) per b_layout.  Cold holds
+ * the old output values of the same selected rows as doubles (row r at
+ * Cold + r*ldcold); it is not read when beta == 0 and may then be NULL.  bias
+ * holds N doubles or is NULL (no bias).  relu != 0 applies max(x, 0) last.
+ * Returns 0, -1 on allocation failure, -2 on a bad layout code. */
+int oracle_gemm_ex_f64(int64_t nrows, const int64_t* rows, int64_t N, int64_t K, int in_fmt,
+                       int b_layout, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                       double alpha, double beta, const double* Cold, int64_t ldcold,
+                       const double* bias, int relu, double* C, int64_t ldc, int nthreads) {
+    if (b_layout != ORACLE_B_ROW_MAJOR && b_layout != ORACLE_B_COL_MAJOR) return -2;
+    int rc = run_rows(in_fmt, b_layout, nrows, rows, N, K, A, lda, B, ldb, C, ldc, nthreads);
+    if (rc != 0) return rc;
+    for (int64_t r = 0; r < nrows; ++r) {
+        double* c = C + r * ldc;
+        for (int64_t j = 0; j < N; ++j) {
+            double v = alpha * c[j];
+            if (beta != 0.0) v += beta * Cold[r * ldcold + j];
+            if (bias) v += bias[j];
+            if (relu && v < 0.0) v = 0.0;
+            c[j] = v;
+        }
+    }
+    return 0;
 }

@@ -119,3 +119,59 @@ def test_mutant_is_caught(tmp_path, name):
         assert failed == []
     else:
         assert failed, "planted mistake %s passed every pin" % name
+
+
+# ---------------------------------------------------------------------------
+# The general form act(alpha*A.B + beta*C_old + bias) and column-major B.
+# Mutants of that code run through the pins of tests/test_oracle_ex_pins.py,
+# with the mutant library swapped in for the oracle's own.
+EX_MUTANTS = {
+    "ex_control": None,
+    "relu_before_bias": ("            if (bias) v += bias[j];\n            if (relu && v < 0.0) v = 0.0;",
+                         "            if (relu && v < 0.0) v = 0.0;\n            if (bias) v += bias[j];"),
+    "bias_by_row": ("if (bias) v += bias[j];", "if (bias) v += bias[r % N];"),
+    "beta_ignored": ("if (beta != 0.0) v += beta * Cold[r * ldcold + j];", "(void)Cold; (void)ldcold;"),
+    "beta_sign": ("v += beta * Cold[r * ldcold + j];", "v -= beta * Cold[r * ldcold + j];"),
+    "alpha_on_bias": ("if (bias) v += bias[j];", "if (bias) v += alpha * bias[j];"),
+    "col_major_read_as_row": ("Bd[k * N + j] = decode_one(in_fmt, B[j * ldb + k]);",
+                              "Bd[k * N + j] = decode_one(in_fmt, B[(k * ldb + j) % (N * ldb)]);"),
+    "col_major_ignores_ldb": ("Bd[k * N + j] = decode_one(in_fmt, B[j * ldb + k]);",
+                              "Bd[k * N + j] = decode_one(in_fmt, B[j * K + k]);"),
+    "relu_clips_to_abs": ("if (relu && v < 0.0) v = 0.0;", "if (relu && v < 0.0) v = -v;"),
+}
+
+
+def _ex_battery(lib, monkeypatch):
+    import oracle
+    from tests import test_oracle_ex_pins as P
+    monkeypatch.setattr(oracle, "_lib", oracle._declare(lib))
+    pins = [("exact_%d" % n, lambda c=c: P.test_general_form_against_exact_rationals(c))
+            for n, c in enumerate(P.CASES)]
+    pins += [
+        ("int_tn_f16", lambda: P.test_column_major_B_integer_fixture_matches_int64_matmul("f16")),
+        ("int_tn_padded", P.test_column_major_B_with_padded_leading_dimension),
+        ("zero_A", P.test_zero_A_leaves_beta_C_plus_bias),
+        ("alpha_zero", P.test_alpha_zero_ignores_the_product),
+        ("pow2_alpha", P.test_power_of_two_alpha_scales_exactly),
+        ("beta_zero_nan", P.test_beta_zero_never_reads_old_output),
+        ("bias_then_relu", P.test_bias_is_per_column_and_added_before_relu),
+        ("rows_mode", P.test_rows_mode_matches_full_general_form),
+    ]
+    failed = []
+    for name, fn in pins:
+        try:
+            fn()
+        except AssertionError:
+            failed.append(name)
+    return failed
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+@pytest.mark.parametrize("name", sorted(EX_MUTANTS))
+def test_general_form_mutant_is_caught(tmp_path, monkeypatch, name):
+    lib = _build(tmp_path, name, EX_MUTANTS[name])
+    failed = _ex_battery(lib, monkeypatch)
+    if name == "ex_control":
+        assert failed == []
+    else:
+        assert failed, "planted mistake %s passed every pin" % name
