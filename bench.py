@@ -31,8 +31,7 @@ METRIC = "GEMM TFLOP/s (2MNK/t) at 4096³ and 8192³ bf16/fp16; % of MFMA peak"
 PEAK_TFLOPS = 2500.0        # MI355X published dense fp16/bf16 MFMA peak
 HBM_GBPS = 8000.0           # MI355X published HBM3E bandwidth
 CODES = {("f16", "f32"): 0, ("f16", "f16"): 1, ("bf16", "f32"): 2, ("bf16", "bf16"): 3}
-KERNEL_SOURCES = ["dense_half_precision_tiled_amd/csrc/gemm_kernels.hip",
-                  "dense_half_precision_tiled_amd/csrc/gemm_dl.hip",
+KERNEL_SOURCES = ["dense_half_precision_tiled_amd/csrc/gemm_dl_kernel.h",
                   "dense_half_precision_tiled_amd/csrc/gemm_internal.h"]
 
 
@@ -55,24 +54,33 @@ def upload(bits, torch):
     return torch.from_numpy(bits.view(np.int16)).cuda()
 
 
-def measure(G, torch, name, steps, warmup, instance=None):
+def measure(G, torch, name, steps, warmup, instance=None, layout="row"):
     """Upload a workload, run one correctness launch into a poisoned C, then
-    time `steps` launches.  Returns a dict with the timing and the buffers."""
+    time `steps` launches.  Returns a dict with the timing and the buffers.
+    layout "col" stores B column-major (its transpose row-major) and calls
+    gemm_run_ex; "row" calls gemm_run."""
     import numpy as np
     from dense_half_precision_tiled_amd import inputs
     A, B, w = inputs.workload_inputs(name)
     M, N, K = w["M"], w["N"], w["K"]
     code = CODES[(w["fmt"], w["out"])]
-    tA, tB = upload(A, torch), upload(B, torch)
+    col = layout == "col"
+    tA, tB = upload(A, torch), upload(np.ascontiguousarray(B.T) if col else B, torch)
     odt = torch.float32 if w["out"] == "f32" else torch.int16
     tC = torch.full((M, N), -1, dtype=torch.int32 if odt == torch.float32 else torch.int16,
                     device="cuda")                      # all-ones bits: NaN poison
     stream = torch.cuda.current_stream()
     s = stream.cuda_stream
-    args = (M, N, K, code, tA.data_ptr(), K, tB.data_ptr(), N, tC.data_ptr(), N, s)
+    ldb = K if col else N
+    args = (M, N, K, code, tA.data_ptr(), K, tB.data_ptr(), ldb, tC.data_ptr(), N, s)
+    ex_tail = (1.0, 0.0, None, 0, s)
 
     def launch():
-        st = G.gemm_run(*args) if instance is None else G.gemm_run_instance(instance, *args)
+        if col:
+            a = args[:4] + (G.GEMM_B_COL_MAJOR,) + args[4:-1] + ex_tail
+            st = G.gemm_run_ex(*a) if instance is None else G.gemm_run_instance_ex(instance, *a)
+        else:
+            st = G.gemm_run(*args) if instance is None else G.gemm_run_instance(instance, *args)
         if st != 0:
             raise RuntimeError("gemm_run failed: %s" % G.gemm_strerror(st))
 
@@ -92,8 +100,14 @@ def measure(G, torch, name, steps, warmup, instance=None):
     wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1) / steps
     flops = 2.0 * M * N * K
-    inst = G.gemm_select_instance(M, N, K, code, tA.data_ptr(), K, tB.data_ptr(), N,
-                                  tC.data_ptr(), N) if instance is None else instance
+    if instance is not None:
+        inst = instance
+    elif col:
+        inst = G.gemm_select_instance_ex(M, N, K, code, G.GEMM_B_COL_MAJOR, tA.data_ptr(), K,
+                                         tB.data_ptr(), ldb, tC.data_ptr(), N, 1.0, 0.0, None, 0)
+    else:
+        inst = G.gemm_select_instance(M, N, K, code, tA.data_ptr(), K, tB.data_ptr(), N,
+                                      tC.data_ptr(), N)
     return {"name": name, "w": w, "A": A, "B": B, "C": tC, "ms": ms, "wall_s": wall,
             "tflops": flops / (ms * 1e-3) / 1e12, "instance": G.gemm_instance_name(inst),
             "alg_bytes": 2 * (M * K + K * N) + (4 if w["out"] == "f32" else 2) * M * N}
@@ -184,6 +198,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="bf16_8192")
     ap.add_argument("--secondary", default="bf16_4096", help="'none' to skip")
     ap.add_argument("--instance", type=int, default=None, help="force a kernel instance id")
+    ap.add_argument("--layout", choices=("row", "col"), default="row",
+                    help="storage order of B: row-major (gemm_run) or column-major (gemm_run_ex)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for cpu_baseline (0 to skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -206,17 +222,18 @@ def main(argv=None):
     from dense_half_precision_tiled_amd import gemm as G
     G.load()
 
-    main_res = measure(G, torch, args.workload, args.steps, args.warmup, args.instance)
+    main_res = measure(G, torch, args.workload, args.steps, args.warmup, args.instance, args.layout)
     sec = None
     if args.secondary and args.secondary != "none":
-        r2 = measure(G, torch, args.secondary, max(args.steps, 50), args.warmup, args.instance)
+        r2 = measure(G, torch, args.secondary, max(args.steps, 50), args.warmup, args.instance,
+                     args.layout)
         sec = {"workload": describe(r2["w"]), "value": round(r2["tflops"], 2), "unit": "TFLOP/s",
                "ms_per_step": round(r2["ms"], 5), "frac_of_peak": round(r2["tflops"] / PEAK_TFLOPS, 4),
                "kernel": r2["instance"]}
         del r2
 
     w = main_res["w"]
-    traffic = traffic_from_profiles(args.workload)
+    traffic = traffic_from_profiles(args.workload + ("" if args.layout == "row" else "_col"))
     line = {
         "metric": METRIC,
         "value": round(main_res["tflops"], 2),
@@ -230,7 +247,8 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": w["fmt"],
         "data": "synthetic",
-        "config": {"workload": describe(w), "M": w["M"], "N": w["N"], "K": w["K"],
+        "config": {"workload": describe(w) + ("" if args.layout == "row" else ", B column-major"),
+                   "M": w["M"], "N": w["N"], "K": w["K"], "b_layout": args.layout,
                    "in": w["fmt"], "out": w["out"], "kernel": main_res["instance"],
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(main_res["tflops"], 2), "peak": PEAK_TFLOPS,

@@ -1,6 +1,7 @@
 """Build libdhpt_gemm.so in-tree with hipcc for gfx950 (no GPU needed)."""
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -12,7 +13,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdhpt_gemm.so")
 ARCH = "gfx950"
 
-SOURCES = ["gemm_api.cpp", "gemm_kernels.hip", "gemm_dl.hip"]
+SOURCES = ["gemm_api.cpp", "gemm_instances.hip", "gemm_dl_nn.hip", "gemm_dl_nn_epi.hip",
+           "gemm_dl_tn.hip", "gemm_dl_tn_epi.hip"]
 
 # Packed-fp32 VALU ops stay disabled in every HIP translation unit.
 HIP_FLAGS = ["-x", "hip", "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
@@ -29,15 +31,20 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     """Compile every source and link the shared library.  Always recompiles."""
     build_dir = os.path.join(PKG, "_build")
     os.makedirs(build_dir, exist_ok=True)
-    objs = []
+    jobs = []
     for src in SOURCES:
         obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
         cmd = [hipcc()] + HIP_FLAGS + list(extra_flags or []) + ["-c", os.path.join(CSRC, src),
                                                                   "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True, stderr=None if verbose else subprocess.PIPE)
-        objs.append(obj)
+        jobs.append((cmd, obj))
+    # one compiler process per translation unit, a few at a time
+    workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        list(ex.map(lambda j: subprocess.run(j[0], check=True,
+                                             stderr=None if verbose else subprocess.PIPE), jobs))
+    objs = [obj for _, obj in jobs]
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp]
     if verbose:

@@ -26,18 +26,30 @@ void extent(const void* p, int64_t rows, int64_t cols, int64_t ld, int esz, uint
     *e = *b + (uintptr_t)(((rows - 1) * ld + cols) * esz);
 }
 
+// The epilogue and layout arguments of gemm_run_ex (gemm_run: the defaults).
+struct Extra {
+    int b_layout = GEMM_B_ROW_MAJOR;
+    float alpha = 1.0f, beta = 0.0f;
+    const float* bias = nullptr;
+    int relu = 0;
+};
+
 // Validate; on success fill `p` and return GEMM_OK (and *noop for empty output).
 int validate(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
-             const void* B, int64_t ldb, const void* C, int64_t ldc, Problem* p, bool* noop) {
+             const void* B, int64_t ldb, const void* C, int64_t ldc, const Extra& x, Problem* p,
+             bool* noop) {
     *noop = false;
     if (dtype < GEMM_F16_F32 || dtype > GEMM_BF16_BF16) return GEMM_ERR_DTYPE;
+    if (x.b_layout != GEMM_B_ROW_MAJOR && x.b_layout != GEMM_B_COL_MAJOR) return GEMM_ERR_LAYOUT;
+    const bool tb = x.b_layout == GEMM_B_COL_MAJOR;
+    const int64_t b_rows = tb ? N : K, b_cols = tb ? K : N;      // B as stored, row-major
     if (M < 0 || N < 0 || K < 0) return GEMM_ERR_DIM;
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return GEMM_ERR_RANGE;
     if (lda < 0 || ldb < 0 || ldc < 0) return GEMM_ERR_LD;
     if (lda > kMaxLd || ldb > kMaxLd || ldc > kMaxLd) return GEMM_ERR_RANGE;
-    if (lda < K || ldb < N || ldc < N) return GEMM_ERR_LD;
+    if (lda < K || ldb < b_cols || ldc < N) return GEMM_ERR_LD;
     // byte extents stay far below 2^63, and the tile grid fits a 32-bit launch
-    if ((M > 1 && lda > kMaxExtent / (M - 1)) || (K > 1 && ldb > kMaxExtent / (K - 1)) ||
+    if ((M > 1 && lda > kMaxExtent / (M - 1)) || (b_rows > 1 && ldb > kMaxExtent / (b_rows - 1)) ||
         (M > 1 && ldc > kMaxExtent / (M - 1)))
         return GEMM_ERR_RANGE;
     if (((M + 127) / 128) * ((N + 127) / 128) > kMaxDim) return GEMM_ERR_RANGE;
@@ -48,40 +60,42 @@ int validate(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t 
     if (reinterpret_cast<uintptr_t>(C) % osz != 0) return GEMM_ERR_ALIGN;
     if (K > 0 && (reinterpret_cast<uintptr_t>(A) % 2 != 0 || reinterpret_cast<uintptr_t>(B) % 2 != 0))
         return GEMM_ERR_ALIGN;
+    if (x.bias != nullptr && reinterpret_cast<uintptr_t>(x.bias) % 4 != 0) return GEMM_ERR_ALIGN;
+    uintptr_t c0, c1;
+    extent(C, M, N, ldc, osz, &c0, &c1);
     if (K > 0) {
-        uintptr_t c0, c1, a0, a1, b0, b1;
-        extent(C, M, N, ldc, osz, &c0, &c1);
+        uintptr_t a0, a1, b0, b1;
         extent(A, M, K, lda, 2, &a0, &a1);
-        extent(B, K, N, ldb, 2, &b0, &b1);
+        extent(B, b_rows, b_cols, ldb, 2, &b0, &b1);
         if (overlaps(c0, c1, a0, a1) || overlaps(c0, c1, b0, b1)) return GEMM_ERR_ALIAS;
+    }
+    if (x.bias != nullptr) {
+        const uintptr_t z0 = reinterpret_cast<uintptr_t>(x.bias), z1 = z0 + (uintptr_t)(4 * N);
+        if (overlaps(c0, c1, z0, z1)) return GEMM_ERR_ALIAS;
     }
     p->M = (int)M; p->N = (int)N; p->K = (int)K; p->dtype = dtype;
     p->A = static_cast<const uint16_t*>(A); p->lda = lda;
     p->B = static_cast<const uint16_t*>(B); p->ldb = ldb;
     p->C = const_cast<void*>(C); p->ldc = ldc;
-    p->vecA = (reinterpret_cast<uintptr_t>(A) % 16 == 0) && (lda % 8 == 0);
-    p->vecB = (reinterpret_cast<uintptr_t>(B) % 16 == 0) && (ldb % 8 == 0);
+    p->transB = tb;
+    p->alpha = x.alpha; p->beta = x.beta; p->bias = x.bias; p->relu = x.relu != 0;
+    p->epi = !(x.alpha == 1.0f && x.beta == 0.0f && x.bias == nullptr && x.relu == 0);
     return GEMM_OK;
 }
 
-int64_t tiles_for(int id, int64_t M, int64_t N) {
-    const dhpt::InstanceInfo& in = dhpt::kInstances[id];
-    return ((M + in.bm - 1) / in.bm) * ((N + in.bn - 1) / in.bn);
-}
+int64_t tiles_for(int tile, int64_t M, int64_t N) { return ((M + tile - 1) / tile) * ((N + tile - 1) / tile); }
 
 // Large (256x256) tiles when they still give at least half a wave over the
 // 256 CUs, otherwise 128x128 tiles.  Within a size, the first instance that
-// supports the problem: the direct-to-LDS kernel for whole tiles, its
-// clamped-edge form for any M and K with N a multiple of 8, and the
-// element-masked kernel for everything else.
+// supports the problem: whole tiles, then clamped edges (any M and K; N a
+// multiple of 8 for row-major B), then the fully masked fallback.
 int choose_instance(const Problem& p) {
-    static const int big_order[] = {10, 11, 2};
-    static const int mid_order[] = {14, 15, 3};
-    const bool big = tiles_for(0, p.M, p.N) >= 128;
-    const int* order = big ? big_order : mid_order;
+    static const int big_order[] = {0, 1, 2};
+    static const int mid_order[] = {3, 4, 5};
+    const int* order = tiles_for(256, p.M, p.N) >= 128 ? big_order : mid_order;
     for (int k = 0; k < 3; ++k)
         if (dhpt::instance_supports(order[k], p)) return order[k];
-    return big ? 2 : 3;
+    return order[2];
 }
 
 int enqueue(int id, const Problem& p, hipStream_t s) {
@@ -91,48 +105,83 @@ int enqueue(int id, const Problem& p, hipStream_t s) {
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
+// K == 0: the product is the zero matrix.  The plain form writes zeros; the
+// general form still has act(beta*C + bias) to evaluate, which the kernels do
+// with an empty k loop.
+int run_validated(int instance, const Problem& p, hipStream_t s) {
+    if (p.K == 0 && !p.epi) {
+        (void)hipGetLastError();
+        return dhpt::launch_zero_fill(p, s) == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+    }
+    if (instance < 0) instance = choose_instance(p);
+    else if (!dhpt::instance_supports(instance, p)) return GEMM_ERR_INSTANCE;
+    return enqueue(instance, p, s);
+}
+
+int run_any(int instance, int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
+            const void* B, int64_t ldb, void* C, int64_t ldc, const Extra& x, void* stream) {
+    Problem p;
+    bool noop;
+    int st = validate(M, N, K, dtype, A, lda, B, ldb, C, ldc, x, &p, &noop);
+    if (st != GEMM_OK || noop) return st;
+    return run_validated(instance, p, static_cast<hipStream_t>(stream));
+}
+
+int select_any(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda, const void* B,
+               int64_t ldb, const void* C, int64_t ldc, const Extra& x) {
+    Problem p;
+    bool noop;
+    int st = validate(M, N, K, dtype, A, lda, B, ldb, C, ldc, x, &p, &noop);
+    if (st != GEMM_OK) return st;
+    if (noop || (K == 0 && !p.epi)) return GEMM_OK;
+    return choose_instance(p);
+}
+
+Extra extra(int b_layout, float alpha, float beta, const float* bias, int relu) {
+    Extra x;
+    x.b_layout = b_layout; x.alpha = alpha; x.beta = beta; x.bias = bias; x.relu = relu;
+    return x;
+}
+
 }  // namespace
 
 extern "C" {
 
 int gemm_run(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
              const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
-    Problem p;
-    bool noop;
-    int st = validate(M, N, K, dtype, A, lda, B, ldb, C, ldc, &p, &noop);
-    if (st != GEMM_OK || noop) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (K == 0) {
-        (void)hipGetLastError();
-        return dhpt::launch_zero_fill(p, s) == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
-    }
-    return enqueue(choose_instance(p), p, s);
+    return run_any(-1, M, N, K, dtype, A, lda, B, ldb, C, ldc, Extra(), stream);
+}
+
+int gemm_run_ex(int64_t M, int64_t N, int64_t K, int dtype, int b_layout, const void* A, int64_t lda,
+                const void* B, int64_t ldb, void* C, int64_t ldc, float alpha, float beta,
+                const float* bias, int relu, void* stream) {
+    return run_any(-1, M, N, K, dtype, A, lda, B, ldb, C, ldc, extra(b_layout, alpha, beta, bias, relu),
+                   stream);
 }
 
 int gemm_run_instance(int instance, int64_t M, int64_t N, int64_t K, int dtype, const void* A,
                       int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
     if (instance < 0 || instance >= dhpt::kNumInstances) return GEMM_ERR_INSTANCE;
-    Problem p;
-    bool noop;
-    int st = validate(M, N, K, dtype, A, lda, B, ldb, C, ldc, &p, &noop);
-    if (st != GEMM_OK || noop) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (K == 0) {
-        (void)hipGetLastError();
-        return dhpt::launch_zero_fill(p, s) == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
-    }
-    if (!dhpt::instance_supports(instance, p)) return GEMM_ERR_INSTANCE;
-    return enqueue(instance, p, s);
+    return run_any(instance, M, N, K, dtype, A, lda, B, ldb, C, ldc, Extra(), stream);
+}
+
+int gemm_run_instance_ex(int instance, int64_t M, int64_t N, int64_t K, int dtype, int b_layout,
+                         const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                         float alpha, float beta, const float* bias, int relu, void* stream) {
+    if (instance < 0 || instance >= dhpt::kNumInstances) return GEMM_ERR_INSTANCE;
+    return run_any(instance, M, N, K, dtype, A, lda, B, ldb, C, ldc,
+                   extra(b_layout, alpha, beta, bias, relu), stream);
 }
 
 int gemm_select_instance(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
                          const void* B, int64_t ldb, const void* C, int64_t ldc) {
-    Problem p;
-    bool noop;
-    int st = validate(M, N, K, dtype, A, lda, B, ldb, C, ldc, &p, &noop);
-    if (st != GEMM_OK) return st;
-    if (noop || K == 0) return GEMM_OK;
-    return choose_instance(p);
+    return select_any(M, N, K, dtype, A, lda, B, ldb, C, ldc, Extra());
+}
+
+int gemm_select_instance_ex(int64_t M, int64_t N, int64_t K, int dtype, int b_layout, const void* A,
+                            int64_t lda, const void* B, int64_t ldb, const void* C, int64_t ldc,
+                            float alpha, float beta, const float* bias, int relu) {
+    return select_any(M, N, K, dtype, A, lda, B, ldb, C, ldc, extra(b_layout, alpha, beta, bias, relu));
 }
 
 int gemm_num_instances(void) { return dhpt::kNumInstances; }
@@ -147,9 +196,9 @@ int64_t gemm_tile_order(int instance, int64_t M, int64_t N, int32_t* tm, int32_t
     if (M < 0 || N < 0) return GEMM_ERR_DIM;
     if (M > kMaxDim || N > kMaxDim) return GEMM_ERR_RANGE;
     const dhpt::InstanceInfo& in = dhpt::kInstances[instance];
-    const int64_t tilesM = (M + in.bm - 1) / in.bm, tilesN = (N + in.bn - 1) / in.bn;
-    const int64_t T = tilesM * tilesN;
+    const int64_t T = tiles_for(in.tile, M, N);
     if (T > kMaxDim) return GEMM_ERR_RANGE;
+    const int64_t tilesM = (M + in.tile - 1) / in.tile, tilesN = (N + in.tile - 1) / in.tile;
     if (tm != nullptr && tn != nullptr) {
         const int64_t n = count < T ? count : T;
         for (int64_t w = 0; w < n; ++w) {
@@ -166,14 +215,16 @@ const char* gemm_strerror(int status) {
     switch (status) {
     case GEMM_OK: return "success";
     case GEMM_ERR_DIM: return "negative dimension";
-    case GEMM_ERR_LD: return "leading dimension smaller than the row length (lda < K, ldb < N or ldc < N)";
+    case GEMM_ERR_LD: return "leading dimension smaller than the row length (lda < K, ldb < N or ldc < N; "
+                             "ldb < K for column-major B)";
     case GEMM_ERR_NULL: return "null pointer for a non-empty operand";
     case GEMM_ERR_DTYPE: return "unknown dtype";
-    case GEMM_ERR_ALIAS: return "C overlaps A or B";
+    case GEMM_ERR_ALIAS: return "C overlaps A, B or the bias";
     case GEMM_ERR_RANGE: return "dimension or leading dimension out of the supported range";
     case GEMM_ERR_LAUNCH: return "kernel launch failed";
     case GEMM_ERR_ALIGN: return "pointer not aligned to its element size";
     case GEMM_ERR_INSTANCE: return "unknown instance, or instance cannot run this shape";
+    case GEMM_ERR_LAYOUT: return "unknown B layout";
     default: return "unknown status";
     }
 }

@@ -1,0 +1,503 @@
+// gemm_dl_kernel.h -- the direct-to-LDS MFMA kernel template for gfx950.
+// Included only by the instantiation units gemm_dl_*.hip.
+//
+// Per workgroup: 4 waves in a 2x2 grid, each owning a (BM/2) x (BN/2) fp32
+// accumulator tile built from v_mfma_f32_32x32x16_{f16,bf16}.  K is streamed
+// in 64-deep slices through two LDS stages:
+//   * global -> LDS with global_load_lds_dwordx4 (16 bytes per lane, 1 KiB
+//     per wave instruction, no VGPR staging), issued while the previous
+//     slice is multiplied -- the multi-stage copy pipeline of the Ada
+//     tensor-core GEMM write-up ("stages" section) and the acquire / copy /
+//     wait / release loop of "GEMM From Naive CUDA to Tensor Cores" ("Where
+//     asynchronous copies and TMA take over"), with vmcnt as the wait and one
+//     workgroup barrier per slice as both the publish and the release;
+//   * A stage: BM rows x 128 bytes (64 k); logical 16-byte chunk c of row r
+//     at physical chunk c ^ (r & 7) ^ ((r >> 3) & 1).  The XOR-of-chunks idea
+//     of "The Asynchronous Kernel: Tensor Cores & TMA" ("The XOR that unties
+//     the banks"), with the row function picked by measuring LDS read rates;
+//   * B stage, row-major B (K x N in memory): 64 rows x 2*BN bytes, row-major
+//     like global memory; chunk c of row k at c ^ 2(k & 3).  B fragments come
+//     from two ds_read_b64_tr_b16 each, which give lane l the 8 values of k
+//     for column l % 32 straight from the row-major tile (the transposing
+//     load of "mma.sync and ldmatrix", gfx950 form);
+//   * B stage, column-major B (BT, N x K in memory, the "TN" layout of the Ada
+//     write-up, section "A row-major (MxK), B column-major"): BN rows x 128
+//     bytes, copied and swizzled exactly like A; B fragments are then plain
+//     ds_read_b128 like A's;
+//   * A fragments: ds_read_b128 (8 consecutive k of one row);
+//   * issue order fixed in source (sched_barrier): one MFMA per slot followed
+//     by the slot's share of next-k-step reads and next-slice copies; the last
+//     FD k-steps of a slice run after the next barrier;
+//   * epilogue: fp32 -> output type with one rounding, stores masked at the
+//     M and N edges ("Turn global loads into shared tiles": predicate the
+//     store, not the barriers).  With EPI, the value stored is
+//     act(alpha * acc + beta * C_old + bias[col]) computed in fp32 before the
+//     one rounding (the fused bias + ReLU epilogue of the Ada write-up and
+//     the general C <- alpha*A*B + beta*C of the naive-to-tensor-core page);
+//     C_old is read only when beta != 0.
+//
+// EDGE modes:
+//   EDGE_NONE:  M % BM == N % BN == K % 64 == 0.
+//   EDGE_CLAMP: any M, K; any N for column-major B, N % 8 == 0 for row-major
+//     B.  Rows of A (and of column-major B) past the edge and 8-column chunks
+//     of row-major B past N are read from a clamped, valid address: those
+//     values only reach outputs that are never stored.  A partial last slice
+//     (K % 64 != 0) is filled through VGPRs with element-exact zero fill.
+//   EDGE_MASKED: any shape.  Every slice is filled through VGPRs with
+//     element-exact zero fill (no asynchronous copies, one stage); the
+//     fallback for row-major B with N % 8 != 0.
+// 16-byte loads from 2-byte-aligned addresses return the exact bytes on
+// gfx950 (pinned by a probe test), so misaligned rows and leading dimensions
+// stay on the vector paths.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "gemm_internal.h"
+
+namespace dhpt {
+namespace dl {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+enum { IN_F16 = 0, IN_BF16 = 1 };
+enum { OUT_F32 = 0, OUT_F16 = 1, OUT_BF16 = 2 };
+enum { EDGE_NONE = 0, EDGE_CLAMP = 1, EDGE_MASKED = 2 };
+
+template <int IN>
+__device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    if constexpr (IN == IN_F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+template <int OUT>
+__device__ __forceinline__ void store_out(void* C, int64_t idx, float v) {
+    if constexpr (OUT == OUT_F32)
+        static_cast<float*>(C)[idx] = v;
+    else if constexpr (OUT == OUT_F16)
+        static_cast<_Float16*>(C)[idx] = (_Float16)v;     // v_cvt_f16_f32: round to nearest even
+    else
+        static_cast<__bf16*>(C)[idx] = (__bf16)v;         // round to nearest even
+}
+
+template <int OUT>
+__device__ __forceinline__ float load_out(const void* C, int64_t idx) {
+    if constexpr (OUT == OUT_F32)
+        return static_cast<const float*>(C)[idx];
+    else if constexpr (OUT == OUT_F16)
+        return (float)static_cast<const _Float16*>(C)[idx];
+    else
+        return (float)static_cast<const __bf16*>(C)[idx];
+}
+
+__device__ __forceinline__ int swz_a(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz_b(int k) { return 2 * (k & 3); }
+
+// One global_load_lds_dwordx4 (this lane's 16 bytes at `src` to LDS byte
+// address lds_base + 16 * lane), issued through inline assembly so that the
+// compiler does not make every later LDS read wait for it; its completion is
+// awaited explicitly (vmcnt) before the barrier that publishes the stage.
+// M0 has no other user in this kernel.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(lds_base) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+#define DL_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// 8 consecutive 16-bit values p[c0 .. c0+7] of which those at index >= limit
+// read as zero; one 16-byte load when all 8 exist.
+__device__ __forceinline__ u32x4 load8_masked(const uint16_t* p, int c0, int limit) {
+    if (c0 + 8 <= limit) return *reinterpret_cast<const u32x4*>(p + c0);
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = (c0 + e < limit) ? (uint32_t)p[c0 + e] : 0u;
+    return u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+}
+
+// The epilogue operands of the general form (unused by the plain kernels).
+struct EpiArgs {
+    float alpha, beta;
+    const float* bias;         // N values, or null
+    int relu;
+};
+
+template <int IN, int OUT, int BM, int BN, int FD, int EDGE, bool BT, bool EPI>
+__global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
+    void* __restrict__ C, int64_t ldc, int M, int N, int K, int tilesM, int tilesN, int group_m,
+    EpiArgs ep) {
+    static_assert((BM == 256 && BN == 256) || (BM == 128 && BN == 128), "tile");
+    static_assert(FD == 1 || FD == 2, "fragment prefetch distance");
+    constexpr int BK = 64, KSTEPS = 4;
+    constexpr int WM = BM / 2, WN = BN / 2;               // wave tile
+    constexpr int TM = WM / 32, TN = WN / 32;             // MFMA blocks per wave
+    constexpr int S = TM * TN;                            // MFMAs (issue slots) per k-step
+    constexpr int NBR = BT ? TN : 2 * TN;                 // B reads per k-step
+    constexpr int R = TM + NBR;                           // LDS reads per k-step
+    constexpr int A_BYTES = BM * 128, BROW = 2 * BN, B_BYTES = BK * BROW;   // BT: BN * 128, same
+    constexpr int STAGE = A_BYTES + B_BYTES;
+    constexpr int NSTAGE = EDGE == EDGE_MASKED ? 1 : 2;
+    constexpr int CA = BM / 32, CB = BN / 32;             // copies per wave per slice (1 KiB each)
+    constexpr int COPIES = CA + CB;
+    constexpr int B_ROWS_PER_COPY = 1024 / BROW;          // row-major B: 2 (BN 256) or 4 (BN 128)
+    constexpr int B_CHUNKS = BN / 8;                      // row-major B: 16-byte chunks per row
+    constexpr int NB = (FD == 1) ? 2 : 4;                 // fragment buffers
+    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
+    const uint32_t smem_base = (uint32_t)(size_t)(lds_char*)smem;
+
+    const int t = threadIdx.x;
+    const int l = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = w >> 1, wn = w & 1;
+
+    int tm, tn;
+    tile_coords(blockIdx.x, tilesM, tilesN, group_m, &tm, &tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    // Copy sources.  A copy i of wave w fills stage rows (BM/4)w + 8i + l/8,
+    // physical chunk l%8; column-major B the same over its BN rows.
+    // Row-major B copy i fills rows 16w + B_ROWS_PER_COPY*i + l/B_CHUNKS,
+    // physical chunk l%B_CHUNKS.
+    const uint16_t* a_src[CA];
+    const uint16_t* b_src[CB];
+    int64_t b_step = BK;
+    uint32_t dma_a = 0, dma_b = 0;
+    if constexpr (EDGE != EDGE_MASKED) {
+#pragma unroll
+        for (int i = 0; i < CA; ++i) {
+            const int r = (BM / 4) * w + 8 * i + (l >> 3);
+            int grow = m0 + r;
+            if constexpr (EDGE == EDGE_CLAMP) grow = grow < M ? grow : M - 1;
+            a_src[i] = A + (int64_t)grow * lda + 8 * ((l & 7) ^ swz_a(r));
+        }
+#pragma unroll
+        for (int i = 0; i < CB; ++i) {
+            if constexpr (BT) {
+                const int r = (BN / 4) * w + 8 * i + (l >> 3);
+                int gcol = n0 + r;
+                if constexpr (EDGE == EDGE_CLAMP) gcol = gcol < N ? gcol : N - 1;
+                b_src[i] = B + (int64_t)gcol * ldb + 8 * ((l & 7) ^ swz_a(r));
+            } else {
+                const int kr = 16 * w + B_ROWS_PER_COPY * i + l / B_CHUNKS;
+                int col = n0 + 8 * ((l % B_CHUNKS) ^ swz_b(kr));
+                if constexpr (EDGE == EDGE_CLAMP) col = col + 8 <= N ? col : N - 8;
+                b_src[i] = B + (int64_t)kr * ldb + col;
+            }
+        }
+        if constexpr (!BT) b_step = (int64_t)BK * ldb;
+        dma_a = smem_base + ((BM / 4) * w) * 128;
+        dma_b = smem_base + A_BYTES + (BT ? ((BN / 4) * w) * 128 : (16 * w) * BROW);
+    }
+
+    // Fragment read offsets (bytes within a stage).
+    const int a_off0 = (wm * WM + (l & 31)) * 128;
+    const int a_sw = swz_a(l & 31);
+    const int g = l >> 4, ip = l & 15;
+    const int b_sw = swz_b(ip >> 2);
+    int b_off[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        if constexpr (BT) {
+            b_off[j] = A_BYTES + (wn * WN + 32 * j + (l & 31)) * 128;
+        } else {
+            const int n = wn * WN + 32 * j + 16 * (g & 1) + 4 * (ip & 3);
+            b_off[j] = A_BYTES + (8 * (g >> 1) + (ip >> 2)) * BROW + (((n >> 3) ^ b_sw) * 16) + (n & 7) * 2;
+        }
+    }
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    u32x4 fa[NB][TM];
+    u32x4 fbt[NB][TN];            // column-major B fragments
+    s16x4 fbh[NB][TN][2];         // row-major B fragments (two transposing reads each)
+
+    // LDS read q (0 .. R-1) of k-step s, in consumption order: A0, then B
+    // (B0 .. B(TN-1), each as lo/hi for row-major B), then A1 .. A(TM-1).
+    auto read_piece = [&](int stage, int s, int buf, int q) {
+        const char* st = smem + stage * STAGE;
+        const int chunk = (2 * s + (l >> 5)) ^ a_sw;      // A rows and column-major B rows alike
+        if (q == 0 || q > NBR) {
+            const int i = (q == 0) ? 0 : q - NBR;
+            fa[buf][i] = *reinterpret_cast<const u32x4*>(st + a_off0 + i * 32 * 128 + chunk * 16);
+        } else if constexpr (BT) {
+            const int j = q - 1;
+            fbt[buf][j] = *reinterpret_cast<const u32x4*>(st + b_off[j] + chunk * 16);
+        } else {
+            const int j = (q - 1) >> 1, h = (q - 1) & 1;
+            const int off = b_off[j] + 16 * s * BROW + h * 4 * BROW;
+            fbh[buf][j][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)((const lds_char*)st + off));
+        }
+    };
+    auto issue_copy = [&](int stage, int i) {
+        if (i < 0 || i >= COPIES) return;              // never taken: callers pass 0 .. COPIES-1
+        if (i < CA) {
+            lds_dma16(a_src[i], dma_a + stage * STAGE + 1024 * i);
+            a_src[i] += BK;
+        } else {
+            lds_dma16(b_src[i - CA], dma_b + stage * STAGE + 1024 * (i - CA));
+            b_src[i - CA] += b_step;
+        }
+    };
+    auto mfma1 = [&](int buf, int q) {                 // MFMA q of a k-step: A block q/TN, B block q%TN
+        const int i = q / TN, j = q % TN;
+        if constexpr (BT) {
+            acc[i][j] = mfma<IN>(fa[buf][i], fbt[buf][j], acc[i][j]);
+        } else {
+            const u32x2 lo = __builtin_bit_cast(u32x2, fbh[buf][j][0]);
+            const u32x2 hi = __builtin_bit_cast(u32x2, fbh[buf][j][1]);
+            acc[i][j] = mfma<IN>(fa[buf][i], u32x4{lo[0], lo[1], hi[0], hi[1]}, acc[i][j]);
+        }
+    };
+
+    // Slice kt through VGPRs: every lane loads its share of the A and B
+    // tiles with zero fill beyond M, N and K and writes it into the stage
+    // layout (the partial last slice of EDGE_CLAMP, every slice of
+    // EDGE_MASKED).
+    auto fill_slice = [&](int stage, int kt) {
+        char* st = smem + stage * STAGE;
+        const int k0 = kt * BK;
+#pragma unroll
+        for (int r = 0; r < BM / 32; ++r) {            // A: BM rows x 8 chunks
+            const int row = (t >> 3) + 32 * r, c = t & 7;
+            const int grow = m0 + row;
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (grow < M) v = load8_masked(A + (int64_t)grow * lda + k0, 8 * c, K - k0);
+            *reinterpret_cast<u32x4*>(st + row * 128 + 16 * (c ^ swz_a(row))) = v;
+        }
+        if constexpr (BT) {
+#pragma unroll
+            for (int r = 0; r < BN / 32; ++r) {        // column-major B: BN rows x 8 chunks
+                const int row = (t >> 3) + 32 * r, c = t & 7;
+                const int gcol = n0 + row;
+                u32x4 v = u32x4{0u, 0u, 0u, 0u};
+                if (gcol < N) v = load8_masked(B + (int64_t)gcol * ldb + k0, 8 * c, K - k0);
+                *reinterpret_cast<u32x4*>(st + A_BYTES + row * 128 + 16 * (c ^ swz_a(row))) = v;
+            }
+        } else {
+            constexpr int ROWS_PER_PASS = 256 / B_CHUNKS;
+#pragma unroll
+            for (int r = 0; r < BK / ROWS_PER_PASS; ++r) {  // row-major B: 64 rows x B_CHUNKS chunks
+                const int row = t / B_CHUNKS + ROWS_PER_PASS * r, c = t % B_CHUNKS;
+                const int gk = k0 + row, col = n0 + 8 * c;
+                u32x4 v = u32x4{0u, 0u, 0u, 0u};
+                if (gk < K && col < N) v = load8_masked(B + (int64_t)gk * ldb, col, N);
+                *reinterpret_cast<u32x4*>(st + A_BYTES + row * BROW + 16 * (c ^ swz_b(row))) = v;
+            }
+        }
+    };
+    // One filled slice, unpipelined: the reads of each k-step, then its MFMAs.
+    auto compute_slice = [&](int stage) {
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+#pragma unroll
+            for (int x = 0; x < R; ++x) read_piece(stage, s, 0, x);
+#pragma unroll
+            for (int q = 0; q < S; ++q) mfma1(0, q);
+        }
+    };
+
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
+
+    // `NS` issue slots (S or 2S): slot q runs MFMA q % S of the k-step held in
+    // buffer mb[q / S], then its share of the reads of k-step rs[q / S] (into
+    // buffer rb[q / S]) and, with do_copy, its share of the next slice's
+    // COPIES copies.  All counts and indices are compile-time constants once
+    // the calls are inlined, so every register-array index is too.
+    auto block = [&](auto do_mfma, int mb0, int mb1, int rstage, int rs0, int rs1, int rb0, int rb1,
+                     auto do_copy, int cstage, auto nslots_c) {
+        constexpr int NS = decltype(nslots_c)::value;
+#pragma unroll
+        for (int q = 0; q < NS; ++q) {
+            const int sub = q / S, qq = q % S;
+            if constexpr (decltype(do_mfma)::value) mfma1(sub ? mb1 : mb0, qq);
+#pragma unroll
+            for (int x = qq * R / S; x < (qq + 1) * R / S; ++x)
+                read_piece(rstage, sub ? rs1 : rs0, sub ? rb1 : rb0, x);
+            if constexpr (decltype(do_copy)::value) {
+#pragma unroll
+                for (int c = q * COPIES / NS; c < (q + 1) * COPIES / NS; ++c) issue_copy(cstage, c);
+            }
+            DL_FENCE();
+        }
+    };
+
+    // One slice of the pipeline over full slices: barrier (copies of slice kt
+    // visible everywhere, slice kt-1 read by everyone), then the previous
+    // slice's last FD k-steps with this slice's first reads and, with
+    // do_copy, the copies of slice kt+1; then the remaining k-steps, each
+    // interleaved with the reads FD k-steps ahead.
+    auto slice = [&](int kt, auto has_prev, auto do_copy) {
+        const int stage = kt & 1, nstage = stage ^ 1;
+        wait_copies();                  // this wave's copies of slice kt have landed
+        __syncthreads();                // everyone's; slice kt-1 is fully read
+        DL_FENCE();
+        using one = std::integral_constant<int, S>;
+        using two = std::integral_constant<int, 2 * S>;
+        if constexpr (FD == 1) {
+            // post-barrier block: previous slice's k-step 3 (buffer 1), reads of k-step 0 (buffer 0)
+            block(has_prev, 1, 1, stage, 0, 0, 0, 0, do_copy, nstage, one{});
+            block(yes{}, 0, 0, stage, 1, 1, 1, 1, no{}, nstage, one{});
+            block(yes{}, 1, 1, stage, 2, 2, 0, 0, no{}, nstage, one{});
+            block(yes{}, 0, 0, stage, 3, 3, 1, 1, no{}, nstage, one{});
+        } else {
+            // post-barrier block: previous slice's k-steps 2, 3 (buffers 2, 3),
+            // reads of k-steps 0, 1 (buffers 0, 1)
+            block(has_prev, 2, 3, stage, 0, 1, 0, 1, do_copy, nstage, two{});
+            block(yes{}, 0, 0, stage, 2, 2, 2, 2, no{}, nstage, one{});
+            block(yes{}, 1, 1, stage, 3, 3, 3, 3, no{}, nstage, one{});
+        }
+    };
+
+    if constexpr (EDGE == EDGE_MASKED) {
+        const int nk = (K + BK - 1) / BK;
+        for (int kt = 0; kt < nk; ++kt) {
+            __syncthreads();            // every wave is done reading the previous slice
+            fill_slice(0, kt);
+            __syncthreads();
+            compute_slice(0);
+        }
+    } else {
+        const int nk_full = K / BK;
+        if (nk_full > 0) {
+#pragma unroll
+            for (int i = 0; i < COPIES; ++i) issue_copy(0, i);          // slice 0 into stage 0
+            if (nk_full == 1) {
+                slice(0, no{}, no{});
+            } else {
+                slice(0, no{}, yes{});
+                for (int kt = 1; kt < nk_full - 1; ++kt) slice(kt, yes{}, yes{});     // steady state
+                slice(nk_full - 1, yes{}, no{});
+            }
+            // the last FD k-steps of the last full slice
+            if constexpr (FD == 2) {
+#pragma unroll
+                for (int q = 0; q < S; ++q) mfma1(2, q);
+#pragma unroll
+                for (int q = 0; q < S; ++q) mfma1(3, q);
+            } else {
+#pragma unroll
+                for (int q = 0; q < S; ++q) mfma1(1, q);
+            }
+        }
+        if constexpr (EDGE == EDGE_CLAMP) {
+            if (K % BK != 0) {
+                // the partial last slice: zero-filled through VGPRs, then its
+                // four k-steps without pipelining (at most one slice in K / 64)
+                const int stage = nk_full & 1;
+                __syncthreads();        // every wave is done reading the stage being refilled
+                fill_slice(stage, nk_full);
+                __syncthreads();
+                compute_slice(stage);
+            }
+        }
+    }
+
+    const int gl = l >> 5;
+    float bias_v[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        bias_v[j] = 0.0f;
+        if constexpr (EPI) {
+            const int col = n0 + wn * WN + 32 * j + (l & 31);
+            if (ep.bias != nullptr && (EDGE == EDGE_NONE || col < N)) bias_v[j] = ep.bias[col];
+        }
+    }
+    // The beta test is uniform: take it once, outside the element loops.
+    auto store_tile = [&](auto read_old) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int col = n0 + wn * WN + 32 * j + (l & 31);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int row = m0 + wm * WM + 32 * i + 8 * (e >> 2) + 4 * gl + (e & 3);
+                    if (EDGE == EDGE_NONE || (row < M && col < N)) {
+                        const int64_t idx = (int64_t)row * ldc + col;
+                        float v = acc[i][j][e];
+                        if constexpr (EPI) {
+                            v = ep.alpha * v;
+                            if constexpr (decltype(read_old)::value) v = fmaf(ep.beta, load_out<OUT>(C, idx), v);
+                            v += bias_v[j];
+                            if (ep.relu && v < 0.0f) v = 0.0f;
+                        }
+                        store_out<OUT>(C, idx, v);
+                    }
+                }
+            }
+        }
+    };
+    if (EPI && ep.beta != 0.0f)
+        store_tile(yes{});
+    else
+        store_tile(no{});
+}
+
+template <int IN, int OUT, int BM, int BN, int FD, int EDGE, bool BT, bool EPI>
+static void launch_typed(const Problem& p, int group_m, hipStream_t s) {
+    const int tilesM = (p.M + BM - 1) / BM, tilesN = (p.N + BN - 1) / BN;
+    const EpiArgs ep{p.alpha, p.beta, p.bias, p.relu};
+    hipLaunchKernelGGL((gemm_dl_kernel<IN, OUT, BM, BN, FD, EDGE, BT, EPI>), dim3((unsigned)(tilesM * tilesN)),
+                       dim3(256), 0, s, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, p.M, p.N, p.K, tilesM, tilesN,
+                       group_m, ep);
+}
+
+template <int BM, int BN, int FD, int EDGE, bool BT, bool EPI>
+static hipError_t launch_dtype(const Problem& p, int group_m, hipStream_t s) {
+    switch (p.dtype) {
+    case 0: launch_typed<IN_F16, OUT_F32, BM, BN, FD, EDGE, BT, EPI>(p, group_m, s); break;
+    case 1: launch_typed<IN_F16, OUT_F16, BM, BN, FD, EDGE, BT, EPI>(p, group_m, s); break;
+    case 2: launch_typed<IN_BF16, OUT_F32, BM, BN, FD, EDGE, BT, EPI>(p, group_m, s); break;
+    default: launch_typed<IN_BF16, OUT_BF16, BM, BN, FD, EDGE, BT, EPI>(p, group_m, s); break;
+    }
+    return hipGetLastError();
+}
+
+// All tile sizes and edge modes for one (FD, BT, EPI) combination.  The
+// masked mode does not pipeline, so it exists only once, under FD == 2.
+template <int FD, bool BT, bool EPI>
+static hipError_t launch_family(int tile, int edge, const Problem& p, int group_m, hipStream_t s) {
+    if (edge == EDGE_MASKED) {
+        if constexpr (FD == 2) {
+            return tile == 256 ? launch_dtype<256, 256, 2, EDGE_MASKED, BT, EPI>(p, group_m, s)
+                               : launch_dtype<128, 128, 2, EDGE_MASKED, BT, EPI>(p, group_m, s);
+        } else {
+            return hipErrorInvalidValue;
+        }
+    }
+    if (tile == 256)
+        return edge == EDGE_NONE ? launch_dtype<256, 256, FD, EDGE_NONE, BT, EPI>(p, group_m, s)
+                                 : launch_dtype<256, 256, FD, EDGE_CLAMP, BT, EPI>(p, group_m, s);
+    return edge == EDGE_NONE ? launch_dtype<128, 128, FD, EDGE_NONE, BT, EPI>(p, group_m, s)
+                             : launch_dtype<128, 128, FD, EDGE_CLAMP, BT, EPI>(p, group_m, s);
+}
+
+}  // namespace dl
+}  // namespace dhpt

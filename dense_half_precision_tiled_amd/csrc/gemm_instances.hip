@@ -1,0 +1,71 @@
+// gemm_instances.hip -- the instance table of the direct-to-LDS kernel family,
+// what each instance can run, its launch, and the K == 0 fill.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_internal.h"
+
+namespace dhpt {
+
+// Every instance walks the output tiles in the XCD-aware grouped order of
+// tile_coords with groups of 8 tile-rows.
+const InstanceInfo kInstances[] = {
+    {"dl_256x256x64_fd2", 256, 2, EDGE_NONE, 8},
+    {"dl_256x256x64_fd2_clamp", 256, 2, EDGE_CLAMP, 8},
+    {"dl_256x256x64_masked", 256, 2, EDGE_MASKED, 8},
+    {"dl_128x128x64_fd2", 128, 2, EDGE_NONE, 8},
+    {"dl_128x128x64_fd2_clamp", 128, 2, EDGE_CLAMP, 8},
+    {"dl_128x128x64_masked", 128, 2, EDGE_MASKED, 8},
+    {"dl_256x256x64_fd1", 256, 1, EDGE_NONE, 8},
+    {"dl_256x256x64_fd1_clamp", 256, 1, EDGE_CLAMP, 8},
+    {"dl_128x128x64_fd1", 128, 1, EDGE_NONE, 8},
+    {"dl_128x128x64_fd1_clamp", 128, 1, EDGE_CLAMP, 8},
+};
+const int kNumInstances = sizeof(kInstances) / sizeof(kInstances[0]);
+
+bool instance_supports(int id, const Problem& p) {
+    if (id < 0 || id >= kNumInstances) return false;
+    const InstanceInfo& in = kInstances[id];
+    if (in.fd == 1 && (p.transB || p.epi)) return false;      // compiled for plain row-major B only
+    switch (in.edge) {
+    case EDGE_NONE: return p.M % in.tile == 0 && p.N % in.tile == 0 && p.K % 64 == 0;
+    case EDGE_CLAMP: return p.transB || (p.N % 8 == 0 && p.N >= 8);
+    case EDGE_MASKED: return true;
+    default: return false;
+    }
+}
+
+hipError_t launch_instance(int id, const Problem& p, hipStream_t s) {
+    const InstanceInfo& in = kInstances[id];
+    if (p.transB)
+        return p.epi ? launch_dl_tn_epi(in.tile, in.fd, in.edge, p, in.group_m, s)
+                     : launch_dl_tn(in.tile, in.fd, in.edge, p, in.group_m, s);
+    return p.epi ? launch_dl_nn_epi(in.tile, in.fd, in.edge, p, in.group_m, s)
+                 : launch_dl_nn(in.tile, in.fd, in.edge, p, in.group_m, s);
+}
+
+// C = 0 over the M x N region (K == 0 with the plain epilogue).
+template <typename T>
+__global__ __launch_bounds__(256) void zero_fill_kernel(T* C, int64_t ldc, int M, int N) {
+    const int64_t total = (int64_t)M * N;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i = idx / N, j = idx - i * N;
+        C[i * ldc + j] = T(0);
+    }
+}
+
+hipError_t launch_zero_fill(const Problem& p, hipStream_t s) {
+    const int64_t total = (int64_t)p.M * p.N;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    const dim3 grid((unsigned)blocks), block(256);
+    if (p.dtype == 0 || p.dtype == 2)
+        hipLaunchKernelGGL(zero_fill_kernel<float>, grid, block, 0, s, static_cast<float*>(p.C), p.ldc, p.M, p.N);
+    else
+        hipLaunchKernelGGL(zero_fill_kernel<uint16_t>, grid, block, 0, s, static_cast<uint16_t*>(p.C), p.ldc,
+                           p.M, p.N);
+    return hipGetLastError();
+}
+
+}  // namespace dhpt

@@ -1,5 +1,6 @@
-// gemm_internal.h -- shared between the C-ABI layer (gemm_api.cpp) and the
-// kernels (gemm_kernels.hip).  Not installed; callers use include/gemm.h.
+// gemm_internal.h -- shared between the C-ABI layer (gemm_api.cpp), the
+// instance table (gemm_instances.hip) and the kernel instantiation units
+// (gemm_dl_*.hip).  Not installed; callers use include/gemm.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -14,39 +15,45 @@ struct Problem {
     const uint16_t* A; int64_t lda;
     const uint16_t* B; int64_t ldb;
     void* C; int64_t ldc;
-    bool vecA, vecB;           // 16-byte aligned base and leading dimension
+    bool transB;               // B stored column-major: B(k, j) at B[j*ldb + k]
+    bool epi;                  // general epilogue (anything but alpha 1, beta 0, no bias, no ReLU)
+    float alpha, beta;
+    const float* bias;         // N fp32 values or null
+    int relu;
 };
 
-// What an instance requires of the problem.
-enum Requirement {
-    REQ_ANY = 0,               // any shape, any alignment (element-masked edges)
-    REQ_TILE_VEC = 1,          // M % bm, N % bn, K % bk == 0 and 16-byte aligned A, B rows
-    REQ_TILE = 2,              // M % bm, N % bn, K % bk == 0 (any 2-byte alignment)
-    REQ_N8 = 3,                // N % 8 == 0 and N >= 8 (clamped edges, zero-filled K tail)
+// Edge handling of an instance (the EDGE modes of gemm_dl_kernel.h).
+enum EdgeMode {
+    EDGE_NONE = 0,             // M % tile, N % tile, K % 64 == 0
+    EDGE_CLAMP = 1,            // any M, K; N % 8 == 0 for row-major B, any N for column-major B
+    EDGE_MASKED = 2,           // any shape
 };
 
-// One compiled tile geometry.  Every instance computes the same function.
+// One compiled tile geometry of the direct-to-LDS family.  Every instance
+// computes the same function with the same per-element operation order.
 struct InstanceInfo {
     const char* name;
-    int bm, bn, bk;            // workgroup tile
-    bool edge;                 // handles partial tiles (masked stores)
+    int tile;                  // square workgroup tile: 256 or 128 (k-slice 64)
+    int fd;                    // fragment prefetch distance in k-steps: 1 or 2
+    int edge;                  // EdgeMode
     int group_m;               // tile-rows per group of the visit order
-    int req;                   // Requirement
 };
 
 extern const InstanceInfo kInstances[];
 extern const int kNumInstances;
 
-// True when instance `id` can run problem `p` (shape multiple of its tile and
-// vector-aligned operands, or an edge instance).
+// True when instance `id` can run problem `p`.
 bool instance_supports(int id, const Problem& p);
 
 hipError_t launch_instance(int id, const Problem& p, hipStream_t stream);
-
-// The direct-to-LDS family (gemm_dl.hip): tile 256 or 128, fragment prefetch
-// distance 1 or 2, edge handling on or off.
-hipError_t launch_dl(int tile, int fd, bool edge, const Problem& p, int group_m, hipStream_t stream);
 hipError_t launch_zero_fill(const Problem& p, hipStream_t stream);
+
+// The instantiation units of gemm_dl_kernel.h: row-major / column-major B,
+// plain / general epilogue.  Only launch_dl_nn has fd == 1 kernels.
+hipError_t launch_dl_nn(int tile, int fd, int edge, const Problem& p, int group_m, hipStream_t stream);
+hipError_t launch_dl_nn_epi(int tile, int fd, int edge, const Problem& p, int group_m, hipStream_t stream);
+hipError_t launch_dl_tn(int tile, int fd, int edge, const Problem& p, int group_m, hipStream_t stream);
+hipError_t launch_dl_tn_epi(int tile, int fd, int edge, const Problem& p, int group_m, hipStream_t stream);
 
 // Workgroup id -> output tile (tm, tn).
 //

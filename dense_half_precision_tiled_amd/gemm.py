@@ -1,9 +1,10 @@
 """Python binding of libdhpt_gemm.so (argument marshalling only).
 
-The functions mirror include/gemm.h one to one (``gemm_run``,
-``gemm_strerror``, ``gemm_select_instance``, ``gemm_num_instances``,
-``gemm_instance_name``, ``gemm_run_instance``, ``gemm_tile_order``) and take
-raw device pointers as Python ints.  ``gemm(A, B, out_dtype)`` is the
+The functions mirror include/gemm.h one to one (``gemm_run``, ``gemm_run_ex``,
+``gemm_strerror``, ``gemm_select_instance``, ``gemm_select_instance_ex``,
+``gemm_num_instances``, ``gemm_instance_name``, ``gemm_run_instance``,
+``gemm_run_instance_ex``, ``gemm_tile_order``) and take raw device pointers as
+Python ints.  ``gemm(A, B, out_dtype)`` is the
 convenience form on torch tensors: it allocates C with ``torch.empty`` and
 passes ``data_ptr()``, the row strides and the current HIP stream.
 
@@ -23,10 +24,12 @@ GEMM_F16_F32, GEMM_F16_F16, GEMM_BF16_F32, GEMM_BF16_BF16 = 0, 1, 2, 3
 GEMM_OK = 0
 GEMM_ERR_DIM, GEMM_ERR_LD, GEMM_ERR_NULL, GEMM_ERR_DTYPE = -1, -2, -3, -4
 GEMM_ERR_ALIAS, GEMM_ERR_RANGE, GEMM_ERR_LAUNCH, GEMM_ERR_ALIGN = -5, -6, -7, -8
-GEMM_ERR_INSTANCE = -9
+GEMM_ERR_INSTANCE, GEMM_ERR_LAYOUT = -9, -10
+GEMM_B_ROW_MAJOR, GEMM_B_COL_MAJOR = 0, 1
 
-EXPORTED = ["gemm_run", "gemm_strerror", "gemm_select_instance", "gemm_num_instances",
-            "gemm_instance_name", "gemm_run_instance", "gemm_tile_order"]
+EXPORTED = ["gemm_run", "gemm_run_ex", "gemm_strerror", "gemm_select_instance",
+            "gemm_select_instance_ex", "gemm_num_instances", "gemm_instance_name",
+            "gemm_run_instance", "gemm_run_instance_ex", "gemm_tile_order"]
 
 _lib = None
 
@@ -49,6 +52,15 @@ def load() -> ctypes.CDLL:
         lib.gemm_run.restype = i32
         lib.gemm_run_instance.argtypes = [i32, i64, i64, i64, i32, vp, i64, vp, i64, vp, i64, vp]
         lib.gemm_run_instance.restype = i32
+        f32 = ctypes.c_float
+        lib.gemm_run_ex.argtypes = [i64, i64, i64, i32, i32, vp, i64, vp, i64, vp, i64, f32, f32, vp,
+                                    i32, vp]
+        lib.gemm_run_ex.restype = i32
+        lib.gemm_run_instance_ex.argtypes = [i32] + lib.gemm_run_ex.argtypes
+        lib.gemm_run_instance_ex.restype = i32
+        lib.gemm_select_instance_ex.argtypes = [i64, i64, i64, i32, i32, vp, i64, vp, i64, vp, i64,
+                                                f32, f32, vp, i32]
+        lib.gemm_select_instance_ex.restype = i32
         lib.gemm_select_instance.argtypes = [i64, i64, i64, i32, vp, i64, vp, i64, vp, i64]
         lib.gemm_select_instance.restype = i32
         lib.gemm_strerror.argtypes = [i32]
@@ -74,6 +86,24 @@ def gemm_run_instance(instance, M, N, K, dtype, A, lda, B, ldb, C, ldc, stream=N
 
 def gemm_select_instance(M, N, K, dtype, A, lda, B, ldb, C, ldc) -> int:
     return load().gemm_select_instance(M, N, K, dtype, A, lda, B, ldb, C, ldc)
+
+
+def gemm_run_ex(M, N, K, dtype, b_layout, A, lda, B, ldb, C, ldc, alpha=1.0, beta=0.0, bias=None,
+                relu=0, stream=None) -> int:
+    return load().gemm_run_ex(M, N, K, dtype, b_layout, A, lda, B, ldb, C, ldc, alpha, beta, bias,
+                              relu, stream)
+
+
+def gemm_run_instance_ex(instance, M, N, K, dtype, b_layout, A, lda, B, ldb, C, ldc, alpha=1.0,
+                         beta=0.0, bias=None, relu=0, stream=None) -> int:
+    return load().gemm_run_instance_ex(instance, M, N, K, dtype, b_layout, A, lda, B, ldb, C, ldc,
+                                       alpha, beta, bias, relu, stream)
+
+
+def gemm_select_instance_ex(M, N, K, dtype, b_layout, A, lda, B, ldb, C, ldc, alpha=1.0, beta=0.0,
+                            bias=None, relu=0) -> int:
+    return load().gemm_select_instance_ex(M, N, K, dtype, b_layout, A, lda, B, ldb, C, ldc, alpha,
+                                          beta, bias, relu)
 
 
 def gemm_strerror(status: int) -> str:

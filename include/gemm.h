@@ -48,9 +48,19 @@ enum {
                                than 2^31-1 output tiles */
     GEMM_ERR_LAUNCH = -7,   /* the HIP runtime rejected the kernel launch */
     GEMM_ERR_ALIGN = -8,    /* a pointer not aligned to its element size */
-    GEMM_ERR_INSTANCE = -9  /* gemm_run_instance: unknown id, or the instance
+    GEMM_ERR_INSTANCE = -9, /* gemm_run_instance: unknown id, or the instance
                                cannot handle this shape/alignment */
+    GEMM_ERR_LAYOUT = -10   /* gemm_run_ex: b_layout not one of gemm_layout_t */
 };
+
+/* Storage order of B for gemm_run_ex (A and C are always row-major). */
+typedef enum {
+    GEMM_B_ROW_MAJOR = 0,   /* B(k,j) at B[k*ldb + j], ldb >= N (gemm_run's layout) */
+    GEMM_B_COL_MAJOR = 1    /* B(k,j) at B[j*ldb + k], ldb >= K: B stored column-major,
+                               i.e. its N x K transpose row-major -- the "TN" layout the
+                               Ada tensor-core GEMM write-up builds on (section "A
+                               row-major (MxK), B column-major") */
+} gemm_layout_t;
 
 /*
  * gemm_run -- enqueue C = A.B on `stream`.
@@ -74,9 +84,11 @@ enum {
  * Sizes: M == 0 or N == 0 is a successful no-op.  K == 0 writes zeros to the
  * M x N region (the product of an M x 0 and a 0 x N matrix).
  *
- * Alignment: only natural element alignment is required.  Leading dimensions
- * and base pointers that are multiples of 16 bytes select the vector-load
- * kernels; anything else runs on the element-masked edge kernels.
+ * Alignment: only natural element alignment is required (2 bytes for A and B;
+ * 4 or 2 bytes for C).  Whole 256x256 (or 128x128) tiles with K a multiple of
+ * 64 run without edge code; other shapes with N a multiple of 8 run with
+ * clamped edge loads and a zero-filled last k-slice; any other N runs on a
+ * fully masked fallback.
  *
  * Returns GEMM_OK once the kernel is enqueued (asynchronous: device faults
  * surface at the caller's next synchronisation), or a GEMM_ERR_* code.
@@ -84,6 +96,40 @@ enum {
 int gemm_run(int64_t M, int64_t N, int64_t K, int dtype,
              const void* A, int64_t lda, const void* B, int64_t ldb,
              void* C, int64_t ldc, void* stream);
+
+/*
+ * gemm_run_ex -- the general form with a fused epilogue, enqueued on `stream`:
+ *
+ *     C[i*ldc + j] <- act( alpha * sum_k A[i*lda + k] * B(k, j)
+ *                          + beta * C[i*ldc + j] + bias[j] )
+ *
+ * for 0 <= i < M, 0 <= j < N: the general C <- alpha*A*B + beta*C that "GEMM
+ * From Naive CUDA to Tensor Cores" opens with, plus the per-column bias and
+ * ReLU that the Ada tensor-core GEMM write-up folds into the epilogue (section
+ * on the fused bias + ReLU epilogue).  The dot product is accumulated in fp32;
+ * the epilogue runs in fp32 on that accumulator (alpha * acc, then
+ * + beta * C_old as a fused multiply-add, then + bias[j], then ReLU) and the
+ * result is rounded once to the output type.
+ *
+ *   b_layout   a gemm_layout_t value: B(k, j) = B[k*ldb + j] (row-major,
+ *              ldb >= N) or B[j*ldb + k] (column-major, ldb >= K).
+ *   alpha      scale of the product.
+ *   beta       scale of the old output.  With beta == 0 the old contents of
+ *              C are never read (they may hold anything, NaN included);
+ *              otherwise C is read in its output type before it is written.
+ *   bias       device pointer to N fp32 values (4-byte aligned), or NULL for
+ *              no bias.  Must not overlap C (GEMM_ERR_ALIAS).
+ *   relu       nonzero: act(x) = max(x, 0) (a NaN stays NaN); zero: identity.
+ *
+ * Other arguments, ownership, sizes and errors as gemm_run, plus
+ * GEMM_ERR_LAYOUT.  K == 0 gives C = act(beta*C + bias).  With b_layout
+ * GEMM_B_ROW_MAJOR, alpha == 1, beta == 0, bias == NULL and relu == 0 the
+ * call is gemm_run, bit for bit.
+ */
+int gemm_run_ex(int64_t M, int64_t N, int64_t K, int dtype, int b_layout,
+                const void* A, int64_t lda, const void* B, int64_t ldb,
+                void* C, int64_t ldc, float alpha, float beta,
+                const float* bias, int relu, void* stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* gemm_strerror(int status);
@@ -102,6 +148,14 @@ int gemm_select_instance(int64_t M, int64_t N, int64_t K, int dtype,
                          const void* A, int64_t lda, const void* B, int64_t ldb,
                          const void* C, int64_t ldc);
 
+/* gemm_select_instance for the arguments of gemm_run_ex (bias is inspected
+ * for alignment and overlap only).  K == 0 with a general epilogue selects an
+ * instance too: it evaluates act(beta*C + bias). */
+int gemm_select_instance_ex(int64_t M, int64_t N, int64_t K, int dtype, int b_layout,
+                            const void* A, int64_t lda, const void* B, int64_t ldb,
+                            const void* C, int64_t ldc, float alpha, float beta,
+                            const float* bias, int relu);
+
 /* Number of instance ids (0 .. gemm_num_instances()-1). */
 int gemm_num_instances(void);
 
@@ -118,6 +172,13 @@ const char* gemm_instance_name(int instance);
 int gemm_run_instance(int instance, int64_t M, int64_t N, int64_t K, int dtype,
                       const void* A, int64_t lda, const void* B, int64_t ldb,
                       void* C, int64_t ldc, void* stream);
+
+/* gemm_run_ex with the instance forced; GEMM_ERR_INSTANCE as gemm_run_instance
+ * (the prefetch-distance-1 instances run only the plain row-major form). */
+int gemm_run_instance_ex(int instance, int64_t M, int64_t N, int64_t K, int dtype,
+                         int b_layout, const void* A, int64_t lda, const void* B,
+                         int64_t ldb, void* C, int64_t ldc, float alpha, float beta,
+                         const float* bias, int relu, void* stream);
 
 /*
  * gemm_tile_order -- host evaluation of an instance's workgroup-to-tile map

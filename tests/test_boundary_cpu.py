@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_strerror_covers_every_status(lib):
-    for st in range(0, -10, -1):
+    for st in range(0, -11, -1):
         s = G.gemm_strerror(st)
         assert s and s != "unknown status"
     assert G.gemm_strerror(12345) == "unknown status"
@@ -95,7 +95,7 @@ def test_unknown_instance(lib):
     assert G.gemm_run_instance(n, 4, 4, 4, 0, PA, 4, PB, 4, PC, 4, None) == G.GEMM_ERR_INSTANCE
     assert G.gemm_instance_name(n) == "?"
     for i in range(n):
-        assert G.gemm_instance_name(i).startswith(("mfma_", "dl_"))
+        assert G.gemm_instance_name(i).startswith("dl_")
 
 
 def _pick(M, N, K, dtype=3, lda=None, ldb=None, ldc=None, pa=PA, pb=PB):
@@ -109,14 +109,71 @@ def test_instance_choice(lib):
     assert _pick(2048, 2048, 2048, 0) == "dl_128x128x64_fd2"
     assert _pick(256, 256, 256, 0) == "dl_128x128x64_fd2"
     # ragged shape, 2-byte-aligned lda, N a multiple of 8: clamped-edge kernel
-    assert _pick(3000, 5000, 4099, 1) == "dl_256x256x64_fd2_edge"
+    assert _pick(3000, 5000, 4099, 1) == "dl_256x256x64_fd2_clamp"
     # misaligned base pointer: unaligned 16-byte loads are fine, same kernel
     assert _pick(4096, 4096, 4096, pa=PA + 2) == "dl_256x256x64_fd2"
-    # K not a multiple of 64: edge kernel with the zero-filled tail slice
-    assert _pick(4096, 4096, 4000) == "dl_256x256x64_fd2_edge"
-    # N not a multiple of 8: element-masked kernel
-    assert _pick(4096, 4100, 4096) == "mfma_256x256x64_edge"
-    assert _pick(100, 7, 33, 0).endswith("_edge")
+    # K not a multiple of 64: clamped-edge kernel with the zero-filled tail slice
+    assert _pick(4096, 4096, 4000) == "dl_256x256x64_fd2_clamp"
+    # N not a multiple of 8 with row-major B: the masked fallback
+    assert _pick(4096, 4100, 4096) == "dl_256x256x64_masked"
+    assert _pick(100, 7, 33, 0) == "dl_128x128x64_masked"
+
+
+def _pick_ex(M, N, K, layout, dtype=3, alpha=1.0, beta=0.0, bias=None, relu=0):
+    ldb = K if layout == G.GEMM_B_COL_MAJOR else N
+    return G.gemm_instance_name(G.gemm_select_instance_ex(
+        M, N, K, dtype, layout, PA, K, PB, ldb, 0x7000000000, N, alpha, beta, bias, relu))
+
+
+def test_instance_choice_general_form(lib):
+    col, row = G.GEMM_B_COL_MAJOR, G.GEMM_B_ROW_MAJOR
+    assert _pick_ex(8192, 8192, 8192, col) == "dl_256x256x64_fd2"
+    # column-major B reads B in rows of K like A: any N stays on the clamped kernel
+    assert _pick_ex(4096, 4100, 4096, col) == "dl_256x256x64_fd2_clamp"
+    assert _pick_ex(100, 7, 33, col, 0) == "dl_128x128x64_fd2_clamp"
+    assert _pick_ex(4096, 4100, 4096, row, relu=1) == "dl_256x256x64_masked"
+    assert _pick_ex(4096, 4096, 4096, row, alpha=2.0, beta=1.0, bias=PC, relu=1) == "dl_256x256x64_fd2"
+    # the plain form through gemm_run_ex selects what gemm_run selects
+    assert _pick_ex(3000, 5000, 4099, row, 1) == _pick(3000, 5000, 4099, 1)
+
+
+def test_general_form_validation(lib):
+    col = G.GEMM_B_COL_MAJOR
+    ex = G.gemm_select_instance_ex
+    # unknown layout
+    assert ex(4, 4, 8, 0, 2, PA, 8, PB, 8, PC, 4, 1.0, 0.0, None, 0) == G.GEMM_ERR_LAYOUT
+    assert G.gemm_run_ex(4, 4, 8, 0, -1, PA, 8, PB, 8, PC, 4, 1.0, 0.0, None, 0, None) == G.GEMM_ERR_LAYOUT
+    # column-major B needs ldb >= K, row-major B needs ldb >= N
+    assert ex(4, 4, 8, 0, col, PA, 8, PB, 7, PC, 4, 1.0, 0.0, None, 0) == G.GEMM_ERR_LD
+    assert ex(4, 16, 8, 0, col, PA, 8, PB, 8, PC, 16, 1.0, 0.0, None, 0) >= 0
+    assert ex(4, 16, 8, 0, 0, PA, 8, PB, 8, PC, 16, 1.0, 0.0, None, 0) == G.GEMM_ERR_LD
+    # bias: 4-byte aligned, not overlapping C
+    assert ex(4, 4, 8, 0, col, PA, 8, PB, 8, PC, 4, 1.0, 0.0, PC + 4096 + 2, 0) == G.GEMM_ERR_ALIGN
+    assert ex(4, 4, 8, 0, col, PA, 8, PB, 8, PC, 4, 1.0, 0.0, PC + 8, 0) == G.GEMM_ERR_ALIAS
+    assert ex(4, 4, 8, 0, col, PA, 8, PB, 8, PC, 4, 1.0, 0.0, PC + 4 * 16, 0) >= 0
+    # C overlapping a column-major B (N x K extent), adjacent is fine
+    b_end = PB + ((4 - 1) * 8 + 8) * 2
+    assert ex(4, 4, 8, 3, col, PA, 8, PB, 8, b_end - 2, 4, 1.0, 0.0, None, 0) == G.GEMM_ERR_ALIAS
+    assert ex(4, 4, 8, 3, col, PA, 8, PB, 8, b_end, 4, 1.0, 0.0, None, 0) >= 0
+    # K == 0: the plain form is a zero fill (no instance); the general form
+    # still evaluates act(beta*C + bias) on an instance
+    assert ex(4, 4, 0, 0, 0, 0, 0, 0, 4, PC, 4, 1.0, 0.0, None, 0) == G.GEMM_OK
+    assert ex(4, 4, 0, 0, 0, 0, 0, 0, 4, PC, 4, 1.0, 1.0, None, 0) >= 0
+    # instances that cannot run a problem refuse it before any launch: the
+    # prefetch-distance-1 kernels exist for the plain row-major form only, and
+    # whole-tile kernels need whole tiles (fake pointers are never touched)
+    for inst in range(G.gemm_num_instances()):
+        name = G.gemm_instance_name(inst)
+        if "_fd1" in name:
+            st = G.gemm_run_instance_ex(inst, 256, 256, 64, 0, col, PA, 64, PB, 64, PC, 256,
+                                        1.0, 0.0, None, 0, None)
+            assert st == G.GEMM_ERR_INSTANCE, name
+            st = G.gemm_run_instance_ex(inst, 256, 256, 64, 0, 0, PA, 64, PB, 256, PC, 256,
+                                        2.0, 0.0, None, 0, None)
+            assert st == G.GEMM_ERR_INSTANCE, name
+        if name.endswith(("x64_fd2", "x64_fd1")):
+            st = G.gemm_run_instance_ex(inst, 4, 4, 8, 0, col, PA, 8, PB, 8, PC, 4, 1.0, 0.0, None, 0, None)
+            assert st == G.GEMM_ERR_INSTANCE, name
 
 
 @pytest.mark.parametrize("shape", [(8192, 8192), (4096, 4096), (2048, 2048), (3000, 5000),
@@ -128,6 +185,7 @@ def test_tile_order_is_a_bijection(lib, shape):
         name = G.gemm_instance_name(inst)
         bm = int(name.split("_")[1].split("x")[0])
         bn = int(name.split("_")[1].split("x")[1])
+        assert bm == bn
         tilesM, tilesN = -(-M // bm), -(-N // bn)
         assert tm.size == tilesM * tilesN
         assert tm.min() >= 0 and tm.max() < tilesM and tn.min() >= 0 and tn.max() < tilesN

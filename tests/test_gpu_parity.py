@@ -22,10 +22,7 @@ from dense_half_precision_tiled_amd import inputs
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-DTYPES = {0: ("f16", "f32"), 1: ("f16", "f16"), 2: ("bf16", "f32"), 3: ("bf16", "bf16")}
-POISON16 = 0x7E11      # a quiet-NaN pattern in both fp16 and bf16
-POISON32 = 0x7FC01234  # a quiet NaN in fp32
-GUARD = 64             # guard elements before and after C
+from tests.gpu_helpers import DTYPES, assert_bound, assert_exact, law_for, run  # noqa: E402
 
 
 @pytest.fixture(scope="module")
@@ -35,80 +32,6 @@ def G():
     from dense_half_precision_tiled_amd import gemm
     gemm.load()      # raises if the library is missing: no fallback
     return gemm
-
-
-def _dev(bits, ld=None, offset=0):
-    """Upload a rows x cols bit matrix into a buffer with row stride ld,
-    starting `offset` elements into the allocation; padding is poisoned."""
-    rows, cols = bits.shape
-    ld = ld or cols
-    buf = np.full(offset + max(rows * ld, 1) + 8, POISON16, dtype=np.uint16)
-    if rows and cols:
-        buf[offset:offset + rows * ld].reshape(rows, ld)[:, :cols] = bits
-    t = torch.from_numpy(buf.view(np.int16)).cuda()
-    return t, t.data_ptr() + 2 * offset, ld
-
-
-def _decode_out(raw, out_fmt):
-    if out_fmt == "f32":
-        return raw.view(np.float32).astype(np.float64)
-    if out_fmt == "f16":
-        return raw.view(np.float16).astype(np.float64)
-    with np.errstate(invalid="ignore"):
-        return (raw.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-
-
-def run(G, A, B, code, lda=None, ldb=None, ldc=None, a_off=0, instance=None, stream=None,
-        expect=0):
-    """C = A.B on the GPU; returns the decoded M x N result.  Checks that the
-    row padding of C and guard bands around it keep their poison."""
-    M, K = A.shape
-    N = B.shape[1]
-    out_fmt = DTYPES[code][1]
-    tA, pA, lda = _dev(A, lda, a_off)
-    tB, pB, ldb = _dev(B, ldb)
-    ldc = ldc or N
-    if out_fmt == "f32":
-        cbuf = np.full(2 * GUARD + max(M * ldc, 1), POISON32, dtype=np.uint32)
-        tC = torch.from_numpy(cbuf.view(np.int32)).cuda()
-        esz = 4
-    else:
-        cbuf = np.full(2 * GUARD + max(M * ldc, 1), POISON16, dtype=np.uint16)
-        tC = torch.from_numpy(cbuf.view(np.int16)).cuda()
-        esz = 2
-    pC = tC.data_ptr() + esz * GUARD
-    s = stream.cuda_stream if stream is not None else torch.cuda.current_stream().cuda_stream
-    if instance is None:
-        st = G.gemm_run(M, N, K, code, pA, lda, pB, ldb, pC, ldc, s)
-    else:
-        st = G.gemm_run_instance(instance, M, N, K, code, pA, lda, pB, ldb, pC, ldc, s)
-    assert st == expect, G.gemm_strerror(st)
-    torch.cuda.synchronize()
-    raw = tC.cpu().numpy().view(np.uint32 if esz == 4 else np.uint16)
-    assert np.all(raw[:GUARD] == cbuf[:GUARD]) and np.all(raw[-GUARD:] == cbuf[-GUARD:]), \
-        "guard band written"
-    body = raw[GUARD:GUARD + M * ldc].reshape(M, ldc) if M else raw[:0].reshape(0, ldc)
-    if ldc > N:
-        assert np.all(body[:, N:] == cbuf[GUARD]), "row padding of C written"
-    return _decode_out(np.ascontiguousarray(body[:, :N]), out_fmt)
-
-
-def assert_bound(y, r, K, out_fmt, what=""):
-    res = oracle.compare(y, r, K, out_fmt)
-    assert res["ok"], "%s: %d elements outside the bound; max_abs %.3g, worst/bound %.3g" % (
-        what, res["n_bad"], res["max_abs"], res["worst_ratio"])
-    return res
-
-
-def assert_exact(y, r, out_fmt, what=""):
-    want = oracle.round_to(r, out_fmt)
-    bad = ~((y == want) | (np.isnan(y) & np.isnan(want)))
-    assert not bad.any(), "%s: %d elements differ, first at %s: %r vs %r" % (
-        what, bad.sum(), np.argwhere(bad)[0], y[bad][0], want[bad][0])
-
-
-def law_for(fmt):
-    return inputs.uniform if fmt == "f16" else inputs.normal
 
 
 # ------------------------------------------------------------ exact fixtures
@@ -190,7 +113,7 @@ def test_padded_leading_dimensions(G, code):
     r = oracle.gemm_f64(A, B, fmt)
     y = run(G, A, B, code, lda=K + 8, ldb=N + 24, ldc=N + 40)
     assert_bound(y, r, K, out, "padded ld")
-    # 2-byte aligned rows and base pointer: the element-masked path
+    # 2-byte aligned rows and base pointer: unaligned 16-byte loads, same bits
     y2 = run(G, A, B, code, lda=K + 1, ldb=N + 3, ldc=N + 1, a_off=1)
     assert_bound(y2, r, K, out, "misaligned")
     assert np.array_equal(y, y2)
@@ -246,13 +169,14 @@ RAGGED = [(129, 131, 67), (300, 260, 130), (1, 513, 65), (129, 136, 67), (300, 2
 
 def _edge_instances(G):
     n = G.gemm_num_instances()
-    return [i for i in range(n) if G.gemm_instance_name(i).endswith("_edge")]
+    return [i for i in range(n) if G.gemm_instance_name(i).endswith(("_clamp", "_masked"))]
 
 
 def _expect_for(G, i, N):
-    """dl_*_edge instances read B in 8-column chunks: they take N % 8 == 0
-    only and refuse other shapes with GEMM_ERR_INSTANCE."""
-    if G.gemm_instance_name(i).startswith("dl_") and N % 8 != 0:
+    """Clamped-edge instances read row-major B in 8-column chunks: they take
+    N % 8 == 0 only and refuse other shapes with GEMM_ERR_INSTANCE; the
+    masked instances take any shape."""
+    if G.gemm_instance_name(i).endswith("_clamp") and N % 8 != 0:
         return G.GEMM_ERR_INSTANCE
     return 0
 
