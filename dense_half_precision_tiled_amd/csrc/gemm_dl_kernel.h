@@ -56,105 +56,10 @@
 
 #include <type_traits>
 
-#include "gemm_internal.h"
+#include "gemm_common.h"
 
 namespace dhpt {
 namespace dl {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) char lds_char;
-
-enum { IN_F16 = 0, IN_BF16 = 1 };
-enum { OUT_F32 = 0, OUT_F16 = 1, OUT_BF16 = 2 };
-enum { EDGE_NONE = 0, EDGE_CLAMP = 1, EDGE_MASKED = 2 };
-
-template <int IN>
-__device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
-    if constexpr (IN == IN_F16)
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-    else
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-template <int OUT>
-__device__ __forceinline__ void store_out(void* C, int64_t idx, float v) {
-    if constexpr (OUT == OUT_F32)
-        static_cast<float*>(C)[idx] = v;
-    else if constexpr (OUT == OUT_F16)
-        static_cast<_Float16*>(C)[idx] = (_Float16)v;     // v_cvt_f16_f32: round to nearest even
-    else
-        static_cast<__bf16*>(C)[idx] = (__bf16)v;         // round to nearest even
-}
-
-template <int OUT>
-__device__ __forceinline__ float load_out(const void* C, int64_t idx) {
-    if constexpr (OUT == OUT_F32)
-        return static_cast<const float*>(C)[idx];
-    else if constexpr (OUT == OUT_F16)
-        return (float)static_cast<const _Float16*>(C)[idx];
-    else
-        return (float)static_cast<const __bf16*>(C)[idx];
-}
-
-__device__ __forceinline__ int swz_a(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-__device__ __forceinline__ int swz_b(int k) { return 2 * (k & 3); }
-
-// One global_load_lds_dwordx4 (this lane's 16 bytes at `src` to LDS byte
-// address lds_base + 16 * lane), issued through inline assembly so that the
-// compiler does not make every later LDS read wait for it; its completion is
-// awaited explicitly (vmcnt) before the barrier that publishes the stage.
-// M0 has no other user in this kernel.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(src), "s"(lds_base) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-#define DL_FENCE() __builtin_amdgcn_sched_barrier(0)
-
-// 8 consecutive 16-bit values p[c0 .. c0+7] of a row p[0 .. limit-1], those at
-// index >= limit reading as zero.  Element loads: any limit >= 1.
-__device__ __forceinline__ u32x4 load8_masked(const uint16_t* p, int c0, int limit) {
-    if (c0 + 8 <= limit) return *reinterpret_cast<const u32x4*>(p + c0);
-    uint32_t h[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) h[e] = (c0 + e < limit) ? (uint32_t)p[c0 + e] : 0u;
-    return u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-}
-
-// The same for limit >= 8, without a branch, in two steps so that a caller
-// can issue every load of a fill before the first shift: load8_at reads the
-// last whole in-row chunk at or before c0, shift8 moves the wanted values
-// down by the distance (8 or more clears the chunk).
-__device__ __forceinline__ u32x4 load8_at(const uint16_t* p, int c0, int limit, int* sh) {
-    const int start = c0 < limit - 8 ? c0 : limit - 8;   // [start, start + 8) lies in the row
-    const int d = c0 - start;                            // 0 whole, 1..7 partial, >= 8 past the end
-    *sh = d < 8 ? d : 8;
-    return *reinterpret_cast<const u32x4*>(p + start);
-}
-__device__ __forceinline__ u32x4 shift8(u32x4 v, int sh) {
-    unsigned __int128 x = __builtin_bit_cast(unsigned __int128, v);
-    x = (x >> (8 * sh)) >> (8 * sh);                     // two shifts of <= 64 bits: 8 clears all
-    return __builtin_bit_cast(u32x4, x);
-}
-
-// The epilogue operands of the general form (unused by the plain kernels).
-struct EpiArgs {
-    float alpha, beta;
-    const float* bias;         // N values, or null
-    int relu;
-};
 
 template <int IN, int OUT, int BM, int BN, int FD, int EDGE, bool BT, bool EPI>
 __global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
@@ -291,78 +196,8 @@ __global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
         }
     };
 
-    // Slice kt through VGPRs: every lane loads its share of the A and B
-    // tiles with zero fill beyond M, N and K and writes it into the stage
-    // layout (the partial last slice of EDGE_CLAMP, every slice of
-    // EDGE_MASKED).  All loads are issued before the first LDS write: rows
-    // past the edge read a clamped valid row and are zeroed afterwards, and
-    // chunks crossing the row end use the branch-free shifted load whenever
-    // the row holds at least 8 values (a uniform test), so one memory round
-    // trip fills the slice.
-    constexpr int NFA = BM / 32;                                  // A chunks per lane
-    constexpr int B_ROWS_PER_PASS = 256 / B_CHUNKS;
-    constexpr int NFB = BT ? BN / 32 : BK / B_ROWS_PER_PASS;      // B chunks per lane
     auto fill_slice = [&](int stage, int kt) {
-        char* st = smem + stage * STAGE;
-        const int k0 = kt * BK;
-        const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
-        u32x4 va[NFA], vb[NFB];
-        const uint16_t* pa[NFA];
-        const uint16_t* pb[NFB];
-        int cb[NFB];
-#pragma unroll
-        for (int r = 0; r < NFA; ++r) {                // A: BM rows x 8 chunks
-            const int grow = m0 + (t >> 3) + 32 * r;
-            pa[r] = A + (int64_t)(grow < M ? grow : M - 1) * lda;
-        }
-#pragma unroll
-        for (int r = 0; r < NFB; ++r) {
-            if constexpr (BT) {                        // column-major B: BN rows x 8 chunks
-                const int gcol = n0 + (t >> 3) + 32 * r;
-                pb[r] = B + (int64_t)(gcol < N ? gcol : N - 1) * ldb;
-                cb[r] = k0 + 8 * (t & 7);
-            } else {                                   // row-major B: 64 rows x B_CHUNKS chunks
-                const int gk = k0 + t / B_CHUNKS + B_ROWS_PER_PASS * r;
-                pb[r] = B + (int64_t)(gk < K ? gk : K - 1) * ldb;
-                cb[r] = n0 + 8 * (t % B_CHUNKS);
-            }
-        }
-        const int ca = k0 + 8 * (t & 7);
-        const int blim = BT ? K : N;                   // valid length of a B row
-        if (K >= 8 && blim >= 8) {                     // every load in flight before the first shift
-            int sha[NFA], shb[NFB];
-#pragma unroll
-            for (int r = 0; r < NFA; ++r) va[r] = load8_at(pa[r], ca, K, &sha[r]);
-#pragma unroll
-            for (int r = 0; r < NFB; ++r) vb[r] = load8_at(pb[r], cb[r], blim, &shb[r]);
-            DL_FENCE();
-#pragma unroll
-            for (int r = 0; r < NFA; ++r) va[r] = shift8(va[r], sha[r]);
-#pragma unroll
-            for (int r = 0; r < NFB; ++r) vb[r] = shift8(vb[r], shb[r]);
-        } else {
-#pragma unroll
-            for (int r = 0; r < NFA; ++r) va[r] = load8_masked(pa[r], ca, K);
-#pragma unroll
-            for (int r = 0; r < NFB; ++r) vb[r] = load8_masked(pb[r], cb[r], blim);
-        }
-#pragma unroll
-        for (int r = 0; r < NFA; ++r) {
-            const int row = (t >> 3) + 32 * r, c = t & 7;
-            *reinterpret_cast<u32x4*>(st + row * 128 + 16 * (c ^ swz_a(row))) = m0 + row < M ? va[r] : zero;
-        }
-#pragma unroll
-        for (int r = 0; r < NFB; ++r) {
-            if constexpr (BT) {
-                const int row = (t >> 3) + 32 * r, c = t & 7;
-                *reinterpret_cast<u32x4*>(st + A_BYTES + row * 128 + 16 * (c ^ swz_a(row))) =
-                    n0 + row < N ? vb[r] : zero;
-            } else {
-                const int row = t / B_CHUNKS + B_ROWS_PER_PASS * r, c = t % B_CHUNKS;
-                *reinterpret_cast<u32x4*>(st + A_BYTES + row * BROW + 16 * (c ^ swz_b(row))) =
-                    k0 + row < K ? vb[r] : zero;
-            }
-        }
+        fill_stage<BM, BN, BT>(smem + stage * STAGE, A, lda, B, ldb, M, N, K, m0, n0, kt * BK, t);
     };
     // One filled slice, unpipelined: the reads of each k-step, then its MFMAs.
     auto compute_slice = [&](int stage) {

@@ -8,25 +8,28 @@
 namespace dhpt {
 
 // Every instance walks the output tiles in the XCD-aware grouped order of
-// tile_coords with groups of 8 tile-rows.
+// tile_coords with groups of 8 tile-rows.  New instances go at the end: the
+// ids are part of the introspection interface.
 const InstanceInfo kInstances[] = {
-    {"dl_256x256x64_fd2", 256, 2, EDGE_NONE, 8},
-    {"dl_256x256x64_fd2_clamp", 256, 2, EDGE_CLAMP, 8},
-    {"dl_256x256x64_masked", 256, 2, EDGE_MASKED, 8},
-    {"dl_128x128x64_fd2", 128, 2, EDGE_NONE, 8},
-    {"dl_128x128x64_fd2_clamp", 128, 2, EDGE_CLAMP, 8},
-    {"dl_128x128x64_masked", 128, 2, EDGE_MASKED, 8},
-    {"dl_256x256x64_fd1", 256, 1, EDGE_NONE, 8},
-    {"dl_256x256x64_fd1_clamp", 256, 1, EDGE_CLAMP, 8},
-    {"dl_128x128x64_fd1", 128, 1, EDGE_NONE, 8},
-    {"dl_128x128x64_fd1_clamp", 128, 1, EDGE_CLAMP, 8},
+    {"dl_256x256x64_fd2", 256, 2, EDGE_NONE, 8, KIND_DL},
+    {"dl_256x256x64_fd2_clamp", 256, 2, EDGE_CLAMP, 8, KIND_DL},
+    {"dl_256x256x64_masked", 256, 2, EDGE_MASKED, 8, KIND_DL},
+    {"dl_128x128x64_fd2", 128, 2, EDGE_NONE, 8, KIND_DL},
+    {"dl_128x128x64_fd2_clamp", 128, 2, EDGE_CLAMP, 8, KIND_DL},
+    {"dl_128x128x64_masked", 128, 2, EDGE_MASKED, 8, KIND_DL},
+    {"dl_256x256x64_fd1", 256, 1, EDGE_NONE, 8, KIND_DL},
+    {"dl_256x256x64_fd1_clamp", 256, 1, EDGE_CLAMP, 8, KIND_DL},
+    {"dl_128x128x64_fd1", 128, 1, EDGE_NONE, 8, KIND_DL},
+    {"dl_128x128x64_fd1_clamp", 128, 1, EDGE_CLAMP, 8, KIND_DL},
+    {"ks_128x128x64", 128, 2, EDGE_NONE, 8, KIND_KS},
+    {"ks_128x128x64_clamp", 128, 2, EDGE_CLAMP, 8, KIND_KS},
 };
 const int kNumInstances = sizeof(kInstances) / sizeof(kInstances[0]);
 
 bool instance_supports(int id, const Problem& p) {
     if (id < 0 || id >= kNumInstances) return false;
     const InstanceInfo& in = kInstances[id];
-    if (in.fd == 1 && (p.transB || p.epi)) return false;      // compiled for plain row-major B only
+    if (in.kind == KIND_DL && in.fd == 1 && (p.transB || p.epi)) return false;   // plain row-major B only
     switch (in.edge) {
     case EDGE_NONE: return p.M % in.tile == 0 && p.N % in.tile == 0 && p.K % 64 == 0;
     case EDGE_CLAMP: return p.transB || (p.N % 8 == 0 && p.N >= 8);
@@ -37,6 +40,8 @@ bool instance_supports(int id, const Problem& p) {
 
 hipError_t launch_instance(int id, const Problem& p, hipStream_t s) {
     const InstanceInfo& in = kInstances[id];
+    if (in.kind == KIND_KS)
+        return p.epi ? launch_ks_epi(in.edge, p, in.group_m, s) : launch_ks(in.edge, p, in.group_m, s);
     if (p.transB)
         return p.epi ? launch_dl_tn_epi(in.tile, in.fd, in.edge, p, in.group_m, s)
                      : launch_dl_tn(in.tile, in.fd, in.edge, p, in.group_m, s);

@@ -29,14 +29,22 @@ enum EdgeMode {
     EDGE_MASKED = 2,           // any shape
 };
 
-// One compiled tile geometry of the direct-to-LDS family.  Every instance
-// computes the same function with the same per-element operation order.
+// Kernel families.
+enum KernelKind {
+    KIND_DL = 0,               // gemm_dl_kernel.h: waves split the output tile
+    KIND_KS = 1,               // gemm_ks_kernel.h: waves split K, 128x128 tile, LDS reduction
+};
+
+// One compiled kernel configuration.  The instances of one kind compute the
+// same function with the same per-element operation order; the two kinds
+// differ in the order the k-steps are summed.
 struct InstanceInfo {
     const char* name;
     int tile;                  // square workgroup tile: 256 or 128 (k-slice 64)
-    int fd;                    // fragment prefetch distance in k-steps: 1 or 2
+    int fd;                    // fragment prefetch distance in k-steps (KIND_DL): 1 or 2
     int edge;                  // EdgeMode
     int group_m;               // tile-rows per group of the visit order
+    int kind;                  // KernelKind
 };
 
 extern const InstanceInfo kInstances[];
@@ -54,6 +62,9 @@ hipError_t launch_dl_nn(int tile, int fd, int edge, const Problem& p, int group_
 hipError_t launch_dl_nn_epi(int tile, int fd, int edge, const Problem& p, int group_m, hipStream_t stream);
 hipError_t launch_dl_tn(int tile, int fd, int edge, const Problem& p, int group_m, hipStream_t stream);
 hipError_t launch_dl_tn_epi(int tile, int fd, int edge, const Problem& p, int group_m, hipStream_t stream);
+// The instantiation units of gemm_ks_kernel.h: plain / general epilogue (both B layouts).
+hipError_t launch_ks(int edge, const Problem& p, int group_m, hipStream_t stream);
+hipError_t launch_ks_epi(int edge, const Problem& p, int group_m, hipStream_t stream);
 
 // Workgroup id -> output tile (tm, tn).
 //

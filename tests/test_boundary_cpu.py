@@ -95,7 +95,7 @@ def test_unknown_instance(lib):
     assert G.gemm_run_instance(n, 4, 4, 4, 0, PA, 4, PB, 4, PC, 4, None) == G.GEMM_ERR_INSTANCE
     assert G.gemm_instance_name(n) == "?"
     for i in range(n):
-        assert G.gemm_instance_name(i).startswith("dl_")
+        assert G.gemm_instance_name(i).startswith(("dl_", "ks_"))
 
 
 def _pick(M, N, K, dtype=3, lda=None, ldb=None, ldc=None, pa=PA, pb=PB):
@@ -106,8 +106,14 @@ def _pick(M, N, K, dtype=3, lda=None, ldb=None, ldc=None, pa=PA, pb=PB):
 def test_instance_choice(lib):
     assert _pick(8192, 8192, 8192) == "dl_256x256x64_fd2"
     assert _pick(4096, 4096, 4096) == "dl_256x256x64_fd2"
-    assert _pick(2048, 2048, 2048, 0) == "dl_128x128x64_fd2"
+    # under 128 tiles of 256x256: 128x128 tiles, K split across the waves when
+    # K >= 2048, otherwise each wave a quarter of the tile
+    assert _pick(2048, 2048, 2048, 0) == "ks_128x128x64"
     assert _pick(256, 256, 256, 0) == "dl_128x128x64_fd2"
+    assert _pick(2048, 2048, 1984, 0) == "dl_128x128x64_fd2"
+    assert _pick(1000, 1000, 2100, 3) == "ks_128x128x64_clamp"
+    assert _pick(1000, 1000, 1000, 3) == "dl_128x128x64_fd2_clamp"
+    assert _pick(1000, 1001, 4096, 3) == "dl_128x128x64_masked"
     # ragged shape, 2-byte-aligned lda, N a multiple of 8: clamped-edge kernel
     assert _pick(3000, 5000, 4099, 1) == "dl_256x256x64_fd2_clamp"
     # misaligned base pointer: unaligned 16-byte loads are fine, same kernel
@@ -171,7 +177,7 @@ def test_general_form_validation(lib):
             st = G.gemm_run_instance_ex(inst, 256, 256, 64, 0, 0, PA, 64, PB, 256, PC, 256,
                                         2.0, 0.0, None, 0, None)
             assert st == G.GEMM_ERR_INSTANCE, name
-        if name.endswith(("x64_fd2", "x64_fd1")):
+        if name.endswith(("x64_fd2", "x64_fd1", "x64")):
             st = G.gemm_run_instance_ex(inst, 4, 4, 8, 0, col, PA, 8, PB, 8, PC, 4, 1.0, 0.0, None, 0, None)
             assert st == G.GEMM_ERR_INSTANCE, name
 
