@@ -12,7 +12,11 @@ Printed: one JSON line with the contract fields plus
   cpu_baseline  the CPU fp64 oracle timed on a bounded sample of output rows
                 of the same workload on this host (and those rows checked
                 against the GPU result);
-  secondary     the same measurement on bf16 4096^3.
+  secondary     the same measurement on bf16 4096^3;
+  other_configs the same on the other workloads (fp16 2048^3, the ragged
+                fp16 3000x5000x4099 shape, fp16 256^3).
+Before the warmups of each workload, untimed launches run for about
+--settle-ms so that the timed launches see a settled shader clock.
 """
 from __future__ import annotations
 
@@ -31,7 +35,9 @@ METRIC = "GEMM TFLOP/s (2MNK/t) at 4096³ and 8192³ bf16/fp16; % of MFMA peak"
 PEAK_TFLOPS = 2500.0        # MI355X published dense fp16/bf16 MFMA peak
 HBM_GBPS = 8000.0           # MI355X published HBM3E bandwidth
 CODES = {("f16", "f32"): 0, ("f16", "f16"): 1, ("bf16", "f32"): 2, ("bf16", "bf16"): 3}
-KERNEL_SOURCES = ["dense_half_precision_tiled_amd/csrc/gemm_dl_kernel.h",
+KERNEL_SOURCES = ["dense_half_precision_tiled_amd/csrc/gemm_common.h",
+                  "dense_half_precision_tiled_amd/csrc/gemm_dl_kernel.h",
+                  "dense_half_precision_tiled_amd/csrc/gemm_ks_kernel.h",
                   "dense_half_precision_tiled_amd/csrc/gemm_internal.h"]
 
 
@@ -54,9 +60,11 @@ def upload(bits, torch):
     return torch.from_numpy(bits.view(np.int16)).cuda()
 
 
-def measure(G, torch, name, steps, warmup, instance=None, layout="row"):
-    """Upload a workload, run one correctness launch into a poisoned C, then
-    time `steps` launches.  Returns a dict with the timing and the buffers.
+def measure(G, torch, name, steps, warmup, instance=None, layout="row", settle_ms=200.0):
+    """Upload a workload, run one correctness launch into a poisoned C, let
+    the clock settle (untimed launches for about settle_ms), run `warmup`
+    untimed launches, then time `steps` launches.  Returns a dict with the
+    timing and the buffers.
     layout "col" stores B column-major (its transpose row-major) and calls
     gemm_run_ex; "row" calls gemm_run."""
     import numpy as np
@@ -86,6 +94,15 @@ def measure(G, torch, name, steps, warmup, instance=None, layout="row"):
 
     launch()
     torch.cuda.synchronize()
+    # The shader clock ramps up over tens of milliseconds of load; without
+    # this, short kernels are timed partly at idle clocks.
+    t_settle = time.perf_counter()
+    n_settle = 0
+    while (time.perf_counter() - t_settle) * 1e3 < settle_ms:
+        for _ in range(8):
+            launch()
+        n_settle += 8
+        torch.cuda.synchronize()
     for _ in range(warmup):
         launch()
     torch.cuda.synchronize()
@@ -108,7 +125,7 @@ def measure(G, torch, name, steps, warmup, instance=None, layout="row"):
     else:
         inst = G.gemm_select_instance(M, N, K, code, tA.data_ptr(), K, tB.data_ptr(), N,
                                       tC.data_ptr(), N)
-    return {"name": name, "w": w, "A": A, "B": B, "C": tC, "ms": ms, "wall_s": wall,
+    return {"name": name, "w": w, "A": A, "B": B, "C": tC, "ms": ms, "wall_s": wall, "settle_launches": n_settle,
             "tflops": flops / (ms * 1e-3) / 1e12, "instance": G.gemm_instance_name(inst),
             "alg_bytes": 2 * (M * K + K * N) + (4 if w["out"] == "f32" else 2) * M * N}
 
@@ -138,18 +155,21 @@ def cpu_baseline(res, budget_s: float):
     M, N, K = w["M"], w["N"], w["K"]
     threads = oracle.default_threads()
     rng = np.random.Generator(np.random.PCG64(1234))
-    # Each call pays a fixed cost (decoding B) plus a cost per row: time 1 and
-    # 5 rows to separate them, then size the sample to the budget.
+    # Each call pays a fixed cost (decoding B) plus a cost per round of
+    # `threads` rows (the rows of a round run in parallel, one per thread):
+    # time one and three rounds to separate them, then size the sample to the
+    # budget in whole rounds.
     times = []
-    for n in (1, 5):
-        rows = rng.integers(0, M, n).astype(np.int64)
+    for n in (threads, 3 * threads):
+        rows = rng.integers(0, M, min(n, M)).astype(np.int64)
         t0 = time.perf_counter()
         oracle.gemm_rows_f64(res["A"], res["B"], rows, w["fmt"], threads)
         times.append(time.perf_counter() - t0)
-    per_row = max((times[1] - times[0]) / 4.0, 1e-6)
-    fixed = max(times[0] - per_row, 0.0)
-    nrows = int(min(M, max(8, (budget_s - fixed) / per_row)))
-    rows = np.array(sorted(set(rng.integers(0, M, nrows).tolist()) | {0, M - 1}), dtype=np.int64)
+    per_round = max((times[1] - times[0]) / 2.0, 1e-6)
+    fixed = max(times[0] - per_round, 0.0)
+    rounds = max(1, int((budget_s - fixed) / per_round))
+    nrows = int(min(M, rounds * threads))
+    rows = np.array(sorted(set(rng.choice(M, max(nrows - 2, 0), replace=False).tolist()) | {0, M - 1}), dtype=np.int64)
     t0 = time.perf_counter()
     r = oracle.gemm_rows_f64(res["A"], res["B"], rows, w["fmt"], threads)
     t = time.perf_counter() - t0
@@ -197,10 +217,14 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="bf16_8192")
     ap.add_argument("--secondary", default="bf16_4096", help="'none' to skip")
+    ap.add_argument("--also", default="f16_2048,f16_ragged,f16_256",
+                    help="comma-separated further workloads reported under other_configs ('none' to skip)")
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed launches for about this long before the warmups (clock ramp-up)")
     ap.add_argument("--instance", type=int, default=None, help="force a kernel instance id")
     ap.add_argument("--layout", choices=("row", "col"), default="row",
                     help="storage order of B: row-major (gemm_run) or column-major (gemm_run_ex)")
-    ap.add_argument("--cpu-budget", type=float, default=12.0,
+    ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle work for cpu_baseline (0 to skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the GEMM, time a plain device copy of BYTES bytes "
@@ -222,15 +246,29 @@ def main(argv=None):
     from dense_half_precision_tiled_amd import gemm as G
     G.load()
 
-    main_res = measure(G, torch, args.workload, args.steps, args.warmup, args.instance, args.layout)
+    main_res = measure(G, torch, args.workload, args.steps, args.warmup, args.instance, args.layout,
+                       args.settle_ms)
+
+    def summary(r):
+        w2 = r["w"]
+        return {"workload": describe(w2), "value": round(r["tflops"], 2), "unit": "TFLOP/s",
+                "ms_per_step": round(r["ms"], 5), "frac_of_peak": round(r["tflops"] / PEAK_TFLOPS, 4),
+                "hbm_gbps_algorithmic": round(r["alg_bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
+                "kernel": r["instance"]}
+
     sec = None
     if args.secondary and args.secondary != "none":
         r2 = measure(G, torch, args.secondary, max(args.steps, 50), args.warmup, args.instance,
-                     args.layout)
-        sec = {"workload": describe(r2["w"]), "value": round(r2["tflops"], 2), "unit": "TFLOP/s",
-               "ms_per_step": round(r2["ms"], 5), "frac_of_peak": round(r2["tflops"] / PEAK_TFLOPS, 4),
-               "kernel": r2["instance"]}
+                     args.layout, args.settle_ms)
+        sec = summary(r2)
         del r2
+    others = []
+    if args.also and args.also != "none" and args.instance is None:
+        for name in args.also.split(","):
+            r3 = measure(G, torch, name, max(args.steps, 200), args.warmup, None, args.layout,
+                         args.settle_ms)
+            others.append(summary(r3))
+            del r3
 
     w = main_res["w"]
     traffic = traffic_from_profiles(args.workload + ("" if args.layout == "row" else "_col"))
@@ -259,6 +297,8 @@ def main(argv=None):
     }
     if sec is not None:
         line["secondary"] = sec
+    if others:
+        line["other_configs"] = others
     if args.cpu_budget > 0:
         line["cpu_baseline"] = cpu_baseline(main_res, args.cpu_budget)
     print(json.dumps(line), flush=True)
