@@ -86,18 +86,26 @@ int validate(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t 
 int64_t tiles_for(int tile, int64_t M, int64_t N) { return ((M + tile - 1) / tile) * ((N + tile - 1) / tile); }
 
 // Large (256x256) tiles when they still give at least half a wave over the
-// 256 CUs.  Otherwise 128x128 tiles: with K >= 2048 the k-split kernel (each
-// wave accumulates the whole tile over a quarter of the k-steps: fewer LDS
-// bytes per MFMA, paid for by a reduction through LDS at the end), else the
-// direct-to-LDS kernel (each wave a quarter of the tile).  Within a family,
-// the first instance that supports the problem: whole tiles, then clamped
-// edges (any M and K; N a multiple of 8 for row-major B), then the fully
-// masked fallback.
+// 256 CUs.  Otherwise:
+//  * K >= 2048 and at least 64 tiles of 128x128: the k-split kernel (each
+//    wave accumulates the whole 128x128 tile over a quarter of the k-steps:
+//    fewer LDS bytes per MFMA, paid for by a reduction through LDS);
+//  * fewer than 128 tiles of 128x128 and K <= 2048: 64x64 tiles, four times
+//    the workgroups (small problems are bound by latency, not by bytes);
+//  * else 128x128 tiles, each wave a quarter of the tile.
+// Within a family, the first instance that supports the problem: whole
+// tiles, then clamped edges (any M and K; N a multiple of 8 for row-major
+// B), then the fully masked fallback (128x128).
 int choose_instance(const Problem& p) {
     static const int big_order[] = {0, 1, 2};
     static const int mid_order[] = {3, 4, 5};
     static const int ks_order[] = {10, 11, 5};
-    const int* order = tiles_for(256, p.M, p.N) >= 128 ? big_order : p.K >= 2048 ? ks_order : mid_order;
+    static const int small_order[] = {12, 13, 5};
+    const int64_t t128 = tiles_for(128, p.M, p.N);
+    const int* order = tiles_for(256, p.M, p.N) >= 128      ? big_order
+                       : (p.K >= 2048 && t128 >= 64)        ? ks_order
+                       : (t128 < 128 && p.K <= 2048)        ? small_order
+                                                            : mid_order;
     for (int k = 0; k < 3; ++k)
         if (dhpt::instance_supports(order[k], p)) return order[k];
     return order[2];

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
     void* __restrict__ C, int64_t ldc, int M, int N, int K, int tilesM, int tilesN, int group_m,
     EpiArgs ep) {
-    static_assert((BM == 256 && BN == 256) || (BM == 128 && BN == 128), "tile");
+    static_assert((BM == 256 && BN == 256) || (BM == 128 && BN == 128) || (BM == 64 && BN == 64), "tile");
     static_assert(FD == 1 || FD == 2, "fragment prefetch distance");
     constexpr int BK = 64, KSTEPS = 4;
     constexpr int WM = BM / 2, WN = BN / 2;               // wave tile
@@ -383,6 +383,14 @@ static hipError_t launch_family(int tile, int edge, const Problem& p, int group_
     if (tile == 256)
         return edge == EDGE_NONE ? launch_dtype<256, 256, FD, EDGE_NONE, BT, EPI>(p, group_m, s)
                                  : launch_dtype<256, 256, FD, EDGE_CLAMP, BT, EPI>(p, group_m, s);
+    if (tile == 64) {
+        if constexpr (FD == 2) {
+            return edge == EDGE_NONE ? launch_dtype<64, 64, 2, EDGE_NONE, BT, EPI>(p, group_m, s)
+                                     : launch_dtype<64, 64, 2, EDGE_CLAMP, BT, EPI>(p, group_m, s);
+        } else {
+            return hipErrorInvalidValue;
+        }
+    }
     return edge == EDGE_NONE ? launch_dtype<128, 128, FD, EDGE_NONE, BT, EPI>(p, group_m, s)
                              : launch_dtype<128, 128, FD, EDGE_CLAMP, BT, EPI>(p, group_m, s);
 }

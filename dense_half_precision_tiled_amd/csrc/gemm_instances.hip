@@ -23,12 +23,17 @@ const InstanceInfo kInstances[] = {
     {"dl_128x128x64_fd1_clamp", 128, 1, EDGE_CLAMP, 8, KIND_DL},
     {"ks_128x128x64", 128, 2, EDGE_NONE, 8, KIND_KS},
     {"ks_128x128x64_clamp", 128, 2, EDGE_CLAMP, 8, KIND_KS},
+    {"dl_64x64x64_fd2", 64, 2, EDGE_NONE, 8, KIND_DL},
+    {"dl_64x64x64_fd2_clamp", 64, 2, EDGE_CLAMP, 8, KIND_DL},
 };
 const int kNumInstances = sizeof(kInstances) / sizeof(kInstances[0]);
 
 bool instance_supports(int id, const Problem& p) {
     if (id < 0 || id >= kNumInstances) return false;
     const InstanceInfo& in = kInstances[id];
+    // one workgroup of 256 lanes per tile: the grid stays within 2^32 lanes
+    const int64_t tiles = ((int64_t)(p.M + in.tile - 1) / in.tile) * ((p.N + in.tile - 1) / in.tile);
+    if (tiles > (int64_t(1) << 24)) return false;
     if (in.kind == KIND_DL && in.fd == 1 && (p.transB || p.epi)) return false;   // plain row-major B only
     switch (in.edge) {
     case EDGE_NONE: return p.M % in.tile == 0 && p.N % in.tile == 0 && p.K % 64 == 0;

@@ -106,13 +106,16 @@ def _pick(M, N, K, dtype=3, lda=None, ldb=None, ldc=None, pa=PA, pb=PB):
 def test_instance_choice(lib):
     assert _pick(8192, 8192, 8192) == "dl_256x256x64_fd2"
     assert _pick(4096, 4096, 4096) == "dl_256x256x64_fd2"
-    # under 128 tiles of 256x256: 128x128 tiles, K split across the waves when
-    # K >= 2048, otherwise each wave a quarter of the tile
+    # under 128 tiles of 256x256: K split across the waves of a 128x128 tile
+    # when K >= 2048 (and >= 64 such tiles); 64x64 tiles for small problems
+    # (under 128 tiles of 128x128, K <= 2048); else 128x128 tiles
     assert _pick(2048, 2048, 2048, 0) == "ks_128x128x64"
-    assert _pick(256, 256, 256, 0) == "dl_128x128x64_fd2"
+    assert _pick(256, 256, 256, 0) == "dl_64x64x64_fd2"
+    assert _pick(1024, 1024, 1024, 0) == "dl_64x64x64_fd2"
+    assert _pick(512, 512, 4096, 0) == "dl_128x128x64_fd2"
     assert _pick(2048, 2048, 1984, 0) == "dl_128x128x64_fd2"
     assert _pick(1000, 1000, 2100, 3) == "ks_128x128x64_clamp"
-    assert _pick(1000, 1000, 1000, 3) == "dl_128x128x64_fd2_clamp"
+    assert _pick(1000, 1000, 1000, 3) == "dl_64x64x64_fd2_clamp"
     assert _pick(1000, 1001, 4096, 3) == "dl_128x128x64_masked"
     # ragged shape, 2-byte-aligned lda, N a multiple of 8: clamped-edge kernel
     assert _pick(3000, 5000, 4099, 1) == "dl_256x256x64_fd2_clamp"
@@ -136,7 +139,7 @@ def test_instance_choice_general_form(lib):
     assert _pick_ex(8192, 8192, 8192, col) == "dl_256x256x64_fd2"
     # column-major B reads B in rows of K like A: any N stays on the clamped kernel
     assert _pick_ex(4096, 4100, 4096, col) == "dl_256x256x64_fd2_clamp"
-    assert _pick_ex(100, 7, 33, col, 0) == "dl_128x128x64_fd2_clamp"
+    assert _pick_ex(100, 7, 33, col, 0) == "dl_64x64x64_fd2_clamp"
     assert _pick_ex(4096, 4100, 4096, row, relu=1) == "dl_256x256x64_masked"
     assert _pick_ex(4096, 4096, 4096, row, alpha=2.0, beta=1.0, bias=PC, relu=1) == "dl_256x256x64_fd2"
     # the plain form through gemm_run_ex selects what gemm_run selects
