@@ -85,10 +85,10 @@ typedef enum {
  * M x N region (the product of an M x 0 and a 0 x N matrix).
  *
  * Alignment: only natural element alignment is required (2 bytes for A and B;
- * 4 or 2 bytes for C).  Whole 256x256 (or 128x128) tiles with K a multiple of
- * 64 run without edge code; other shapes with N a multiple of 8 run with
- * clamped edge loads and a zero-filled last k-slice; any other N runs on a
- * fully masked fallback.
+ * 4 or 2 bytes for C).  Whole tiles (256x256, 128x128 or 64x64, chosen by
+ * the number of tiles and K) with K a multiple of 64 run without edge code;
+ * other shapes with N a multiple of 8 run with clamped edge loads and a
+ * zero-filled last k-slice; any other N runs on a fully masked fallback.
  *
  * Returns GEMM_OK once the kernel is enqueued (asynchronous: device faults
  * surface at the caller's next synchronisation), or a GEMM_ERR_* code.
@@ -135,9 +135,13 @@ int gemm_run_ex(int64_t M, int64_t N, int64_t K, int dtype, int b_layout,
 const char* gemm_strerror(int status);
 
 /*
- * Kernel instances.  Each instance is one compiled tile geometry; all compute
- * the same function.  gemm_run picks one from the shape, the alignment and the
- * number of output tiles.
+ * Kernel instances.  Each instance is one compiled kernel configuration; all
+ * compute the same function.  Two families: "dl_*" (the waves of a workgroup
+ * split its output tile; instances of this family give identical bits) and
+ * "ks_*" (the four waves split K over a 128x128 tile and their partial sums
+ * are added in a fixed order, so repeated calls give identical bits; the
+ * rounding differs from the dl family within the accuracy bound).  gemm_run
+ * picks one from the shape, the alignment, K and the number of output tiles.
  *
  * gemm_select_instance returns the id gemm_run would use for these arguments
  * (pointers are only inspected for alignment, never dereferenced; no GPU call
