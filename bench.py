@@ -210,6 +210,93 @@ def copy_calibration(torch, nbytes: int, steps: int, warmup: int) -> int:
     return 0
 
 
+def loop_for(G, torch, name, seconds: float) -> int:
+    """Run one workload (or, for name "mfma_probe", the MFMA issue-rate probe:
+    eight independent 32x32x16 bf16 chains per wave, one wave per SIMD on
+    every CU) back to back for `seconds`; print the achieved rate."""
+    if name == "mfma_probe":
+        import ctypes
+        P = ctypes.CDLL(os.path.join(ROOT, "tests", "probes", "libdhpt_probes.so"))
+        P.probe_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        blocks, iters = 256, 200000
+        cyc = torch.zeros(blocks * 4, dtype=torch.int64, device="cuda")
+        sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+        n, ms, t0 = 0, 0.0, time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if P.probe_mfma_rate(1, blocks, iters, cyc.data_ptr(), sink.data_ptr()) != 0:
+                raise RuntimeError("probe launch failed")
+            e1.record()
+            torch.cuda.synchronize()
+            ms += e0.elapsed_time(e1)
+            n += 1
+        flops = n * blocks * 4 * iters * 8 * 32768.0
+    else:
+        import numpy as np
+        from dense_half_precision_tiled_amd import inputs
+        A, B, w = inputs.workload_inputs(name)
+        M, N, K = w["M"], w["N"], w["K"]
+        tA, tB = upload(A, torch), upload(B, torch)
+        tC = torch.empty((M, N), dtype=torch.float32 if w["out"] == "f32" else torch.int16, device="cuda")
+        args = (M, N, K, CODES[(w["fmt"], w["out"])], tA.data_ptr(), K, tB.data_ptr(), N, tC.data_ptr(), N,
+                torch.cuda.current_stream().cuda_stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n, t0 = 0, time.perf_counter()
+        e0.record()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(16):
+                if G.gemm_run(*args) != 0:
+                    raise RuntimeError("gemm_run failed")
+            n += 16
+            torch.cuda.synchronize()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        flops = n * 2.0 * M * N * K
+    print(json.dumps({"loop": name, "launches": n, "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}), flush=True)
+    return 0
+
+
+def power_sample(name: str, seconds: float) -> int:
+    """Sample socket power and the eight XCD graphics clocks (amd-smi) while a
+    child process runs `bench.py --loop-seconds` on one workload.  This
+    process never touches the GPU; the child is started with subprocess (no
+    exec)."""
+    import statistics
+    import subprocess
+
+    def sample():
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True, timeout=60)
+        d = json.loads(r.stdout)["gpu_data"][0]
+        clks = [d["clock"][k]["clk"]["value"] for k in d["clock"] if k.startswith("gfx_")]
+        return d["power"]["socket_power"]["value"], clks
+
+    idle_p, idle_c = sample()
+    child = subprocess.Popen([sys.executable, "-u", os.path.abspath(__file__), "--workload", name,
+                              "--loop-seconds", str(seconds)], stdout=subprocess.PIPE, text=True)
+    time.sleep(min(2.0, seconds / 4))
+    samples = []
+    t0 = time.time()
+    while child.poll() is None and time.time() - t0 < seconds:
+        p, c = sample()
+        if statistics.mean(c) > 1000:           # busy: the loop has started
+            samples.append((p, c))
+        time.sleep(0.3)
+    out = child.communicate(timeout=300)[0]
+    rate = json.loads([ln for ln in out.splitlines() if ln.startswith("{")][-1])
+    res = {"power_sample": name, "seconds": seconds, "loop": rate, "idle_power_w": idle_p,
+           "samples": len(samples)}
+    if samples:
+        res.update({"power_w_mean": round(statistics.mean(s[0] for s in samples), 1),
+                    "power_w_min": min(s[0] for s in samples), "power_w_max": max(s[0] for s in samples),
+                    "gfx_clk_mhz_mean": round(statistics.mean(statistics.mean(s[1]) for s in samples), 1),
+                    "gfx_clk_mhz_xcd_min": min(min(s[1]) for s in samples),
+                    "gfx_clk_mhz_xcd_max": max(max(s[1]) for s in samples)})
+    print(json.dumps(res), flush=True)
+    return child.returncode
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -226,6 +313,10 @@ def main(argv=None):
                     help="storage order of B: row-major (gemm_run) or column-major (gemm_run_ex)")
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle work for cpu_baseline (0 to skip)")
+    ap.add_argument("--loop-seconds", type=float, default=0.0,
+                    help="instead of the timed bench, run --workload (or 'mfma_probe') back to back this long")
+    ap.add_argument("--power-sample", type=float, default=0.0, metavar="SECONDS",
+                    help="run --workload in a child process for SECONDS and sample power and clocks with amd-smi")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the GEMM, time a plain device copy of BYTES bytes "
                          "(the reference kernel for scaling HBM byte counters)")
@@ -236,6 +327,8 @@ def main(argv=None):
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         return 2
 
+    if args.power_sample > 0:
+        return power_sample(args.workload, args.power_sample)
     import torch
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
@@ -245,6 +338,8 @@ def main(argv=None):
 
     from dense_half_precision_tiled_amd import gemm as G
     G.load()
+    if args.loop_seconds > 0:
+        return loop_for(G, torch, args.workload, args.loop_seconds)
 
     main_res = measure(G, torch, args.workload, args.steps, args.warmup, args.instance, args.layout,
                        args.settle_ms)
