@@ -17,6 +17,11 @@ Printed: one JSON line with the contract fields plus
                 fp16 3000x5000x4099 shape, fp16 256^3).
 Before the warmups of each workload, untimed launches run for about
 --settle-ms so that the timed launches see a settled shader clock.
+
+Other modes: --copy-calibration (the plain copy that scales the HBM byte
+counters), --loop-seconds (one workload back to back, or the MFMA-only probe)
+and --power-sample (that loop in a child process, with amd-smi power and clock
+samples taken by this process, which never touches the GPU).
 """
 from __future__ import annotations
 
