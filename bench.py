@@ -40,15 +40,21 @@ METRIC = "GEMM TFLOP/s (2MNK/t) at 4096³ and 8192³ bf16/fp16; % of MFMA peak"
 PEAK_TFLOPS = 2500.0        # MI355X published dense fp16/bf16 MFMA peak
 HBM_GBPS = 8000.0           # MI355X published HBM3E bandwidth
 CODES = {("f16", "f32"): 0, ("f16", "f16"): 1, ("bf16", "f32"): 2, ("bf16", "bf16"): 3}
-KERNEL_SOURCES = ["dense_half_precision_tiled_amd/csrc/gemm_common.h",
-                  "dense_half_precision_tiled_amd/csrc/gemm_dl_kernel.h",
-                  "dense_half_precision_tiled_amd/csrc/gemm_ks_kernel.h",
-                  "dense_half_precision_tiled_amd/csrc/gemm_internal.h"]
+# The sources each kernel family is compiled from: a counter summary stays
+# valid for a workload while these are unchanged.
+FAMILY_SOURCES = {
+    "dl": ["dense_half_precision_tiled_amd/csrc/gemm_common.h",
+           "dense_half_precision_tiled_amd/csrc/gemm_dl_kernel.h",
+           "dense_half_precision_tiled_amd/csrc/gemm_internal.h"],
+    "ks": ["dense_half_precision_tiled_amd/csrc/gemm_common.h",
+           "dense_half_precision_tiled_amd/csrc/gemm_ks_kernel.h",
+           "dense_half_precision_tiled_amd/csrc/gemm_internal.h"],
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(family: str) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in FAMILY_SOURCES[family]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -135,19 +141,23 @@ def measure(G, torch, name, steps, warmup, instance=None, layout="row", settle_m
             "alg_bytes": 2 * (M * K + K * N) + (4 if w["out"] == "f32" else 2) * M * N}
 
 
-def traffic_from_profiles(name: str):
+def traffic_from_profiles(name: str, instance_name: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when that summary is missing or was taken on other kernel sources."""
+    None when that summary is missing, was taken on another kernel, or on
+    other sources of the kernel's family."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         with open(path) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
-    if d.get("kernel_source_hash") != kernel_source_hash():
-        return None
     entry = d.get("workloads", {}).get(name)
-    return None if entry is None else entry.get("hbm_bytes_per_launch")
+    family = instance_name.split("_")[0]
+    if entry is None or family not in FAMILY_SOURCES or entry.get("instance") != instance_name:
+        return None
+    if entry.get("source_hash") != kernel_source_hash(family):
+        return None
+    return entry.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(res, budget_s: float):
@@ -371,7 +381,8 @@ def main(argv=None):
             del r3
 
     w = main_res["w"]
-    traffic = traffic_from_profiles(args.workload + ("" if args.layout == "row" else "_col"))
+    traffic = traffic_from_profiles(args.workload + ("" if args.layout == "row" else "_col"),
+                                    main_res["instance"])
     line = {
         "metric": METRIC,
         "value": round(main_res["tflops"], 2),

@@ -45,10 +45,6 @@ namespace ks {
 
 using namespace dl;
 
-#ifndef KS_STAGES
-#define KS_STAGES 4
-#endif
-
 // s_waitcnt vmcnt(n) with n a compile-time constant.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -68,12 +64,14 @@ __global__ __launch_bounds__(256, 1) void gemm_ks_kernel(
     constexpr int R = TM + NBR;                            // LDS reads per wave per slice
     constexpr int A_BYTES = BM * 128, BROW = 2 * BN, B_BYTES = BK * BROW;   // BT: BN * 128, same
     constexpr int STAGE = A_BYTES + B_BYTES;               // 32 KiB
-    constexpr int NST = KS_STAGES;                         // stages in the ring
+    constexpr int NST = 4;                                 // stages in the ring (3, 4, 5 measure the same)
     constexpr int CA = BM / 32, CB = BN / 32;              // copies per wave per slice (1 KiB each)
     constexpr int COPIES = CA + CB;
     constexpr int B_ROWS_PER_COPY = 1024 / BROW;           // row-major B: 4 rows per copy
     constexpr int B_CHUNKS = BN / 8;                       // row-major B: 16-byte chunks per row
+    constexpr int RED_SLOT = 2 * 4 * 64 * 16;              // reduction: 2 blocks x 4 quads x 64 lanes x 16 B
     static_assert(NST * STAGE <= 160 * 1024, "LDS");
+    static_assert(NST * STAGE >= 12 * RED_SLOT, "the reduction's 12 slots reuse the stages");
     __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
     const uint32_t smem_base = (uint32_t)(size_t)(lds_char*)smem;
 
@@ -268,13 +266,16 @@ __global__ __launch_bounds__(256, 1) void gemm_ks_kernel(
     // the fixed order wave 0 + wave 1 + wave 2 + wave 3, and stores them.
     // Two rounds of two column blocks; in each, wave w writes its partial of
     // the other waves' row blocks into slot (v, w) (2 blocks x 4 quads x 16
-    // bytes per lane, lanes contiguous: 8 KiB) and keeps its own in
-    // registers.
+    // bytes per lane, lanes contiguous: 8 KiB; the 12 slots with v != w are
+    // numbered 3v + (w < v ? w : w - 1)) and keeps its own in registers.
     wait_vm<0>();
     __syncthreads();                                   // every wave is done with the stages
     const int gl = l >> 5;
     float4* red = reinterpret_cast<float4*>(smem);
-    auto slot = [&](int v, int src, int jj, int qd) { return ((((v * 4 + src) * 2 + jj) * 4 + qd) * 64) + l; };
+    auto slot = [&](int v, int src, int jj, int qd) {      // float4 index of slot (v, src), v != src
+        const int sl = 3 * v + (src < v ? src : src > v ? src - 1 : 0);   // src == v: any valid slot
+        return (((sl * 2 + jj) * 4 + qd) * 64) + l;
+    };
     const bool read_old = EPI && ep.beta != 0.0f;
     const int row_base = m0 + 32 * w + 4 * gl;
 #pragma unroll
