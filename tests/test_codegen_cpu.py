@@ -1,0 +1,119 @@
+"""Code-generation checks of the gfx950 kernels (CPU only: hipcc cross-compiles).
+
+Each instantiation unit is compiled to device assembly and every GEMM kernel in
+it is checked for properties the design relies on:
+* no scratch (spill) access between a kernel's first and last MFMA: the main
+  loop runs from registers and LDS only;
+* no scratch at all in the whole-tile kernels with the plain epilogue (the
+  configurations of the large workloads);
+* M0 is written only by the asynchronous-copy helper (its s_mov_b32 m0 is
+  followed by s_nop 0 and the global_load_lds it addresses), so no other code
+  can move a copy's LDS destination;
+* every kernel uses at most 512 VGPR+AGPR registers (one wave per SIMD) and the
+  MFMA instructions the design names.
+"""
+import concurrent.futures
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+from dense_half_precision_tiled_amd import build as B
+
+UNITS = ["gemm_dl_nn.hip", "gemm_dl_nn_epi.hip", "gemm_dl_tn.hip", "gemm_dl_tn_epi.hip",
+         "gemm_ks.hip", "gemm_ks_epi.hip"]
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.hipcc()), reason="hipcc not available")
+
+
+def _compile(unit, outdir):
+    out = os.path.join(outdir, unit + ".s")
+    cmd = [B.hipcc()] + [f for f in B.HIP_FLAGS if f != "-fPIC"] + \
+        ["--cuda-device-only", "-S", os.path.join(B.CSRC, unit), "-o", out]
+    subprocess.run(cmd, check=True, stderr=subprocess.DEVNULL)
+    return unit, out
+
+
+@pytest.fixture(scope="module")
+def kernels():
+    """{mangled kernel name: (unit, list of instruction lines, metadata dict)}."""
+    d = tempfile.mkdtemp(prefix="dhpt_asm_")
+    try:
+        with concurrent.futures.ThreadPoolExecutor(min(6, os.cpu_count() or 1)) as ex:
+            outs = list(ex.map(lambda u: _compile(u, d), UNITS))
+        res = {}
+        for unit, path in outs:
+            text = open(path).read().split("\n")
+            cur = None
+            for ln in text:
+                m = re.match(r"^(_ZN4dhpt\S*gemm_\w\w_kernel\S*):", ln)
+                if m:
+                    cur = m.group(1)
+                    res[cur] = (unit, [], {})
+                    continue
+                if cur is not None and ln.startswith(".Lfunc_end"):
+                    cur = None
+                elif cur is not None:
+                    s = ln.split(";")[0].strip()
+                    if s:
+                        res[cur][1].append(s)
+                m = re.match(r"^\s*\.set\s+(_ZN4dhpt\S*gemm_\w\w_kernel\S*)\.(\w+),\s*(\d+)", ln)
+                if m and m.group(1) in res:
+                    res[m.group(1)][2][m.group(2)] = int(m.group(3))
+        return res
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+
+
+def _short(name):
+    return re.search(r"kernelI(.*?)EEv", name).group(1)
+
+
+def test_every_unit_has_kernels(kernels):
+    units = {u for u, _, _ in kernels.values()}
+    assert units == set(UNITS)
+    assert len(kernels) >= 100
+
+
+def test_no_scratch_inside_the_mfma_loop(kernels):
+    for name, (unit, ins, meta) in kernels.items():
+        mf = [i for i, s in enumerate(ins) if s.startswith("v_mfma_f32_")]
+        assert mf, name
+        inside = [ins[i] for i in range(mf[0], mf[-1]) if ins[i].startswith("scratch_")]
+        assert not inside, "%s (%s): %d scratch accesses between MFMAs, e.g. %s" % (
+            _short(name), unit, len(inside), inside[0])
+
+
+def test_whole_tile_plain_kernels_use_no_scratch(kernels):
+    # template arguments <IN, OUT, BM, BN, FD, EDGE=0, BT, EPI=false> (dl) and
+    # <IN, OUT, EDGE=0, BT, EPI=false> (ks)
+    checked = 0
+    for name, (unit, ins, meta) in kernels.items():
+        args = re.findall(r"Li(\d+)E|Lb(\d)E", _short(name))
+        vals = [int(a or b) for a, b in args]
+        edge, epi = (vals[5], vals[7]) if "gemm_dl_kernel" in name else (vals[2], vals[4])
+        if edge == 0 and epi == 0:
+            assert meta.get("private_seg_size", 0) == 0, "%s uses %d bytes of scratch" % (
+                _short(name), meta["private_seg_size"])
+            checked += 1
+    assert checked >= 24
+
+
+def test_m0_is_written_only_by_the_copy_helper(kernels):
+    for name, (unit, ins, meta) in kernels.items():
+        for i, s in enumerate(ins):
+            if re.search(r"\bm0\b", s.split(",")[0] if "," in s else s) and not s.startswith("global_load_lds"):
+                # a write of m0: only the helper's s_mov_b32 m0, sN; s_nop 0; global_load_lds
+                assert s.startswith("s_mov_b32 m0,"), "%s: %s" % (_short(name), s)
+                assert ins[i + 1] == "s_nop 0", "%s: %s then %s" % (_short(name), s, ins[i + 1])
+                assert ins[i + 2].startswith("global_load_lds_dwordx4"), "%s: %s" % (_short(name), ins[i + 2])
+
+
+def test_register_budget_and_mfma_shape(kernels):
+    for name, (unit, ins, meta) in kernels.items():
+        assert meta["num_vgpr"] + meta["num_agpr"] <= 512, _short(name)
+        ops = {s.split()[0] for s in ins if s.startswith("v_mfma")}
+        assert ops <= {"v_mfma_f32_32x32x16_f16", "v_mfma_f32_32x32x16_bf16"}, (_short(name), ops)
