@@ -19,7 +19,7 @@ Before the warmups of each workload, untimed launches run for about
 --settle-ms so that the timed launches see a settled shader clock.
 
 Other modes: --copy-calibration (the plain copy that scales the HBM byte
-counters), --loop-seconds (one workload back to back, or the MFMA-only probe)
+counters), --loop-seconds (one workload back to back, or an MFMA-only probe)
 and --power-sample (that loop in a child process, with amd-smi power and clock
 samples taken by this process, which never touches the GPU).
 """
@@ -226,10 +226,35 @@ def copy_calibration(torch, nbytes: int, steps: int, warmup: int) -> int:
 
 
 def loop_for(G, torch, name, seconds: float) -> int:
-    """Run one workload (or, for name "mfma_probe", the MFMA issue-rate probe:
-    eight independent 32x32x16 bf16 chains per wave, one wave per SIMD on
-    every CU) back to back for `seconds`; print the achieved rate."""
-    if name == "mfma_probe":
+    """Run one workload back to back for `seconds` and print the achieved rate.
+    Besides the GEMM workloads, three MFMA-only probes (32x32x16, eight
+    independent accumulators per wave, one wave per SIMD on every CU):
+    "mfma_probe" with constant operands, and "mfma_probe_bf16_data" /
+    "mfma_probe_f16_data" with operands drawn like the bf16 (N(0,1)) and fp16
+    (U[-1,1)) workloads' inputs, rotating so that consecutive MFMAs see new
+    values as in a GEMM."""
+    if name in ("mfma_probe_bf16_data", "mfma_probe_f16_data"):
+        import ctypes
+        from dense_half_precision_tiled_amd import inputs
+        P = ctypes.CDLL(os.path.join(ROOT, "tests", "probes", "libdhpt_probes.so"))
+        P.probe_mfma_data.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        bf16 = int(name == "mfma_probe_bf16_data")
+        bits = inputs.normal((16 * 64 * 8,), 7, inputs.BF16) if bf16 else inputs.uniform((16 * 64 * 8,), 7, inputs.F16)
+        ops = upload(bits, torch)
+        blocks, iters = 256, 50000
+        sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+        n, ms, t0 = 0, 0.0, time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if P.probe_mfma_data(bf16, blocks, iters, ops.data_ptr(), sink.data_ptr()) != 0:
+                raise RuntimeError("probe launch failed")
+            e1.record()
+            torch.cuda.synchronize()
+            ms += e0.elapsed_time(e1)
+            n += 1
+        flops = n * blocks * 4 * iters * 32 * 32768.0
+    elif name == "mfma_probe":
         import ctypes
         P = ctypes.CDLL(os.path.join(ROOT, "tests", "probes", "libdhpt_probes.so"))
         P.probe_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
@@ -329,7 +354,8 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle work for cpu_baseline (0 to skip)")
     ap.add_argument("--loop-seconds", type=float, default=0.0,
-                    help="instead of the timed bench, run --workload (or 'mfma_probe') back to back this long")
+                    help="instead of the timed bench, run --workload (or one of the MFMA-only probes 'mfma_probe', "
+                         "'mfma_probe_bf16_data', 'mfma_probe_f16_data') back to back this long")
     ap.add_argument("--power-sample", type=float, default=0.0, metavar="SECONDS",
                     help="run --workload in a child process for SECONDS and sample power and clocks with amd-smi")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",

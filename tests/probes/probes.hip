@@ -114,6 +114,45 @@ __global__ __launch_bounds__(256) void probe_mfma_rate_kernel(int iters, uint64_
     if (s == 12345.0f) sink[0] = s;
 }
 
+// The same MFMA stream fed with data: every lane loads 16 operand register
+// sets (8 for A, 8 for B, 16 bytes each) from ops[16 * 64] and the MFMAs of
+// one iteration rotate through them, so consecutive MFMAs see different
+// operands as in a GEMM's k-loop (the constant-operand kernel above keeps the
+// multiplier inputs still).  iters x 32 MFMAs per wave; one wave per SIMD.
+template <bool BF16>
+__global__ __launch_bounds__(256, 1) void probe_mfma_data_kernel(const u32x4* ops, int iters, float* sink) {
+    const int l = threadIdx.x & 63;
+    u32x4 a[8], b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = ops[(2 * i) * 64 + l];
+        b[i] = ops[(2 * i + 1) * 64 + l];
+    }
+    f32x16 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = (f32x16){};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const u32x4 av = a[(i + r) & 7], bv = b[(i + 3 * r) & 7];
+                if constexpr (BF16)
+                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                                     __builtin_bit_cast(bf16x8, bv), acc[i], 0, 0, 0);
+                else
+                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, av),
+                                                                    __builtin_bit_cast(f16x8, bv), acc[i], 0, 0, 0);
+            }
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s += acc[i][e];
+    if (s == 12345.0f) sink[0] = s;
+}
+
 // LDS throughput: every wave of 4 per block issues `iters` x 8 LDS
 // instructions of one kind and lane 0 records the shader cycles.  Lane l of
 // wave w uses byte address addr[64 w + l] (masked to the 64 KiB buffer and
@@ -322,6 +361,16 @@ int probe_mfma_rate(int bf16, int blocks, int iters, uint64_t* cycles, float* si
         hipLaunchKernelGGL(probe_mfma_rate_kernel<true>, dim3(blocks), dim3(256), 0, 0, iters, cycles, sink);
     else
         hipLaunchKernelGGL(probe_mfma_rate_kernel<false>, dim3(blocks), dim3(256), 0, 0, iters, cycles, sink);
+    return (int)hipDeviceSynchronize();
+}
+
+// ops: 16 x 64 lanes x 16 bytes of fp16 (bf16 = 0) or bf16 (bf16 = 1) values.
+int probe_mfma_data(int bf16, int blocks, int iters, const void* ops, float* sink) {
+    const u32x4* o = (const u32x4*)ops;
+    if (bf16)
+        hipLaunchKernelGGL(probe_mfma_data_kernel<true>, dim3(blocks), dim3(256), 0, 0, o, iters, sink);
+    else
+        hipLaunchKernelGGL(probe_mfma_data_kernel<false>, dim3(blocks), dim3(256), 0, 0, o, iters, sink);
     return (int)hipDeviceSynchronize();
 }
 
