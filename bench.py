@@ -9,6 +9,12 @@ untimed warmups.  TFLOP/s counts 2MNK per step.
 
 Printed: one JSON line with the contract fields plus
   roofline      the GEMM kernel against the dense bf16/fp16 MFMA peak;
+  repeats       the timed launches cut into five equal repeats (events on the
+                launch stream): mean, median, min and max of their per-launch
+                means;
+  cold_l2       single launches of the main workload, each after reading a
+                512 MiB buffer so that neither the L2s nor the Infinity Cache
+                hold A or B (the repeated launches above run warm);
   cpu_baseline  the CPU fp64 oracle timed on a bounded sample of output rows
                 of the same workload on this host (and those rows checked
                 against the GPU result);
@@ -117,16 +123,23 @@ def measure(G, torch, name, steps, warmup, instance=None, layout="row", settle_m
     for _ in range(warmup):
         launch()
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
+    # The timed launches are cut into up to five equal repeats by events on
+    # the launch stream; the step time is over all of them, and the spread of
+    # the per-repeat means is reported beside it.
+    nrep = max(1, min(5, steps))
+    bounds = [round(i * steps / nrep) for i in range(nrep + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in bounds]
+    evs[0].record(stream)
     t0 = time.perf_counter()
-    for _ in range(steps):
-        launch()
-    ev1.record(stream)
+    for i in range(nrep):
+        for _ in range(bounds[i + 1] - bounds[i]):
+            launch()
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / steps
+    ms = evs[0].elapsed_time(evs[-1]) / max(steps, 1)
+    rep_ms = [evs[i].elapsed_time(evs[i + 1]) / (bounds[i + 1] - bounds[i])
+              for i in range(nrep) if bounds[i + 1] > bounds[i]]
     flops = 2.0 * M * N * K
     if instance is not None:
         inst = instance
@@ -136,9 +149,44 @@ def measure(G, torch, name, steps, warmup, instance=None, layout="row", settle_m
     else:
         inst = G.gemm_select_instance(M, N, K, code, tA.data_ptr(), K, tB.data_ptr(), N,
                                       tC.data_ptr(), N)
-    return {"name": name, "w": w, "A": A, "B": B, "C": tC, "ms": ms, "wall_s": wall, "settle_launches": n_settle,
+    return {"name": name, "w": w, "A": A, "B": B, "C": tC, "ms": ms, "rep_ms": rep_ms, "launch": launch,
+            "wall_s": wall, "settle_launches": n_settle,
             "tflops": flops / (ms * 1e-3) / 1e12, "instance": G.gemm_instance_name(inst),
             "alg_bytes": 2 * (M * K + K * N) + (4 if w["out"] == "f32" else 2) * M * N}
+
+
+def repeats(res):
+    import statistics
+    r = res["rep_ms"]
+    return {"n": len(r), "ms_mean": round(statistics.mean(r), 5), "ms_median": round(statistics.median(r), 5),
+            "ms_min": round(min(r), 5), "ms_max": round(max(r), 5)}
+
+
+def measure_cold(torch, res, launches: int, flush_bytes: int = 512 << 20):
+    """Single launches with cold caches: before each, read a buffer larger
+    than the L2s and the Infinity Cache together (a sum over it, so the
+    caches hold only clean lines of that buffer), then time the one launch
+    with events on its stream."""
+    import statistics
+    flush = torch.ones(flush_bytes // 4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(launches):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        total = flush.sum()
+        e0.record(stream)
+        res["launch"]()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if int(total.item()) != flush_bytes // 4:
+            raise RuntimeError("flush buffer read back wrong")
+        times.append(e0.elapsed_time(e1))
+    del flush
+    w = res["w"]
+    ms = statistics.mean(times)
+    return {"launches": launches, "flush_bytes": flush_bytes, "ms_mean": round(ms, 5),
+            "ms_median": round(statistics.median(times), 5),
+            "value": round(2.0 * w["M"] * w["N"] * w["K"] / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s"}
 
 
 def traffic_from_profiles(name: str, instance_name: str):
@@ -353,6 +401,9 @@ def main(argv=None):
                     help="storage order of B: row-major (gemm_run) or column-major (gemm_run_ex)")
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle work for cpu_baseline (0 to skip)")
+    ap.add_argument("--cold", type=int, default=5, metavar="LAUNCHES",
+                    help="also time this many single launches of the main workload with cold caches "
+                         "(a 512 MiB buffer read before each; 0 to skip)")
     ap.add_argument("--loop-seconds", type=float, default=0.0,
                     help="instead of the timed bench, run --workload (or one of the MFMA-only probes 'mfma_probe', "
                          "'mfma_probe_bf16_data', 'mfma_probe_f16_data') back to back this long")
@@ -390,7 +441,7 @@ def main(argv=None):
         return {"workload": describe(w2), "value": round(r["tflops"], 2), "unit": "TFLOP/s",
                 "ms_per_step": round(r["ms"], 5), "frac_of_peak": round(r["tflops"] / PEAK_TFLOPS, 4),
                 "hbm_gbps_algorithmic": round(r["alg_bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
-                "kernel": r["instance"]}
+                "kernel": r["instance"], "repeats": repeats(r)}
 
     sec = None
     if args.secondary and args.secondary != "none":
@@ -432,6 +483,9 @@ def main(argv=None):
                      "algorithmic_bytes": main_res["alg_bytes"],
                      "hbm_gbps_algorithmic": round(main_res["alg_bytes"] / (main_res["ms"] * 1e-3) / 1e9, 1)},
     }
+    line["repeats"] = repeats(main_res)
+    if args.cold > 0:
+        line["cold_l2"] = measure_cold(torch, main_res, args.cold)
     if sec is not None:
         line["secondary"] = sec
     if others:
