@@ -250,7 +250,23 @@ def cpu_baseline(res, budget_s: float):
                       % (rows.size, M, N, K, t),
             "seconds": round(t, 3),
             "parity_on_sample": {"ok": check["ok"], "max_abs": check["max_abs"],
-                                 "max_rel": check["max_rel"], "n_bad": check["n_bad"]}}
+                                 "max_rel": check["max_rel"], "n_bad": check["n_bad"]},
+            "single_thread": single_thread_oracle()}
+
+
+def single_thread_oracle():
+    """Per-core figure: the whole fp16 256^3 product on one host thread."""
+    from dense_half_precision_tiled_amd import inputs
+    import oracle
+    A, B, w = inputs.workload_inputs("f16_256")
+    best = float("inf")
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.gemm_f64(A, B, w["fmt"], 1)
+        best = min(best, time.perf_counter() - t0)
+    return {"workload": "fp16 256x256x256, full product", "threads": 1,
+            "value": round(2.0 * w["M"] * w["N"] * w["K"] / best / 1e9, 3), "unit": "GFLOP/s",
+            "seconds": round(best, 4)}
 
 
 def copy_calibration(torch, nbytes: int, steps: int, warmup: int) -> int:

@@ -202,6 +202,22 @@ def test_tile_order_is_a_bijection(lib, shape):
         assert np.unique(flat).size == flat.size
 
 
+def _panels(tm, tn):
+    """Distinct A row-panels plus B column-panels that a set of tiles needs."""
+    return np.unique(tm).size + np.unique(tn).size
+
+
+def test_panel_count_page_example():
+    """The page's count for eight tiles in flight ("The Asynchronous Kernel:
+    Tensor Cores & TMA", section "Scheduling is geometry"): eight tiles along
+    one row of the tile grid need one A panel and eight B panels, nine in
+    all; the same eight as a 4x2 block need four and two, six."""
+    row = np.arange(8)
+    assert _panels(np.zeros(8, int), row) == 9
+    blk_m, blk_n = np.divmod(np.arange(8), 2)
+    assert _panels(blk_m, blk_n) == 6
+
+
 @pytest.mark.parametrize("n", [4096, 8192])
 def test_tile_order_keeps_each_xcd_compact(lib, n):
     """The first 32 workgroups dealt to one XCD (w = x, x+8, x+16, ... under
@@ -212,6 +228,6 @@ def test_tile_order_keeps_each_xcd_compact(lib, n):
     tiles_n = n // 256
     for x in range(8):
         sel = np.arange(x, 256, 8)
-        panels = np.unique(tm[sel]).size + np.unique(tn[sel]).size
+        panels = _panels(tm[sel], tn[sel])
         row_major = np.unique(sel // tiles_n).size + np.unique(sel % tiles_n).size
         assert panels <= 12 and panels <= row_major, (x, panels, row_major)
