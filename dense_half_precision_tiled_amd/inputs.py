@@ -1,11 +1,13 @@
 """Seeded synthetic inputs for C = A.B (shared by the GPU tests, the bench and
 the oracle's tests; it holds no GEMM arithmetic).
 
-Every generator returns row-major ``uint16`` bit patterns of fp16 or bf16
-values.  Samples come from ``numpy.random.Generator(PCG64(seed))``.  They are
-rounded to the half format by a library conversion: numpy's correctly rounded
-float64 -> float16 cast for fp16, torch's float32 -> bfloat16 cast (round to
-nearest, ties to even) for bf16.
+Every generator returns row-major bit patterns: ``uint16`` for fp16 and bf16
+values, ``uint8`` for the 8-bit float formats E4M3 and E5M2 (OCP OFP8).
+Samples come from ``numpy.random.Generator(PCG64(seed))``.  They are rounded
+to the input format by a library conversion: numpy's correctly rounded
+float64 -> float16 cast for fp16, torch's float32 -> bfloat16 /
+float8_e4m3fn / float8_e5m2 casts (round to nearest, ties to even) for the
+others.
 
 Workload recipes (the shapes and value laws of the GEMM configurations):
 
@@ -21,7 +23,8 @@ from __future__ import annotations
 
 import numpy as np
 
-F16, BF16 = "f16", "bf16"
+F16, BF16, E4M3, E5M2 = "f16", "bf16", "e4m3", "e5m2"
+EIGHT_BIT = (E4M3, E5M2)
 
 
 def _rng(seed: int) -> np.random.Generator:
@@ -35,6 +38,13 @@ def _to_bits(x: np.ndarray, fmt: str) -> np.ndarray:
         import torch
         t = torch.from_numpy(np.ascontiguousarray(x.astype(np.float32)))
         return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    if fmt in EIGHT_BIT:
+        import torch
+        dt = torch.float8_e4m3fn if fmt == E4M3 else torch.float8_e5m2
+        t = torch.from_numpy(np.ascontiguousarray(x.astype(np.float32))).to(dt)
+        if not bool(torch.isfinite(t.to(torch.float32)).all()):
+            raise ValueError("value outside the range of %s" % fmt)
+        return t.view(torch.uint8).numpy().copy()
     raise ValueError("unknown format %r" % (fmt,))
 
 
@@ -43,7 +53,7 @@ def uniform(shape, seed: int, fmt: str = F16, lo: float = -1.0, hi: float = 1.0)
 
 
 def normal(shape, seed: int, fmt: str = BF16) -> np.ndarray:
-    if fmt == BF16:
+    if fmt == BF16 or fmt in EIGHT_BIT:
         x = _rng(seed).standard_normal(size=shape, dtype=np.float32)
     else:
         x = _rng(seed).standard_normal(size=shape)
@@ -65,14 +75,17 @@ def from_values(values, fmt: str) -> np.ndarray:
     return bits
 
 
-def padded(bits: np.ndarray, ld: int, fill: int = 0x7E00) -> np.ndarray:
+def padded(bits: np.ndarray, ld: int, fill: int | None = None) -> np.ndarray:
     """Copy a rows x cols matrix into a rows x ld buffer (ld >= cols); the
-    padding columns hold ``fill`` (a NaN pattern by default, so any read of
-    them shows up in the result).  Returns the full rows x ld array."""
+    padding columns hold ``fill`` (by default a NaN pattern of the format:
+    0x7E00 for 16-bit, 0x7F for 8-bit patterns, so any read of them shows up
+    in the result).  Returns the full rows x ld array."""
     rows, cols = bits.shape
     if ld < cols:
         raise ValueError("ld < cols")
-    out = np.full((rows, ld), fill, dtype=np.uint16)
+    if fill is None:
+        fill = 0x7F if bits.dtype == np.uint8 else 0x7E00
+    out = np.full((rows, ld), fill, dtype=bits.dtype)
     out[:, :cols] = bits
     return out
 
@@ -85,6 +98,10 @@ WORKLOADS = {
     "bf16_4096": dict(M=4096, N=4096, K=4096, fmt=BF16, out="bf16", law="normal", c=3),
     "bf16_8192": dict(M=8192, N=8192, K=8192, fmt=BF16, out="bf16", law="normal", c=4),
     "f16_ragged": dict(M=3000, N=5000, K=4099, fmt=F16, out="f16", law="uniform", c=5),
+    # 8-bit float inputs; these run with B stored column-major
+    "e4m3_8192": dict(M=8192, N=8192, K=8192, fmt=E4M3, out="bf16", law="normal", c=6),
+    "e4m3_4096": dict(M=4096, N=4096, K=4096, fmt=E4M3, out="bf16", law="normal", c=7),
+    "e5m2_8192": dict(M=8192, N=8192, K=8192, fmt=E5M2, out="bf16", law="normal", c=8),
 }
 
 

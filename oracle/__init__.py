@@ -11,7 +11,9 @@ the comparison rule that decides parity:
 * ``gemm_f64`` / ``gemm_rows_f64``: C[i][j] = sum_k A[i][k]*B[k][j] in fp64, k
   ascending, on exactly decoded fp16/bf16 inputs (the "arithmetic correctness
   reference" of "GEMM From Naive CUDA to Tensor Cores", section "The
-  two-reference testing protocol").
+  two-reference testing protocol"), or on 8-bit float inputs in the OCP OFP8
+  E4M3 / E5M2 formats (uint8 bit patterns; the 8-bit float the Ada
+  tensor-core GEMM write-up leaves untested).
 * ``round_to`` / ``ulp``: IEEE round-to-nearest-even to fp32/fp16/bf16 and the
   spacing of those formats (same page, section "What FP32 accumulation
   preserves, and what it can't recover").
@@ -34,7 +36,7 @@ import subprocess
 
 import numpy as np
 
-IN_F16, IN_BF16 = 0, 1
+IN_F16, IN_BF16, IN_E4M3, IN_E5M2 = 0, 1, 2, 3
 OUT_F32, OUT_F16, OUT_BF16 = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -63,7 +65,7 @@ def _load():
 
 def _declare(lib):
     """Set the argument and result types of the oracle's exported functions."""
-    i64, u16p, f64p, i64p = (ctypes.c_int64, ctypes.POINTER(ctypes.c_uint16),
+    i64, u16p, f64p, i64p = (ctypes.c_int64, ctypes.c_void_p,
                              ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64))
     lib.oracle_gemm_f64.argtypes = [i64, i64, i64, ctypes.c_int, u16p, i64, u16p, i64,
                                     f64p, i64, ctypes.c_int]
@@ -85,6 +87,10 @@ def _declare(lib):
     lib.oracle_decode_f16.restype = ctypes.c_double
     lib.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
     lib.oracle_decode_bf16.restype = ctypes.c_double
+    lib.oracle_decode_e4m3.argtypes = [ctypes.c_uint8]
+    lib.oracle_decode_e4m3.restype = ctypes.c_double
+    lib.oracle_decode_e5m2.argtypes = [ctypes.c_uint8]
+    lib.oracle_decode_e5m2.restype = ctypes.c_double
     return lib
 
 
@@ -92,12 +98,25 @@ def _ptr(a: np.ndarray, ctype):
     return a.ctypes.data_as(ctypes.POINTER(ctype))
 
 
+def _vptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
 def _fmt_in(in_fmt) -> int:
     if in_fmt in ("f16", "fp16", "float16", IN_F16):
         return IN_F16
     if in_fmt in ("bf16", "bfloat16", IN_BF16):
         return IN_BF16
+    if in_fmt in ("e4m3", IN_E4M3):
+        return IN_E4M3
+    if in_fmt in ("e5m2", IN_E5M2):
+        return IN_E5M2
     raise ValueError("unknown input format %r" % (in_fmt,))
+
+
+def _bits_dtype(in_fmt):
+    """Storage of one input bit pattern: uint8 for the 8-bit formats."""
+    return np.uint8 if _fmt_in(in_fmt) in (IN_E4M3, IN_E5M2) else np.uint16
 
 
 def _fmt_out(out_fmt) -> int:
@@ -110,15 +129,21 @@ def _fmt_out(out_fmt) -> int:
     raise ValueError("unknown output format %r" % (out_fmt,))
 
 
-def _as_bits_2d(x: np.ndarray) -> np.ndarray:
+def _as_bits_2d(x: np.ndarray, in_fmt) -> np.ndarray:
     x = np.asarray(x)
-    if x.dtype != np.uint16:
-        raise TypeError("oracle inputs are uint16 bit patterns, got %s" % x.dtype)
+    want = _bits_dtype(in_fmt)
+    if x.dtype != want:
+        raise TypeError("%s inputs are %s bit patterns, got %s" % (in_fmt, np.dtype(want).name, x.dtype))
     if x.ndim != 2:
         raise ValueError("oracle inputs are 2-D")
-    if x.strides[1] != 2:
+    if x.strides[1] != x.itemsize:
         x = np.ascontiguousarray(x)
     return x
+
+
+def _ld(x: np.ndarray) -> int:
+    """Row stride of a 2-D bit array in elements."""
+    return x.strides[0] // x.itemsize
 
 
 def default_threads() -> int:
@@ -129,16 +154,15 @@ def default_threads() -> int:
 
 
 def gemm_f64(A_bits, B_bits, in_fmt, threads: int | None = None) -> np.ndarray:
-    """Full C = A.B in fp64 from fp16/bf16 bit patterns (row-major, any row stride)."""
-    A = _as_bits_2d(A_bits)
-    B = _as_bits_2d(B_bits)
+    """Full C = A.B in fp64 from input bit patterns (row-major, any row stride)."""
+    A = _as_bits_2d(A_bits, in_fmt)
+    B = _as_bits_2d(B_bits, in_fmt)
     M, K = A.shape
     K2, N = B.shape
     if K != K2:
         raise ValueError("inner dimensions differ: %d vs %d" % (K, K2))
     C = np.zeros((M, N), dtype=np.float64)
-    rc = _load().oracle_gemm_f64(M, N, K, _fmt_in(in_fmt), _ptr(A, ctypes.c_uint16),
-                                 A.strides[0] // 2, _ptr(B, ctypes.c_uint16), B.strides[0] // 2,
+    rc = _load().oracle_gemm_f64(M, N, K, _fmt_in(in_fmt), _vptr(A), _ld(A), _vptr(B), _ld(B),
                                  _ptr(C, ctypes.c_double), N, threads or default_threads())
     if rc != 0:
         raise MemoryError("oracle allocation failed")
@@ -147,8 +171,8 @@ def gemm_f64(A_bits, B_bits, in_fmt, threads: int | None = None) -> np.ndarray:
 
 def gemm_rows_f64(A_bits, B_bits, rows, in_fmt, threads: int | None = None) -> np.ndarray:
     """Rows ``rows`` of C = A.B in fp64 (len(rows) x N)."""
-    A = _as_bits_2d(A_bits)
-    B = _as_bits_2d(B_bits)
+    A = _as_bits_2d(A_bits, in_fmt)
+    B = _as_bits_2d(B_bits, in_fmt)
     M, K = A.shape
     K2, N = B.shape
     if K != K2:
@@ -158,8 +182,7 @@ def gemm_rows_f64(A_bits, B_bits, rows, in_fmt, threads: int | None = None) -> n
         raise IndexError("row index out of range")
     C = np.zeros((r.size, N), dtype=np.float64)
     rc = _load().oracle_gemm_rows_f64(r.size, _ptr(r, ctypes.c_int64), N, K, _fmt_in(in_fmt),
-                                      _ptr(A, ctypes.c_uint16), A.strides[0] // 2,
-                                      _ptr(B, ctypes.c_uint16), B.strides[0] // 2,
+                                      _vptr(A), _ld(A), _vptr(B), _ld(B),
                                       _ptr(C, ctypes.c_double), N, threads or default_threads())
     if rc != 0:
         raise MemoryError("oracle allocation failed")
@@ -167,11 +190,10 @@ def gemm_rows_f64(A_bits, B_bits, rows, in_fmt, threads: int | None = None) -> n
 
 
 def decode(bits, in_fmt) -> np.ndarray:
-    """fp16/bf16 bit patterns -> exact float64 values (oracle's own decoder)."""
-    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    """Input bit patterns -> exact float64 values (oracle's own decoder)."""
+    b = np.ascontiguousarray(np.asarray(bits, dtype=_bits_dtype(in_fmt)))
     out = np.empty(b.shape, dtype=np.float64)
-    _load().oracle_decode_array(_fmt_in(in_fmt), _ptr(b, ctypes.c_uint16),
-                                _ptr(out, ctypes.c_double), b.size)
+    _load().oracle_decode_array(_fmt_in(in_fmt), _vptr(b), _ptr(out, ctypes.c_double), b.size)
     return out
 
 
@@ -254,8 +276,8 @@ def gemm_ex_f64(A_bits, B_bits, in_fmt, b_layout="row", alpha=1.0, beta=0.0, C_o
     is given); ignored when beta == 0.  bias: N float64 values or None.
     relu: apply max(x, 0) last.  rows: output rows to compute (None = all).
     """
-    A = _as_bits_2d(A_bits)
-    B = _as_bits_2d(B_bits)
+    A = _as_bits_2d(A_bits, in_fmt)
+    B = _as_bits_2d(B_bits, in_fmt)
     lay = _layout(b_layout)
     M, K = A.shape
     K2, N = B.shape if lay == B_ROW_MAJOR else B.shape[::-1]
@@ -283,8 +305,7 @@ def gemm_ex_f64(A_bits, B_bits, in_fmt, b_layout="row", alpha=1.0, beta=0.0, C_o
             raise ValueError("bias must have N = %d values" % N)
         bias_p = _ptr(bz, ctypes.c_double)
     rc = _load().oracle_gemm_ex_f64(r.size, _ptr(r, ctypes.c_int64), N, K, _fmt_in(in_fmt), lay,
-                                    _ptr(A, ctypes.c_uint16), A.strides[0] // 2,
-                                    _ptr(B, ctypes.c_uint16), B.strides[0] // 2,
+                                    _vptr(A), _ld(A), _vptr(B), _ld(B),
                                     float(alpha), float(beta), cold_p, ldcold, bias_p,
                                     1 if relu else 0, _ptr(C, ctypes.c_double), N,
                                     threads or default_threads())

@@ -13,14 +13,18 @@
  *   ("GEMM From Naive CUDA to Tensor Cores", opening section and
  *   "Compute one output before launching a warp").
  *
- * Precision contract: the inputs are fp16 or bf16 bit patterns.  Each one is
- * decoded exactly to a double by the bit-level decoders below, and the dot
- * product is accumulated in double, k ascending for every (i, j).  This is the
+ * Precision contract: the inputs are fp16 or bf16 bit patterns (uint16), or
+ * 8-bit float patterns (uint8) in the E4M3 or E5M2 formats of the OCP 8-bit
+ * floating point specification (OFP8), the 8-bit float the Ada tensor-core
+ * GEMM write-up leaves as its untested next step.  Each one is decoded
+ * exactly to a double by the bit-level decoders below, and the dot product is
+ * accumulated in double, k ascending for every (i, j).  This is the
  * "arithmetic correctness reference" of the two-reference protocol on the same
  * page (section "The two-reference testing protocol": round the inputs to the
  * half format, then accumulate in FP64).  Products of two fp16 (11-bit
- * significand) or two bf16 (8-bit significand) values are exact in double, so
- * the only rounding is the fp64 summation, bounded by (K-1) * 2^-53 * sum|a*b|.
+ * significand), two bf16 (8-bit) or two 8-bit float (4- or 3-bit) values are
+ * exact in double, so the only rounding is the fp64 summation, bounded by
+ * (K-1) * 2^-53 * sum|a*b|.
  *
  * Output rounding: oracle_round_to() rounds a double to fp32, fp16 or bf16
  * with IEEE round-to-nearest, ties to even (the mode the rounding demo in
@@ -46,7 +50,10 @@
  * Parity pins (tests/test_oracle_pins.py): the page's 2x3 . 3x2 worked example,
  * exact rational brute force on tiny shapes, closed forms (all-ones,
  * identity, permutation, rank-1), the two-reference example, the fp16 rounding
- * table of the precision section, and numpy's IEEE float16 conversion.
+ * table of the precision section, and numpy's IEEE float16 conversion.  The
+ * 8-bit formats (tests/test_oracle_f8_pins.py): every code against torch's
+ * float8 types, E5M2 as the top byte of binary16, the OFP8 limits, exact
+ * rationals and int64 matmuls.
  */
 #include <math.h>
 #include <pthread.h>
@@ -54,7 +61,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORACLE_IN_F16 = 0, ORACLE_IN_BF16 = 1 };
+enum { ORACLE_IN_F16 = 0, ORACLE_IN_BF16 = 1, ORACLE_IN_E4M3 = 2, ORACLE_IN_E5M2 = 3 };
 enum { ORACLE_OUT_F32 = 0, ORACLE_OUT_F16 = 1, ORACLE_OUT_BF16 = 2 };
 enum { ORACLE_B_ROW_MAJOR = 0, ORACLE_B_COL_MAJOR = 1 };
 
@@ -90,8 +97,50 @@ double oracle_decode_bf16(uint16_t h) {
     return sign ? -v : v;
 }
 
-static double decode_one(int in_fmt, uint16_t h) {
-    return in_fmt == ORACLE_IN_BF16 ? oracle_decode_bf16(h) : oracle_decode_f16(h);
+/* OFP8 E4M3: 1 sign bit, 4 exponent bits (bias 7), 3 fraction bits, no
+ * infinities; exponent 15 with fraction 7 is NaN, so exponent 15 otherwise
+ * holds normal numbers (largest 448).
+ * Normal:    (8 + f) * 2^(e - 10)         Subnormal: f * 2^-9 */
+double oracle_decode_e4m3(uint8_t b) {
+    int sign = (b >> 7) & 1;
+    int e = (b >> 3) & 0xf;
+    int f = b & 0x7;
+    double v;
+    if (e == 15 && f == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)f, -9);
+    else
+        v = ldexp((double)(8 + f), e - 10);
+    return sign ? -v : v;
+}
+
+/* OFP8 E5M2: 1 sign bit, 5 exponent bits (bias 15), 2 fraction bits, IEEE
+ * special values (exponent 31: infinity for fraction 0, else NaN).
+ * Normal:    (4 + f) * 2^(e - 17)         Subnormal: f * 2^-16 */
+double oracle_decode_e5m2(uint8_t b) {
+    int sign = (b >> 7) & 1;
+    int e = (b >> 2) & 0x1f;
+    int f = b & 0x3;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -16);
+    else if (e == 31)
+        v = (f != 0) ? NAN : INFINITY;
+    else
+        v = ldexp((double)(4 + f), e - 17);
+    return sign ? -v : v;
+}
+
+/* Element idx of an operand stored as bit patterns of in_fmt: uint16 for
+ * the 16-bit formats, uint8 for the 8-bit ones. */
+static double load_in(int in_fmt, const void* base, int64_t idx) {
+    switch (in_fmt) {
+    case ORACLE_IN_BF16: return oracle_decode_bf16(((const uint16_t*)base)[idx]);
+    case ORACLE_IN_E4M3: return oracle_decode_e4m3(((const uint8_t*)base)[idx]);
+    case ORACLE_IN_E5M2: return oracle_decode_e5m2(((const uint8_t*)base)[idx]);
+    default:             return oracle_decode_f16(((const uint16_t*)base)[idx]);
+    }
 }
 
 /* Round-to-nearest-even of a non-negative double q to an integer, written
@@ -151,8 +200,8 @@ double oracle_ulp(int out_fmt, double r) {
     return ldexp(1.0, e - p + 1);
 }
 
-void oracle_decode_array(int in_fmt, const uint16_t* src, double* dst, int64_t n) {
-    for (int64_t t = 0; t < n; ++t) dst[t] = decode_one(in_fmt, src[t]);
+void oracle_decode_array(int in_fmt, const void* src, double* dst, int64_t n) {
+    for (int64_t t = 0; t < n; ++t) dst[t] = load_in(in_fmt, src, t);
 }
 
 /* ------------------------------------------------------------------------
@@ -161,7 +210,7 @@ void oracle_decode_array(int in_fmt, const uint16_t* src, double* dst, int64_t n
  * which is k ascending for every (i, j).  B is decoded once into doubles.
  * ------------------------------------------------------------------------ */
 typedef struct {
-    const uint16_t* A; int64_t lda;
+    const void* A; int64_t lda;      /* elements of in_fmt */
     const double* Bd;              /* K x N decoded, row-major, stride N */
     double* C; int64_t ldc;
     const int64_t* rows;           /* NULL: rows r0..r1-1 of A; else rows[r] */
@@ -176,9 +225,8 @@ static void* oracle_worker(void* arg) {
         int64_t i = jb->rows ? jb->rows[r] : r;
         double* c = jb->C + r * jb->ldc;
         for (int64_t j = 0; j < jb->N; ++j) c[j] = 0.0;
-        const uint16_t* arow = jb->A + i * jb->lda;
         for (int64_t k = 0; k < jb->K; ++k) {
-            double a = decode_one(jb->in_fmt, arow[k]);
+            double a = load_in(jb->in_fmt, jb->A, i * jb->lda + k);
             const double* b = jb->Bd + k * jb->N;
             for (int64_t j = 0; j < jb->N; ++j) c[j] += a * b[j];
         }
@@ -187,7 +235,7 @@ static void* oracle_worker(void* arg) {
 }
 
 static int run_rows(int in_fmt, int b_layout, int64_t nrows, const int64_t* rows, int64_t N,
-                    int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                    int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
                     double* C, int64_t ldc, int nthreads) {
     if (nrows <= 0 || N <= 0) return 0;
     double* Bd = NULL;
@@ -197,10 +245,10 @@ static int run_rows(int in_fmt, int b_layout, int64_t nrows, const int64_t* rows
         if (b_layout == ORACLE_B_COL_MAJOR) {
             /* B(k, j) = B[j*ldb + k]: column j of the K x N operand is row j in memory */
             for (int64_t j = 0; j < N; ++j)
-                for (int64_t k = 0; k < K; ++k) Bd[k * N + j] = decode_one(in_fmt, B[j * ldb + k]);
+                for (int64_t k = 0; k < K; ++k) Bd[k * N + j] = load_in(in_fmt, B, j * ldb + k);
         } else {
             for (int64_t k = 0; k < K; ++k)
-                oracle_decode_array(in_fmt, B + k * ldb, Bd + k * N, N);
+                for (int64_t j = 0; j < N; ++j) Bd[k * N + j] = load_in(in_fmt, B, k * ldb + j);
         }
     }
     if (nthreads < 1) nthreads = 1;
@@ -229,16 +277,17 @@ static int run_rows(int in_fmt, int b_layout, int64_t nrows, const int64_t* rows
 }
 
 /* Full product: C (M x N doubles, stride ldc) = A (M x K, stride lda) *
- * B (K x N, stride ldb).  Returns 0, or -1 on allocation failure. */
+ * B (K x N, stride ldb); strides in elements of in_fmt.  Returns 0, or -1 on
+ * allocation failure. */
 int oracle_gemm_f64(int64_t M, int64_t N, int64_t K, int in_fmt,
-                    const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                    const void* A, int64_t lda, const void* B, int64_t ldb,
                     double* C, int64_t ldc, int nthreads) {
     return run_rows(in_fmt, ORACLE_B_ROW_MAJOR, M, NULL, N, K, A, lda, B, ldb, C, ldc, nthreads);
 }
 
 /* Selected rows only: C is nrows x N (stride ldc); output row r is row rows[r]. */
 int oracle_gemm_rows_f64(int64_t nrows, const int64_t* rows, int64_t N, int64_t K, int in_fmt,
-                         const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                         const void* A, int64_t lda, const void* B, int64_t ldb,
                          double* C, int64_t ldc, int nthreads) {
     return run_rows(in_fmt, ORACLE_B_ROW_MAJOR, nrows, rows, N, K, A, lda, B, ldb, C, ldc, nthreads);
 }
@@ -250,7 +299,7 @@ int oracle_gemm_rows_f64(int64_t nrows, const int64_t* rows, int64_t N, int64_t 
  * holds N doubles or is NULL (no bias).  relu != 0 applies max(x, 0) last.
  * Returns 0, -1 on allocation failure, -2 on a bad layout code. */
 int oracle_gemm_ex_f64(int64_t nrows, const int64_t* rows, int64_t N, int64_t K, int in_fmt,
-                       int b_layout, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                       int b_layout, const void* A, int64_t lda, const void* B, int64_t ldb,
                        double alpha, double beta, const double* Cold, int64_t ldcold,
                        const double* bias, int relu, double* C, int64_t ldc, int nthreads) {
     if (b_layout != ORACLE_B_ROW_MAJOR && b_layout != ORACLE_B_COL_MAJOR) return -2;

@@ -153,6 +153,48 @@ __global__ __launch_bounds__(256, 1) void probe_mfma_data_kernel(const u32x4* op
     if (s == 12345.0f) sink[0] = s;
 }
 
+// v_mfma_f32_32x32x64_f8f6f4 with both operands in one 8-bit float format
+// (FMT 0: E4M3, 1: E5M2; zero scale operands select the unscaled form).
+// Lane l's 32 operand bytes are a[32l .. 32l+31] and b[32l .. 32l+31];
+// d[16l + i] receives accumulator element i of lane l.
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+template <int FMT>
+__global__ void probe_mfma_f8_kernel(const uint32_t* a, const uint32_t* b, float* d) {
+    const int l = threadIdx.x;
+    i32x8 av, bv;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        av[j] = (int32_t)a[8 * l + j];
+        bv[j] = (int32_t)b[8 * l + j];
+    }
+    f32x16 acc = {};
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, FMT, FMT, 0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) d[16 * l + i] = acc[i];
+}
+
+// Issue rate of v_mfma_f32_32x32x64_f8f6f4 (E4M3), as probe_mfma_rate_kernel:
+// eight independent accumulators, register-resident operands.
+__global__ __launch_bounds__(256) void probe_mfma_f8_rate_kernel(int iters, uint64_t* cycles, float* sink) {
+    i32x8 av = {0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838};
+    i32x8 bv = av;
+    f32x16 acc[8];
+    for (int i = 0; i < 8; ++i) acc[i] = (f32x16){};
+    __syncthreads();
+    const uint64_t t0 = __builtin_readcyclecounter();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i], 0, 0, 0, 0, 0, 0);
+    }
+    float s = 0.0f;
+    for (int i = 0; i < 8; ++i) s += acc[i][0];
+    const uint64_t t1 = __builtin_readcyclecounter();
+    const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    if ((threadIdx.x & 63) == 0) cycles[wave] = t1 - t0;
+    if (s == 12345.0f) sink[0] = s;
+}
+
 // LDS throughput: every wave of 4 per block issues `iters` x 8 LDS
 // instructions of one kind and lane 0 records the shader cycles.  Lane l of
 // wave w uses byte address addr[64 w + l] (masked to the 64 KiB buffer and
@@ -371,6 +413,20 @@ int probe_mfma_data(int bf16, int blocks, int iters, const void* ops, float* sin
         hipLaunchKernelGGL(probe_mfma_data_kernel<true>, dim3(blocks), dim3(256), 0, 0, o, iters, sink);
     else
         hipLaunchKernelGGL(probe_mfma_data_kernel<false>, dim3(blocks), dim3(256), 0, 0, o, iters, sink);
+    return (int)hipDeviceSynchronize();
+}
+
+// fmt: 0 E4M3, 1 E5M2.  a, b: 64 lanes x 32 bytes; d: 64 x 16 floats.
+int probe_mfma_f8(int fmt, const uint32_t* a, const uint32_t* b, float* d) {
+    if (fmt == 0)
+        hipLaunchKernelGGL(probe_mfma_f8_kernel<0>, dim3(1), dim3(64), 0, 0, a, b, d);
+    else
+        hipLaunchKernelGGL(probe_mfma_f8_kernel<1>, dim3(1), dim3(64), 0, 0, a, b, d);
+    return (int)hipDeviceSynchronize();
+}
+
+int probe_mfma_f8_rate(int blocks, int iters, uint64_t* cycles, float* sink) {
+    hipLaunchKernelGGL(probe_mfma_f8_rate_kernel, dim3(blocks), dim3(256), 0, 0, iters, cycles, sink);
     return (int)hipDeviceSynchronize();
 }
 

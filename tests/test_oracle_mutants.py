@@ -25,11 +25,18 @@ MUTANTS = {
     "dropped_last_k": ("for (int64_t k = 0; k < jb->K; ++k) {", "for (int64_t k = 0; k + 1 < jb->K; ++k) {"),
     "sign_dropped_f16": ("    return sign ? -v : v;\n}\n\n/* bfloat16", "    (void)sign; return v;\n}\n\n/* bfloat16"),
     "transposed_B": ("c[j] += a * b[j];", "c[j] += a * jb->Bd[(j % jb->K) * jb->N + (k % jb->N)]; (void)b;"),
-    "ignores_lda": ("const uint16_t* arow = jb->A + i * jb->lda;", "const uint16_t* arow = jb->A + i * jb->K;"),
+    "ignores_lda": ("load_in(jb->in_fmt, jb->A, i * jb->lda + k)", "load_in(jb->in_fmt, jb->A, i * jb->K + k)"),
     "subnormal_scale": ("v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);"),
     "bf16_bias": ("v = ldexp((double)(128 + f), e - 134);", "v = ldexp((double)(128 + f), e - 133);"),
     "ties_away": ("return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;", "return fl + 1.0;"),
     "accumulate_in_float": ("c[j] += a * b[j];", "c[j] = (float)(c[j] + a * b[j]);"),
+    "e4m3_bias": ("v = ldexp((double)(8 + f), e - 10);", "v = ldexp((double)(8 + f), e - 9);"),
+    "e4m3_exp15_all_nan": ("if (e == 15 && f == 7)", "if (e == 15)"),
+    "e4m3_sign_dropped": ("    return sign ? -v : v;\n}\n\n/* OFP8 E5M2", "    (void)sign; return v;\n}\n\n/* OFP8 E5M2"),
+    "e5m2_subnormal_scale": ("v = ldexp((double)f, -16);", "v = ldexp((double)f, -17);"),
+    "e5m2_hidden_bit": ("v = ldexp((double)(4 + f), e - 17);", "v = ldexp((double)(8 + f), e - 18);"),
+    "byte_read_as_halfword": ("oracle_decode_e4m3(((const uint8_t*)base)[idx])",
+                              "oracle_decode_e4m3((uint8_t)((const uint16_t*)base)[idx])"),
 }
 
 
@@ -45,7 +52,7 @@ def _build(tmp_path, name, mutation):
     subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", str(c), "-o", str(so),
                            "-lm", "-lpthread"])
     lib = ctypes.CDLL(str(so))
-    i64, u16p, f64p = ctypes.c_int64, ctypes.POINTER(ctypes.c_uint16), ctypes.POINTER(ctypes.c_double)
+    i64, u16p, f64p = ctypes.c_int64, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)
     lib.oracle_gemm_f64.argtypes = [i64, i64, i64, ctypes.c_int, u16p, i64, u16p, i64, f64p, i64,
                                     ctypes.c_int]
     lib.oracle_decode_array.argtypes = [ctypes.c_int, u16p, f64p, i64]
@@ -54,13 +61,16 @@ def _build(tmp_path, name, mutation):
     return lib
 
 
+FMT_CODE = {"f16": 0, "bf16": 1, "e4m3": 2, "e5m2": 3}
+
+
 def _gemm(lib, A, B, fmt):
     M, K = A.shape
     N = B.shape[1]
     C = np.zeros((M, N))
-    lib.oracle_gemm_f64(M, N, K, 0 if fmt == "f16" else 1,
-                        A.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)), A.strides[0] // 2,
-                        B.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)), B.strides[0] // 2,
+    lib.oracle_gemm_f64(M, N, K, FMT_CODE[fmt],
+                        ctypes.c_void_p(A.ctypes.data), A.strides[0] // A.itemsize,
+                        ctypes.c_void_p(B.ctypes.data), B.strides[0] // B.itemsize,
                         C.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), N, 2)
     return C
 
@@ -96,12 +106,33 @@ def _battery(lib):
     for fmt, ref in (("f16", bits.view(np.float16).astype(np.float64)),
                      ("bf16", bf16_ref)):
         out = np.empty(65536)
-        lib.oracle_decode_array(0 if fmt == "f16" else 1,
-                                bits.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)),
+        lib.oracle_decode_array(FMT_CODE[fmt], ctypes.c_void_p(bits.ctypes.data),
                                 out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), 65536)
         fin = np.isfinite(ref)
         if not np.array_equal(out[fin], ref[fin]):
             failed.append("decode_" + fmt)
+    # 8-bit decoders against torch's float8 types, specials included
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    for fmt, dt in (("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)):
+        ref = torch.from_numpy(codes.copy()).view(dt).to(torch.float64).numpy()
+        out = np.empty(256)
+        lib.oracle_decode_array(FMT_CODE[fmt], ctypes.c_void_p(codes.ctypes.data),
+                                out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), 256)
+        if not (np.array_equal(np.isnan(out), np.isnan(ref)) and
+                np.array_equal(out[~np.isnan(ref)], ref[~np.isnan(ref)])):
+            failed.append("decode_" + fmt)
+    # 8-bit integer fixture with padded (NaN-filled) leading dimensions
+    for fmt in ("e4m3", "e5m2"):
+        A = inputs.padded(inputs.ints((13, 41), 15, fmt), 56)[:, :41]
+        B = inputs.padded(inputs.ints((41, 17), 16, fmt), 24)[:, :17]
+        Av = torch.from_numpy(np.ascontiguousarray(A)).view(
+            torch.float8_e4m3fn if fmt == "e4m3" else torch.float8_e5m2).to(torch.float64).numpy()
+        Bv = torch.from_numpy(np.ascontiguousarray(B)).view(
+            torch.float8_e4m3fn if fmt == "e4m3" else torch.float8_e5m2).to(torch.float64).numpy()
+        exact = Av.astype(np.int64) @ Bv.astype(np.int64)
+        if not np.array_equal(_gemm(lib, A, B, fmt), exact.astype(np.float64)):
+            failed.append("int_fixture_" + fmt)
     # rounding ties against numpy's IEEE float16 cast
     ties = 1.0 + (np.arange(0, 1000) + 0.5) * 2.0 ** -10   # halfway between fp16 neighbours in [1, 2)
     got = np.array([lib.oracle_round_to(1, float(t)) for t in ties])
@@ -133,10 +164,10 @@ EX_MUTANTS = {
     "beta_ignored": ("if (beta != 0.0) v += beta * Cold[r * ldcold + j];", "(void)Cold; (void)ldcold;"),
     "beta_sign": ("v += beta * Cold[r * ldcold + j];", "v -= beta * Cold[r * ldcold + j];"),
     "alpha_on_bias": ("if (bias) v += bias[j];", "if (bias) v += alpha * bias[j];"),
-    "col_major_read_as_row": ("Bd[k * N + j] = decode_one(in_fmt, B[j * ldb + k]);",
-                              "Bd[k * N + j] = decode_one(in_fmt, B[(k * ldb + j) % (N * ldb)]);"),
-    "col_major_ignores_ldb": ("Bd[k * N + j] = decode_one(in_fmt, B[j * ldb + k]);",
-                              "Bd[k * N + j] = decode_one(in_fmt, B[j * K + k]);"),
+    "col_major_read_as_row": ("Bd[k * N + j] = load_in(in_fmt, B, j * ldb + k);",
+                              "Bd[k * N + j] = load_in(in_fmt, B, (k * ldb + j) % (N * ldb));"),
+    "col_major_ignores_ldb": ("Bd[k * N + j] = load_in(in_fmt, B, j * ldb + k);",
+                              "Bd[k * N + j] = load_in(in_fmt, B, j * K + k);"),
     "relu_clips_to_abs": ("if (relu && v < 0.0) v = 0.0;", "if (relu && v < 0.0) v = -v;"),
 }
 
