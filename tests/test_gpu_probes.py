@@ -34,8 +34,10 @@ def P():
     lib.probe_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
     lib.probe_lds_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp]
     lib.probe_dma_rate.argtypes = [ctypes.c_int, ctypes.c_int, vp, ctypes.c_int, vp, vp]
+    lib.probe_mfma_f8.argtypes = [ctypes.c_int, vp, vp, vp]
+    lib.probe_mfma_f8_rate.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
     for f in (lib.probe_tr16, lib.probe_load_lds, lib.probe_mfma, lib.probe_mfma_rate,
-              lib.probe_lds_rate, lib.probe_dma_rate):
+              lib.probe_lds_rate, lib.probe_dma_rate, lib.probe_mfma_f8, lib.probe_mfma_f8_rate):
         f.restype = ctypes.c_int
     return lib
 
@@ -107,6 +109,81 @@ def test_mfma_operand_and_accumulator_maps(P, kind):
             for i in range(4):
                 got[4 * (l // 16) + i, l % 16] = d[4 * l + i]
     assert np.array_equal(got, A @ B)
+
+
+def _run_mfma_f8(P, fmt, A_codes, B_codes):
+    """One v_mfma_f32_32x32x64_f8f6f4 on a 32 x 64 A and a 64 x 32 B of 8-bit
+    codes, placed as the GEMM kernels place them: lane l holds row (A) or
+    column (B) l % 32 and the 32 consecutive k from 32 (l / 32); the 32 x 32
+    result is read with the 32x32 accumulator map of test_mfma_operand_and_accumulator_maps."""
+    a = np.zeros((64, 32), np.uint8)
+    b = np.zeros((64, 32), np.uint8)
+    for l in range(64):
+        a[l] = A_codes[l % 32, 32 * (l // 32):32 * (l // 32) + 32]
+        b[l] = B_codes[32 * (l // 32):32 * (l // 32) + 32, l % 32]
+    ta = torch.from_numpy(a.reshape(-1).view(np.int32).copy()).cuda()
+    tb = torch.from_numpy(b.reshape(-1).view(np.int32).copy()).cuda()
+    td = torch.zeros(1024, dtype=torch.float32, device="cuda")
+    assert P.probe_mfma_f8(0 if fmt == "e4m3" else 1, ta.data_ptr(), tb.data_ptr(), td.data_ptr()) == 0
+    d = td.cpu().numpy().astype(np.float64)
+    got = np.zeros((32, 32))
+    for l in range(64):
+        for i in range(16):
+            got[8 * (i // 4) + 4 * (l // 32) + i % 4, l % 32] = d[16 * l + i]
+    return got
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_mfma_f8_operand_map(P, fmt):
+    """With A and B placed alike (lane half h and byte p both mean k = 32h + p),
+    the 8-bit MFMA returns exactly A.B: the k assignment the kernels rely on is
+    shared by the two operands."""
+    import oracle
+    from dense_half_precision_tiled_amd import inputs
+    for seed in (1, 2, 3):
+        A = inputs.ints((32, 64), 70 + seed, fmt)
+        B = inputs.ints((64, 32), 80 + seed, fmt)
+        want = oracle.decode(A, fmt) @ oracle.decode(B, fmt)
+        assert np.array_equal(_run_mfma_f8(P, fmt, A, B), want)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_mfma_f8_decodes_every_code(P, fmt):
+    """Every finite code, multiplied by 1.0 and summed with exact zeros, comes
+    back as the oracle's OFP8 value: the MFMA reads E4M3 / E5M2 as the OCP
+    formats.  (NaN and infinity codes are left out: they would poison every
+    sum of their row.)"""
+    import oracle
+    codes = ((64 * np.arange(32)[:, None] + np.arange(64)[None, :]) % 256).astype(np.uint8)
+    vals = oracle.decode(codes, fmt)
+    codes = np.where(np.isfinite(vals), codes, 0).astype(np.uint8)
+    vals = oracle.decode(codes, fmt)
+    one = 0x38 if fmt == "e4m3" else 0x3C
+    for t in (0, 1):                   # B selects k = j + 32 t for column j
+        B = np.zeros((64, 32), np.uint8)
+        B[np.arange(32) + 32 * t, np.arange(32)] = one
+        got = _run_mfma_f8(P, fmt, codes, B)
+        assert np.array_equal(got, vals[:, 32 * t:32 * t + 32]), t
+
+
+def test_mfma_f8_issue_rate(P):
+    """Eight independent v_mfma_f32_32x32x64_f8f6f4 per wave, one wave per SIMD
+    on every CU: FLOP per shader clock per CU against the 8192 of the CDNA4
+    design for 8-bit inputs (twice the 16-bit rate)."""
+    blocks, iters = 256, 2000
+    cyc = torch.zeros(blocks * 4, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    P.probe_mfma_f8_rate(blocks, 100, cyc.data_ptr(), sink.data_ptr())
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    assert P.probe_mfma_f8_rate(blocks, iters, cyc.data_ptr(), sink.data_ptr()) == 0
+    e1.record()
+    torch.cuda.synchronize()
+    cycles = float(cyc.cpu().numpy().mean())
+    flop = 4 * iters * 8 * 131072.0
+    ms = e0.elapsed_time(e1)
+    print("mfma e4m3: %.0f FLOP/clk/CU, %.0f TFLOP/s" % (flop / cycles, blocks * flop / ms / 1e9))
+    assert 7000 < flop / cycles <= 8192 * 1.01
 
 
 def test_mfma_issue_rate(P):
@@ -210,12 +287,13 @@ def test_dma_rate(P):
         del src
 
 
-@pytest.mark.parametrize("offset", [0, 2, 6, 10, 14])
+@pytest.mark.parametrize("offset", [0, 1, 2, 3, 6, 7, 10, 13, 14, 15])
 def test_unaligned_16_byte_global_loads(P, offset):
     """Record whether global_load_dwordx4 and global_load_lds_dwordx4 return
-    the 16 bytes at a 2-byte-aligned address (unaligned mode) or those of the
-    aligned-down address (strict mode).  The GEMM's misaligned-A path relies on
-    this: it is pinned here."""
+    the 16 bytes at an unaligned address (unaligned mode) or those of the
+    aligned-down address (strict mode), at even and odd byte offsets.  The
+    GEMM's misaligned-row paths rely on exact bytes (2-byte-aligned rows of
+    16-bit values, any byte alignment for 8-bit rows): pinned here."""
     P.probe_unaligned.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     P.probe_unaligned.restype = ctypes.c_int
     nbytes = 4096
@@ -230,4 +308,4 @@ def test_unaligned_16_byte_global_loads(P, offset):
     down = np.stack([host[(offset + 32 * l) & ~15: ((offset + 32 * l) & ~15) + 16] for l in range(64)])
     kind = lambda got: "exact" if np.array_equal(got, exact) else ("aligned-down" if np.array_equal(got, down) else "other")
     print("offset %2d: global_load_dwordx4 -> %s, global_load_lds_dwordx4 -> %s" % (offset, kind(vec), kind(lds)))
-    assert kind(vec) != "other" and kind(lds) != "other"
+    assert kind(vec) == "exact" and kind(lds) == "exact"
