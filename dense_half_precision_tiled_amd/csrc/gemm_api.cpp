@@ -16,7 +16,8 @@ constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxLd = int64_t(1) << 40;
 constexpr int64_t kMaxExtent = int64_t(1) << 47;   // elements spanned by one operand
 
-int out_elem_size(int dtype) { return (dtype == GEMM_F16_F32 || dtype == GEMM_BF16_F32) ? 4 : 2; }
+int out_elem_size(int dtype) { return dhpt::dtype_out_f32(dtype) ? 4 : 2; }
+int in_elem_size(int dtype) { return dhpt::dtype_in8(dtype) ? 1 : 2; }
 
 bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; }
 
@@ -39,9 +40,10 @@ int validate(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t 
              const void* B, int64_t ldb, const void* C, int64_t ldc, const Extra& x, Problem* p,
              bool* noop) {
     *noop = false;
-    if (dtype < GEMM_F16_F32 || dtype > GEMM_BF16_BF16) return GEMM_ERR_DTYPE;
+    if (dtype < GEMM_F16_F32 || dtype > GEMM_E5M2_BF16) return GEMM_ERR_DTYPE;
     if (x.b_layout != GEMM_B_ROW_MAJOR && x.b_layout != GEMM_B_COL_MAJOR) return GEMM_ERR_LAYOUT;
     const bool tb = x.b_layout == GEMM_B_COL_MAJOR;
+    if (dhpt::dtype_in8(dtype) && !tb) return GEMM_ERR_LAYOUT;   // 8-bit inputs: column-major B
     const int64_t b_rows = tb ? N : K, b_cols = tb ? K : N;      // B as stored, row-major
     if (M < 0 || N < 0 || K < 0) return GEMM_ERR_DIM;
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return GEMM_ERR_RANGE;
@@ -56,17 +58,17 @@ int validate(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t 
     if (M == 0 || N == 0) { *noop = true; return GEMM_OK; }
     if (C == nullptr) return GEMM_ERR_NULL;
     if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_ERR_NULL;
-    const int osz = out_elem_size(dtype);
+    const int osz = out_elem_size(dtype), isz = in_elem_size(dtype);
     if (reinterpret_cast<uintptr_t>(C) % osz != 0) return GEMM_ERR_ALIGN;
-    if (K > 0 && (reinterpret_cast<uintptr_t>(A) % 2 != 0 || reinterpret_cast<uintptr_t>(B) % 2 != 0))
+    if (K > 0 && (reinterpret_cast<uintptr_t>(A) % isz != 0 || reinterpret_cast<uintptr_t>(B) % isz != 0))
         return GEMM_ERR_ALIGN;
     if (x.bias != nullptr && reinterpret_cast<uintptr_t>(x.bias) % 4 != 0) return GEMM_ERR_ALIGN;
     uintptr_t c0, c1;
     extent(C, M, N, ldc, osz, &c0, &c1);
     if (K > 0) {
         uintptr_t a0, a1, b0, b1;
-        extent(A, M, K, lda, 2, &a0, &a1);
-        extent(B, b_rows, b_cols, ldb, 2, &b0, &b1);
+        extent(A, M, K, lda, isz, &a0, &a1);
+        extent(B, b_rows, b_cols, ldb, isz, &b0, &b1);
         if (overlaps(c0, c1, a0, a1) || overlaps(c0, c1, b0, b1)) return GEMM_ERR_ALIAS;
     }
     if (x.bias != nullptr) {
@@ -96,7 +98,16 @@ int64_t tiles_for(int tile, int64_t M, int64_t N) { return ((M + tile - 1) / til
 // Within a family, the first instance that supports the problem: whole
 // tiles, then clamped edges (any M and K; N a multiple of 8 for row-major
 // B), then the fully masked fallback (128x128).
+//
+// 8-bit inputs (column-major B): 256x256 tiles when they give at least half a
+// wave, else 128x128 tiles when those give at least half a wave, else 64x64;
+// whole tiles, then clamped edges (which cover every shape).
 int choose_instance(const Problem& p) {
+    if (dhpt::dtype_in8(p.dtype)) {
+        static const int big8[] = {14, 15}, mid8[] = {16, 17}, small8[] = {18, 19};
+        const int* o = tiles_for(256, p.M, p.N) >= 128 ? big8 : tiles_for(128, p.M, p.N) >= 128 ? mid8 : small8;
+        return dhpt::instance_supports(o[0], p) ? o[0] : o[1];
+    }
     static const int big_order[] = {0, 1, 2};
     static const int mid_order[] = {3, 4, 5};
     static const int ks_order[] = {10, 11, 5};
@@ -237,7 +248,7 @@ const char* gemm_strerror(int status) {
     case GEMM_ERR_LAUNCH: return "kernel launch failed";
     case GEMM_ERR_ALIGN: return "pointer not aligned to its element size";
     case GEMM_ERR_INSTANCE: return "unknown instance, or instance cannot run this shape";
-    case GEMM_ERR_LAYOUT: return "unknown B layout";
+    case GEMM_ERR_LAYOUT: return "unknown B layout, or row-major B with 8-bit inputs (they need column-major B)";
     default: return "unknown status";
     }
 }

@@ -1,5 +1,5 @@
 // gemm_common.h -- device helpers shared by the gfx950 GEMM kernel templates
-// (gemm_dl_kernel.h, gemm_ks_kernel.h): operand types, the MFMA and output
+// (gemm_dl_kernel.h, gemm_ks_kernel.h): operand types, the MFMAs and output
 // conversions, the LDS swizzles, the asynchronous global -> LDS copy, and the
 // zero-filling slice fill through VGPRs used at ragged edges.
 #pragma once
@@ -20,9 +20,15 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) char lds_char;
 
-enum { IN_F16 = 0, IN_BF16 = 1 };
+// Input formats: fp16 and bf16 (2-byte elements), and the 8-bit floats E4M3
+// and E5M2 of the OCP 8-bit floating point specification (1-byte elements).
+enum { IN_F16 = 0, IN_BF16 = 1, IN_E4M3 = 2, IN_E5M2 = 3 };
+template <int IN>
+constexpr bool kIn8 = IN == IN_E4M3 || IN == IN_E5M2;
 enum { OUT_F32 = 0, OUT_F16 = 1, OUT_BF16 = 2 };
 enum { EDGE_NONE = 0, EDGE_CLAMP = 1, EDGE_MASKED = 2 };
 
@@ -34,6 +40,19 @@ __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
     else
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// v_mfma_f32_32x32x64_f8f6f4 with A and B in one 8-bit format: lane l holds
+// row (A) or column (B) l % 32 and 32 values of k, the same 32 for A and B
+// (the probe tests pin that the two operands share their k assignment, and
+// that format codes 0 and 1 read E4M3 and E5M2).  The scale operands are 0,
+// which selects the unscaled instruction.
+template <int IN>
+__device__ __forceinline__ f32x16 mfma8(u32x8 a, u32x8 b, f32x16 c) {
+    constexpr int fmt = IN == IN_E4M3 ? 0 : 1;
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8, a),
+                                                            __builtin_bit_cast(i32x8, b), c, fmt, fmt,
+                                                            0, 0, 0, 0);
 }
 
 template <int OUT>
@@ -76,29 +95,45 @@ __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)
 
 #define DL_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-// 8 consecutive 16-bit values p[c0 .. c0+7] of a row p[0 .. limit-1], those at
-// index >= limit reading as zero.  Element loads: any limit >= 1.
-__device__ __forceinline__ u32x4 load8_masked(const uint16_t* p, int c0, int limit) {
-    if (c0 + 8 <= limit) return *reinterpret_cast<const u32x4*>(p + c0);
-    uint32_t h[8];
+// Element type of an operand's bit patterns: uint16_t for the 16-bit
+// formats, uint8_t for the 8-bit ones.
+template <int ESZ>
+using elem_t = std::conditional_t<ESZ == 2, uint16_t, uint8_t>;
+
+// One 16-byte chunk of a row of ESZ-byte elements: CH = 16 / ESZ consecutive
+// values p[c0 .. c0+CH-1] of the row p[0 .. limit-1], those at index >= limit
+// reading as zero.  Element loads: any limit >= 1.
+template <int ESZ>
+__device__ __forceinline__ u32x4 load_chunk_masked(const elem_t<ESZ>* p, int c0, int limit) {
+    constexpr int CH = 16 / ESZ;
+    if (c0 + CH <= limit) return *reinterpret_cast<const u32x4*>(p + c0);
+    uint32_t h[CH];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) h[e] = (c0 + e < limit) ? (uint32_t)p[c0 + e] : 0u;
-    return u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    for (int e = 0; e < CH; ++e) h[e] = (c0 + e < limit) ? (uint32_t)p[c0 + e] : 0u;
+    if constexpr (ESZ == 2)
+        return u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    else
+        return u32x4{h[0] | (h[1] << 8) | (h[2] << 16) | (h[3] << 24), h[4] | (h[5] << 8) | (h[6] << 16) | (h[7] << 24),
+                     h[8] | (h[9] << 8) | (h[10] << 16) | (h[11] << 24),
+                     h[12] | (h[13] << 8) | (h[14] << 16) | (h[15] << 24)};
 }
 
-// The same for limit >= 8, without a branch, in two steps so that a caller
-// can issue every load of a fill before the first shift: load8_at reads the
-// last whole in-row chunk at or before c0, shift8 moves the wanted values
-// down by the distance (8 or more clears the chunk).
-__device__ __forceinline__ u32x4 load8_at(const uint16_t* p, int c0, int limit, int* sh) {
-    const int start = c0 < limit - 8 ? c0 : limit - 8;   // [start, start + 8) lies in the row
-    const int d = c0 - start;                            // 0 whole, 1..7 partial, >= 8 past the end
-    *sh = d < 8 ? d : 8;
+// The same for limit >= CH, without a branch, in two steps so that a caller
+// can issue every load of a fill before the first shift: load_chunk_at reads
+// the last whole in-row chunk at or before c0, shift_chunk moves the wanted
+// values down by the distance (CH or more clears the chunk).
+template <int ESZ>
+__device__ __forceinline__ u32x4 load_chunk_at(const elem_t<ESZ>* p, int c0, int limit, int* sh) {
+    constexpr int CH = 16 / ESZ;
+    const int start = c0 < limit - CH ? c0 : limit - CH;    // [start, start + CH) lies in the row
+    const int d = c0 - start;                               // 0 whole, 1..CH-1 partial, >= CH past the end
+    *sh = d < CH ? d : CH;
     return *reinterpret_cast<const u32x4*>(p + start);
 }
-__device__ __forceinline__ u32x4 shift8(u32x4 v, int sh) {
+template <int ESZ>
+__device__ __forceinline__ u32x4 shift_chunk(u32x4 v, int sh) {
     unsigned __int128 x = __builtin_bit_cast(unsigned __int128, v);
-    x = (x >> (8 * sh)) >> (8 * sh);                     // two shifts of <= 64 bits: 8 clears all
+    x = (x >> (4 * ESZ * sh)) >> (4 * ESZ * sh);            // two shifts of <= 64 bits: CH clears all
     return __builtin_bit_cast(u32x4, x);
 }
 
@@ -109,65 +144,72 @@ struct EpiArgs {
     int relu;
 };
 
-// One 64-deep slice (k0 .. k0+63) of the A rows m0 .. m0+BM-1 and of B
-// (columns n0 .. n0+BN-1) into the LDS stage `st` through VGPRs, with every
-// value outside M x K (A) and K x N (B) read as zero, in the stage layout of
-// the direct-to-LDS copies: A BM rows x 128 bytes, chunk c of row r at
+// One slice (128 bytes of every row: k0 .. k0+63 for 2-byte elements,
+// k0 .. k0+127 for 1-byte ones) of the A rows m0 .. m0+BM-1 and of B (columns
+// n0 .. n0+BN-1) into the LDS stage `st` through VGPRs, with every value
+// outside M x K (A) and K x N (B) read as zero, in the stage layout of the
+// direct-to-LDS copies: A BM rows x 128 bytes, chunk c of row r at
 // c ^ swz_a(r); row-major B 64 rows x 2*BN bytes, chunk c of row k at
 // c ^ swz_b(k); column-major B BN rows x 128 bytes like A.  All 256 lanes of
 // the workgroup take part.  All loads are issued before the first LDS write:
 // rows past the edge read a clamped valid row and are zeroed afterwards, and
 // chunks crossing the row end use the branch-free shifted load whenever the
-// row holds at least 8 values (a uniform test), so one memory round trip
-// fills the slice.
-template <int BM, int BN, bool BT>
+// row holds at least one chunk of values (a uniform test), so one memory
+// round trip fills the slice.  ESZ is the element size in bytes; 1-byte
+// elements only come with column-major B.
+template <int BM, int BN, bool BT, int ESZ = 2>
 __device__ __forceinline__ void fill_stage(char* st, const uint16_t* A, int64_t lda,
                                            const uint16_t* B, int64_t ldb, int M, int N,
                                            int K, int m0, int n0, int k0, int t) {
+    static_assert(ESZ == 2 || (ESZ == 1 && BT), "1-byte elements: column-major B only");
+    constexpr int CH = 16 / ESZ;                                  // elements per 16-byte chunk
     constexpr int BK = 64, A_BYTES = BM * 128, BROW = 2 * BN, B_CHUNKS = BN / 8;
     constexpr int NFA = BM / 32;                                  // A chunks per lane
     constexpr int B_ROWS_PER_PASS = 256 / B_CHUNKS;
     constexpr int NFB = BT ? BN / 32 : BK / B_ROWS_PER_PASS;      // B chunks per lane
+    using E = elem_t<ESZ>;
+    const E* const Ae = reinterpret_cast<const E*>(A);
+    const E* const Be = reinterpret_cast<const E*>(B);
     const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
     u32x4 va[NFA], vb[NFB];
-    const uint16_t* pa[NFA];
-    const uint16_t* pb[NFB];
+    const E* pa[NFA];
+    const E* pb[NFB];
     int cb[NFB];
 #pragma unroll
     for (int r = 0; r < NFA; ++r) {                // A: BM rows x 8 chunks
         const int grow = m0 + (t >> 3) + 32 * r;
-        pa[r] = A + (int64_t)(grow < M ? grow : M - 1) * lda;
+        pa[r] = Ae + (int64_t)(grow < M ? grow : M - 1) * lda;
     }
 #pragma unroll
     for (int r = 0; r < NFB; ++r) {
         if constexpr (BT) {                        // column-major B: BN rows x 8 chunks
             const int gcol = n0 + (t >> 3) + 32 * r;
-            pb[r] = B + (int64_t)(gcol < N ? gcol : N - 1) * ldb;
-            cb[r] = k0 + 8 * (t & 7);
+            pb[r] = Be + (int64_t)(gcol < N ? gcol : N - 1) * ldb;
+            cb[r] = k0 + CH * (t & 7);
         } else {                                   // row-major B: 64 rows x B_CHUNKS chunks
             const int gk = k0 + t / B_CHUNKS + B_ROWS_PER_PASS * r;
-            pb[r] = B + (int64_t)(gk < K ? gk : K - 1) * ldb;
+            pb[r] = Be + (int64_t)(gk < K ? gk : K - 1) * ldb;
             cb[r] = n0 + 8 * (t % B_CHUNKS);
         }
     }
-    const int ca = k0 + 8 * (t & 7);
+    const int ca = k0 + CH * (t & 7);
     const int blim = BT ? K : N;                   // valid length of a B row
-    if (K >= 8 && blim >= 8) {                     // every load in flight before the first shift
+    if (K >= CH && blim >= CH) {                   // every load in flight before the first shift
         int sha[NFA], shb[NFB];
 #pragma unroll
-        for (int r = 0; r < NFA; ++r) va[r] = load8_at(pa[r], ca, K, &sha[r]);
+        for (int r = 0; r < NFA; ++r) va[r] = load_chunk_at<ESZ>(pa[r], ca, K, &sha[r]);
 #pragma unroll
-        for (int r = 0; r < NFB; ++r) vb[r] = load8_at(pb[r], cb[r], blim, &shb[r]);
+        for (int r = 0; r < NFB; ++r) vb[r] = load_chunk_at<ESZ>(pb[r], cb[r], blim, &shb[r]);
         DL_FENCE();
 #pragma unroll
-        for (int r = 0; r < NFA; ++r) va[r] = shift8(va[r], sha[r]);
+        for (int r = 0; r < NFA; ++r) va[r] = shift_chunk<ESZ>(va[r], sha[r]);
 #pragma unroll
-        for (int r = 0; r < NFB; ++r) vb[r] = shift8(vb[r], shb[r]);
+        for (int r = 0; r < NFB; ++r) vb[r] = shift_chunk<ESZ>(vb[r], shb[r]);
     } else {
 #pragma unroll
-        for (int r = 0; r < NFA; ++r) va[r] = load8_masked(pa[r], ca, K);
+        for (int r = 0; r < NFA; ++r) va[r] = load_chunk_masked<ESZ>(pa[r], ca, K);
 #pragma unroll
-        for (int r = 0; r < NFB; ++r) vb[r] = load8_masked(pb[r], cb[r], blim);
+        for (int r = 0; r < NFB; ++r) vb[r] = load_chunk_masked<ESZ>(pb[r], cb[r], blim);
     }
 #pragma unroll
     for (int r = 0; r < NFA; ++r) {

@@ -36,19 +36,29 @@
 //     the general C <- alpha*A*B + beta*C of the naive-to-tensor-core page);
 //     C_old is read only when beta != 0.
 //
-// EDGE modes:
-//   EDGE_NONE:  M % BM == N % BN == K % 64 == 0.
+// 8-bit float inputs (IN_E4M3, IN_E5M2; column-major B only): a slice is
+// still 128 bytes of every A and B row, now 128 values of k, multiplied as two
+// 64-deep k-steps of v_mfma_f32_32x32x64_f8f6f4.  A lane's fragment is 32
+// consecutive k (two ds_read_b128 of the same swizzled rows), the same k for
+// A and B; the fragments of the next k-step are read while the current one
+// is multiplied (FD == 1: at 64 deep a k-step is as long as two of the
+// 16-bit ones).  Stage layout, swizzle, copies and epilogue are those of the
+// 16-bit column-major-B kernel.  The 8-bit float of the Ada write-up's
+// precision notes, built here for gfx950's double-rate 8-bit MFMA.
+//
+// EDGE modes (BK = 64 for 16-bit inputs, 128 for 8-bit ones):
+//   EDGE_NONE:  M % BM == N % BN == K % BK == 0.
 //   EDGE_CLAMP: any M, K; any N for column-major B, N % 8 == 0 for row-major
 //     B.  Rows of A (and of column-major B) past the edge and 8-column chunks
 //     of row-major B past N are read from a clamped, valid address: those
 //     values only reach outputs that are never stored.  A partial last slice
-//     (K % 64 != 0) is filled through VGPRs with element-exact zero fill.
+//     (K % BK != 0) is filled through VGPRs with element-exact zero fill.
 //   EDGE_MASKED: any shape.  Every slice is filled through VGPRs with
 //     element-exact zero fill (no asynchronous copies, one stage); the
 //     fallback for row-major B with N % 8 != 0.
-// 16-byte loads from 2-byte-aligned addresses return the exact bytes on
-// gfx950 (pinned by a probe test), so misaligned rows and leading dimensions
-// stay on the vector paths.
+// 16-byte loads from any byte address return the exact bytes on gfx950
+// (pinned by a probe test), so misaligned rows and leading dimensions stay on
+// the vector paths.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -68,13 +78,17 @@ __global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
     EpiArgs ep) {
     static_assert((BM == 256 && BN == 256) || (BM == 128 && BN == 128) || (BM == 64 && BN == 64), "tile");
     static_assert(FD == 1 || FD == 2, "fragment prefetch distance");
-    constexpr int BK = 64, KSTEPS = 4;
+    constexpr bool F8 = kIn8<IN>;
+    static_assert(!F8 || (BT && FD == 1 && EDGE != EDGE_MASKED), "8-bit inputs: column-major B, FD 1");
+    constexpr int ESZ = F8 ? 1 : 2;                       // bytes per input element
+    constexpr int BK = F8 ? 128 : 64, KSTEPS = F8 ? 2 : 4;   // k per slice (128 bytes of a row), MFMA k-steps
+    constexpr int RPF = F8 ? 2 : 1;                       // ds_read_b128 per A (or column-major B) fragment
     constexpr int WM = BM / 2, WN = BN / 2;               // wave tile
     constexpr int TM = WM / 32, TN = WN / 32;             // MFMA blocks per wave
     constexpr int S = TM * TN;                            // MFMAs (issue slots) per k-step
-    constexpr int NBR = BT ? TN : 2 * TN;                 // B reads per k-step
-    constexpr int R = TM + NBR;                           // LDS reads per k-step
-    constexpr int A_BYTES = BM * 128, BROW = 2 * BN, B_BYTES = BK * BROW;   // BT: BN * 128, same
+    constexpr int NBR = BT ? RPF * TN : 2 * TN;           // B reads per k-step
+    constexpr int R = RPF * TM + NBR;                     // LDS reads per k-step
+    constexpr int A_BYTES = BM * 128, BROW = 2 * BN, B_BYTES = BT ? BN * 128 : 64 * BROW;
     constexpr int STAGE = A_BYTES + B_BYTES;
     constexpr int NSTAGE = EDGE == EDGE_MASKED ? 1 : 2;
     constexpr int CA = BM / 32, CB = BN / 32;             // copies per wave per slice (1 KiB each)
@@ -98,8 +112,13 @@ __global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
     // physical chunk l%8; column-major B the same over its BN rows.
     // Row-major B copy i fills rows 16w + B_ROWS_PER_COPY*i + l/B_CHUNKS,
     // physical chunk l%B_CHUNKS.
-    const uint16_t* a_src[CA];
-    const uint16_t* b_src[CB];
+    // Copy sources, in elements: a slice advances every A row (and every
+    // column-major B row) by BK values (128 bytes), and row-major B by BK rows.
+    using E = elem_t<ESZ>;
+    const E* const Ae = reinterpret_cast<const E*>(A);
+    const E* const Be = reinterpret_cast<const E*>(B);
+    const E* a_src[CA];
+    const E* b_src[CB];
     int64_t b_step = BK;
     uint32_t dma_a = 0, dma_b = 0;
     if constexpr (EDGE != EDGE_MASKED) {
@@ -108,7 +127,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
             const int r = (BM / 4) * w + 8 * i + (l >> 3);
             int grow = m0 + r;
             if constexpr (EDGE == EDGE_CLAMP) grow = grow < M ? grow : M - 1;
-            a_src[i] = A + (int64_t)grow * lda + 8 * ((l & 7) ^ swz_a(r));
+            a_src[i] = Ae + (int64_t)grow * lda + (16 / ESZ) * ((l & 7) ^ swz_a(r));
         }
 #pragma unroll
         for (int i = 0; i < CB; ++i) {
@@ -116,12 +135,12 @@ __global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
                 const int r = (BN / 4) * w + 8 * i + (l >> 3);
                 int gcol = n0 + r;
                 if constexpr (EDGE == EDGE_CLAMP) gcol = gcol < N ? gcol : N - 1;
-                b_src[i] = B + (int64_t)gcol * ldb + 8 * ((l & 7) ^ swz_a(r));
+                b_src[i] = Be + (int64_t)gcol * ldb + (16 / ESZ) * ((l & 7) ^ swz_a(r));
             } else {
                 const int kr = 16 * w + B_ROWS_PER_COPY * i + l / B_CHUNKS;
                 int col = n0 + 8 * ((l % B_CHUNKS) ^ swz_b(kr));
                 if constexpr (EDGE == EDGE_CLAMP) col = col + 8 <= N ? col : N - 8;
-                b_src[i] = B + (int64_t)kr * ldb + col;
+                b_src[i] = Be + (int64_t)kr * ldb + col;
             }
         }
         if constexpr (!BT) b_step = (int64_t)BK * ldb;
@@ -156,11 +175,31 @@ __global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
     u32x4 fa[NB][TM];
     u32x4 fbt[NB][TN];            // column-major B fragments
     s16x4 fbh[NB][TN][2];         // row-major B fragments (two transposing reads each)
+    u32x8 fa8[NB][TM], fb8[NB][TN];   // 8-bit inputs: 32 k per lane
 
     // LDS read q (0 .. R-1) of k-step s, in consumption order: A0, then B
     // (B0 .. B(TN-1), each as lo/hi for row-major B), then A1 .. A(TM-1).
+    // 8-bit inputs: every fragment in two halves (logical chunks 4s + 2h and
+    // 4s + 2h + 1 of its row, h = l / 32), in the same order.
     auto read_piece = [&](int stage, int s, int buf, int q) {
         const char* st = smem + stage * STAGE;
+        if constexpr (F8) {
+            const int f = q >> 1, half = q & 1;
+            const int chunk = (4 * s + 2 * (l >> 5) + half) ^ a_sw;
+            u32x4 v;
+            if (f == 0 || f > TN) {
+                const int i = (f == 0) ? 0 : f - TN;
+                v = *reinterpret_cast<const u32x4*>(st + a_off0 + i * 32 * 128 + chunk * 16);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) fa8[buf][i][4 * half + e] = v[e];
+            } else {
+                const int j = f - 1;
+                v = *reinterpret_cast<const u32x4*>(st + b_off[j] + chunk * 16);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) fb8[buf][j][4 * half + e] = v[e];
+            }
+            return;
+        }
         const int chunk = (2 * s + (l >> 5)) ^ a_sw;      // A rows and column-major B rows alike
         if (q == 0 || q > NBR) {
             const int i = (q == 0) ? 0 : q - NBR;
@@ -187,7 +226,9 @@ __global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
     };
     auto mfma1 = [&](int buf, int q) {                 // MFMA q of a k-step: A block q/TN, B block q%TN
         const int i = q / TN, j = q % TN;
-        if constexpr (BT) {
+        if constexpr (F8) {
+            acc[i][j] = mfma8<IN>(fa8[buf][i], fb8[buf][j], acc[i][j]);
+        } else if constexpr (BT) {
             acc[i][j] = mfma<IN>(fa[buf][i], fbt[buf][j], acc[i][j]);
         } else {
             const u32x2 lo = __builtin_bit_cast(u32x2, fbh[buf][j][0]);
@@ -197,7 +238,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
     };
 
     auto fill_slice = [&](int stage, int kt) {
-        fill_stage<BM, BN, BT>(smem + stage * STAGE, A, lda, B, ldb, M, N, K, m0, n0, kt * BK, t);
+        fill_stage<BM, BN, BT, ESZ>(smem + stage * STAGE, A, lda, B, ldb, M, N, K, m0, n0, kt * BK, t);
     };
     // One filled slice, unpipelined: the reads of each k-step, then its MFMAs.
     auto compute_slice = [&](int stage) {
@@ -248,7 +289,11 @@ __global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
         DL_FENCE();
         using one = std::integral_constant<int, S>;
         using two = std::integral_constant<int, 2 * S>;
-        if constexpr (FD == 1) {
+        if constexpr (F8) {
+            // post-barrier block: previous slice's k-step 1 (buffer 1), reads of k-step 0 (buffer 0)
+            block(has_prev, 1, 1, stage, 0, 0, 0, 0, do_copy, nstage, one{});
+            block(yes{}, 0, 0, stage, 1, 1, 1, 1, no{}, nstage, one{});
+        } else if constexpr (FD == 1) {
             // post-barrier block: previous slice's k-step 3 (buffer 1), reads of k-step 0 (buffer 0)
             block(has_prev, 1, 1, stage, 0, 0, 0, 0, do_copy, nstage, one{});
             block(yes{}, 0, 0, stage, 1, 1, 1, 1, no{}, nstage, one{});
@@ -297,7 +342,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
         if constexpr (EDGE == EDGE_CLAMP) {
             if (K % BK != 0) {
                 // the partial last slice: zero-filled through VGPRs, then its
-                // four k-steps without pipelining (at most one slice in K / 64)
+                // k-steps without pipelining (at most one slice in K / BK)
                 const int stage = nk_full & 1;
                 __syncthreads();        // every wave is done reading the stage being refilled
                 fill_slice(stage, nk_full);
@@ -363,9 +408,40 @@ static hipError_t launch_dtype(const Problem& p, int group_m, hipStream_t s) {
     case 0: launch_typed<IN_F16, OUT_F32, BM, BN, FD, EDGE, BT, EPI>(p, group_m, s); break;
     case 1: launch_typed<IN_F16, OUT_F16, BM, BN, FD, EDGE, BT, EPI>(p, group_m, s); break;
     case 2: launch_typed<IN_BF16, OUT_F32, BM, BN, FD, EDGE, BT, EPI>(p, group_m, s); break;
-    default: launch_typed<IN_BF16, OUT_BF16, BM, BN, FD, EDGE, BT, EPI>(p, group_m, s); break;
+    case 3: launch_typed<IN_BF16, OUT_BF16, BM, BN, FD, EDGE, BT, EPI>(p, group_m, s); break;
+    default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+// The 8-bit input dtypes (4 .. 9: E4M3 then E5M2, each to fp32, fp16, bf16).
+template <int BM, int BN, int EDGE, bool EPI>
+static hipError_t launch_dtype8(const Problem& p, int group_m, hipStream_t s) {
+    switch (p.dtype) {
+    case 4: launch_typed<IN_E4M3, OUT_F32, BM, BN, 1, EDGE, true, EPI>(p, group_m, s); break;
+    case 5: launch_typed<IN_E4M3, OUT_F16, BM, BN, 1, EDGE, true, EPI>(p, group_m, s); break;
+    case 6: launch_typed<IN_E4M3, OUT_BF16, BM, BN, 1, EDGE, true, EPI>(p, group_m, s); break;
+    case 7: launch_typed<IN_E5M2, OUT_F32, BM, BN, 1, EDGE, true, EPI>(p, group_m, s); break;
+    case 8: launch_typed<IN_E5M2, OUT_F16, BM, BN, 1, EDGE, true, EPI>(p, group_m, s); break;
+    case 9: launch_typed<IN_E5M2, OUT_BF16, BM, BN, 1, EDGE, true, EPI>(p, group_m, s); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// All tile sizes and the whole-tile / clamped edge modes for 8-bit inputs
+// (column-major B; clamped edges cover every shape).
+template <bool EPI>
+static hipError_t launch_family8(int tile, int edge, const Problem& p, int group_m, hipStream_t s) {
+    if (edge != EDGE_NONE && edge != EDGE_CLAMP) return hipErrorInvalidValue;
+    if (tile == 256)
+        return edge == EDGE_NONE ? launch_dtype8<256, 256, EDGE_NONE, EPI>(p, group_m, s)
+                                 : launch_dtype8<256, 256, EDGE_CLAMP, EPI>(p, group_m, s);
+    if (tile == 128)
+        return edge == EDGE_NONE ? launch_dtype8<128, 128, EDGE_NONE, EPI>(p, group_m, s)
+                                 : launch_dtype8<128, 128, EDGE_CLAMP, EPI>(p, group_m, s);
+    return edge == EDGE_NONE ? launch_dtype8<64, 64, EDGE_NONE, EPI>(p, group_m, s)
+                             : launch_dtype8<64, 64, EDGE_CLAMP, EPI>(p, group_m, s);
 }
 
 // All tile sizes and edge modes for one (FD, BT, EPI) combination.  The

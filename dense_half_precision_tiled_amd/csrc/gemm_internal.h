@@ -12,6 +12,8 @@ namespace dhpt {
 struct Problem {
     int M, N, K;
     int dtype;                 // gemm_dtype_t
+    // Input bit patterns: 2-byte elements (fp16, bf16) or 1-byte elements
+    // (8-bit floats); leading dimensions in elements.
     const uint16_t* A; int64_t lda;
     const uint16_t* B; int64_t ldb;
     void* C; int64_t ldc;
@@ -22,9 +24,13 @@ struct Problem {
     int relu;
 };
 
+// dtype facts shared by the API and the instance table.
+inline bool dtype_in8(int dtype) { return dtype >= 4 && dtype <= 9; }           // 8-bit float inputs
+inline bool dtype_out_f32(int dtype) { return dtype == 0 || dtype == 2 || dtype == 4 || dtype == 7; }
+
 // Edge handling of an instance (the EDGE modes of gemm_dl_kernel.h).
 enum EdgeMode {
-    EDGE_NONE = 0,             // M % tile, N % tile, K % 64 == 0
+    EDGE_NONE = 0,             // M % tile, N % tile, K % 64 == 0 (K % 128 for 8-bit inputs)
     EDGE_CLAMP = 1,            // any M, K; N % 8 == 0 for row-major B, any N for column-major B
     EDGE_MASKED = 2,           // any shape
 };
@@ -45,6 +51,7 @@ struct InstanceInfo {
     int edge;                  // EdgeMode
     int group_m;               // tile-rows per group of the visit order
     int kind;                  // KernelKind
+    int in8;                   // 1: 8-bit float inputs (and column-major B) only; 0: 16-bit inputs only
 };
 
 extern const InstanceInfo kInstances[];
@@ -62,6 +69,9 @@ hipError_t launch_dl_nn(int tile, int fd, int edge, const Problem& p, int group_
 hipError_t launch_dl_nn_epi(int tile, int fd, int edge, const Problem& p, int group_m, hipStream_t stream);
 hipError_t launch_dl_tn(int tile, int fd, int edge, const Problem& p, int group_m, hipStream_t stream);
 hipError_t launch_dl_tn_epi(int tile, int fd, int edge, const Problem& p, int group_m, hipStream_t stream);
+// The 8-bit-input units of gemm_dl_kernel.h (column-major B, fd 1): plain / general epilogue.
+hipError_t launch_dl_f8(int tile, int edge, const Problem& p, int group_m, hipStream_t stream);
+hipError_t launch_dl_f8_epi(int tile, int edge, const Problem& p, int group_m, hipStream_t stream);
 // The instantiation units of gemm_ks_kernel.h: plain / general epilogue (both B layouts).
 hipError_t launch_ks(int edge, const Problem& p, int group_m, hipStream_t stream);
 hipError_t launch_ks_epi(int edge, const Problem& p, int group_m, hipStream_t stream);

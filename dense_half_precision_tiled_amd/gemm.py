@@ -6,7 +6,9 @@ The functions mirror include/gemm.h one to one (``gemm_run``, ``gemm_run_ex``,
 ``gemm_run_instance_ex``, ``gemm_tile_order``) and take raw device pointers as
 Python ints.  ``gemm(A, B, out_dtype)`` is the
 convenience form on torch tensors: it allocates C with ``torch.empty`` and
-passes ``data_ptr()``, the row strides and the current HIP stream.
+passes ``data_ptr()``, the strides and the current HIP stream (gemm_run for a
+row-major B, gemm_run_ex with GEMM_B_COL_MAJOR for a column-major B, which the
+8-bit float inputs require).
 
 There is no fallback: if the library is not built, every call raises.
 """
@@ -21,6 +23,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdhpt_gemm.so")
 
 GEMM_F16_F32, GEMM_F16_F16, GEMM_BF16_F32, GEMM_BF16_BF16 = 0, 1, 2, 3
+GEMM_E4M3_F32, GEMM_E4M3_F16, GEMM_E4M3_BF16 = 4, 5, 6
+GEMM_E5M2_F32, GEMM_E5M2_F16, GEMM_E5M2_BF16 = 7, 8, 9
 GEMM_OK = 0
 GEMM_ERR_DIM, GEMM_ERR_LD, GEMM_ERR_NULL, GEMM_ERR_DTYPE = -1, -2, -3, -4
 GEMM_ERR_ALIAS, GEMM_ERR_RANGE, GEMM_ERR_LAUNCH, GEMM_ERR_ALIGN = -5, -6, -7, -8
@@ -137,7 +141,13 @@ def _dtype_code(in_dtype, out_dtype) -> int:
     table = {(torch.float16, torch.float32): GEMM_F16_F32,
              (torch.float16, torch.float16): GEMM_F16_F16,
              (torch.bfloat16, torch.float32): GEMM_BF16_F32,
-             (torch.bfloat16, torch.bfloat16): GEMM_BF16_BF16}
+             (torch.bfloat16, torch.bfloat16): GEMM_BF16_BF16,
+             (torch.float8_e4m3fn, torch.float32): GEMM_E4M3_F32,
+             (torch.float8_e4m3fn, torch.float16): GEMM_E4M3_F16,
+             (torch.float8_e4m3fn, torch.bfloat16): GEMM_E4M3_BF16,
+             (torch.float8_e5m2, torch.float32): GEMM_E5M2_F32,
+             (torch.float8_e5m2, torch.float16): GEMM_E5M2_F16,
+             (torch.float8_e5m2, torch.bfloat16): GEMM_E5M2_BF16}
     try:
         return table[(in_dtype, out_dtype)]
     except KeyError:
@@ -152,12 +162,21 @@ def _row_major_ld(t, name):
     return max(t.stride(0), t.shape[1]) if t.shape[0] <= 1 else t.stride(0)
 
 
-def gemm(A, B, out_dtype=None, out=None, instance: int | None = None, stream=None):
-    """C = A @ B on the GPU through gemm_run (or gemm_run_instance).
+def _is_col_major(t) -> bool:
+    return t.dim() == 2 and t.shape[0] > 1 and t.stride(0) == 1 and t.stride(1) >= t.shape[0]
 
-    A: [M, K], B: [K, N] row-major fp16/bf16 CUDA tensors (row strides may
-    exceed the row length).  out_dtype defaults to the input dtype.  ``out``
-    may be a preallocated row-major [M, N] tensor (its row stride is ldc).
+
+def gemm(A, B, out_dtype=None, out=None, instance: int | None = None, stream=None):
+    """C = A @ B on the GPU through gemm_run / gemm_run_ex (or their forced-
+    instance forms).
+
+    A: [M, K] row-major CUDA tensor of fp16, bf16, float8_e4m3fn or
+    float8_e5m2 (row strides may exceed the row length).  B: [K, N] of the
+    same dtype, row-major, or column-major (the transpose of a row-major
+    [N, K] tensor, e.g. ``Bt.t()``); 8-bit inputs need the column-major B.
+    out_dtype defaults to the input dtype for 16-bit inputs and to bfloat16
+    for 8-bit ones.  ``out`` may be a preallocated row-major [M, N] tensor (its
+    row stride is ldc).
     """
     import torch
     if A.dtype != B.dtype:
@@ -166,16 +185,24 @@ def gemm(A, B, out_dtype=None, out=None, instance: int | None = None, stream=Non
     K2, N = B.shape
     if K != K2:
         raise ValueError("inner dimensions differ")
+    in8 = A.dtype in (torch.float8_e4m3fn, torch.float8_e5m2)
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype or A.dtype, device=A.device)
+        out = torch.empty((M, N), dtype=out_dtype or (torch.bfloat16 if in8 else A.dtype), device=A.device)
     elif out_dtype is not None and out.dtype != out_dtype:
         raise TypeError("out has dtype %s" % out.dtype)
     code = _dtype_code(A.dtype, out.dtype)
-    lda, ldb, ldc = _row_major_ld(A, "A"), _row_major_ld(B, "B"), _row_major_ld(out, "C")
+    lda, ldc = _row_major_ld(A, "A"), _row_major_ld(out, "C")
+    col = _is_col_major(B)
+    ldb = B.stride(1) if col else _row_major_ld(B, "B")
     if stream is None:
         stream = torch.cuda.current_stream(A.device).cuda_stream
-    args = (M, N, K, code, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc, stream)
-    st = gemm_run(*args) if instance is None else gemm_run_instance(instance, *args)
+    if col:
+        args = (M, N, K, code, GEMM_B_COL_MAJOR, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc,
+                1.0, 0.0, None, 0, stream)
+        st = gemm_run_ex(*args) if instance is None else gemm_run_instance_ex(instance, *args)
+    else:
+        args = (M, N, K, code, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc, stream)
+        st = gemm_run(*args) if instance is None else gemm_run_instance(instance, *args)
     if st != GEMM_OK:
         raise GemmError(st)
     return out

@@ -17,6 +17,12 @@
  * input, FP32 accumulate contract of the Ada tensor-core GEMM write-up, section
  * "D = A . B"), then converted once to the output type (fp32 as is; fp16 and
  * bf16 by IEEE round-to-nearest-even).
+ *
+ * 8-bit float inputs (the GEMM_E4M3_* and GEMM_E5M2_* dtypes) extend the same
+ * contract to the E4M3 and E5M2 formats of the OCP 8-bit floating point
+ * specification (OFP8), the 8-bit float the Ada write-up's precision notes
+ * leave as the next step: products accumulated in fp32, one rounding to the
+ * output type.  They take B column-major (gemm_run_ex with GEMM_B_COL_MAJOR).
  */
 #ifndef DHPT_GEMM_H
 #define DHPT_GEMM_H
@@ -32,7 +38,14 @@ typedef enum {
     GEMM_F16_F32 = 0,   /* fp16 A, B -> fp32 C */
     GEMM_F16_F16 = 1,   /* fp16 A, B -> fp16 C */
     GEMM_BF16_F32 = 2,  /* bf16 A, B -> fp32 C */
-    GEMM_BF16_BF16 = 3  /* bf16 A, B -> bf16 C */
+    GEMM_BF16_BF16 = 3, /* bf16 A, B -> bf16 C */
+    /* 8-bit float A, B (1-byte elements, OFP8 E4M3 / E5M2; column-major B only) */
+    GEMM_E4M3_F32 = 4,  /* E4M3 A, B -> fp32 C */
+    GEMM_E4M3_F16 = 5,  /* E4M3 A, B -> fp16 C */
+    GEMM_E4M3_BF16 = 6, /* E4M3 A, B -> bf16 C */
+    GEMM_E5M2_F32 = 7,  /* E5M2 A, B -> fp32 C */
+    GEMM_E5M2_F16 = 8,  /* E5M2 A, B -> fp16 C */
+    GEMM_E5M2_BF16 = 9  /* E5M2 A, B -> bf16 C */
 } gemm_dtype_t;
 
 /* Status codes.  Every error is returned before anything is enqueued. */
@@ -50,7 +63,8 @@ enum {
     GEMM_ERR_ALIGN = -8,    /* a pointer not aligned to its element size */
     GEMM_ERR_INSTANCE = -9, /* gemm_run_instance: unknown id, or the instance
                                cannot handle this shape/alignment */
-    GEMM_ERR_LAYOUT = -10   /* gemm_run_ex: b_layout not one of gemm_layout_t */
+    GEMM_ERR_LAYOUT = -10   /* gemm_run_ex: b_layout not one of gemm_layout_t; or an
+                               8-bit dtype with row-major B (gemm_run included) */
 };
 
 /* Storage order of B for gemm_run_ex (A and C are always row-major). */
@@ -68,7 +82,7 @@ typedef enum {
  *   M, N, K    logical sizes (A is M x K, B is K x N, C is M x N).
  *   dtype      a gemm_dtype_t value.
  *   A, lda     device pointer to row-major A; element (i,k) at A[i*lda + k]
- *              (16-bit elements), lda >= K.
+ *              (16-bit elements; 8-bit for the 8-bit dtypes), lda >= K.
  *   B, ldb     device pointer to row-major B; element (k,j) at B[k*ldb + j],
  *              ldb >= N.
  *   C, ldc     device pointer to row-major C; element (i,j) at C[i*ldc + j]
@@ -84,10 +98,11 @@ typedef enum {
  * Sizes: M == 0 or N == 0 is a successful no-op.  K == 0 writes zeros to the
  * M x N region (the product of an M x 0 and a 0 x N matrix).
  *
- * Alignment: only natural element alignment is required (2 bytes for A and B;
- * 4 or 2 bytes for C).  Whole tiles (256x256, 128x128 or 64x64, chosen by
- * the number of tiles and K) with K a multiple of 64 run without edge code;
- * other shapes with N a multiple of 8 run with clamped edge loads and a
+ * Alignment: only natural element alignment is required (2 bytes for 16-bit
+ * A and B, none for 8-bit ones; 4 or 2 bytes for C).  Whole tiles (256x256,
+ * 128x128 or 64x64, chosen by the number of tiles and K) with K a multiple of
+ * 64 (128 for 8-bit inputs) run without edge code; other shapes with N a
+ * multiple of 8 (any N with column-major B) run with clamped edge loads and a
  * zero-filled last k-slice; any other N runs on a fully masked fallback.
  *
  * Returns GEMM_OK once the kernel is enqueued (asynchronous: device faults
@@ -136,12 +151,14 @@ const char* gemm_strerror(int status);
 
 /*
  * Kernel instances.  Each instance is one compiled kernel configuration; all
- * compute the same function.  Two families: "dl_*" (the waves of a workgroup
- * split its output tile; instances of this family give identical bits) and
- * "ks_*" (the four waves split K over a 128x128 tile and their partial sums
- * are added in a fixed order, so repeated calls give identical bits; the
- * rounding differs from the dl family within the accuracy bound).  gemm_run
- * picks one from the shape, the alignment, K and the number of output tiles.
+ * compute the same function.  Three families: "dl_*" (the waves of a
+ * workgroup split its output tile; instances of this family give identical
+ * bits), "ks_*" (the four waves split K over a 128x128 tile and their partial
+ * sums are added in a fixed order, so repeated calls give identical bits; the
+ * rounding differs from the dl family within the accuracy bound), and
+ * "dl8_*" (the dl kernel for 8-bit inputs, which run only there; identical
+ * bits within the family).  gemm_run picks one from the dtype, the shape, the
+ * alignment, K and the number of output tiles.
  *
  * gemm_select_instance returns the id gemm_run would use for these arguments
  * (pointers are only inspected for alignment, never dereferenced; no GPU call

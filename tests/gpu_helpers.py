@@ -7,22 +7,27 @@ import torch
 import oracle
 from dense_half_precision_tiled_amd import inputs
 
-DTYPES = {0: ("f16", "f32"), 1: ("f16", "f16"), 2: ("bf16", "f32"), 3: ("bf16", "bf16")}
+DTYPES = {0: ("f16", "f32"), 1: ("f16", "f16"), 2: ("bf16", "f32"), 3: ("bf16", "bf16"),
+          4: ("e4m3", "f32"), 5: ("e4m3", "f16"), 6: ("e4m3", "bf16"),
+          7: ("e5m2", "f32"), 8: ("e5m2", "f16"), 9: ("e5m2", "bf16")}
 POISON16 = 0x7E11      # a quiet-NaN pattern in both fp16 and bf16
+POISON8 = 0x7F         # NaN in both E4M3 and E5M2
 POISON32 = 0x7FC01234  # a quiet NaN in fp32
 GUARD = 64             # guard elements before and after C
 
 
 def _dev(bits, ld=None, offset=0):
-    """Upload a rows x cols bit matrix into a buffer with row stride ld,
-    starting `offset` elements into the allocation; padding is poisoned."""
+    """Upload a rows x cols bit matrix (uint16, or uint8 for 8-bit inputs)
+    into a buffer with row stride ld, starting `offset` elements into the
+    allocation; padding is poisoned."""
     rows, cols = bits.shape
     ld = ld or cols
-    buf = np.full(offset + max(rows * ld, 1) + 8, POISON16, dtype=np.uint16)
+    esz = bits.dtype.itemsize
+    buf = np.full(offset + max(rows * ld, 1) + 16, POISON16 if esz == 2 else POISON8, dtype=bits.dtype)
     if rows and cols:
         buf[offset:offset + rows * ld].reshape(rows, ld)[:, :cols] = bits
-    t = torch.from_numpy(buf.view(np.int16)).cuda()
-    return t, t.data_ptr() + 2 * offset, ld
+    t = torch.from_numpy(buf.view(np.int16) if esz == 2 else buf.view(np.int8)).cuda()
+    return t, t.data_ptr() + esz * offset, ld
 
 
 def decode_out(raw, out_fmt):
@@ -100,8 +105,8 @@ def run(G, A, B, code, lda=None, ldb=None, ldc=None, a_off=0, instance=None, str
     return decode_out(np.ascontiguousarray(body[:, :N]), out_fmt)
 
 
-def assert_bound(y, r, K, out_fmt, what=""):
-    res = oracle.compare(y, r, K, out_fmt)
+def assert_bound(y, r, K, out_fmt, what="", extra=None):
+    res = oracle.compare(y, r, K, out_fmt, extra=extra)
     assert res["ok"], "%s: %d elements outside the bound; max_abs %.3g, worst/bound %.3g" % (
         what, res["n_bad"], res["max_abs"], res["worst_ratio"])
     return res

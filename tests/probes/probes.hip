@@ -173,6 +173,25 @@ __global__ void probe_mfma_f8_kernel(const uint32_t* a, const uint32_t* b, float
     for (int i = 0; i < 16; ++i) d[16 * l + i] = acc[i];
 }
 
+// The same MFMA with an incoming accumulator: d = c + A.B, with c[16l + i]
+// the accumulator element i of lane l (the 32x32 accumulator map).
+template <int FMT>
+__global__ void probe_mfma_f8_acc_kernel(const uint32_t* a, const uint32_t* b, const float* c, float* d) {
+    const int l = threadIdx.x;
+    i32x8 av, bv;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        av[j] = (int32_t)a[8 * l + j];
+        bv[j] = (int32_t)b[8 * l + j];
+    }
+    f32x16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = c[16 * l + i];
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, FMT, FMT, 0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) d[16 * l + i] = acc[i];
+}
+
 // Issue rate of v_mfma_f32_32x32x64_f8f6f4 (E4M3), as probe_mfma_rate_kernel:
 // eight independent accumulators, register-resident operands.
 __global__ __launch_bounds__(256) void probe_mfma_f8_rate_kernel(int iters, uint64_t* cycles, float* sink) {
@@ -422,6 +441,14 @@ int probe_mfma_f8(int fmt, const uint32_t* a, const uint32_t* b, float* d) {
         hipLaunchKernelGGL(probe_mfma_f8_kernel<0>, dim3(1), dim3(64), 0, 0, a, b, d);
     else
         hipLaunchKernelGGL(probe_mfma_f8_kernel<1>, dim3(1), dim3(64), 0, 0, a, b, d);
+    return (int)hipDeviceSynchronize();
+}
+
+int probe_mfma_f8_acc(int fmt, const uint32_t* a, const uint32_t* b, const float* c, float* d) {
+    if (fmt == 0)
+        hipLaunchKernelGGL(probe_mfma_f8_acc_kernel<0>, dim3(1), dim3(64), 0, 0, a, b, c, d);
+    else
+        hipLaunchKernelGGL(probe_mfma_f8_acc_kernel<1>, dim3(1), dim3(64), 0, 0, a, b, c, d);
     return (int)hipDeviceSynchronize();
 }
 

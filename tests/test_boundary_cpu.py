@@ -50,7 +50,9 @@ def test_strerror_covers_every_status(lib):
     ((-1, 4, 4, 0, PA, 4, PB, 4, PC, 4), G.GEMM_ERR_DIM),
     ((4, -1, 4, 0, PA, 4, PB, 4, PC, 4), G.GEMM_ERR_DIM),
     ((4, 4, -1, 0, PA, 4, PB, 4, PC, 4), G.GEMM_ERR_DIM),
-    ((4, 4, 4, 7, PA, 4, PB, 4, PC, 4), G.GEMM_ERR_DTYPE),
+    ((4, 4, 4, 10, PA, 4, PB, 4, PC, 4), G.GEMM_ERR_DTYPE),
+    ((4, 4, 4, 4, PA, 4, PB, 4, PC, 4), G.GEMM_ERR_LAYOUT),        # 8-bit inputs need column-major B
+    ((4, 4, 4, 9, PA, 4, PB, 4, PC, 4), G.GEMM_ERR_LAYOUT),
     ((4, 4, 4, -1, PA, 4, PB, 4, PC, 4), G.GEMM_ERR_DTYPE),
     ((4, 4, 8, 0, PA, 7, PB, 4, PC, 4), G.GEMM_ERR_LD),
     ((4, 4, 8, 0, PA, 8, PB, 3, PC, 4), G.GEMM_ERR_LD),
@@ -95,7 +97,7 @@ def test_unknown_instance(lib):
     assert G.gemm_run_instance(n, 4, 4, 4, 0, PA, 4, PB, 4, PC, 4, None) == G.GEMM_ERR_INSTANCE
     assert G.gemm_instance_name(n) == "?"
     for i in range(n):
-        assert G.gemm_instance_name(i).startswith(("dl_", "ks_"))
+        assert G.gemm_instance_name(i).startswith(("dl_", "ks_", "dl8_"))
 
 
 def _pick(M, N, K, dtype=3, lda=None, ldb=None, ldc=None, pa=PA, pb=PB):
@@ -144,6 +146,42 @@ def test_instance_choice_general_form(lib):
     assert _pick_ex(4096, 4096, 4096, row, alpha=2.0, beta=1.0, bias=PC, relu=1) == "dl_256x256x64_fd2"
     # the plain form through gemm_run_ex selects what gemm_run selects
     assert _pick_ex(3000, 5000, 4099, row, 1) == _pick(3000, 5000, 4099, 1)
+
+
+def test_instance_choice_8bit_inputs(lib):
+    """8-bit float inputs run on the dl8 instances only, with column-major B;
+    tile size by the number of tiles, clamped edges for anything but whole
+    tiles with K a multiple of 128."""
+    col = G.GEMM_B_COL_MAJOR
+    for dt in range(4, 10):
+        assert _pick_ex(8192, 8192, 8192, col, dt) == "dl8_256x256x128"
+    assert _pick_ex(4096, 4096, 4096, col, 6) == "dl8_256x256x128"
+    assert _pick_ex(4096, 4096, 4160, col, 6) == "dl8_256x256x128_clamp"      # K % 128 == 64
+    assert _pick_ex(2048, 2048, 2048, col, 4) == "dl8_128x128x128"
+    assert _pick_ex(3000, 5000, 4099, col, 5) == "dl8_256x256x128_clamp"
+    assert _pick_ex(256, 256, 256, col, 4) == "dl8_64x64x128"
+    assert _pick_ex(100, 7, 33, col, 7) == "dl8_64x64x128_clamp"
+    # odd byte addresses and leading dimensions are fine for 1-byte elements
+    ex = G.gemm_select_instance_ex
+    assert ex(4096, 4096, 4096, 6, col, PA + 1, 4097, PB + 3, 4099, PC, 4096, 1.0, 0.0, None, 0) >= 0
+    # 16-bit dtypes never land on the 8-bit instances and vice versa
+    ids = {G.gemm_instance_name(i): i for i in range(G.gemm_num_instances())}
+    st = G.gemm_run_instance_ex(ids["dl8_256x256x128"], 256, 256, 128, 3, col, PA, 128, PB, 128, PC, 256,
+                                1.0, 0.0, None, 0, None)
+    assert st == G.GEMM_ERR_INSTANCE
+    st = G.gemm_run_instance_ex(ids["dl_256x256x64_fd2"], 256, 256, 128, 4, col, PA, 128, PB, 128, PC, 256,
+                                1.0, 0.0, None, 0, None)
+    assert st == G.GEMM_ERR_INSTANCE
+    # an 8-bit whole-tile instance needs K % 128 == 0
+    st = G.gemm_run_instance_ex(ids["dl8_256x256x128"], 256, 256, 64, 4, col, PA, 64, PB, 64, PC, 256,
+                                1.0, 0.0, None, 0, None)
+    assert st == G.GEMM_ERR_INSTANCE
+    # row-major B with 8-bit inputs: a layout error on every entry point
+    assert ex(256, 256, 256, 4, 0, PA, 256, PB, 256, PC, 256, 1.0, 0.0, None, 0) == G.GEMM_ERR_LAYOUT
+    # extents count 1-byte elements: C starting right after an 8-bit A is no alias
+    a_end = PA + 4 * 128
+    assert ex(4, 4, 128, 4, col, PA, 128, PB, 128, a_end, 4, 1.0, 0.0, None, 0) >= 0
+    assert ex(4, 4, 128, 4, col, PA, 128, PB, 128, a_end - 4, 4, 1.0, 0.0, None, 0) == G.GEMM_ERR_ALIAS
 
 
 def test_general_form_validation(lib):

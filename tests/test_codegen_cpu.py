@@ -10,7 +10,8 @@ it is checked for properties the design relies on:
   followed by s_nop 0 and the global_load_lds it addresses), so no other code
   can move a copy's LDS destination;
 * every kernel uses at most 512 VGPR+AGPR registers (one wave per SIMD) and the
-  MFMA instructions the design names.
+  MFMA instructions the design names (32x32x16 for 16-bit inputs, the unscaled
+  32x32x64 8-bit form for 8-bit inputs).
 """
 import concurrent.futures
 import os
@@ -24,7 +25,7 @@ import pytest
 from dense_half_precision_tiled_amd import build as B
 
 UNITS = ["gemm_dl_nn.hip", "gemm_dl_nn_epi.hip", "gemm_dl_tn.hip", "gemm_dl_tn_epi.hip",
-         "gemm_ks.hip", "gemm_ks_epi.hip"]
+         "gemm_ks.hip", "gemm_ks_epi.hip", "gemm_dl_f8.hip", "gemm_dl_f8_epi.hip"]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(B.hipcc()), reason="hipcc not available")
 
@@ -42,7 +43,7 @@ def kernels():
     """{mangled kernel name: (unit, list of instruction lines, metadata dict)}."""
     d = tempfile.mkdtemp(prefix="dhpt_asm_")
     try:
-        with concurrent.futures.ThreadPoolExecutor(min(6, os.cpu_count() or 1)) as ex:
+        with concurrent.futures.ThreadPoolExecutor(min(8, os.cpu_count() or 1)) as ex:
             outs = list(ex.map(lambda u: _compile(u, d), UNITS))
         res = {}
         for unit, path in outs:
@@ -99,7 +100,7 @@ def test_whole_tile_plain_kernels_use_no_scratch(kernels):
             assert meta.get("private_seg_size", 0) == 0, "%s uses %d bytes of scratch" % (
                 _short(name), meta["private_seg_size"])
             checked += 1
-    assert checked >= 24
+    assert checked >= 36
 
 
 def test_m0_is_written_only_by_the_copy_helper(kernels):
@@ -116,4 +117,7 @@ def test_register_budget_and_mfma_shape(kernels):
     for name, (unit, ins, meta) in kernels.items():
         assert meta["num_vgpr"] + meta["num_agpr"] <= 512, _short(name)
         ops = {s.split()[0] for s in ins if s.startswith("v_mfma")}
-        assert ops <= {"v_mfma_f32_32x32x16_f16", "v_mfma_f32_32x32x16_bf16"}, (_short(name), ops)
+        if unit.startswith("gemm_dl_f8"):
+            assert ops == {"v_mfma_f32_32x32x64_f8f6f4"}, (_short(name), ops)
+        else:
+            assert ops <= {"v_mfma_f32_32x32x16_f16", "v_mfma_f32_32x32x16_bf16"}, (_short(name), ops)

@@ -1,0 +1,201 @@
+"""GPU parity of the 8-bit float inputs (E4M3 and E5M2 of the OCP 8-bit
+floating point specification; B column-major), through the C ABI, against the
+CPU oracle.
+
+Bars (as for the 16-bit inputs):
+* exact fixtures (the page's worked example, small integers, multiples of
+  0.25): every element equals round_to(out_fmt, oracle), bit for bit;
+* random N(0, 1) inputs rounded to the 8-bit format: |y - r| <= K * 2^-20
+  (fp32 output) or ulp_fmt(r) + K * 2^-20 (fp16/bf16 output), plus the
+  8-bit MFMA's alignment loss oracle.align_bound8 (each group of 8
+  consecutive k keeps 13 binades below its largest product; pinned by
+  test_mfma_f8_alignment_model) for every checked element;
+* the six 8-bit instances (three tile sizes, whole or clamped edges) give
+  identical bits where they all apply;
+* memory outside the M x N region of C is never written (checked by run()).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from dense_half_precision_tiled_amd import inputs
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from tests.gpu_helpers import DTYPES, assert_bound, assert_exact, run  # noqa: E402
+
+CODES8 = [4, 5, 6, 7, 8, 9]
+
+
+@pytest.fixture(scope="module")
+def G():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from dense_half_precision_tiled_amd import gemm
+    gemm.load()      # raises if the library is missing: no fallback
+    return gemm
+
+
+def _run_tn(G, A, B, code, **kw):
+    """A (M x K) and B (K x N) as bit patterns; B is passed column-major."""
+    return run(G, A, np.ascontiguousarray(B.T), code, layout=G.GEMM_B_COL_MAJOR, **kw)
+
+
+def _oracle(A, B, fmt):
+    return oracle.gemm_ex_f64(A, np.ascontiguousarray(B.T), fmt, b_layout="col")
+
+
+def _extra(A, B, fmt, rows=None):
+    return oracle.align_bound8(A, B, fmt, rows=rows)
+
+
+@pytest.mark.parametrize("code", CODES8)
+def test_worked_example(G, code):
+    with open(os.path.join(os.path.dirname(__file__), "golden", "worked_example_2x3x2.json")) as f:
+        g = json.load(f)
+    fmt, out = DTYPES[code]
+    y = _run_tn(G, inputs.from_values(g["A"], fmt), inputs.from_values(g["B"], fmt), code)
+    assert y.tolist() == g["C"]
+
+
+@pytest.mark.parametrize("code", CODES8)
+@pytest.mark.parametrize("shape", [(256, 256, 256), (512, 768, 1024), (257, 263, 251), (300, 520, 4099),
+                                   (64, 1000, 2048), (1, 1, 1), (5, 3, 15), (33, 17, 129)])
+def test_integer_and_quarter_grid_bit_exact(G, code, shape):
+    """Integers in {-2..2} and multiples of 0.25 in [-2, 2] are exact in both
+    8-bit formats; every partial sum is exact in fp32, so each output is the
+    correctly rounded exact value."""
+    M, N, K = shape
+    fmt, out = DTYPES[code]
+    for law, s in ((inputs.ints, 300), (inputs.quarter, 310)):
+        A = law((M, K), s + code, fmt)
+        B = law((K, N), s + 1 + code, fmt)
+        print("8-bit exact", code, shape, law.__name__, flush=True)
+        assert_exact(_run_tn(G, A, B, code), _oracle(A, B, fmt), out, "%s %s %s" % (code, shape, law.__name__))
+
+
+@pytest.mark.parametrize("code", CODES8)
+@pytest.mark.parametrize("shape", [(1024, 1024, 1024), (4096, 2048, 512), (384, 640, 896),
+                                   (1000, 1001, 777), (96, 50, 4160), (2, 300, 7)])
+def test_random_inputs_within_bound(G, code, shape):
+    M, N, K = shape
+    fmt, out = DTYPES[code]
+    A = inputs.normal((M, K), 400 + code, fmt)
+    B = inputs.normal((K, N), 401 + code, fmt)
+    print("8-bit random", code, shape, flush=True)
+    y = _run_tn(G, A, B, code)
+    assert_bound(y, _oracle(A, B, fmt), K, out, "%s %s" % (code, shape), extra=_extra(A, B, fmt))
+
+
+@pytest.mark.parametrize("code", [4, 9])
+def test_odd_leading_dimensions_and_offsets(G, code):
+    """1-byte elements: rows may start at any byte (odd lda, ldb, base)."""
+    M, N, K = 333, 520, 1111
+    fmt, out = DTYPES[code]
+    A = inputs.normal((M, K), 500, fmt)
+    B = inputs.normal((K, N), 501, fmt)
+    r = _oracle(A, B, fmt)
+    x = _extra(A, B, fmt)
+    ys = []
+    for lda, ldb, a_off in ((K + 1, K + 3, 1), (K + 5, K, 3), (K, K + 7, 0), (K + 16, K + 16, 15)):
+        print("8-bit strides", code, lda, ldb, a_off, flush=True)
+        y = _run_tn(G, A, B, code, lda=lda, ldb=ldb, ldc=N + 5, a_off=a_off)
+        assert_bound(y, r, K, out, "lda %d ldb %d off %d" % (lda, ldb, a_off), extra=x)
+        ys.append(y)
+    for y in ys[1:]:                     # strides and offsets move data only
+        assert np.array_equal(y, ys[0], equal_nan=True)
+
+
+def test_instances_agree_bitwise(G):
+    """Tile size and edge handling move data only: the six 8-bit instances
+    give identical bits on a shape they all run."""
+    M, N, K = 512, 512, 1024
+    ids = [i for i in range(G.gemm_num_instances()) if G.gemm_instance_name(i).startswith("dl8_")]
+    assert len(ids) == 6
+    for code in (4, 8):
+        fmt, out = DTYPES[code]
+        A = inputs.normal((M, K), 600, fmt)
+        B = inputs.normal((K, N), 601, fmt)
+        ys = []
+        for i in ids:
+            print("8-bit instance", G.gemm_instance_name(i), code, flush=True)
+            ys.append(_run_tn(G, A, B, code, instance=i))
+        for i, y in zip(ids[1:], ys[1:]):
+            assert np.array_equal(y, ys[0], equal_nan=True), G.gemm_instance_name(i)
+        assert_bound(ys[0], _oracle(A, B, fmt), K, out, extra=_extra(A, B, fmt))
+
+
+@pytest.mark.parametrize("code", [4, 6, 8])
+def test_general_form(G, code):
+    M, N, K = 300, 264, 700
+    fmt, out = DTYPES[code]
+    A = inputs.normal((M, K), 700, fmt)
+    B = inputs.normal((K, N), 701, fmt)
+    Bs = np.ascontiguousarray(B.T)
+    from tests.gpu_helpers import decode_out, encode_out
+    cold = decode_out(encode_out(np.random.Generator(np.random.PCG64(702)).uniform(-4, 4, (M, N)), out), out)
+    bias = np.random.Generator(np.random.PCG64(703)).uniform(-2, 2, N).astype(np.float32).astype(np.float64)
+    for alpha, beta, b, relu in ((0.5, 0.0, None, 0), (-2.0, 1.0, bias, 1), (1.0, -0.5, bias, 0)):
+        print("8-bit general", code, alpha, beta, b is not None, relu, flush=True)
+        y = run(G, A, Bs, code, layout=G.GEMM_B_COL_MAJOR, alpha=alpha, beta=beta, bias=b, relu=relu,
+                c_init=encode_out(cold, out))
+        r = oracle.gemm_ex_f64(A, Bs, fmt, b_layout="col", alpha=alpha, beta=beta, C_old=cold, bias=b,
+                               relu=bool(relu))
+        dot = oracle.gemm_ex_f64(A, Bs, fmt, b_layout="col")
+        res = oracle.compare_ex(y, r, K, out, alpha=alpha, beta=beta, C_old=cold, bias=b, dot=dot,
+                                extra=_extra(A, B, fmt))
+        assert res["ok"], res
+
+
+def test_zero_K(G):
+    """K == 0: the plain form writes zeros; the general form gives act(beta*C + bias)."""
+    M, N = 70, 90
+    A = np.zeros((M, 0), np.uint8)
+    B = np.zeros((0, N), np.uint8)
+    assert np.array_equal(_run_tn(G, A, B, 4), np.zeros((M, N)))
+    from tests.gpu_helpers import encode_out
+    y = run(G, A, np.zeros((N, 0), np.uint8), 4, layout=G.GEMM_B_COL_MAJOR, beta=2.0,
+            c_init=encode_out(np.ones((M, N)), "f32"))
+    assert np.array_equal(y, np.full((M, N), 2.0))
+
+
+def test_torch_binding_with_float8_tensors(G):
+    """gemm.gemm on torch float8 tensors with B as a transposed view."""
+    M, N, K = 500, 384, 640
+    A = inputs.normal((M, K), 800, "e4m3")
+    B = inputs.normal((K, N), 801, "e4m3")
+    tA = torch.from_numpy(A).cuda().view(torch.float8_e4m3fn)
+    tBt = torch.from_numpy(np.ascontiguousarray(B.T)).cuda().view(torch.float8_e4m3fn)
+    y = G.gemm(tA, tBt.t(), torch.float32)
+    torch.cuda.synchronize()
+    assert_bound(y.cpu().numpy().astype(np.float64), _oracle(A, B, "e4m3"), K, "f32",
+                 extra=_extra(A, B, "e4m3"))
+    with pytest.raises(G.GemmError):
+        G.gemm(tA, tBt.t().contiguous(), torch.float32)        # row-major B: layout error
+
+
+@pytest.mark.parametrize("name", ["e4m3_8192", "e5m2_8192"])
+def test_full_size_sampled(G, name):
+    A, B, w = inputs.workload_inputs(name)
+    code = {("e4m3", "bf16"): 6, ("e5m2", "bf16"): 9}[(w["fmt"], w["out"])]
+    print("full-size workload", name, flush=True)
+    y = _run_tn(G, A, B, code)
+    from tests.test_gpu_parity import _sample_rows
+    rows = _sample_rows(w["M"], n=8)
+    r = oracle.gemm_ex_f64(A, np.ascontiguousarray(B.T), w["fmt"], b_layout="col", rows=rows)
+    res = assert_bound(y[rows], r, w["K"], w["out"], name, extra=_extra(A, B, w["fmt"], rows=rows))
+    print(name, "sampled rows", rows.size, "max_abs %.3g" % res["max_abs"], flush=True)
+    # Freivalds over the whole matrix: |y x - A (B x)| <= sum_j bound_ij for x in {-1, 1}^N,
+    # with bound_ij at most acc + ulp(2 max|y_i.|) + 7 2^-13 sum_g maxA[i,g] max_j maxB[g,j]
+    Ad, Bd = oracle.decode(A, w["fmt"]), oracle.decode(B, w["fmt"])
+    G8 = w["K"] // 8
+    maxA = np.abs(Ad).reshape(w["M"], G8, 8).max(axis=2)
+    maxB = np.abs(Bd).reshape(G8, 8, w["N"]).max(axis=1).max(axis=1)
+    row_extra = 7 * 2.0 ** -13 * (maxA @ maxB)
+    per = oracle.bound(w["K"], w["out"], np.abs(y).max(axis=1) * 2.0) + row_extra
+    x = np.random.Generator(np.random.PCG64(98)).choice(np.array([-1.0, 1.0]), size=w["N"])
+    assert np.all(np.abs(y @ x - Ad @ (Bd @ x)) <= w["N"] * per), "Freivalds check failed"
