@@ -20,7 +20,9 @@ Printed: one JSON line with the contract fields plus
                 against the GPU result);
   secondary     the same measurement on bf16 4096^3;
   other_configs the same on the other workloads (fp16 2048^3, the ragged
-                fp16 3000x5000x4099 shape, fp16 256^3).
+                fp16 3000x5000x4099 shape, fp16 256^3, and the 8-bit float
+                E4M3 8192^3 -> bf16 with B column-major, against the dense
+                fp8 peak of 5.0 PFLOP/s).
 Before the warmups of each workload, untimed launches run for about
 --settle-ms so that the timed launches see a settled shader clock.
 
@@ -45,13 +47,20 @@ if ROOT not in sys.path:
 METRIC = "GEMM TFLOP/s (2MNK/t) at 4096³ and 8192³ bf16/fp16; % of MFMA peak"
 PEAK_TFLOPS = 2500.0        # MI355X published dense fp16/bf16 MFMA peak
 HBM_GBPS = 8000.0           # MI355X published HBM3E bandwidth
-CODES = {("f16", "f32"): 0, ("f16", "f16"): 1, ("bf16", "f32"): 2, ("bf16", "bf16"): 3}
+CODES = {("f16", "f32"): 0, ("f16", "f16"): 1, ("bf16", "f32"): 2, ("bf16", "bf16"): 3,
+         ("e4m3", "f32"): 4, ("e4m3", "f16"): 5, ("e4m3", "bf16"): 6,
+         ("e5m2", "f32"): 7, ("e5m2", "f16"): 8, ("e5m2", "bf16"): 9}
+EIGHT_BIT = ("e4m3", "e5m2")
+PEAK8_TFLOPS = 5000.0       # MI355X published dense fp8 MFMA peak
 # The sources each kernel family is compiled from: a counter summary stays
 # valid for a workload while these are unchanged.
 FAMILY_SOURCES = {
     "dl": ["dense_half_precision_tiled_amd/csrc/gemm_common.h",
            "dense_half_precision_tiled_amd/csrc/gemm_dl_kernel.h",
            "dense_half_precision_tiled_amd/csrc/gemm_internal.h"],
+    "dl8": ["dense_half_precision_tiled_amd/csrc/gemm_common.h",
+            "dense_half_precision_tiled_amd/csrc/gemm_dl_kernel.h",
+            "dense_half_precision_tiled_amd/csrc/gemm_internal.h"],
     "ks": ["dense_half_precision_tiled_amd/csrc/gemm_common.h",
            "dense_half_precision_tiled_amd/csrc/gemm_ks_kernel.h",
            "dense_half_precision_tiled_amd/csrc/gemm_internal.h"],
@@ -67,14 +76,19 @@ def kernel_source_hash(family: str) -> str:
 
 
 def describe(w) -> str:
-    return "%s GEMM C=A.B M=%d N=%d K=%d row-major, %s inputs, fp32 accumulate, %s output" % (
+    return "%s GEMM C=A.B M=%d N=%d K=%d %s, %s inputs, fp32 accumulate, %s output" % (
         w["fmt"], w["M"], w["N"], w["K"],
+        "A row-major, B column-major" if w["fmt"] in EIGHT_BIT else "row-major",
         "U[-1,1)" if w["law"] == "uniform" else "N(0,1)", w["out"])
+
+
+def peak_for(w) -> float:
+    return PEAK8_TFLOPS if w["fmt"] in EIGHT_BIT else PEAK_TFLOPS
 
 
 def upload(bits, torch):
     import numpy as np
-    return torch.from_numpy(bits.view(np.int16)).cuda()
+    return torch.from_numpy(bits.view(np.int16) if bits.dtype.itemsize == 2 else bits.view(np.int8)).cuda()
 
 
 def measure(G, torch, name, steps, warmup, instance=None, layout="row", settle_ms=200.0):
@@ -89,7 +103,7 @@ def measure(G, torch, name, steps, warmup, instance=None, layout="row", settle_m
     A, B, w = inputs.workload_inputs(name)
     M, N, K = w["M"], w["N"], w["K"]
     code = CODES[(w["fmt"], w["out"])]
-    col = layout == "col"
+    col = layout == "col" or w["fmt"] in EIGHT_BIT         # 8-bit inputs take B column-major
     tA, tB = upload(A, torch), upload(np.ascontiguousarray(B.T) if col else B, torch)
     odt = torch.float32 if w["out"] == "f32" else torch.int16
     tC = torch.full((M, N), -1, dtype=torch.int32 if odt == torch.float32 else torch.int16,
@@ -154,7 +168,7 @@ def measure(G, torch, name, steps, warmup, instance=None, layout="row", settle_m
     return {"name": name, "w": w, "A": A, "B": B, "C": tC, "ms": ms, "rep_ms": rep_ms, "launch": launch,
             "wall_s": wall, "settle_launches": n_settle,
             "tflops": flops / (ms * 1e-3) / 1e12, "instance": G.gemm_instance_name(inst),
-            "alg_bytes": 2 * (M * K + K * N) + (4 if w["out"] == "f32" else 2) * M * N}
+            "alg_bytes": (1 if w["fmt"] in EIGHT_BIT else 2) * (M * K + K * N) + (4 if w["out"] == "f32" else 2) * M * N}
 
 
 def repeats(res):
@@ -343,16 +357,21 @@ def loop_for(G, torch, name, seconds: float) -> int:
         from dense_half_precision_tiled_amd import inputs
         A, B, w = inputs.workload_inputs(name)
         M, N, K = w["M"], w["N"], w["K"]
-        tA, tB = upload(A, torch), upload(B, torch)
+        col = w["fmt"] in EIGHT_BIT
+        tA, tB = upload(A, torch), upload(np.ascontiguousarray(B.T) if col else B, torch)
         tC = torch.empty((M, N), dtype=torch.float32 if w["out"] == "f32" else torch.int16, device="cuda")
-        args = (M, N, K, CODES[(w["fmt"], w["out"])], tA.data_ptr(), K, tB.data_ptr(), N, tC.data_ptr(), N,
-                torch.cuda.current_stream().cuda_stream)
+        s = torch.cuda.current_stream().cuda_stream
+        code = CODES[(w["fmt"], w["out"])]
+        args = (M, N, K, code, tA.data_ptr(), K, tB.data_ptr(), N, tC.data_ptr(), N, s)
+        if col:
+            args = (M, N, K, code, G.GEMM_B_COL_MAJOR, tA.data_ptr(), K, tB.data_ptr(), K, tC.data_ptr(), N,
+                    1.0, 0.0, None, 0, s)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         n, t0 = 0, time.perf_counter()
         e0.record()
         while time.perf_counter() - t0 < seconds:
             for _ in range(16):
-                if G.gemm_run(*args) != 0:
+                if (G.gemm_run_ex(*args) if col else G.gemm_run(*args)) != 0:
                     raise RuntimeError("gemm_run failed")
             n += 16
             torch.cuda.synchronize()
@@ -410,7 +429,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="bf16_8192")
     ap.add_argument("--secondary", default="bf16_4096", help="'none' to skip")
-    ap.add_argument("--also", default="f16_2048,f16_ragged,f16_256",
+    ap.add_argument("--also", default="f16_2048,f16_ragged,f16_256,e4m3_8192",
                     help="comma-separated further workloads reported under other_configs ('none' to skip)")
     ap.add_argument("--settle-ms", type=float, default=200.0,
                     help="untimed launches for about this long before the warmups (clock ramp-up)")
@@ -457,7 +476,8 @@ def main(argv=None):
     def summary(r):
         w2 = r["w"]
         return {"workload": describe(w2), "value": round(r["tflops"], 2), "unit": "TFLOP/s",
-                "ms_per_step": round(r["ms"], 5), "frac_of_peak": round(r["tflops"] / PEAK_TFLOPS, 4),
+                "ms_per_step": round(r["ms"], 5), "frac_of_peak": round(r["tflops"] / peak_for(w2), 4),
+                "peak": peak_for(w2),
                 "hbm_gbps_algorithmic": round(r["alg_bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
                 "kernel": r["instance"], "repeats": repeats(r)}
 
@@ -495,8 +515,8 @@ def main(argv=None):
                    "M": w["M"], "N": w["N"], "K": w["K"], "b_layout": args.layout,
                    "in": w["fmt"], "out": w["out"], "kernel": main_res["instance"],
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": round(main_res["tflops"], 2), "peak": PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(main_res["tflops"] / PEAK_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(main_res["tflops"], 2), "peak": peak_for(w),
+                     "unit": "TFLOP/s", "frac": round(main_res["tflops"] / peak_for(w), 4),
                      "traffic": traffic,
                      "algorithmic_bytes": main_res["alg_bytes"],
                      "hbm_gbps_algorithmic": round(main_res["alg_bytes"] / (main_res["ms"] * 1e-3) / 1e9, 1)},
