@@ -479,7 +479,8 @@ def main(argv=None):
                 "ms_per_step": round(r["ms"], 5), "frac_of_peak": round(r["tflops"] / peak_for(w2), 4),
                 "peak": peak_for(w2),
                 "hbm_gbps_algorithmic": round(r["alg_bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
-                "kernel": r["instance"], "repeats": repeats(r)}
+                "kernel": r["instance"], "repeats": repeats(r),
+                "traffic": traffic_from_profiles(r["name"], r["instance"])}
 
     sec = None
     if args.secondary and args.secondary != "none":

@@ -119,5 +119,10 @@ def assert_exact(y, r, out_fmt, what=""):
         what, bad.sum(), np.argwhere(bad)[0], y[bad][0], want[bad][0])
 
 
+def instances16(G):
+    """Ids of the instances that run 16-bit inputs (all but the dl8_* ones)."""
+    return [i for i in range(G.gemm_num_instances()) if not G.gemm_instance_name(i).startswith("dl8_")]
+
+
 def law_for(fmt):
     return inputs.uniform if fmt == "f16" else inputs.normal

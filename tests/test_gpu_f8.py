@@ -88,7 +88,9 @@ def test_random_inputs_within_bound(G, code, shape):
     B = inputs.normal((K, N), 401 + code, fmt)
     print("8-bit random", code, shape, flush=True)
     y = _run_tn(G, A, B, code)
-    assert_bound(y, _oracle(A, B, fmt), K, out, "%s %s" % (code, shape), extra=_extra(A, B, fmt))
+    res = assert_bound(y, _oracle(A, B, fmt), K, out, "%s %s" % (code, shape), extra=_extra(A, B, fmt))
+    print("8-bit random", code, shape, "max_abs %.3g worst err/bound %.4f" % (res["max_abs"], res["worst_ratio"]),
+          flush=True)
 
 
 @pytest.mark.parametrize("code", [4, 9])
@@ -149,6 +151,31 @@ def test_general_form(G, code):
         res = oracle.compare_ex(y, r, K, out, alpha=alpha, beta=beta, C_old=cold, bias=b, dot=dot,
                                 extra=_extra(A, B, fmt))
         assert res["ok"], res
+
+
+def test_general_form_every_instance(G):
+    """alpha, beta, bias and ReLU on each of the six 8-bit instances (0.25-grid
+    inputs: the result is exact), on whole tiles and on a ragged shape for the
+    clamped ones."""
+    from tests.gpu_helpers import encode_out
+    ids = [i for i in range(G.gemm_num_instances()) if G.gemm_instance_name(i).startswith("dl8_")]
+    for (M, N, K) in ((512, 512, 1024), (300, 264, 700)):
+        A = inputs.quarter((M, K), 901, "e5m2")
+        B = inputs.quarter((K, N), 902, "e5m2")
+        Bs = np.ascontiguousarray(B.T)
+        cold = np.random.Generator(np.random.PCG64(903)).integers(-8, 9, (M, N)).astype(np.float64)
+        bias = np.arange(N, dtype=np.float64) * 0.25 - 30.0
+        r = oracle.gemm_ex_f64(A, Bs, "e5m2", b_layout="col", alpha=0.5, beta=2.0, C_old=cold, bias=bias, relu=True)
+        for i in ids:
+            name = G.gemm_instance_name(i)
+            whole = not name.endswith("_clamp")
+            tile = int(name.split("_")[1].split("x")[0])
+            expect = G.GEMM_ERR_INSTANCE if whole and (M % tile or N % tile or K % 128) else 0
+            print("8-bit epilogue", name, (M, N, K), flush=True)
+            y = run(G, A, Bs, 7, instance=i, layout=G.GEMM_B_COL_MAJOR, alpha=0.5, beta=2.0, bias=bias, relu=1,
+                    c_init=encode_out(cold, "f32"), expect=expect)
+            if expect == 0:
+                assert_exact(y, r, "f32", name)
 
 
 def test_zero_K(G):

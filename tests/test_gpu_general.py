@@ -89,7 +89,8 @@ def test_col_major_equals_row_major_bitwise(G, code, shape):
 
 
 def _fd2_instances(G):
-    return [i for i in range(G.gemm_num_instances()) if "_fd1" not in G.gemm_instance_name(i)]
+    from tests.gpu_helpers import instances16
+    return [i for i in instances16(G) if "_fd1" not in G.gemm_instance_name(i)]
 
 
 RAGGED = [(129, 131, 67), (300, 260, 130), (1, 513, 65), (255, 8, 200), (8, 1031, 63),

@@ -22,7 +22,7 @@ from dense_half_precision_tiled_amd import inputs
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-from tests.gpu_helpers import DTYPES, assert_bound, assert_exact, law_for, run  # noqa: E402
+from tests.gpu_helpers import DTYPES, assert_bound, assert_exact, instances16, law_for, run  # noqa: E402
 
 
 @pytest.fixture(scope="module")
@@ -152,14 +152,13 @@ def test_instances_agree_bitwise(G):
     order: identical bits.  The two families (dl: waves split the tile; ks:
     waves split K and sum four partial tiles) add the k-steps in different
     orders, so across families only the bound applies."""
-    n = G.gemm_num_instances()
     for code in (0, 3):
         fmt, out = DTYPES[code]
         A = law_for(fmt)((512, 512), 101, fmt)
         B = law_for(fmt)((512, 512), 102, fmt)
         r = oracle.gemm_f64(A, B, fmt)
         first = {}
-        for i in range(n):
+        for i in instances16(G):
             name = G.gemm_instance_name(i)
             print("instance", name, code, flush=True)
             y = run(G, A, B, code, instance=i)
@@ -193,8 +192,7 @@ RAGGED = [(129, 131, 67), (300, 260, 130), (1, 513, 65), (129, 136, 67), (300, 2
 
 
 def _edge_instances(G):
-    n = G.gemm_num_instances()
-    return [i for i in range(n) if G.gemm_instance_name(i).endswith(("_clamp", "_masked"))]
+    return [i for i in instances16(G) if G.gemm_instance_name(i).endswith(("_clamp", "_masked"))]
 
 
 def _expect_for(G, i, N):
