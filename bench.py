@@ -307,13 +307,33 @@ def copy_calibration(torch, nbytes: int, steps: int, warmup: int) -> int:
 
 def loop_for(G, torch, name, seconds: float) -> int:
     """Run one workload back to back for `seconds` and print the achieved rate.
-    Besides the GEMM workloads, three MFMA-only probes (32x32x16, eight
-    independent accumulators per wave, one wave per SIMD on every CU):
-    "mfma_probe" with constant operands, and "mfma_probe_bf16_data" /
-    "mfma_probe_f16_data" with operands drawn like the bf16 (N(0,1)) and fp16
-    (U[-1,1)) workloads' inputs, rotating so that consecutive MFMAs see new
-    values as in a GEMM."""
-    if name in ("mfma_probe_bf16_data", "mfma_probe_f16_data"):
+    Besides the GEMM workloads, MFMA-only probes (eight independent
+    accumulators per wave, one wave per SIMD on every CU): "mfma_probe"
+    (32x32x16, constant operands), "mfma_probe_bf16_data" /
+    "mfma_probe_f16_data" (32x32x16, operands drawn like the bf16 N(0,1) and
+    fp16 U[-1,1) workloads' inputs, rotating so that consecutive MFMAs see new
+    values as in a GEMM) and "mfma_probe_e4m3_data" (the 8-bit 32x32x64 MFMA
+    on rotating N(0,1) E4M3 operands)."""
+    if name == "mfma_probe_e4m3_data":
+        import ctypes
+        from dense_half_precision_tiled_amd import inputs
+        P = ctypes.CDLL(os.path.join(ROOT, "tests", "probes", "libdhpt_probes.so"))
+        P.probe_mfma_data_f8.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        ops = upload(inputs.normal((32 * 64 * 16,), 7, inputs.E4M3), torch)
+        blocks, iters = 256, 25000
+        sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+        n, ms, t0 = 0, 0.0, time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if P.probe_mfma_data_f8(blocks, iters, ops.data_ptr(), sink.data_ptr()) != 0:
+                raise RuntimeError("probe launch failed")
+            e1.record()
+            torch.cuda.synchronize()
+            ms += e0.elapsed_time(e1)
+            n += 1
+        flops = n * blocks * 4 * iters * 32 * 131072.0
+    elif name in ("mfma_probe_bf16_data", "mfma_probe_f16_data"):
         import ctypes
         from dense_half_precision_tiled_amd import inputs
         P = ctypes.CDLL(os.path.join(ROOT, "tests", "probes", "libdhpt_probes.so"))
@@ -443,7 +463,7 @@ def main(argv=None):
                          "(a 512 MiB buffer read before each; 0 to skip)")
     ap.add_argument("--loop-seconds", type=float, default=0.0,
                     help="instead of the timed bench, run --workload (or one of the MFMA-only probes 'mfma_probe', "
-                         "'mfma_probe_bf16_data', 'mfma_probe_f16_data') back to back this long")
+                         "'mfma_probe_bf16_data', 'mfma_probe_f16_data', 'mfma_probe_e4m3_data') back to back this long")
     ap.add_argument("--power-sample", type=float, default=0.0, metavar="SECONDS",
                     help="run --workload in a child process for SECONDS and sample power and clocks with amd-smi")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",

@@ -214,6 +214,38 @@ __global__ __launch_bounds__(256) void probe_mfma_f8_rate_kernel(int iters, uint
     if (s == 12345.0f) sink[0] = s;
 }
 
+// The 8-bit form of the data-fed stream: v_mfma_f32_32x32x64_f8f6f4 (E4M3),
+// 8 operand register sets of 32 bytes per lane for A and for B from
+// ops[16 * 2 * 64] (16-byte units), rotating as above; iters x 32 MFMAs per wave.
+__global__ __launch_bounds__(256, 1) void probe_mfma_data_f8_kernel(const u32x4* ops, int iters, float* sink) {
+    const int l = threadIdx.x & 63;
+    i32x8 a[8], b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const u32x4 a0 = ops[(4 * i) * 64 + l], a1 = ops[(4 * i + 1) * 64 + l];
+        const u32x4 b0 = ops[(4 * i + 2) * 64 + l], b1 = ops[(4 * i + 3) * 64 + l];
+        a[i] = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+        b[i] = i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+    }
+    f32x16 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = (f32x16){};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[(i + r) & 7], b[(i + 3 * r) & 7], acc[i],
+                                                                         0, 0, 0, 0, 0, 0);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s += acc[i][e];
+    if (s == 12345.0f) sink[0] = s;
+}
+
 // LDS throughput: every wave of 4 per block issues `iters` x 8 LDS
 // instructions of one kind and lane 0 records the shader cycles.  Lane l of
 // wave w uses byte address addr[64 w + l] (masked to the 64 KiB buffer and
@@ -449,6 +481,12 @@ int probe_mfma_f8_acc(int fmt, const uint32_t* a, const uint32_t* b, const float
         hipLaunchKernelGGL(probe_mfma_f8_acc_kernel<0>, dim3(1), dim3(64), 0, 0, a, b, c, d);
     else
         hipLaunchKernelGGL(probe_mfma_f8_acc_kernel<1>, dim3(1), dim3(64), 0, 0, a, b, c, d);
+    return (int)hipDeviceSynchronize();
+}
+
+// ops: 32 x 64 lanes x 16 bytes of E4M3 values.
+int probe_mfma_data_f8(int blocks, int iters, const void* ops, float* sink) {
+    hipLaunchKernelGGL(probe_mfma_data_f8_kernel, dim3(blocks), dim3(256), 0, 0, (const u32x4*)ops, iters, sink);
     return (int)hipDeviceSynchronize();
 }
 
