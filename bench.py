@@ -75,10 +75,11 @@ def kernel_source_hash(family: str) -> str:
     return h.hexdigest()[:16]
 
 
-def describe(w) -> str:
+def describe(w, layout=None) -> str:
+    lay = layout or w.get("layout", "row")
     return "%s GEMM C=A.B M=%d N=%d K=%d %s, %s inputs, fp32 accumulate, %s output" % (
         w["fmt"], w["M"], w["N"], w["K"],
-        "A row-major, B column-major" if w["fmt"] in EIGHT_BIT else "row-major",
+        "A row-major, B column-major" if lay == "col" else "row-major",
         "U[-1,1)" if w["law"] == "uniform" else "N(0,1)", w["out"])
 
 
@@ -91,19 +92,20 @@ def upload(bits, torch):
     return torch.from_numpy(bits.view(np.int16) if bits.dtype.itemsize == 2 else bits.view(np.int8)).cuda()
 
 
-def measure(G, torch, name, steps, warmup, instance=None, layout="row", settle_ms=200.0):
+def measure(G, torch, name, steps, warmup, instance=None, layout=None, settle_ms=200.0):
     """Upload a workload, run one correctness launch into a poisoned C, let
     the clock settle (untimed launches for about settle_ms), run `warmup`
     untimed launches, then time `steps` launches.  Returns a dict with the
     timing and the buffers.
     layout "col" stores B column-major (its transpose row-major) and calls
-    gemm_run_ex; "row" calls gemm_run."""
+    gemm_run_ex; "row" calls gemm_run; None takes the workload's own."""
     import numpy as np
     from dense_half_precision_tiled_amd import inputs
     A, B, w = inputs.workload_inputs(name)
     M, N, K = w["M"], w["N"], w["K"]
     code = CODES[(w["fmt"], w["out"])]
-    col = layout == "col" or w["fmt"] in EIGHT_BIT         # 8-bit inputs take B column-major
+    layout = layout or w.get("layout", "row")
+    col = layout == "col"
     tA, tB = upload(A, torch), upload(np.ascontiguousarray(B.T) if col else B, torch)
     odt = torch.float32 if w["out"] == "f32" else torch.int16
     tC = torch.full((M, N), -1, dtype=torch.int32 if odt == torch.float32 else torch.int16,
@@ -165,7 +167,8 @@ def measure(G, torch, name, steps, warmup, instance=None, layout="row", settle_m
     else:
         inst = G.gemm_select_instance(M, N, K, code, tA.data_ptr(), K, tB.data_ptr(), N,
                                       tC.data_ptr(), N)
-    return {"name": name, "w": w, "A": A, "B": B, "C": tC, "ms": ms, "rep_ms": rep_ms, "launch": launch,
+    return {"name": name, "w": w, "layout": layout, "A": A, "B": B, "C": tC, "ms": ms, "rep_ms": rep_ms,
+            "launch": launch,
             "wall_s": wall, "settle_launches": n_settle,
             "tflops": flops / (ms * 1e-3) / 1e12, "instance": G.gemm_instance_name(inst),
             "alg_bytes": (1 if w["fmt"] in EIGHT_BIT else 2) * (M * K + K * N) + (4 if w["out"] == "f32" else 2) * M * N}
@@ -377,7 +380,7 @@ def loop_for(G, torch, name, seconds: float) -> int:
         from dense_half_precision_tiled_amd import inputs
         A, B, w = inputs.workload_inputs(name)
         M, N, K = w["M"], w["N"], w["K"]
-        col = w["fmt"] in EIGHT_BIT
+        col = w.get("layout", "row") == "col"
         tA, tB = upload(A, torch), upload(np.ascontiguousarray(B.T) if col else B, torch)
         tC = torch.empty((M, N), dtype=torch.float32 if w["out"] == "f32" else torch.int16, device="cuda")
         s = torch.cuda.current_stream().cuda_stream
@@ -454,8 +457,9 @@ def main(argv=None):
     ap.add_argument("--settle-ms", type=float, default=200.0,
                     help="untimed launches for about this long before the warmups (clock ramp-up)")
     ap.add_argument("--instance", type=int, default=None, help="force a kernel instance id")
-    ap.add_argument("--layout", choices=("row", "col"), default="row",
-                    help="storage order of B: row-major (gemm_run) or column-major (gemm_run_ex)")
+    ap.add_argument("--layout", choices=("row", "col"), default=None,
+                    help="storage order of B: row-major (gemm_run) or column-major (gemm_run_ex); "
+                         "default: the workload's own (row-major for the 16-bit ones, column-major for 8-bit)")
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle work for cpu_baseline (0 to skip)")
     ap.add_argument("--cold", type=int, default=5, metavar="LAUNCHES",
@@ -495,12 +499,13 @@ def main(argv=None):
 
     def summary(r):
         w2 = r["w"]
-        return {"workload": describe(w2), "value": round(r["tflops"], 2), "unit": "TFLOP/s",
+        return {"workload": describe(w2, r["layout"]), "value": round(r["tflops"], 2), "unit": "TFLOP/s",
                 "ms_per_step": round(r["ms"], 5), "frac_of_peak": round(r["tflops"] / peak_for(w2), 4),
                 "peak": peak_for(w2),
                 "hbm_gbps_algorithmic": round(r["alg_bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
                 "kernel": r["instance"], "repeats": repeats(r),
-                "traffic": traffic_from_profiles(r["name"], r["instance"])}
+                "traffic": traffic_from_profiles(
+                    r["name"] + ("" if r["layout"] == w2.get("layout", "row") else "_" + r["layout"]), r["instance"])}
 
     sec = None
     if args.secondary and args.secondary != "none":
@@ -517,7 +522,8 @@ def main(argv=None):
             del r3
 
     w = main_res["w"]
-    traffic = traffic_from_profiles(args.workload + ("" if args.layout == "row" else "_col"),
+    lay = main_res["layout"]
+    traffic = traffic_from_profiles(args.workload + ("" if lay == w.get("layout", "row") else "_" + lay),
                                     main_res["instance"])
     line = {
         "metric": METRIC,
@@ -532,8 +538,8 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": w["fmt"],
         "data": "synthetic",
-        "config": {"workload": describe(w) + ("" if args.layout == "row" else ", B column-major"),
-                   "M": w["M"], "N": w["N"], "K": w["K"], "b_layout": args.layout,
+        "config": {"workload": describe(w, lay),
+                   "M": w["M"], "N": w["N"], "K": w["K"], "b_layout": lay,
                    "in": w["fmt"], "out": w["out"], "kernel": main_res["instance"],
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(main_res["tflops"], 2), "peak": peak_for(w),

@@ -15,7 +15,7 @@ ARCH = "gfx950"
 
 SOURCES = ["gemm_api.cpp", "gemm_instances.hip", "gemm_dl_nn.hip", "gemm_dl_nn_epi.hip",
            "gemm_dl_tn.hip", "gemm_dl_tn_epi.hip", "gemm_ks.hip", "gemm_ks_epi.hip",
-           "gemm_dl_f8.hip", "gemm_dl_f8_epi.hip"]
+           "gemm_dl_f8_tn.hip", "gemm_dl_f8_tn_epi.hip", "gemm_dl_f8_nn.hip", "gemm_dl_f8_nn_epi.hip"]
 
 # Packed-fp32 VALU ops stay disabled in every HIP translation unit.
 HIP_FLAGS = ["-x", "hip", "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",

@@ -43,7 +43,6 @@ int validate(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t 
     if (dtype < GEMM_F16_F32 || dtype > GEMM_E5M2_BF16) return GEMM_ERR_DTYPE;
     if (x.b_layout != GEMM_B_ROW_MAJOR && x.b_layout != GEMM_B_COL_MAJOR) return GEMM_ERR_LAYOUT;
     const bool tb = x.b_layout == GEMM_B_COL_MAJOR;
-    if (dhpt::dtype_in8(dtype) && !tb) return GEMM_ERR_LAYOUT;   // 8-bit inputs: column-major B
     const int64_t b_rows = tb ? N : K, b_cols = tb ? K : N;      // B as stored, row-major
     if (M < 0 || N < 0 || K < 0) return GEMM_ERR_DIM;
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return GEMM_ERR_RANGE;
@@ -99,14 +98,17 @@ int64_t tiles_for(int tile, int64_t M, int64_t N) { return ((M + tile - 1) / til
 // tiles, then clamped edges (any M and K; N a multiple of 8 for row-major
 // B), then the fully masked fallback (128x128).
 //
-// 8-bit inputs (column-major B): 256x256 tiles when they give at least half a
-// wave, else 128x128 tiles when those give at least half a wave, else 64x64;
-// whole tiles, then clamped edges (which cover every shape).
+// 8-bit inputs: 256x256 tiles when they give at least half a wave, else
+// 128x128 tiles when those give at least half a wave, else 64x64; whole
+// tiles, then clamped edges (every shape with column-major B, N % 16 == 0
+// with row-major B), then the masked fallback (row-major B, any N).
 int choose_instance(const Problem& p) {
     if (dhpt::dtype_in8(p.dtype)) {
-        static const int big8[] = {14, 15}, mid8[] = {16, 17}, small8[] = {18, 19};
+        static const int big8[] = {14, 15, 20}, mid8[] = {16, 17, 21}, small8[] = {18, 19, 21};
         const int* o = tiles_for(256, p.M, p.N) >= 128 ? big8 : tiles_for(128, p.M, p.N) >= 128 ? mid8 : small8;
-        return dhpt::instance_supports(o[0], p) ? o[0] : o[1];
+        for (int k = 0; k < 3; ++k)
+            if (dhpt::instance_supports(o[k], p)) return o[k];
+        return o[2];
     }
     static const int big_order[] = {0, 1, 2};
     static const int mid_order[] = {3, 4, 5};
@@ -248,7 +250,7 @@ const char* gemm_strerror(int status) {
     case GEMM_ERR_LAUNCH: return "kernel launch failed";
     case GEMM_ERR_ALIGN: return "pointer not aligned to its element size";
     case GEMM_ERR_INSTANCE: return "unknown instance, or instance cannot run this shape";
-    case GEMM_ERR_LAYOUT: return "unknown B layout, or row-major B with 8-bit inputs (they need column-major B)";
+    case GEMM_ERR_LAYOUT: return "unknown B layout";
     default: return "unknown status";
     }
 }

@@ -22,6 +22,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) char lds_char;
 
 // Input formats: fp16 and bf16 (2-byte elements), and the 8-bit floats E4M3
@@ -77,6 +78,15 @@ __device__ __forceinline__ float load_out(const void* C, int64_t idx) {
 
 __device__ __forceinline__ int swz_a(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int swz_b(int k) { return 2 * (k & 3); }
+// Row-major 8-bit B, CPR 16-byte chunks per row: chunk c of row k sits at
+// c ^ swz_b8<CPR>(k).  A ds_read_b64_tr_b8 pass (32 lanes) reads chunks c, c+1
+// (c even) of 8 consecutive rows; the XOR puts those 16 chunks on 16
+// different groups of 4 banks for every row length used (256, 128, 64 bytes).
+template <int CPR>
+__device__ __forceinline__ int swz_b8(int k) {
+    constexpr int R = 16 / CPR;                 // rows per 64-bank cycle
+    return 2 * ((k / R) & (CPR / 2 - 1));
+}
 
 // One global_load_lds_dwordx4 (this lane's 16 bytes at `src` to LDS byte
 // address lds_base + 16 * lane), issued through inline assembly so that the
@@ -149,24 +159,24 @@ struct EpiArgs {
 // n0 .. n0+BN-1) into the LDS stage `st` through VGPRs, with every value
 // outside M x K (A) and K x N (B) read as zero, in the stage layout of the
 // direct-to-LDS copies: A BM rows x 128 bytes, chunk c of row r at
-// c ^ swz_a(r); row-major B 64 rows x 2*BN bytes, chunk c of row k at
-// c ^ swz_b(k); column-major B BN rows x 128 bytes like A.  All 256 lanes of
-// the workgroup take part.  All loads are issued before the first LDS write:
-// rows past the edge read a clamped valid row and are zeroed afterwards, and
-// chunks crossing the row end use the branch-free shifted load whenever the
-// row holds at least one chunk of values (a uniform test), so one memory
-// round trip fills the slice.  ESZ is the element size in bytes; 1-byte
-// elements only come with column-major B.
+// c ^ swz_a(r); row-major B 128/ESZ rows x ESZ*BN bytes, chunk c of row k at
+// c ^ swz_b(k) (2-byte elements) or c ^ swz_b8(k) (1-byte); column-major B BN
+// rows x 128 bytes like A.  All 256 lanes of the workgroup take part.  All
+// loads are issued before the first LDS write: rows past the edge read a
+// clamped valid row and are zeroed afterwards, and chunks crossing the row
+// end use the branch-free shifted load whenever the row holds at least one
+// chunk of values (a uniform test), so one memory round trip fills the slice.
+// ESZ is the element size in bytes.
 template <int BM, int BN, bool BT, int ESZ = 2>
 __device__ __forceinline__ void fill_stage(char* st, const uint16_t* A, int64_t lda,
                                            const uint16_t* B, int64_t ldb, int M, int N,
                                            int K, int m0, int n0, int k0, int t) {
-    static_assert(ESZ == 2 || (ESZ == 1 && BT), "1-byte elements: column-major B only");
     constexpr int CH = 16 / ESZ;                                  // elements per 16-byte chunk
-    constexpr int BK = 64, A_BYTES = BM * 128, BROW = 2 * BN, B_CHUNKS = BN / 8;
+    constexpr int BKR = 128 / ESZ;                                // k (B rows) per slice
+    constexpr int A_BYTES = BM * 128, BROW = ESZ * BN, B_CHUNKS = BROW / 16;
     constexpr int NFA = BM / 32;                                  // A chunks per lane
     constexpr int B_ROWS_PER_PASS = 256 / B_CHUNKS;
-    constexpr int NFB = BT ? BN / 32 : BK / B_ROWS_PER_PASS;      // B chunks per lane
+    constexpr int NFB = BT ? BN / 32 : BKR / B_ROWS_PER_PASS;     // B chunks per lane
     using E = elem_t<ESZ>;
     const E* const Ae = reinterpret_cast<const E*>(A);
     const E* const Be = reinterpret_cast<const E*>(B);
@@ -189,7 +199,7 @@ __device__ __forceinline__ void fill_stage(char* st, const uint16_t* A, int64_t 
         } else {                                   // row-major B: 64 rows x B_CHUNKS chunks
             const int gk = k0 + t / B_CHUNKS + B_ROWS_PER_PASS * r;
             pb[r] = Be + (int64_t)(gk < K ? gk : K - 1) * ldb;
-            cb[r] = n0 + 8 * (t % B_CHUNKS);
+            cb[r] = n0 + CH * (t % B_CHUNKS);
         }
     }
     const int ca = k0 + CH * (t & 7);
@@ -224,8 +234,12 @@ __device__ __forceinline__ void fill_stage(char* st, const uint16_t* A, int64_t 
                 n0 + row < N ? vb[r] : zero;
         } else {
             const int row = t / B_CHUNKS + B_ROWS_PER_PASS * r, c = t % B_CHUNKS;
-            *reinterpret_cast<u32x4*>(st + A_BYTES + row * BROW + 16 * (c ^ swz_b(row))) =
-                k0 + row < K ? vb[r] : zero;
+            if constexpr (ESZ == 2)
+                *reinterpret_cast<u32x4*>(st + A_BYTES + row * BROW + 16 * (c ^ swz_b(row))) =
+                    k0 + row < K ? vb[r] : zero;
+            else
+                *reinterpret_cast<u32x4*>(st + A_BYTES + row * BROW + 16 * (c ^ swz_b8<B_CHUNKS>(row))) =
+                    k0 + row < K ? vb[r] : zero;
         }
     }
 }

@@ -36,21 +36,24 @@
 //     the general C <- alpha*A*B + beta*C of the naive-to-tensor-core page);
 //     C_old is read only when beta != 0.
 //
-// 8-bit float inputs (IN_E4M3, IN_E5M2; column-major B only): a slice is
-// still 128 bytes of every A and B row, now 128 values of k, multiplied as two
+// 8-bit float inputs (IN_E4M3, IN_E5M2): a slice is still 128 bytes of every
+// A row (and column-major B row), now 128 values of k, multiplied as two
 // 64-deep k-steps of v_mfma_f32_32x32x64_f8f6f4.  A lane's fragment is 32
-// consecutive k (two ds_read_b128 of the same swizzled rows), the same k for
-// A and B; the fragments of the next k-step are read while the current one
-// is multiplied (FD == 1: at 64 deep a k-step is as long as two of the
-// 16-bit ones).  Stage layout, swizzle, copies and epilogue are those of the
-// 16-bit column-major-B kernel.  The 8-bit float of the Ada write-up's
-// precision notes, built here for gfx950's double-rate 8-bit MFMA.
+// consecutive k, the same k for A and B: two ds_read_b128 of a swizzled A (or
+// column-major B) row, or, for row-major B (128 rows x BN bytes, chunk c of
+// row k at c ^ swz_b8(k)), four ds_read_b64_tr_b8, each handing every lane 8
+// values of k of its column.  The fragments of the next k-step are read while
+// the current one is multiplied (FD == 1: at 64 deep a k-step is as long as
+// two of the 16-bit ones).  Copies and epilogue are those of the 16-bit
+// kernel.  The 8-bit float of the Ada write-up's precision notes, built here
+// for gfx950's double-rate 8-bit MFMA.
 //
 // EDGE modes (BK = 64 for 16-bit inputs, 128 for 8-bit ones):
 //   EDGE_NONE:  M % BM == N % BN == K % BK == 0.
-//   EDGE_CLAMP: any M, K; any N for column-major B, N % 8 == 0 for row-major
-//     B.  Rows of A (and of column-major B) past the edge and 8-column chunks
-//     of row-major B past N are read from a clamped, valid address: those
+//   EDGE_CLAMP: any M, K; any N for column-major B, N % 8 == 0 (N % 16 == 0
+//     for 8-bit inputs) for row-major B.  Rows of A (and of column-major B)
+//     past the edge and 16-byte column chunks of row-major B past N are read
+//     from a clamped, valid address: those
 //     values only reach outputs that are never stored.  A partial last slice
 //     (K % BK != 0) is filled through VGPRs with element-exact zero fill.
 //   EDGE_MASKED: any shape.  Every slice is filled through VGPRs with
@@ -79,22 +82,25 @@ __global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
     static_assert((BM == 256 && BN == 256) || (BM == 128 && BN == 128) || (BM == 64 && BN == 64), "tile");
     static_assert(FD == 1 || FD == 2, "fragment prefetch distance");
     constexpr bool F8 = kIn8<IN>;
-    static_assert(!F8 || (BT && FD == 1 && EDGE != EDGE_MASKED), "8-bit inputs: column-major B, FD 1");
+    static_assert(!F8 || FD == 1, "8-bit inputs: fragment prefetch one k-step");
     constexpr int ESZ = F8 ? 1 : 2;                       // bytes per input element
     constexpr int BK = F8 ? 128 : 64, KSTEPS = F8 ? 2 : 4;   // k per slice (128 bytes of a row), MFMA k-steps
     constexpr int RPF = F8 ? 2 : 1;                       // ds_read_b128 per A (or column-major B) fragment
     constexpr int WM = BM / 2, WN = BN / 2;               // wave tile
     constexpr int TM = WM / 32, TN = WN / 32;             // MFMA blocks per wave
     constexpr int S = TM * TN;                            // MFMAs (issue slots) per k-step
-    constexpr int NBR = BT ? RPF * TN : 2 * TN;           // B reads per k-step
+    constexpr int PB = BT ? RPF : (F8 ? 4 : 2);           // LDS reads per B fragment
+    constexpr int NBR = PB * TN;                          // B reads per k-step
     constexpr int R = RPF * TM + NBR;                     // LDS reads per k-step
-    constexpr int A_BYTES = BM * 128, BROW = 2 * BN, B_BYTES = BT ? BN * 128 : 64 * BROW;
+    constexpr int BROW = ESZ * BN;                        // row-major B: bytes per k row
+    constexpr int A_BYTES = BM * 128, B_BYTES = BT ? BN * 128 : (128 / ESZ) * BROW;
     constexpr int STAGE = A_BYTES + B_BYTES;
     constexpr int NSTAGE = EDGE == EDGE_MASKED ? 1 : 2;
     constexpr int CA = BM / 32, CB = BN / 32;             // copies per wave per slice (1 KiB each)
     constexpr int COPIES = CA + CB;
-    constexpr int B_ROWS_PER_COPY = 1024 / BROW;          // row-major B: 2 (BN 256) or 4 (BN 128)
-    constexpr int B_CHUNKS = BN / 8;                      // row-major B: 16-byte chunks per row
+    constexpr int B_ROWS_PER_COPY = 1024 / BROW;          // row-major B: k rows per 1 KiB copy
+    constexpr int B_CHUNKS = BROW / 16;                   // row-major B: 16-byte chunks per row
+    constexpr int B_ROWS_PER_WAVE = (128 / ESZ) / 4;      // row-major B: k rows each wave copies
     constexpr int NB = (FD == 1) ? 2 : 4;                 // fragment buffers
     __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
     const uint32_t smem_base = (uint32_t)(size_t)(lds_char*)smem;
@@ -137,15 +143,16 @@ __global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
                 if constexpr (EDGE == EDGE_CLAMP) gcol = gcol < N ? gcol : N - 1;
                 b_src[i] = Be + (int64_t)gcol * ldb + (16 / ESZ) * ((l & 7) ^ swz_a(r));
             } else {
-                const int kr = 16 * w + B_ROWS_PER_COPY * i + l / B_CHUNKS;
-                int col = n0 + 8 * ((l % B_CHUNKS) ^ swz_b(kr));
-                if constexpr (EDGE == EDGE_CLAMP) col = col + 8 <= N ? col : N - 8;
+                const int kr = B_ROWS_PER_WAVE * w + B_ROWS_PER_COPY * i + l / B_CHUNKS;
+                const int sw = F8 ? swz_b8<B_CHUNKS>(kr) : swz_b(kr);
+                int col = n0 + (16 / ESZ) * ((l % B_CHUNKS) ^ sw);
+                if constexpr (EDGE == EDGE_CLAMP) col = col + 16 / ESZ <= N ? col : N - 16 / ESZ;
                 b_src[i] = Be + (int64_t)kr * ldb + col;
             }
         }
         if constexpr (!BT) b_step = (int64_t)BK * ldb;
         dma_a = smem_base + ((BM / 4) * w) * 128;
-        dma_b = smem_base + A_BYTES + (BT ? ((BN / 4) * w) * 128 : (16 * w) * BROW);
+        dma_b = smem_base + A_BYTES + (BT ? ((BN / 4) * w) * 128 : (B_ROWS_PER_WAVE * w) * BROW);
     }
 
     // Fragment read offsets (bytes within a stage).
@@ -156,7 +163,15 @@ __global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
     int b_off[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-        if constexpr (BT) {
+        if constexpr (F8 && !BT) {
+            // tr8 read: lane 2jj + hh of 16-lane group G addresses row k = 32 (G / 2) + jj (+ 8 per
+            // read, + 64 per k-step: the swizzle term does not change) and the 8 bytes of half hh
+            // of chunk c of the lane group's 16 columns; every lane receives its own column.
+            const int G = l >> 4, jj = (l & 15) >> 1, hh = l & 1;
+            const int kb = 32 * (G >> 1) + jj;
+            const int c = (wn * WN + 32 * j + 16 * (G & 1)) >> 4;
+            b_off[j] = A_BYTES + kb * BROW + 16 * (c ^ swz_b8<B_CHUNKS>(kb)) + 8 * hh;
+        } else if constexpr (BT) {
             b_off[j] = A_BYTES + (wn * WN + 32 * j + (l & 31)) * 128;
         } else {
             const int n = wn * WN + 32 * j + 16 * (g & 1) + 4 * (ip & 3);
@@ -184,19 +199,27 @@ __global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
     auto read_piece = [&](int stage, int s, int buf, int q) {
         const char* st = smem + stage * STAGE;
         if constexpr (F8) {
-            const int f = q >> 1, half = q & 1;
-            const int chunk = (4 * s + 2 * (l >> 5) + half) ^ a_sw;
-            u32x4 v;
-            if (f == 0 || f > TN) {
-                const int i = (f == 0) ? 0 : f - TN;
-                v = *reinterpret_cast<const u32x4*>(st + a_off0 + i * 32 * 128 + chunk * 16);
+            if (q < RPF || q >= RPF + NBR) {                 // A fragment i, half `half`
+                const int i = q < RPF ? 0 : 1 + (q - RPF - NBR) / RPF;
+                const int half = q < RPF ? q : (q - RPF - NBR) % RPF;
+                const int chunk = (4 * s + 2 * (l >> 5) + half) ^ a_sw;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(st + a_off0 + i * 32 * 128 + chunk * 16);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) fa8[buf][i][4 * half + e] = v[e];
-            } else {
-                const int j = f - 1;
-                v = *reinterpret_cast<const u32x4*>(st + b_off[j] + chunk * 16);
+            } else {                                         // B fragment j, piece `piece`
+                const int j = (q - RPF) / PB, piece = (q - RPF) % PB;
+                if constexpr (BT) {
+                    const int chunk = (4 * s + 2 * (l >> 5) + piece) ^ a_sw;
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(st + b_off[j] + chunk * 16);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) fb8[buf][j][4 * half + e] = v[e];
+                    for (int e = 0; e < 4; ++e) fb8[buf][j][4 * piece + e] = v[e];
+                } else {
+                    const int off = b_off[j] + (64 * s + 8 * piece) * BROW;
+                    const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (__attribute__((address_space(3))) i32x2*)((const lds_char*)st + off));
+                    fb8[buf][j][2 * piece] = (uint32_t)v[0];
+                    fb8[buf][j][2 * piece + 1] = (uint32_t)v[1];
+                }
             }
             return;
         }
@@ -415,33 +438,41 @@ static hipError_t launch_dtype(const Problem& p, int group_m, hipStream_t s) {
 }
 
 // The 8-bit input dtypes (4 .. 9: E4M3 then E5M2, each to fp32, fp16, bf16).
-template <int BM, int BN, int EDGE, bool EPI>
+template <int BM, int BN, int EDGE, bool BT, bool EPI>
 static hipError_t launch_dtype8(const Problem& p, int group_m, hipStream_t s) {
     switch (p.dtype) {
-    case 4: launch_typed<IN_E4M3, OUT_F32, BM, BN, 1, EDGE, true, EPI>(p, group_m, s); break;
-    case 5: launch_typed<IN_E4M3, OUT_F16, BM, BN, 1, EDGE, true, EPI>(p, group_m, s); break;
-    case 6: launch_typed<IN_E4M3, OUT_BF16, BM, BN, 1, EDGE, true, EPI>(p, group_m, s); break;
-    case 7: launch_typed<IN_E5M2, OUT_F32, BM, BN, 1, EDGE, true, EPI>(p, group_m, s); break;
-    case 8: launch_typed<IN_E5M2, OUT_F16, BM, BN, 1, EDGE, true, EPI>(p, group_m, s); break;
-    case 9: launch_typed<IN_E5M2, OUT_BF16, BM, BN, 1, EDGE, true, EPI>(p, group_m, s); break;
+    case 4: launch_typed<IN_E4M3, OUT_F32, BM, BN, 1, EDGE, BT, EPI>(p, group_m, s); break;
+    case 5: launch_typed<IN_E4M3, OUT_F16, BM, BN, 1, EDGE, BT, EPI>(p, group_m, s); break;
+    case 6: launch_typed<IN_E4M3, OUT_BF16, BM, BN, 1, EDGE, BT, EPI>(p, group_m, s); break;
+    case 7: launch_typed<IN_E5M2, OUT_F32, BM, BN, 1, EDGE, BT, EPI>(p, group_m, s); break;
+    case 8: launch_typed<IN_E5M2, OUT_F16, BM, BN, 1, EDGE, BT, EPI>(p, group_m, s); break;
+    case 9: launch_typed<IN_E5M2, OUT_BF16, BM, BN, 1, EDGE, BT, EPI>(p, group_m, s); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-// All tile sizes and the whole-tile / clamped edge modes for 8-bit inputs
-// (column-major B; clamped edges cover every shape).
-template <bool EPI>
+// All tile sizes and edge modes for 8-bit inputs and one B layout.  Clamped
+// edges cover every shape for column-major B and N % 16 == 0 for row-major
+// B; the masked mode (256 and 128 tiles, row-major B) takes any N.
+template <bool BT, bool EPI>
 static hipError_t launch_family8(int tile, int edge, const Problem& p, int group_m, hipStream_t s) {
-    if (edge != EDGE_NONE && edge != EDGE_CLAMP) return hipErrorInvalidValue;
+    if (edge == EDGE_MASKED) {
+        if constexpr (!BT) {
+            return tile == 256 ? launch_dtype8<256, 256, EDGE_MASKED, BT, EPI>(p, group_m, s)
+                               : launch_dtype8<128, 128, EDGE_MASKED, BT, EPI>(p, group_m, s);
+        } else {
+            return hipErrorInvalidValue;
+        }
+    }
     if (tile == 256)
-        return edge == EDGE_NONE ? launch_dtype8<256, 256, EDGE_NONE, EPI>(p, group_m, s)
-                                 : launch_dtype8<256, 256, EDGE_CLAMP, EPI>(p, group_m, s);
+        return edge == EDGE_NONE ? launch_dtype8<256, 256, EDGE_NONE, BT, EPI>(p, group_m, s)
+                                 : launch_dtype8<256, 256, EDGE_CLAMP, BT, EPI>(p, group_m, s);
     if (tile == 128)
-        return edge == EDGE_NONE ? launch_dtype8<128, 128, EDGE_NONE, EPI>(p, group_m, s)
-                                 : launch_dtype8<128, 128, EDGE_CLAMP, EPI>(p, group_m, s);
-    return edge == EDGE_NONE ? launch_dtype8<64, 64, EDGE_NONE, EPI>(p, group_m, s)
-                             : launch_dtype8<64, 64, EDGE_CLAMP, EPI>(p, group_m, s);
+        return edge == EDGE_NONE ? launch_dtype8<128, 128, EDGE_NONE, BT, EPI>(p, group_m, s)
+                                 : launch_dtype8<128, 128, EDGE_CLAMP, BT, EPI>(p, group_m, s);
+    return edge == EDGE_NONE ? launch_dtype8<64, 64, EDGE_NONE, BT, EPI>(p, group_m, s)
+                             : launch_dtype8<64, 64, EDGE_CLAMP, BT, EPI>(p, group_m, s);
 }
 
 // All tile sizes and edge modes for one (FD, BT, EPI) combination.  The

@@ -25,13 +25,15 @@ const InstanceInfo kInstances[] = {
     {"ks_128x128x64_clamp", 128, 2, EDGE_CLAMP, 8, KIND_KS},
     {"dl_64x64x64_fd2", 64, 2, EDGE_NONE, 8, KIND_DL},
     {"dl_64x64x64_fd2_clamp", 64, 2, EDGE_CLAMP, 8, KIND_DL},
-    // 8-bit float inputs, column-major B: 128-deep slices, fragment prefetch one 64-deep k-step
+    // 8-bit float inputs: 128-deep slices, fragment prefetch one 64-deep k-step
     {"dl8_256x256x128", 256, 1, EDGE_NONE, 8, KIND_DL, 1},
     {"dl8_256x256x128_clamp", 256, 1, EDGE_CLAMP, 8, KIND_DL, 1},
     {"dl8_128x128x128", 128, 1, EDGE_NONE, 8, KIND_DL, 1},
     {"dl8_128x128x128_clamp", 128, 1, EDGE_CLAMP, 8, KIND_DL, 1},
     {"dl8_64x64x128", 64, 1, EDGE_NONE, 8, KIND_DL, 1},
     {"dl8_64x64x128_clamp", 64, 1, EDGE_CLAMP, 8, KIND_DL, 1},
+    {"dl8_256x256x128_masked", 256, 1, EDGE_MASKED, 8, KIND_DL, 1},
+    {"dl8_128x128x128_masked", 128, 1, EDGE_MASKED, 8, KIND_DL, 1},
 };
 const int kNumInstances = sizeof(kInstances) / sizeof(kInstances[0]);
 
@@ -42,21 +44,27 @@ bool instance_supports(int id, const Problem& p) {
     const int64_t tiles = ((int64_t)(p.M + in.tile - 1) / in.tile) * ((p.N + in.tile - 1) / in.tile);
     if (tiles > (int64_t(1) << 24)) return false;
     if ((in.in8 != 0) != dtype_in8(p.dtype)) return false;                       // input width
-    if (in.in8 && !p.transB) return false;                                       // 8-bit: column-major B
     if (!in.in8 && in.kind == KIND_DL && in.fd == 1 && (p.transB || p.epi)) return false;   // plain row-major B only
     switch (in.edge) {
     case EDGE_NONE: return p.M % in.tile == 0 && p.N % in.tile == 0 && p.K % (in.in8 ? 128 : 64) == 0;
-    case EDGE_CLAMP: return p.transB || (p.N % 8 == 0 && p.N >= 8);
-    case EDGE_MASKED: return true;
+    case EDGE_CLAMP: {
+        const int chunk = in.in8 ? 16 : 8;                 // row-major B: whole 16-byte column chunks
+        return p.transB || (p.N % chunk == 0 && p.N >= chunk);
+    }
+    case EDGE_MASKED: return !(in.in8 && p.transB);      // 8-bit masked kernels: row-major B
     default: return false;
     }
 }
 
 hipError_t launch_instance(int id, const Problem& p, hipStream_t s) {
     const InstanceInfo& in = kInstances[id];
-    if (in.in8)
-        return p.epi ? launch_dl_f8_epi(in.tile, in.edge, p, in.group_m, s)
-                     : launch_dl_f8(in.tile, in.edge, p, in.group_m, s);
+    if (in.in8) {
+        if (p.transB)
+            return p.epi ? launch_dl_f8_tn_epi(in.tile, in.edge, p, in.group_m, s)
+                         : launch_dl_f8_tn(in.tile, in.edge, p, in.group_m, s);
+        return p.epi ? launch_dl_f8_nn_epi(in.tile, in.edge, p, in.group_m, s)
+                     : launch_dl_f8_nn(in.tile, in.edge, p, in.group_m, s);
+    }
     if (in.kind == KIND_KS)
         return p.epi ? launch_ks_epi(in.edge, p, in.group_m, s) : launch_ks(in.edge, p, in.group_m, s);
     if (p.transB)

@@ -31,7 +31,7 @@ inline bool dtype_out_f32(int dtype) { return dtype == 0 || dtype == 2 || dtype 
 // Edge handling of an instance (the EDGE modes of gemm_dl_kernel.h).
 enum EdgeMode {
     EDGE_NONE = 0,             // M % tile, N % tile, K % 64 == 0 (K % 128 for 8-bit inputs)
-    EDGE_CLAMP = 1,            // any M, K; N % 8 == 0 for row-major B, any N for column-major B
+    EDGE_CLAMP = 1,            // any M, K; N % 8 == 0 (16 for 8-bit) for row-major B, any N column-major
     EDGE_MASKED = 2,           // any shape
 };
 
@@ -51,7 +51,7 @@ struct InstanceInfo {
     int edge;                  // EdgeMode
     int group_m;               // tile-rows per group of the visit order
     int kind;                  // KernelKind
-    int in8;                   // 1: 8-bit float inputs (and column-major B) only; 0: 16-bit inputs only
+    int in8;                   // 1: 8-bit float inputs only; 0: 16-bit inputs only
 };
 
 extern const InstanceInfo kInstances[];
@@ -69,9 +69,12 @@ hipError_t launch_dl_nn(int tile, int fd, int edge, const Problem& p, int group_
 hipError_t launch_dl_nn_epi(int tile, int fd, int edge, const Problem& p, int group_m, hipStream_t stream);
 hipError_t launch_dl_tn(int tile, int fd, int edge, const Problem& p, int group_m, hipStream_t stream);
 hipError_t launch_dl_tn_epi(int tile, int fd, int edge, const Problem& p, int group_m, hipStream_t stream);
-// The 8-bit-input units of gemm_dl_kernel.h (column-major B, fd 1): plain / general epilogue.
-hipError_t launch_dl_f8(int tile, int edge, const Problem& p, int group_m, hipStream_t stream);
-hipError_t launch_dl_f8_epi(int tile, int edge, const Problem& p, int group_m, hipStream_t stream);
+// The 8-bit-input units of gemm_dl_kernel.h (fd 1): column-major / row-major B,
+// plain / general epilogue.
+hipError_t launch_dl_f8_tn(int tile, int edge, const Problem& p, int group_m, hipStream_t stream);
+hipError_t launch_dl_f8_tn_epi(int tile, int edge, const Problem& p, int group_m, hipStream_t stream);
+hipError_t launch_dl_f8_nn(int tile, int edge, const Problem& p, int group_m, hipStream_t stream);
+hipError_t launch_dl_f8_nn_epi(int tile, int edge, const Problem& p, int group_m, hipStream_t stream);
 // The instantiation units of gemm_ks_kernel.h: plain / general epilogue (both B layouts).
 hipError_t launch_ks(int edge, const Problem& p, int group_m, hipStream_t stream);
 hipError_t launch_ks_epi(int edge, const Problem& p, int group_m, hipStream_t stream);

@@ -7,8 +7,7 @@ The functions mirror include/gemm.h one to one (``gemm_run``, ``gemm_run_ex``,
 Python ints.  ``gemm(A, B, out_dtype)`` is the
 convenience form on torch tensors: it allocates C with ``torch.empty`` and
 passes ``data_ptr()``, the strides and the current HIP stream (gemm_run for a
-row-major B, gemm_run_ex with GEMM_B_COL_MAJOR for a column-major B, which the
-8-bit float inputs require).
+row-major B, gemm_run_ex with GEMM_B_COL_MAJOR for a column-major B).
 
 There is no fallback: if the library is not built, every call raises.
 """
@@ -173,7 +172,7 @@ def gemm(A, B, out_dtype=None, out=None, instance: int | None = None, stream=Non
     A: [M, K] row-major CUDA tensor of fp16, bf16, float8_e4m3fn or
     float8_e5m2 (row strides may exceed the row length).  B: [K, N] of the
     same dtype, row-major, or column-major (the transpose of a row-major
-    [N, K] tensor, e.g. ``Bt.t()``); 8-bit inputs need the column-major B.
+    [N, K] tensor, e.g. ``Bt.t()``).
     out_dtype defaults to the input dtype for 16-bit inputs and to bfloat16
     for 8-bit ones.  ``out`` may be a preallocated row-major [M, N] tensor (its
     row stride is ldc).

@@ -22,7 +22,7 @@
  * contract to the E4M3 and E5M2 formats of the OCP 8-bit floating point
  * specification (OFP8), the 8-bit float the Ada write-up's precision notes
  * leave as the next step: products accumulated in fp32, one rounding to the
- * output type.  They take B column-major (gemm_run_ex with GEMM_B_COL_MAJOR).
+ * output type.  Both B layouts are accepted.
  */
 #ifndef DHPT_GEMM_H
 #define DHPT_GEMM_H
@@ -39,7 +39,7 @@ typedef enum {
     GEMM_F16_F16 = 1,   /* fp16 A, B -> fp16 C */
     GEMM_BF16_F32 = 2,  /* bf16 A, B -> fp32 C */
     GEMM_BF16_BF16 = 3, /* bf16 A, B -> bf16 C */
-    /* 8-bit float A, B (1-byte elements, OFP8 E4M3 / E5M2; column-major B only) */
+    /* 8-bit float A, B (1-byte elements, OFP8 E4M3 / E5M2) */
     GEMM_E4M3_F32 = 4,  /* E4M3 A, B -> fp32 C */
     GEMM_E4M3_F16 = 5,  /* E4M3 A, B -> fp16 C */
     GEMM_E4M3_BF16 = 6, /* E4M3 A, B -> bf16 C */
@@ -63,8 +63,7 @@ enum {
     GEMM_ERR_ALIGN = -8,    /* a pointer not aligned to its element size */
     GEMM_ERR_INSTANCE = -9, /* gemm_run_instance: unknown id, or the instance
                                cannot handle this shape/alignment */
-    GEMM_ERR_LAYOUT = -10   /* gemm_run_ex: b_layout not one of gemm_layout_t; or an
-                               8-bit dtype with row-major B (gemm_run included) */
+    GEMM_ERR_LAYOUT = -10   /* gemm_run_ex: b_layout not one of gemm_layout_t */
 };
 
 /* Storage order of B for gemm_run_ex (A and C are always row-major). */
@@ -102,8 +101,9 @@ typedef enum {
  * A and B, none for 8-bit ones; 4 or 2 bytes for C).  Whole tiles (256x256,
  * 128x128 or 64x64, chosen by the number of tiles and K) with K a multiple of
  * 64 (128 for 8-bit inputs) run without edge code; other shapes with N a
- * multiple of 8 (any N with column-major B) run with clamped edge loads and a
- * zero-filled last k-slice; any other N runs on a fully masked fallback.
+ * multiple of 8 (16 for 8-bit inputs; any N with column-major B) run with
+ * clamped edge loads and a zero-filled last k-slice; any other N runs on a
+ * fully masked fallback.
  *
  * Returns GEMM_OK once the kernel is enqueued (asynchronous: device faults
  * surface at the caller's next synchronisation), or a GEMM_ERR_* code.

@@ -19,6 +19,22 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// ds_read_b64_tr_b8: LDS byte i holds (i >> shift) & 255 (two runs, shift 0
+// and 8, name the source byte of every result byte).  Lane l reads at byte
+// address addr[l] (8-byte aligned, < 2048); out[8l+j] receives byte j of the
+// lane's 8-byte result.
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+__global__ void probe_tr8_kernel(const int32_t* addr, int shift, uint8_t* out) {
+    __shared__ uint8_t lds[2048];
+    const int l = threadIdx.x;
+    for (int i = l; i < 2048; i += 64) lds[i] = (uint8_t)((i >> shift) & 255);
+    __syncthreads();
+    const int a = addr[l] & 2040;                 // in range and 8-byte aligned
+    const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) i32x2*)((__attribute__((address_space(3))) uint8_t*)lds + a));
+    for (int j = 0; j < 8; ++j) out[8 * l + j] = (uint8_t)((uint32_t)v[j >> 2] >> (8 * (j & 3)));
+}
+
 // ds_read_b64_tr_b16: LDS holds 1024 16-bit values equal to their index.
 // Lane l reads at byte address addr[l] (8-byte aligned, < 2048); out[4l+j]
 // receives element j of the lane's result.
@@ -430,6 +446,11 @@ int probe_lds_rate(int kind, int blocks, int iters, const int32_t* addr_table, u
 
 int probe_tr16(const int32_t* addr, int16_t* out) {
     hipLaunchKernelGGL(probe_tr16_kernel, dim3(1), dim3(64), 0, 0, addr, out);
+    return (int)hipDeviceSynchronize();
+}
+
+int probe_tr8(const int32_t* addr, int shift, uint8_t* out) {
+    hipLaunchKernelGGL(probe_tr8_kernel, dim3(1), dim3(64), 0, 0, addr, shift, out);
     return (int)hipDeviceSynchronize();
 }
 

@@ -51,8 +51,6 @@ def test_strerror_covers_every_status(lib):
     ((4, -1, 4, 0, PA, 4, PB, 4, PC, 4), G.GEMM_ERR_DIM),
     ((4, 4, -1, 0, PA, 4, PB, 4, PC, 4), G.GEMM_ERR_DIM),
     ((4, 4, 4, 10, PA, 4, PB, 4, PC, 4), G.GEMM_ERR_DTYPE),
-    ((4, 4, 4, 4, PA, 4, PB, 4, PC, 4), G.GEMM_ERR_LAYOUT),        # 8-bit inputs need column-major B
-    ((4, 4, 4, 9, PA, 4, PB, 4, PC, 4), G.GEMM_ERR_LAYOUT),
     ((4, 4, 4, -1, PA, 4, PB, 4, PC, 4), G.GEMM_ERR_DTYPE),
     ((4, 4, 8, 0, PA, 7, PB, 4, PC, 4), G.GEMM_ERR_LD),
     ((4, 4, 8, 0, PA, 8, PB, 3, PC, 4), G.GEMM_ERR_LD),
@@ -149,9 +147,9 @@ def test_instance_choice_general_form(lib):
 
 
 def test_instance_choice_8bit_inputs(lib):
-    """8-bit float inputs run on the dl8 instances only, with column-major B;
-    tile size by the number of tiles, clamped edges for anything but whole
-    tiles with K a multiple of 128."""
+    """8-bit float inputs run on the dl8 instances only; tile size by the
+    number of tiles, clamped edges for anything but whole tiles with K a
+    multiple of 128 (row-major B: N % 16 == 0), else the masked fallback."""
     col = G.GEMM_B_COL_MAJOR
     for dt in range(4, 10):
         assert _pick_ex(8192, 8192, 8192, col, dt) == "dl8_256x256x128"
@@ -176,8 +174,19 @@ def test_instance_choice_8bit_inputs(lib):
     st = G.gemm_run_instance_ex(ids["dl8_256x256x128"], 256, 256, 64, 4, col, PA, 64, PB, 64, PC, 256,
                                 1.0, 0.0, None, 0, None)
     assert st == G.GEMM_ERR_INSTANCE
-    # row-major B with 8-bit inputs: a layout error on every entry point
-    assert ex(256, 256, 256, 4, 0, PA, 256, PB, 256, PC, 256, 1.0, 0.0, None, 0) == G.GEMM_ERR_LAYOUT
+    # row-major B: the same tiles; N % 16 != 0 falls to the masked kernels
+    assert _pick(8192, 8192, 8192, 6) == "dl8_256x256x128"
+    assert _pick(3000, 5008, 4099, 5) == "dl8_256x256x128_clamp"
+    assert _pick(3000, 5000, 4099, 5) == "dl8_256x256x128_masked"        # 5000 % 16 == 8
+    assert _pick(4096, 4104, 4096, 4) == "dl8_256x256x128_masked"
+    assert _pick(1000, 1001, 777, 9) == "dl8_128x128x128_masked"
+    assert _pick(100, 7, 33, 7) == "dl8_128x128x128_masked"
+    assert _pick(256, 256, 256, 4) == "dl8_64x64x128"
+    assert _pick(2048, 2048, 2048, 4, pa=PA + 1) == "dl8_128x128x128"
+    # column-major B never lands on a masked 8-bit kernel (it has no column-major form)
+    st = G.gemm_run_instance_ex(ids["dl8_256x256x128_masked"], 256, 256, 128, 4, col, PA, 128, PB, 128, PC, 256,
+                                1.0, 0.0, None, 0, None)
+    assert st == G.GEMM_ERR_INSTANCE
     # extents count 1-byte elements: C starting right after an 8-bit A is no alias
     a_end = PA + 4 * 128
     assert ex(4, 4, 128, 4, col, PA, 128, PB, 128, a_end, 4, 1.0, 0.0, None, 0) >= 0

@@ -25,7 +25,8 @@ import pytest
 from dense_half_precision_tiled_amd import build as B
 
 UNITS = ["gemm_dl_nn.hip", "gemm_dl_nn_epi.hip", "gemm_dl_tn.hip", "gemm_dl_tn_epi.hip",
-         "gemm_ks.hip", "gemm_ks_epi.hip", "gemm_dl_f8.hip", "gemm_dl_f8_epi.hip"]
+         "gemm_ks.hip", "gemm_ks_epi.hip", "gemm_dl_f8_tn.hip", "gemm_dl_f8_tn_epi.hip",
+         "gemm_dl_f8_nn.hip", "gemm_dl_f8_nn_epi.hip"]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(B.hipcc()), reason="hipcc not available")
 

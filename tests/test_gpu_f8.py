@@ -1,6 +1,6 @@
 """GPU parity of the 8-bit float inputs (E4M3 and E5M2 of the OCP 8-bit
-floating point specification; B column-major), through the C ABI, against the
-CPU oracle.
+floating point specification; B row-major through gemm_run, or column-major
+through gemm_run_ex), through the C ABI, against the CPU oracle.
 
 Bars (as for the 16-bit inputs):
 * exact fixtures (the page's worked example, small integers, multiples of
@@ -10,8 +10,8 @@ Bars (as for the 16-bit inputs):
   8-bit MFMA's alignment loss oracle.align_bound8 (each group of 8
   consecutive k keeps 13 binades below its largest product; pinned by
   test_mfma_f8_alignment_model) for every checked element;
-* the six 8-bit instances (three tile sizes, whole or clamped edges) give
-  identical bits where they all apply;
+* the 8-bit instances (three tile sizes; whole, clamped or masked edges)
+  give identical bits where they apply, and so do the two B layouts;
 * memory outside the M x N region of C is never written (checked by run()).
 """
 import json
@@ -45,6 +45,13 @@ def _run_tn(G, A, B, code, **kw):
     return run(G, A, np.ascontiguousarray(B.T), code, layout=G.GEMM_B_COL_MAJOR, **kw)
 
 
+def _run_lay(G, A, B, code, lay, **kw):
+    """B row-major through gemm_run ("row"), or column-major ("col")."""
+    if lay == "col":
+        return _run_tn(G, A, B, code, **kw)
+    return run(G, A, B, code, **kw)
+
+
 def _oracle(A, B, fmt):
     return oracle.gemm_ex_f64(A, np.ascontiguousarray(B.T), fmt, b_layout="col")
 
@@ -53,19 +60,21 @@ def _extra(A, B, fmt, rows=None):
     return oracle.align_bound8(A, B, fmt, rows=rows)
 
 
+@pytest.mark.parametrize("lay", ["row", "col"])
 @pytest.mark.parametrize("code", CODES8)
-def test_worked_example(G, code):
+def test_worked_example(G, code, lay):
     with open(os.path.join(os.path.dirname(__file__), "golden", "worked_example_2x3x2.json")) as f:
         g = json.load(f)
     fmt, out = DTYPES[code]
-    y = _run_tn(G, inputs.from_values(g["A"], fmt), inputs.from_values(g["B"], fmt), code)
+    y = _run_lay(G, inputs.from_values(g["A"], fmt), inputs.from_values(g["B"], fmt), code, lay)
     assert y.tolist() == g["C"]
 
 
+@pytest.mark.parametrize("lay", ["row", "col"])
 @pytest.mark.parametrize("code", CODES8)
 @pytest.mark.parametrize("shape", [(256, 256, 256), (512, 768, 1024), (257, 263, 251), (300, 520, 4099),
-                                   (64, 1000, 2048), (1, 1, 1), (5, 3, 15), (33, 17, 129)])
-def test_integer_and_quarter_grid_bit_exact(G, code, shape):
+                                   (64, 1000, 2048), (1, 1, 1), (5, 3, 15), (33, 17, 129), (130, 48, 300)])
+def test_integer_and_quarter_grid_bit_exact(G, code, shape, lay):
     """Integers in {-2..2} and multiples of 0.25 in [-2, 2] are exact in both
     8-bit formats; every partial sum is exact in fp32, so each output is the
     correctly rounded exact value."""
@@ -74,38 +83,42 @@ def test_integer_and_quarter_grid_bit_exact(G, code, shape):
     for law, s in ((inputs.ints, 300), (inputs.quarter, 310)):
         A = law((M, K), s + code, fmt)
         B = law((K, N), s + 1 + code, fmt)
-        print("8-bit exact", code, shape, law.__name__, flush=True)
-        assert_exact(_run_tn(G, A, B, code), _oracle(A, B, fmt), out, "%s %s %s" % (code, shape, law.__name__))
+        print("8-bit exact", code, shape, lay, law.__name__, flush=True)
+        assert_exact(_run_lay(G, A, B, code, lay), _oracle(A, B, fmt), out,
+                     "%s %s %s %s" % (code, shape, lay, law.__name__))
 
 
+@pytest.mark.parametrize("lay", ["row", "col"])
 @pytest.mark.parametrize("code", CODES8)
 @pytest.mark.parametrize("shape", [(1024, 1024, 1024), (4096, 2048, 512), (384, 640, 896),
-                                   (1000, 1001, 777), (96, 50, 4160), (2, 300, 7)])
-def test_random_inputs_within_bound(G, code, shape):
+                                   (1000, 1001, 777), (96, 50, 4160), (2, 300, 7), (700, 528, 333)])
+def test_random_inputs_within_bound(G, code, shape, lay):
     M, N, K = shape
     fmt, out = DTYPES[code]
     A = inputs.normal((M, K), 400 + code, fmt)
     B = inputs.normal((K, N), 401 + code, fmt)
-    print("8-bit random", code, shape, flush=True)
-    y = _run_tn(G, A, B, code)
+    print("8-bit random", code, shape, lay, flush=True)
+    y = _run_lay(G, A, B, code, lay)
     res = assert_bound(y, _oracle(A, B, fmt), K, out, "%s %s" % (code, shape), extra=_extra(A, B, fmt))
     print("8-bit random", code, shape, "max_abs %.3g worst err/bound %.4f" % (res["max_abs"], res["worst_ratio"]),
           flush=True)
 
 
+@pytest.mark.parametrize("lay", ["row", "col"])
 @pytest.mark.parametrize("code", [4, 9])
-def test_odd_leading_dimensions_and_offsets(G, code):
+def test_odd_leading_dimensions_and_offsets(G, code, lay):
     """1-byte elements: rows may start at any byte (odd lda, ldb, base)."""
-    M, N, K = 333, 520, 1111
+    M, N, K = 333, 528, 1111
     fmt, out = DTYPES[code]
     A = inputs.normal((M, K), 500, fmt)
     B = inputs.normal((K, N), 501, fmt)
     r = _oracle(A, B, fmt)
     x = _extra(A, B, fmt)
     ys = []
-    for lda, ldb, a_off in ((K + 1, K + 3, 1), (K + 5, K, 3), (K, K + 7, 0), (K + 16, K + 16, 15)):
-        print("8-bit strides", code, lda, ldb, a_off, flush=True)
-        y = _run_tn(G, A, B, code, lda=lda, ldb=ldb, ldc=N + 5, a_off=a_off)
+    ldb0 = K if lay == "col" else N
+    for lda, ldb, a_off in ((K + 1, ldb0 + 3, 1), (K + 5, ldb0, 3), (K, ldb0 + 7, 0), (K + 16, ldb0 + 16, 15)):
+        print("8-bit strides", code, lay, lda, ldb, a_off, flush=True)
+        y = _run_lay(G, A, B, code, lay, lda=lda, ldb=ldb, ldc=N + 5, a_off=a_off)
         assert_bound(y, r, K, out, "lda %d ldb %d off %d" % (lda, ldb, a_off), extra=x)
         ys.append(y)
     for y in ys[1:]:                     # strides and offsets move data only
@@ -113,22 +126,28 @@ def test_odd_leading_dimensions_and_offsets(G, code):
 
 
 def test_instances_agree_bitwise(G):
-    """Tile size and edge handling move data only: the six 8-bit instances
-    give identical bits on a shape they all run."""
+    """Tile size, edge handling and the B layout move data only: every 8-bit
+    instance, with B row-major and (all but the masked ones) column-major,
+    gives identical bits on a shape they all run."""
     M, N, K = 512, 512, 1024
     ids = [i for i in range(G.gemm_num_instances()) if G.gemm_instance_name(i).startswith("dl8_")]
-    assert len(ids) == 6
+    assert len(ids) == 8
     for code in (4, 8):
         fmt, out = DTYPES[code]
         A = inputs.normal((M, K), 600, fmt)
         B = inputs.normal((K, N), 601, fmt)
         ys = []
         for i in ids:
-            print("8-bit instance", G.gemm_instance_name(i), code, flush=True)
-            ys.append(_run_tn(G, A, B, code, instance=i))
-        for i, y in zip(ids[1:], ys[1:]):
-            assert np.array_equal(y, ys[0], equal_nan=True), G.gemm_instance_name(i)
-        assert_bound(ys[0], _oracle(A, B, fmt), K, out, extra=_extra(A, B, fmt))
+            name = G.gemm_instance_name(i)
+            for lay in ("row", "col"):
+                masked_col = lay == "col" and name.endswith("_masked")
+                print("8-bit instance", name, code, lay, flush=True)
+                y = _run_lay(G, A, B, code, lay, instance=i, expect=G.GEMM_ERR_INSTANCE if masked_col else 0)
+                if not masked_col:
+                    ys.append((name + " " + lay, y))
+        for name, y in ys[1:]:
+            assert np.array_equal(y, ys[0][1], equal_nan=True), name
+        assert_bound(ys[0][1], _oracle(A, B, fmt), K, out, extra=_extra(A, B, fmt))
 
 
 @pytest.mark.parametrize("code", [4, 6, 8])
@@ -154,28 +173,35 @@ def test_general_form(G, code):
 
 
 def test_general_form_every_instance(G):
-    """alpha, beta, bias and ReLU on each of the six 8-bit instances (0.25-grid
-    inputs: the result is exact), on whole tiles and on a ragged shape for the
-    clamped ones."""
+    """alpha, beta, bias and ReLU on every 8-bit instance and both B layouts
+    (0.25-grid inputs: the result is exact), on whole tiles and on a ragged
+    shape (N % 16 != 0: the row-major clamped kernels refuse it, the masked
+    ones take it)."""
     from tests.gpu_helpers import encode_out
     ids = [i for i in range(G.gemm_num_instances()) if G.gemm_instance_name(i).startswith("dl8_")]
     for (M, N, K) in ((512, 512, 1024), (300, 264, 700)):
         A = inputs.quarter((M, K), 901, "e5m2")
         B = inputs.quarter((K, N), 902, "e5m2")
-        Bs = np.ascontiguousarray(B.T)
         cold = np.random.Generator(np.random.PCG64(903)).integers(-8, 9, (M, N)).astype(np.float64)
         bias = np.arange(N, dtype=np.float64) * 0.25 - 30.0
-        r = oracle.gemm_ex_f64(A, Bs, "e5m2", b_layout="col", alpha=0.5, beta=2.0, C_old=cold, bias=bias, relu=True)
+        r = oracle.gemm_ex_f64(A, B, "e5m2", alpha=0.5, beta=2.0, C_old=cold, bias=bias, relu=True)
         for i in ids:
             name = G.gemm_instance_name(i)
-            whole = not name.endswith("_clamp")
             tile = int(name.split("_")[1].split("x")[0])
-            expect = G.GEMM_ERR_INSTANCE if whole and (M % tile or N % tile or K % 128) else 0
-            print("8-bit epilogue", name, (M, N, K), flush=True)
-            y = run(G, A, Bs, 7, instance=i, layout=G.GEMM_B_COL_MAJOR, alpha=0.5, beta=2.0, bias=bias, relu=1,
-                    c_init=encode_out(cold, "f32"), expect=expect)
-            if expect == 0:
-                assert_exact(y, r, "f32", name)
+            for lay in ("row", "col"):
+                if name.endswith("_masked"):
+                    ok = lay == "row"
+                elif name.endswith("_clamp"):
+                    ok = lay == "col" or N % 16 == 0
+                else:
+                    ok = M % tile == 0 and N % tile == 0 and K % 128 == 0
+                print("8-bit epilogue", name, lay, (M, N, K), flush=True)
+                Bs = np.ascontiguousarray(B.T) if lay == "col" else B
+                y = run(G, A, Bs, 7, instance=i, layout=G.GEMM_B_COL_MAJOR if lay == "col" else G.GEMM_B_ROW_MAJOR,
+                        alpha=0.5, beta=2.0, bias=bias, relu=1, c_init=encode_out(cold, "f32"),
+                        expect=0 if ok else G.GEMM_ERR_INSTANCE)
+                if ok:
+                    assert_exact(y, r, "f32", "%s %s" % (name, lay))
 
 
 def test_zero_K(G):
@@ -201,16 +227,17 @@ def test_torch_binding_with_float8_tensors(G):
     torch.cuda.synchronize()
     assert_bound(y.cpu().numpy().astype(np.float64), _oracle(A, B, "e4m3"), K, "f32",
                  extra=_extra(A, B, "e4m3"))
-    with pytest.raises(G.GemmError):
-        G.gemm(tA, tBt.t().contiguous(), torch.float32)        # row-major B: layout error
+    y2 = G.gemm(tA, tBt.t().contiguous(), torch.float32)      # row-major B through gemm_run
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
 
 
-@pytest.mark.parametrize("name", ["e4m3_8192", "e5m2_8192"])
-def test_full_size_sampled(G, name):
+@pytest.mark.parametrize("name,lay", [("e4m3_8192", "col"), ("e5m2_8192", "col"), ("e4m3_8192", "row")])
+def test_full_size_sampled(G, name, lay):
     A, B, w = inputs.workload_inputs(name)
     code = {("e4m3", "bf16"): 6, ("e5m2", "bf16"): 9}[(w["fmt"], w["out"])]
-    print("full-size workload", name, flush=True)
-    y = _run_tn(G, A, B, code)
+    print("full-size workload", name, lay, flush=True)
+    y = _run_lay(G, A, B, code, lay)
     from tests.test_gpu_parity import _sample_rows
     rows = _sample_rows(w["M"], n=8)
     r = oracle.gemm_ex_f64(A, np.ascontiguousarray(B.T), w["fmt"], b_layout="col", rows=rows)

@@ -35,6 +35,8 @@ def P():
     lib.probe_lds_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp]
     lib.probe_dma_rate.argtypes = [ctypes.c_int, ctypes.c_int, vp, ctypes.c_int, vp, vp]
     lib.probe_mfma_f8.argtypes = [ctypes.c_int, vp, vp, vp]
+    lib.probe_tr8.argtypes = [vp, ctypes.c_int, vp]
+    lib.probe_tr8.restype = ctypes.c_int
     lib.probe_mfma_f8_acc.argtypes = [ctypes.c_int, vp, vp, vp, vp]
     lib.probe_mfma_f8_acc.restype = ctypes.c_int
     lib.probe_mfma_f8_rate.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
@@ -62,6 +64,30 @@ def test_ds_read_tr16_b64_layout(P, pattern):
         for j in range(4):
             src_lane = 16 * g + 4 * j + i // 4
             assert got[l, j] == addr[src_lane] // 2 + i % 4, (l, j)
+
+
+@pytest.mark.parametrize("pattern", ["linear", "perm5", "rows16"])
+def test_ds_read_tr8_b64_layout(P, pattern):
+    """Within each group of 16 lanes, lane i receives byte i % 8 of the 8-byte
+    rows addressed by lanes 2j + i/8 of its group, j = 0..7: one read hands
+    every lane a column of an 8 x 16 block of bytes (8 values of k of one
+    column of a row-major 8-bit tile).  Each source byte is named by two runs
+    (LDS byte n holds n & 255, then n >> 8)."""
+    addr = {"linear": [8 * l for l in range(64)],
+            "perm5": [8 * ((5 * l) % 64) for l in range(64)],
+            "rows16": [128 * ((l % 16) // 2) + 8 * (l % 2) + 16 * (l // 16) for l in range(64)]}[pattern]
+    assert all(a % 8 == 0 and 0 <= a <= 2040 for a in addr)
+    a = torch.tensor(addr, dtype=torch.int32, device="cuda")
+    src = np.zeros(512, np.int64)
+    for shift in (0, 8):
+        o = torch.zeros(512, dtype=torch.uint8, device="cuda")
+        assert P.probe_tr8(a.data_ptr(), shift, o.data_ptr()) == 0
+        src += o.cpu().numpy().astype(np.int64) << shift
+    src = src.reshape(64, 8)
+    for l in range(64):
+        g, i = l // 16, l % 16
+        for j in range(8):
+            assert src[l, j] == addr[16 * g + 2 * j + i // 8] + i % 8, (l, j)
 
 
 def test_global_load_lds_dwordx4_layout(P):
