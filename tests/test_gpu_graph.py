@@ -7,7 +7,8 @@ Each replay is checked bit for bit against the eager call on the same inputs,
 with eager work between the replays (new A written into the captured buffer,
 C poisoned), and the eager results against the oracle.  Cases cover every
 kernel geometry the selection uses (64x64, 128x128 split over waves or over
-K, 256x256) and the general epilogue with column-major B.
+K, 256x256), the general epilogue with column-major B, and 8-bit inputs in
+both B layouts.
 """
 import numpy as np
 import pytest
@@ -30,7 +31,8 @@ def G():
 
 
 def _dev(bits):
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+    b = np.ascontiguousarray(bits)
+    return torch.from_numpy(b.view(np.int16) if b.dtype == np.uint16 else b.view(np.int8)).cuda()
 
 
 # (M, N, K, dtype code, B layout, expected kernel family prefix)
@@ -40,6 +42,8 @@ CASES = [
     (1536, 1536, 1024, 3, "row", "dl_128x128"),     # 144 tiles of 128^2
     (2048, 4096, 512, 0, "row", "dl_256x256"),      # 128 tiles of 256^2
     (300, 264, 200, 1, "col", "dl_64x64"),          # general epilogue, column-major B, clamped edges
+    (2048, 2048, 1024, 6, "row", "dl8_128x128"),    # 8-bit inputs (E4M3 -> bf16), row-major B
+    (520, 392, 300, 7, "col", "dl8_64x64"),         # 8-bit inputs, general epilogue, column-major B
 ]
 
 
@@ -100,9 +104,11 @@ def test_graph_replay_matches_eager(G, case):
 
     for A, e in zip(As, eager):
         y = decode_out(e, out)
+        extra = oracle.align_bound8(A, B, fmt) if fmt in ("e4m3", "e5m2") else None
         if col:
             r = oracle.gemm_ex_f64(A, Bst, fmt, b_layout="col", alpha=alpha, relu=bool(relu))
-            res = oracle.compare_ex(y, r, K, out, alpha=alpha, dot=oracle.gemm_ex_f64(A, Bst, fmt, b_layout="col"))
+            res = oracle.compare_ex(y, r, K, out, alpha=alpha, dot=oracle.gemm_ex_f64(A, Bst, fmt, b_layout="col"),
+                                    extra=extra)
             assert res["ok"], res
         else:
-            assert_bound(y, oracle.gemm_f64(A, B, fmt), K, out, "eager %s" % name)
+            assert_bound(y, oracle.gemm_f64(A, B, fmt), K, out, "eager %s" % name, extra=extra)

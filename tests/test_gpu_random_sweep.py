@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
+from dense_half_precision_tiled_amd import inputs
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -99,3 +100,64 @@ def test_random_sweep(G):
         assert res["ok"], "%s: %s" % (desc, res)
     print("ran", ran, "refused", refused, flush=True)
     assert ran >= N_CASES // 2
+
+
+N_CASES8 = 120
+
+
+def test_random_sweep_8bit(G):
+    """The same sweep for the 8-bit inputs (E4M3 / E5M2, every output type):
+    both B layouts, odd leading dimensions and byte offsets, epilogues, and
+    forced 8-bit instances; the bound adds the 8-bit MFMA's alignment loss."""
+    rng = np.random.Generator(np.random.PCG64(20260202))
+    ids8 = [i for i in range(G.gemm_num_instances()) if G.gemm_instance_name(i).startswith("dl8_")]
+    dims = [1, 3, 16, 17, 64, 100, 127, 128, 129, 255, 256, 257, 300, 513]
+    ran = refused = 0
+    for case in range(N_CASES8):
+        M, N, K = (int(rng.choice(dims)) for _ in range(3))
+        if rng.random() < 0.2:
+            K = int(rng.choice([1024, 1100]))
+            M, N = int(rng.choice([256, 384])), int(rng.choice([256, 272]))
+        code = int(rng.integers(4, 10))
+        col = bool(rng.random() < 0.5)
+        pad = rng.random() < 0.5
+        lda = K + (int(rng.integers(1, 24)) if pad else 0)
+        ldb = (K if col else N) + (int(rng.integers(1, 24)) if pad else 0)
+        ldc = N + (int(rng.integers(1, 24)) if pad else 0)
+        a_off = int(rng.integers(0, 16)) if rng.random() < 0.3 else 0
+        epi = rng.random() < 0.5
+        alpha = float(rng.choice([1.0, 0.5, -2.0])) if epi else 1.0
+        beta = float(rng.choice([0.0, 1.0, -0.5])) if epi else 0.0
+        use_bias = bool(epi and rng.random() < 0.5)
+        relu = int(epi and rng.random() < 0.5)
+        inst = int(rng.choice(ids8)) if rng.random() < 0.4 else None
+        fmt, out = DTYPES[code]
+        A = inputs.normal((M, K), 19000 + 3 * case, fmt)
+        B = inputs.normal((K, N), 19001 + 3 * case, fmt)
+        Bs = np.ascontiguousarray(B.T) if col else B
+        cold = decode_out(encode_out(np.random.Generator(np.random.PCG64(19002 + 3 * case)).uniform(-4, 4, (M, N)),
+                                     out), out)
+        bias = np.random.Generator(np.random.PCG64(500 + case)).uniform(-2, 2, N) if use_bias else None
+        bias32 = None if bias is None else bias.astype(np.float32).astype(np.float64)
+        layout = G.GEMM_B_COL_MAJOR if col else G.GEMM_B_ROW_MAJOR
+        desc = "case %d M %d N %d K %d code %d col %s lda %d ldb %d ldc %d off %d inst %s" % (
+            case, M, N, K, code, col, lda, ldb, ldc, a_off, inst)
+        print(desc, flush=True)
+        try:
+            y = run(G, A, Bs, code, lda=lda, ldb=ldb, ldc=ldc, a_off=a_off, instance=inst, layout=layout,
+                    alpha=alpha, beta=beta, bias=bias, relu=relu, c_init=encode_out(cold, out))
+        except AssertionError as e:
+            if inst is not None and "cannot run this shape" in str(e):
+                refused += 1
+                continue
+            raise
+        ran += 1
+        lay = "col" if col else "row"
+        r = oracle.gemm_ex_f64(A, Bs, fmt, b_layout=lay, alpha=alpha, beta=beta, C_old=cold, bias=bias32,
+                               relu=bool(relu))
+        dot = oracle.gemm_ex_f64(A, Bs, fmt, b_layout=lay)
+        res = oracle.compare_ex(y, r, K, out, alpha=alpha, beta=beta, C_old=cold, bias=bias32, dot=dot,
+                                extra=oracle.align_bound8(A, B, fmt))
+        assert res["ok"], "%s: %s" % (desc, res)
+    print("8-bit sweep: ran", ran, "refused", refused, flush=True)
+    assert ran >= N_CASES8 // 2
