@@ -102,6 +102,7 @@ WORKLOADS = {
     "e4m3_8192": dict(M=8192, N=8192, K=8192, fmt=E4M3, out="bf16", law="normal", c=6, layout="col"),
     "e4m3_4096": dict(M=4096, N=4096, K=4096, fmt=E4M3, out="bf16", law="normal", c=7, layout="col"),
     "e5m2_8192": dict(M=8192, N=8192, K=8192, fmt=E5M2, out="bf16", law="normal", c=8, layout="col"),
+    "e4m3_2048": dict(M=2048, N=2048, K=2048, fmt=E4M3, out="f32", law="normal", c=9, layout="col"),
 }
 
 
