@@ -1,0 +1,98 @@
+"""Limits and concurrency of the boundary on the GPU.
+
+* Leading dimensions past 2^31 elements: a row offset i * ld no longer fits in
+  32 bits, so every address the kernels form from it must be 64-bit.  The
+  operands live in device buffers of several GiB of which only the used rows
+  are written (device-side copies; nothing that size crosses from the host).
+* Two streams: the library keeps no state and allocates nothing, so two
+  different products enqueued on two streams at once both come out right.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from dense_half_precision_tiled_amd import inputs
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from tests.gpu_helpers import assert_bound, decode_out  # noqa: E402
+
+BIG = (1 << 31) + 64        # elements: row 1 starts past 2^31
+
+
+@pytest.fixture(scope="module")
+def G():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from dense_half_precision_tiled_amd import gemm
+    gemm.load()      # raises if the library is missing: no fallback
+    return gemm
+
+
+def _rows_at(bits, ld, dtype):
+    """A device buffer of (rows - 1) * ld + cols elements holding `bits` row by
+    row at stride ld; the gaps are left unwritten."""
+    rows, cols = bits.shape
+    buf = torch.empty((rows - 1) * ld + cols, dtype=dtype, device="cuda")
+    src = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16 if bits.dtype == np.uint16 else np.int8)).cuda()
+    for r in range(rows):
+        buf[r * ld:r * ld + cols].copy_(src[r])
+    return buf
+
+
+@pytest.mark.parametrize("code,fmt,out,layout", [(3, "bf16", "bf16", "row"), (0, "f16", "f32", "col"),
+                                                  (4, "e4m3", "f32", "row"), (6, "e4m3", "bf16", "col")])
+def test_leading_dimensions_past_2_pow_31(G, code, fmt, out, layout):
+    col = layout == "col"
+    M, N, K = 3, (2 if col else 256), 320       # column-major B holds N rows at stride ld: keep N small
+    in8 = fmt in ("e4m3", "e5m2")
+    idt = torch.int8 if in8 else torch.int16
+    A = inputs.normal((M, K), 1201, fmt) if fmt != "f16" else inputs.uniform((M, K), 1201, fmt)
+    B = inputs.normal((K, N), 1202, fmt) if fmt != "f16" else inputs.uniform((K, N), 1202, fmt)
+    Bs = np.ascontiguousarray(B.T) if col else B
+    tA = _rows_at(A, BIG, idt)
+    tB = _rows_at(Bs, BIG, idt) if col else torch.from_numpy(B.view(np.int16 if not in8 else np.int8)).cuda()
+    ldb = BIG if col else N
+    tC = torch.full(((M - 1) * BIG + N,), -1, dtype=torch.int32 if out == "f32" else torch.int16, device="cuda")
+    print("large ld", code, layout, flush=True)
+    st = G.gemm_run_ex(M, N, K, code, G.GEMM_B_COL_MAJOR if col else G.GEMM_B_ROW_MAJOR, tA.data_ptr(), BIG,
+                       tB.data_ptr(), ldb, tC.data_ptr(), BIG, 1.0, 0.0, None, 0,
+                       torch.cuda.current_stream().cuda_stream)
+    assert st == 0, G.gemm_strerror(st)
+    torch.cuda.synchronize()
+    rows = torch.stack([tC[r * BIG:r * BIG + N] for r in range(M)]).cpu().numpy()
+    y = decode_out(rows.view(np.uint32 if out == "f32" else np.uint16), out)
+    # the gap after row 0 was never written
+    gap = tC[N:N + 4096].cpu().numpy().view(np.int32 if out == "f32" else np.int16)
+    assert np.all(gap == -1)
+    extra = oracle.align_bound8(A, B, fmt) if in8 else None
+    assert_bound(y, oracle.gemm_f64(A, B, fmt), K, out, "ld 2^31+64", extra=extra)
+    del tA, tB, tC
+    torch.cuda.empty_cache()
+
+
+def test_two_streams_at_once(G):
+    """Two different products on two streams, enqueued back to back without a
+    synchronisation between them, each checked against the oracle."""
+    cases = [(2048, 1024, 1536, 3, "bf16", "bf16"), (1000, 1200, 900, 4, "e4m3", "f32")]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    keep = []
+    for (M, N, K, code, fmt, out), s in zip(cases, streams):
+        A = inputs.normal((M, K), 1300 + code, fmt)
+        B = inputs.normal((K, N), 1310 + code, fmt)
+        v = np.int8 if A.dtype == np.uint8 else np.int16
+        tA = torch.from_numpy(A.view(v)).cuda()
+        tB = torch.from_numpy(B.view(v)).cuda()
+        tC = torch.empty((M, N), dtype=torch.int32 if out == "f32" else torch.int16, device="cuda")
+        keep.append((A, B, tA, tB, tC, M, N, K, code, fmt, out, s))
+    torch.cuda.synchronize()
+    for (A, B, tA, tB, tC, M, N, K, code, fmt, out, s) in keep:
+        for _ in range(3):
+            st = G.gemm_run(M, N, K, code, tA.data_ptr(), K, tB.data_ptr(), N, tC.data_ptr(), N, s.cuda_stream)
+            assert st == 0, G.gemm_strerror(st)
+    torch.cuda.synchronize()
+    for (A, B, tA, tB, tC, M, N, K, code, fmt, out, s) in keep:
+        y = decode_out(tC.cpu().numpy().view(np.uint32 if out == "f32" else np.uint16), out)
+        extra = oracle.align_bound8(A, B, fmt) if fmt == "e4m3" else None
+        assert_bound(y, oracle.gemm_f64(A, B, fmt), K, out, "stream %s" % fmt, extra=extra)
