@@ -2,8 +2,9 @@
 // Included only by the instantiation units gemm_dl_*.hip.
 //
 // Per workgroup: 4 waves in a 2x2 grid, each owning a (BM/2) x (BN/2) fp32
-// accumulator tile built from v_mfma_f32_32x32x16_{f16,bf16}.  K is streamed
-// in 64-deep slices through two LDS stages:
+// accumulator tile built from v_mfma_f32_32x32x16_{f16,bf16} (16-bit inputs;
+// the 8-bit form below).  K is streamed in 64-deep slices through two LDS
+// stages:
 //   * global -> LDS with global_load_lds_dwordx4 (16 bytes per lane, 1 KiB
 //     per wave instruction, no VGPR staging), issued while the previous
 //     slice is multiplied -- the multi-stage copy pipeline of the Ada
@@ -53,12 +54,12 @@
 //   EDGE_CLAMP: any M, K; any N for column-major B, N % 8 == 0 (N % 16 == 0
 //     for 8-bit inputs) for row-major B.  Rows of A (and of column-major B)
 //     past the edge and 16-byte column chunks of row-major B past N are read
-//     from a clamped, valid address: those
-//     values only reach outputs that are never stored.  A partial last slice
-//     (K % BK != 0) is filled through VGPRs with element-exact zero fill.
+//     from a clamped, valid address: those values only reach outputs that are
+//     never stored.  A partial last slice (K % BK != 0) is filled through
+//     VGPRs with element-exact zero fill.
 //   EDGE_MASKED: any shape.  Every slice is filled through VGPRs with
 //     element-exact zero fill (no asynchronous copies, one stage); the
-//     fallback for row-major B with N % 8 != 0.
+//     fallback for row-major B with N % 8 != 0 (N % 16 != 0 for 8-bit inputs).
 // 16-byte loads from any byte address return the exact bytes on gfx950
 // (pinned by a probe test), so misaligned rows and leading dimensions stay on
 // the vector paths.
