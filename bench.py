@@ -67,11 +67,21 @@ FAMILY_SOURCES = {
 }
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments and with whitespace runs collapsed, so
+    that rewording a comment does not count as a change of the kernel (the
+    sources hold no string literal with comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(family: str) -> str:
     h = hashlib.sha256()
     for rel in FAMILY_SOURCES[family]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
