@@ -52,16 +52,20 @@ CODES = {("f16", "f32"): 0, ("f16", "f16"): 1, ("bf16", "f32"): 2, ("bf16", "bf1
          ("e5m2", "f32"): 7, ("e5m2", "f16"): 8, ("e5m2", "bf16"): 9}
 EIGHT_BIT = ("e4m3", "e5m2")
 PEAK8_TFLOPS = 5000.0       # MI355X published dense fp8 MFMA peak
-# The sources each kernel family is compiled from: a counter summary stays
-# valid for a workload while these are unchanged.
+# The sources each kernel family is compiled from, with the instance table
+# (which holds the tile visit order): a counter summary stays valid for a
+# workload while these are unchanged.
 FAMILY_SOURCES = {
     "dl": ["dense_half_precision_tiled_amd/csrc/gemm_common.h",
            "dense_half_precision_tiled_amd/csrc/gemm_dl_kernel.h",
-           "dense_half_precision_tiled_amd/csrc/gemm_internal.h"],
+           "dense_half_precision_tiled_amd/csrc/gemm_internal.h",
+           "dense_half_precision_tiled_amd/csrc/gemm_instances.hip"],
     "dl8": ["dense_half_precision_tiled_amd/csrc/gemm_common.h",
             "dense_half_precision_tiled_amd/csrc/gemm_dl_kernel.h",
-            "dense_half_precision_tiled_amd/csrc/gemm_internal.h"],
-    "ks": ["dense_half_precision_tiled_amd/csrc/gemm_common.h",
+            "dense_half_precision_tiled_amd/csrc/gemm_internal.h",
+            "dense_half_precision_tiled_amd/csrc/gemm_instances.hip"],
+    "ks": ["dense_half_precision_tiled_amd/csrc/gemm_instances.hip",
+           "dense_half_precision_tiled_amd/csrc/gemm_common.h",
            "dense_half_precision_tiled_amd/csrc/gemm_ks_kernel.h",
            "dense_half_precision_tiled_amd/csrc/gemm_internal.h"],
 }

@@ -8,32 +8,37 @@
 namespace dhpt {
 
 // Every instance walks the output tiles in the XCD-aware grouped order of
-// tile_coords with groups of 8 tile-rows.  New instances go at the end: the
-// ids are part of the introspection interface.
+// tile_coords with groups of 4 tile-rows: the 32 tiles an XCD runs at once
+// cover 4 tile-rows x 8 tile-columns (12 panels, the minimum for 32 tiles,
+// as 8 x 4 would be), and at 8192^3 each XCD keeps the same 4 A row-panels
+// for the whole launch while all eight walk the same B column-panels
+// together (measured: +2.4% at 8192^3, +1.5% at 4096^3 over groups of 8).
+// New instances go at the end: the ids are part of the introspection
+// interface.
 const InstanceInfo kInstances[] = {
-    {"dl_256x256x64_fd2", 256, 2, EDGE_NONE, 8, KIND_DL},
-    {"dl_256x256x64_fd2_clamp", 256, 2, EDGE_CLAMP, 8, KIND_DL},
-    {"dl_256x256x64_masked", 256, 2, EDGE_MASKED, 8, KIND_DL},
-    {"dl_128x128x64_fd2", 128, 2, EDGE_NONE, 8, KIND_DL},
-    {"dl_128x128x64_fd2_clamp", 128, 2, EDGE_CLAMP, 8, KIND_DL},
-    {"dl_128x128x64_masked", 128, 2, EDGE_MASKED, 8, KIND_DL},
-    {"dl_256x256x64_fd1", 256, 1, EDGE_NONE, 8, KIND_DL},
-    {"dl_256x256x64_fd1_clamp", 256, 1, EDGE_CLAMP, 8, KIND_DL},
-    {"dl_128x128x64_fd1", 128, 1, EDGE_NONE, 8, KIND_DL},
-    {"dl_128x128x64_fd1_clamp", 128, 1, EDGE_CLAMP, 8, KIND_DL},
-    {"ks_128x128x64", 128, 2, EDGE_NONE, 8, KIND_KS},
-    {"ks_128x128x64_clamp", 128, 2, EDGE_CLAMP, 8, KIND_KS},
-    {"dl_64x64x64_fd2", 64, 2, EDGE_NONE, 8, KIND_DL},
-    {"dl_64x64x64_fd2_clamp", 64, 2, EDGE_CLAMP, 8, KIND_DL},
+    {"dl_256x256x64_fd2", 256, 2, EDGE_NONE, 4, KIND_DL},
+    {"dl_256x256x64_fd2_clamp", 256, 2, EDGE_CLAMP, 4, KIND_DL},
+    {"dl_256x256x64_masked", 256, 2, EDGE_MASKED, 4, KIND_DL},
+    {"dl_128x128x64_fd2", 128, 2, EDGE_NONE, 4, KIND_DL},
+    {"dl_128x128x64_fd2_clamp", 128, 2, EDGE_CLAMP, 4, KIND_DL},
+    {"dl_128x128x64_masked", 128, 2, EDGE_MASKED, 4, KIND_DL},
+    {"dl_256x256x64_fd1", 256, 1, EDGE_NONE, 4, KIND_DL},
+    {"dl_256x256x64_fd1_clamp", 256, 1, EDGE_CLAMP, 4, KIND_DL},
+    {"dl_128x128x64_fd1", 128, 1, EDGE_NONE, 4, KIND_DL},
+    {"dl_128x128x64_fd1_clamp", 128, 1, EDGE_CLAMP, 4, KIND_DL},
+    {"ks_128x128x64", 128, 2, EDGE_NONE, 4, KIND_KS},
+    {"ks_128x128x64_clamp", 128, 2, EDGE_CLAMP, 4, KIND_KS},
+    {"dl_64x64x64_fd2", 64, 2, EDGE_NONE, 4, KIND_DL},
+    {"dl_64x64x64_fd2_clamp", 64, 2, EDGE_CLAMP, 4, KIND_DL},
     // 8-bit float inputs: 128-deep slices, fragment prefetch one 64-deep k-step
-    {"dl8_256x256x128", 256, 1, EDGE_NONE, 8, KIND_DL, 1},
-    {"dl8_256x256x128_clamp", 256, 1, EDGE_CLAMP, 8, KIND_DL, 1},
-    {"dl8_128x128x128", 128, 1, EDGE_NONE, 8, KIND_DL, 1},
-    {"dl8_128x128x128_clamp", 128, 1, EDGE_CLAMP, 8, KIND_DL, 1},
-    {"dl8_64x64x128", 64, 1, EDGE_NONE, 8, KIND_DL, 1},
-    {"dl8_64x64x128_clamp", 64, 1, EDGE_CLAMP, 8, KIND_DL, 1},
-    {"dl8_256x256x128_masked", 256, 1, EDGE_MASKED, 8, KIND_DL, 1},
-    {"dl8_128x128x128_masked", 128, 1, EDGE_MASKED, 8, KIND_DL, 1},
+    {"dl8_256x256x128", 256, 1, EDGE_NONE, 4, KIND_DL, 1},
+    {"dl8_256x256x128_clamp", 256, 1, EDGE_CLAMP, 4, KIND_DL, 1},
+    {"dl8_128x128x128", 128, 1, EDGE_NONE, 4, KIND_DL, 1},
+    {"dl8_128x128x128_clamp", 128, 1, EDGE_CLAMP, 4, KIND_DL, 1},
+    {"dl8_64x64x128", 64, 1, EDGE_NONE, 4, KIND_DL, 1},
+    {"dl8_64x64x128_clamp", 64, 1, EDGE_CLAMP, 4, KIND_DL, 1},
+    {"dl8_256x256x128_masked", 256, 1, EDGE_MASKED, 4, KIND_DL, 1},
+    {"dl8_128x128x128_masked", 128, 1, EDGE_MASKED, 4, KIND_DL, 1},
 };
 const int kNumInstances = sizeof(kInstances) / sizeof(kInstances[0]);
 
