@@ -154,6 +154,18 @@ struct EpiArgs {
     int relu;
 };
 
+// The general epilogue's fp32 value, in one fixed order: alpha * acc
+// (rounded), plus beta * C_old in one fused step when C_old is read, plus the
+// bias (rounded), then ReLU.  Contraction is off, so every instantiation
+// (every output type) computes this same value before its one rounding.
+__device__ __forceinline__ float epi_value(float acc, const EpiArgs& ep, bool read_old, float old, float bias) {
+#pragma clang fp contract(off)
+    float v = ep.alpha * acc;
+    if (read_old) v = fmaf(ep.beta, old, v);
+    v = v + bias;
+    return (ep.relu && v < 0.0f) ? 0.0f : v;
+}
+
 // One slice (128 bytes of every row: k0 .. k0+63 for 2-byte elements,
 // k0 .. k0+127 for 1-byte ones) of the A rows m0 .. m0+BM-1 and of B (columns
 // n0 .. n0+BN-1) into the LDS stage `st` through VGPRs, with every value

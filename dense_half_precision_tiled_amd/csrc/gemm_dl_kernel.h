@@ -376,34 +376,45 @@ __global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
         }
     }
 
-    const int gl = l >> 5;
+    // Lane index of the epilogue's addresses.  In the edge modes it is
+    // recomputed here (v_mbcnt in a volatile asm, no input), so that the
+    // addresses are formed after the main loop: hoisted above a partial last
+    // slice they would stay live through its VGPR fill and push accumulators
+    // to scratch.
+    int le = l;
+    if constexpr (EDGE != EDGE_NONE)
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(le));
+    const int gl = le >> 5;
+
     float bias_v[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
         bias_v[j] = 0.0f;
         if constexpr (EPI) {
-            const int col = n0 + wn * WN + 32 * j + (l & 31);
+            const int col = n0 + wn * WN + 32 * j + (le & 31);
             if (ep.bias != nullptr && (EDGE == EDGE_NONE || col < N)) bias_v[j] = ep.bias[col];
         }
     }
-    // The beta test is uniform: take it once, outside the element loops.
-    auto store_tile = [&](auto read_old) {
+    // The beta test and the interior test are uniform: take them once,
+    // outside the element loops.  A tile wholly inside M x N stores without
+    // per-element masks (a branch per element costs more than the store).
+    auto store_tile = [&](auto read_old, auto masked) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-                const int col = n0 + wn * WN + 32 * j + (l & 31);
+                const int col = n0 + wn * WN + 32 * j + (le & 31);
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int row = m0 + wm * WM + 32 * i + 8 * (e >> 2) + 4 * gl + (e & 3);
-                    if (EDGE == EDGE_NONE || (row < M && col < N)) {
+                    if (!decltype(masked)::value || (row < M && col < N)) {
                         const int64_t idx = (int64_t)row * ldc + col;
                         float v = acc[i][j][e];
                         if constexpr (EPI) {
-                            v = ep.alpha * v;
-                            if constexpr (decltype(read_old)::value) v = fmaf(ep.beta, load_out<OUT>(C, idx), v);
-                            v += bias_v[j];
-                            if (ep.relu && v < 0.0f) v = 0.0f;
+                            constexpr bool ro = decltype(read_old)::value;
+                            float old = 0.0f;
+                            if constexpr (ro) old = load_out<OUT>(C, idx);
+                            v = epi_value(v, ep, ro, old, bias_v[j]);
                         }
                         store_out<OUT>(C, idx, v);
                     }
@@ -411,10 +422,20 @@ __global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
             }
         }
     };
+    auto store_edge = [&](auto read_old) {
+        if constexpr (EDGE == EDGE_NONE) {
+            store_tile(read_old, no{});
+        } else {
+            if (m0 + BM <= M && n0 + BN <= N)
+                store_tile(read_old, no{});
+            else
+                store_tile(read_old, yes{});
+        }
+    };
     if (EPI && ep.beta != 0.0f)
-        store_tile(yes{});
+        store_edge(yes{});
     else
-        store_tile(no{});
+        store_edge(no{});
 }
 
 template <int IN, int OUT, int BM, int BN, int FD, int EDGE, bool BT, bool EPI>

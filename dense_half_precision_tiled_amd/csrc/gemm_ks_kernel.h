@@ -322,10 +322,8 @@ __global__ __launch_bounds__(256, 1) void gemm_ks_kernel(
                     const int64_t idx = (int64_t)row * ldc + col;
                     float y = x[e];
                     if constexpr (EPI) {
-                        y = ep.alpha * y;
-                        if (read_old) y = fmaf(ep.beta, load_out<OUT>(C, idx), y);
-                        y += bias_v;
-                        if (ep.relu && y < 0.0f) y = 0.0f;
+                        const float old = read_old ? load_out<OUT>(C, idx) : 0.0f;
+                        y = epi_value(y, ep, read_old, old, bias_v);
                     }
                     store_out<OUT>(C, idx, y);
                 }

@@ -50,15 +50,17 @@ def encode_out(values, out_fmt):
 
 
 def run(G, A, B, code, lda=None, ldb=None, ldc=None, a_off=0, instance=None, stream=None,
-        expect=0, layout=None, alpha=1.0, beta=0.0, bias=None, relu=0, c_init=None):
+        expect=0, layout=None, alpha=1.0, beta=0.0, bias=None, relu=0, c_init=None, c_off=0):
     """C = A.B (or the general form) on the GPU; returns the decoded M x N result.
 
     B is the operand as stored: K x N for row-major, N x K for column-major
     (layout = G.GEMM_B_COL_MAJOR).  With layout None the call goes through
     gemm_run / gemm_run_instance, otherwise through the _ex entry points.
     c_init: M x N output-format bit patterns written into C before the call
-    (default: poison).  bias: N float64 values or None.  Checks that the row
-    padding of C and guard bands around it keep their poison."""
+    (default: poison).  bias: N float64 values or None.  c_off: C starts that
+    many elements past the guard band (an odd c_off leaves a 2-byte-aligned C).
+    Checks that the row padding of C and guard bands around it keep their
+    poison."""
     M, K = A.shape
     N = B.shape[0] if layout == G.GEMM_B_COL_MAJOR else B.shape[1]
     out_fmt = DTYPES[code][1]
@@ -66,15 +68,15 @@ def run(G, A, B, code, lda=None, ldb=None, ldc=None, a_off=0, instance=None, str
     tB, pB, ldb = _dev(B, ldb)
     ldc = ldc or N
     if out_fmt == "f32":
-        cbuf = np.full(2 * GUARD + max(M * ldc, 1), POISON32, dtype=np.uint32)
+        cbuf = np.full(2 * GUARD + c_off + max(M * ldc, 1), POISON32, dtype=np.uint32)
         esz = 4
     else:
-        cbuf = np.full(2 * GUARD + max(M * ldc, 1), POISON16, dtype=np.uint16)
+        cbuf = np.full(2 * GUARD + c_off + max(M * ldc, 1), POISON16, dtype=np.uint16)
         esz = 2
     if c_init is not None and M and N:
-        cbuf[GUARD:GUARD + M * ldc].reshape(M, ldc)[:, :N] = c_init
+        cbuf[GUARD + c_off:GUARD + c_off + M * ldc].reshape(M, ldc)[:, :N] = c_init
     tC = torch.from_numpy(cbuf.view(np.int32 if esz == 4 else np.int16)).cuda()
-    pC = tC.data_ptr() + esz * GUARD
+    pC = tC.data_ptr() + esz * (GUARD + c_off)
     tbias = None
     pbias = None
     if bias is not None:
@@ -96,9 +98,9 @@ def run(G, A, B, code, lda=None, ldb=None, ldc=None, a_off=0, instance=None, str
     assert st == expect, G.gemm_strerror(st)
     torch.cuda.synchronize()
     raw = tC.cpu().numpy().view(np.uint32 if esz == 4 else np.uint16)
-    assert np.all(raw[:GUARD] == cbuf[:GUARD]) and np.all(raw[-GUARD:] == cbuf[-GUARD:]), \
+    assert np.all(raw[:GUARD + c_off] == cbuf[:GUARD + c_off]) and np.all(raw[-GUARD:] == cbuf[-GUARD:]), \
         "guard band written"
-    body = raw[GUARD:GUARD + M * ldc].reshape(M, ldc) if M else raw[:0].reshape(0, ldc)
+    body = raw[GUARD + c_off:GUARD + c_off + M * ldc].reshape(M, ldc) if M else raw[:0].reshape(0, ldc)
     if ldc > N:
         assert np.all(body[:, N:] == (POISON32 if esz == 4 else POISON16)), "row padding of C written"
     del tbias
