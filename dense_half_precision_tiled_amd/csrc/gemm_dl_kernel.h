@@ -119,22 +119,28 @@ __global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
     // physical chunk l%8; column-major B the same over its BN rows.
     // Row-major B copy i fills rows 16w + B_ROWS_PER_COPY*i + l/B_CHUNKS,
     // physical chunk l%B_CHUNKS.
-    // Copy sources, in elements: a slice advances every A row (and every
-    // column-major B row) by BK values (128 bytes), and row-major B by BK rows.
-    using E = elem_t<ESZ>;
-    const E* const Ae = reinterpret_cast<const E*>(A);
-    const E* const Be = reinterpret_cast<const E*>(B);
-    const E* a_src[CA];
-    const E* b_src[CB];
-    int64_t b_step = BK;
+    // Each operand has a uniform base (scalar registers: the tile's first row
+    // of A, and the tile's first column, or first row for column-major B)
+    // that a slice advances by 128 bytes of every A row (and column-major B
+    // row) or by BK rows of row-major B; each copy has a 32-bit byte offset of
+    // this lane's 16 bytes from it, fixed for the whole K loop.  The host
+    // sends problems whose offsets do not fit in 32 bits to the masked
+    // kernels (copy_offsets_fit).
+    const char* a_base = reinterpret_cast<const char*>(A);
+    const char* b_base = reinterpret_cast<const char*>(B);
+    uint32_t a_vo[CA];
+    uint32_t b_vo[CB];
+    int64_t b_step = BK * ESZ;                            // bytes per slice
     uint32_t dma_a = 0, dma_b = 0;
     if constexpr (EDGE != EDGE_MASKED) {
+        a_base += (int64_t)m0 * lda * ESZ;
+        b_base += BT ? (int64_t)n0 * ldb * ESZ : (int64_t)n0 * ESZ;
 #pragma unroll
         for (int i = 0; i < CA; ++i) {
             const int r = (BM / 4) * w + 8 * i + (l >> 3);
             int grow = m0 + r;
             if constexpr (EDGE == EDGE_CLAMP) grow = grow < M ? grow : M - 1;
-            a_src[i] = Ae + (int64_t)grow * lda + (16 / ESZ) * ((l & 7) ^ swz_a(r));
+            a_vo[i] = (uint32_t)(((int64_t)(grow - m0) * lda + (16 / ESZ) * ((l & 7) ^ swz_a(r))) * ESZ);
         }
 #pragma unroll
         for (int i = 0; i < CB; ++i) {
@@ -142,16 +148,16 @@ __global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
                 const int r = (BN / 4) * w + 8 * i + (l >> 3);
                 int gcol = n0 + r;
                 if constexpr (EDGE == EDGE_CLAMP) gcol = gcol < N ? gcol : N - 1;
-                b_src[i] = Be + (int64_t)gcol * ldb + (16 / ESZ) * ((l & 7) ^ swz_a(r));
+                b_vo[i] = (uint32_t)(((int64_t)(gcol - n0) * ldb + (16 / ESZ) * ((l & 7) ^ swz_a(r))) * ESZ);
             } else {
                 const int kr = B_ROWS_PER_WAVE * w + B_ROWS_PER_COPY * i + l / B_CHUNKS;
                 const int sw = F8 ? swz_b8<B_CHUNKS>(kr) : swz_b(kr);
                 int col = n0 + (16 / ESZ) * ((l % B_CHUNKS) ^ sw);
                 if constexpr (EDGE == EDGE_CLAMP) col = col + 16 / ESZ <= N ? col : N - 16 / ESZ;
-                b_src[i] = Be + (int64_t)kr * ldb + col;
+                b_vo[i] = (uint32_t)(((int64_t)kr * ldb + (col - n0)) * ESZ);
             }
         }
-        if constexpr (!BT) b_step = (int64_t)BK * ldb;
+        if constexpr (!BT) b_step = (int64_t)BK * ldb * ESZ;
         dma_a = smem_base + ((BM / 4) * w) * 128;
         dma_b = smem_base + A_BYTES + (BT ? ((BN / 4) * w) * 128 : (B_ROWS_PER_WAVE * w) * BROW);
     }
@@ -240,12 +246,14 @@ __global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
     };
     auto issue_copy = [&](int stage, int i) {
         if (i < 0 || i >= COPIES) return;              // never taken: callers pass 0 .. COPIES-1
+        // a slice's copies are issued in index order: the bases move on after
+        // the last copy of their operand
         if (i < CA) {
-            lds_dma16(a_src[i], dma_a + stage * STAGE + 1024 * i);
-            a_src[i] += BK;
+            lds_dma16(a_base, a_vo[i], dma_a + stage * STAGE + 1024 * i);
+            if (i == CA - 1) a_base += BK * ESZ;
         } else {
-            lds_dma16(b_src[i - CA], dma_b + stage * STAGE + 1024 * (i - CA));
-            b_src[i - CA] += b_step;
+            lds_dma16(b_base, b_vo[i - CA], dma_b + stage * STAGE + 1024 * (i - CA));
+            if (i == COPIES - 1) b_base += b_step;
         }
     };
     auto mfma1 = [&](int buf, int q) {                 // MFMA q of a k-step: A block q/TN, B block q%TN
@@ -476,17 +484,13 @@ static hipError_t launch_dtype8(const Problem& p, int group_m, hipStream_t s) {
 
 // All tile sizes and edge modes for 8-bit inputs and one B layout.  Clamped
 // edges cover every shape for column-major B and N % 16 == 0 for row-major
-// B; the masked mode (256 and 128 tiles, row-major B) takes any N.
+// B; the masked mode (256 and 128 tiles) takes any shape and any leading
+// dimension.
 template <bool BT, bool EPI>
 static hipError_t launch_family8(int tile, int edge, const Problem& p, int group_m, hipStream_t s) {
-    if (edge == EDGE_MASKED) {
-        if constexpr (!BT) {
-            return tile == 256 ? launch_dtype8<256, 256, EDGE_MASKED, BT, EPI>(p, group_m, s)
-                               : launch_dtype8<128, 128, EDGE_MASKED, BT, EPI>(p, group_m, s);
-        } else {
-            return hipErrorInvalidValue;
-        }
-    }
+    if (edge == EDGE_MASKED)
+        return tile == 256 ? launch_dtype8<256, 256, EDGE_MASKED, BT, EPI>(p, group_m, s)
+                           : launch_dtype8<128, 128, EDGE_MASKED, BT, EPI>(p, group_m, s);
     if (tile == 256)
         return edge == EDGE_NONE ? launch_dtype8<256, 256, EDGE_NONE, BT, EPI>(p, group_m, s)
                                  : launch_dtype8<256, 256, EDGE_CLAMP, BT, EPI>(p, group_m, s);

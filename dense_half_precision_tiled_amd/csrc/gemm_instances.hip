@@ -42,6 +42,21 @@ const InstanceInfo kInstances[] = {
 };
 const int kNumInstances = sizeof(kInstances) / sizeof(kInstances[0]);
 
+// The asynchronous-copy kernels (whole-tile and clamped modes) address each
+// lane's 16 bytes as a 32-bit byte offset from a per-tile base: at most
+// tile - 1 rows of A (or of column-major B) plus a 128-byte slice, or one
+// slice's 128 / esz rows of row-major B plus a tile width.  The offsets are
+// kept below 2^31, where a signed and an unsigned reading of the offset
+// agree.  Problems beyond that (leading dimensions of millions of elements)
+// take the masked kernels, which fill through VGPRs with 64-bit addresses.
+static bool copy_offsets_fit(const Problem& p, int tile, int esz) {
+    const uint64_t lim = 0x7FFFFFFFull;
+    const uint64_t a = (uint64_t)(tile - 1) * (uint64_t)p.lda * esz + 128;
+    const uint64_t b = p.transB ? (uint64_t)(tile - 1) * (uint64_t)p.ldb * esz + 128
+                                : (uint64_t)128 * (uint64_t)p.ldb + (uint64_t)tile * esz;
+    return a <= lim && b <= lim;
+}
+
 bool instance_supports(int id, const Problem& p) {
     if (id < 0 || id >= kNumInstances) return false;
     const InstanceInfo& in = kInstances[id];
@@ -50,13 +65,14 @@ bool instance_supports(int id, const Problem& p) {
     if (tiles > (int64_t(1) << 24)) return false;
     if ((in.in8 != 0) != dtype_in8(p.dtype)) return false;                       // input width
     if (!in.in8 && in.kind == KIND_DL && in.fd == 1 && (p.transB || p.epi)) return false;   // plain row-major B only
+    if (in.edge != EDGE_MASKED && !copy_offsets_fit(p, in.tile, in.in8 ? 1 : 2)) return false;
     switch (in.edge) {
     case EDGE_NONE: return p.M % in.tile == 0 && p.N % in.tile == 0 && p.K % (in.in8 ? 128 : 64) == 0;
     case EDGE_CLAMP: {
         const int chunk = in.in8 ? 16 : 8;                 // row-major B: whole 16-byte column chunks
         return p.transB || (p.N % chunk == 0 && p.N >= chunk);
     }
-    case EDGE_MASKED: return !(in.in8 && p.transB);      // 8-bit masked kernels: row-major B
+    case EDGE_MASKED: return true;                       // any shape, any leading dimension
     default: return false;
     }
 }

@@ -83,15 +83,19 @@ __global__ __launch_bounds__(256, 1) void gemm_ks_kernel(
     tile_coords(blockIdx.x, tilesM, tilesN, group_m, &tm, &tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
-    // Copy sources: the addressing of the 128x128 direct-to-LDS kernel.
-    const uint16_t* a_src[CA];
-    const uint16_t* b_src[CB];
+    // Copy sources: the addressing of the 128x128 direct-to-LDS kernel (a
+    // uniform base per operand, advanced one slice at a time, and 32-bit
+    // per-lane byte offsets fixed for the whole K loop).
+    const char* a_base = reinterpret_cast<const char*>(A) + (int64_t)m0 * lda * 2;
+    const char* b_base = reinterpret_cast<const char*>(B) + (BT ? (int64_t)n0 * ldb * 2 : (int64_t)n0 * 2);
+    uint32_t a_vo[CA];
+    uint32_t b_vo[CB];
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
         const int r = (BM / 4) * w + 8 * i + (l >> 3);
         int grow = m0 + r;
         if constexpr (EDGE == dl::EDGE_CLAMP) grow = grow < M ? grow : M - 1;
-        a_src[i] = A + (int64_t)grow * lda + 8 * ((l & 7) ^ swz_a(r));
+        a_vo[i] = (uint32_t)(((int64_t)(grow - m0) * lda + 8 * ((l & 7) ^ swz_a(r))) * 2);
     }
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
@@ -99,15 +103,15 @@ __global__ __launch_bounds__(256, 1) void gemm_ks_kernel(
             const int r = (BN / 4) * w + 8 * i + (l >> 3);
             int gcol = n0 + r;
             if constexpr (EDGE == dl::EDGE_CLAMP) gcol = gcol < N ? gcol : N - 1;
-            b_src[i] = B + (int64_t)gcol * ldb + 8 * ((l & 7) ^ swz_a(r));
+            b_vo[i] = (uint32_t)(((int64_t)(gcol - n0) * ldb + 8 * ((l & 7) ^ swz_a(r))) * 2);
         } else {
             const int kr = 16 * w + B_ROWS_PER_COPY * i + l / B_CHUNKS;
             int col = n0 + 8 * ((l % B_CHUNKS) ^ swz_b(kr));
             if constexpr (EDGE == dl::EDGE_CLAMP) col = col + 8 <= N ? col : N - 8;
-            b_src[i] = B + (int64_t)kr * ldb + col;
+            b_vo[i] = (uint32_t)(((int64_t)kr * ldb + (col - n0)) * 2);
         }
     }
-    const int64_t b_step = BT ? (int64_t)BK : (int64_t)BK * ldb;
+    const int64_t a_step = (int64_t)BK * 2, b_step = BT ? (int64_t)BK * 2 : (int64_t)BK * ldb * 2;   // bytes
     const uint32_t dma_a = smem_base + ((BM / 4) * w) * 128;
     const uint32_t dma_b = smem_base + A_BYTES + (BT ? ((BN / 4) * w) * 128 : (16 * w) * BROW);
 
@@ -163,12 +167,14 @@ __global__ __launch_bounds__(256, 1) void gemm_ks_kernel(
     // copies and waits for the same count; it lands in a stage nobody reads
     // again.
     auto issue_copy = [&](int stage, int i, bool real) {
+        // a slice's copies are issued in index order: the bases move on after
+        // the last copy of their operand
         if (i < CA) {
-            lds_dma16(real ? a_src[i] : a_src[i] - BK, dma_a + stage * STAGE + 1024 * i);
-            a_src[i] += real ? BK : 0;
+            lds_dma16(real ? a_base : a_base - a_step, a_vo[i], dma_a + stage * STAGE + 1024 * i);
+            if (i == CA - 1 && real) a_base += a_step;
         } else {
-            lds_dma16(real ? b_src[i - CA] : b_src[i - CA] - b_step, dma_b + stage * STAGE + 1024 * (i - CA));
-            b_src[i - CA] += real ? b_step : 0;
+            lds_dma16(real ? b_base : b_base - b_step, b_vo[i - CA], dma_b + stage * STAGE + 1024 * (i - CA));
+            if (i == COPIES - 1 && real) b_base += b_step;
         }
     };
     auto mfma1 = [&](int buf, int q) {                 // MFMA q: A block q/TN, B block q%TN

@@ -103,7 +103,11 @@ typedef enum {
  * 64 (128 for 8-bit inputs) run without edge code; other shapes with N a
  * multiple of 8 (16 for 8-bit inputs; any N with column-major B) run with
  * clamped edge loads and a zero-filled last k-slice; any other N runs on a
- * fully masked fallback.
+ * fully masked fallback, and so do leading dimensions so large that one
+ * tile's rows of A (or of column-major B), or one 128-byte slice's rows of
+ * row-major B, span 2 GiB or more (about 4.2 million 16-bit elements per row
+ * at 256x256 tiles): the faster kernels address their copies as 31-bit
+ * offsets from a per-tile base.
  *
  * Returns GEMM_OK once the kernel is enqueued (asynchronous: device faults
  * surface at the caller's next synchronisation), or a GEMM_ERR_* code.

@@ -128,6 +128,31 @@ def test_instance_choice(lib):
     assert _pick(100, 7, 33, 0) == "dl_128x128x64_masked"
 
 
+def test_copy_offsets_beyond_31_bits_take_the_masked_kernels(lib):
+    """The whole-tile and clamped kernels address their copies as byte
+    offsets below 2^31 from a per-tile base: the farthest is tile - 1 rows of
+    A (or of column-major B) plus one 128-byte slice, or the 128 bytes' worth
+    of k rows of row-major B plus a tile width.  One element more of leading
+    dimension and the choice falls to the masked kernel of the same tiles."""
+    far = dict(pa=1 << 40, pb=2 << 40)        # operands far apart: no aliasing at these extents
+    lim = 2 ** 31 - 1
+    L = (lim - 128) // (255 * 2)               # A rows, 256x256 tiles, 2-byte elements
+    assert _pick(4096, 4096, 4096, lda=L, **far) == "dl_256x256x64_fd2"
+    assert _pick(4096, 4096, 4096, lda=L + 1, **far) == "dl_256x256x64_masked"
+    L = (lim - 256 * 2) // 128                 # row-major B: 64 rows of 2-byte elements per slice
+    assert _pick(4096, 4096, 4096, ldb=L, **far) == "dl_256x256x64_fd2"
+    assert _pick(4096, 4096, 4096, ldb=L + 1, **far) == "dl_256x256x64_masked"
+    L = (lim - 128) // (127 * 2)               # the k-split kernel's 128x128 tiles
+    assert _pick(2048, 2048, 2048, 0, lda=L, **far) == "ks_128x128x64"
+    assert _pick(2048, 2048, 2048, 0, lda=L + 1, **far) == "dl_128x128x64_masked"
+    L = (lim - 128) // 255                     # column-major 8-bit B: 255 rows of 1-byte elements
+    col = G.GEMM_B_COL_MAJOR
+    pick8 = lambda ldb: G.gemm_instance_name(G.gemm_select_instance_ex(
+        8192, 8192, 8192, 6, col, far["pa"], 8192, far["pb"], ldb, 0x7000000000, 8192, 1.0, 0.0, None, 0))
+    assert pick8(L) == "dl8_256x256x128"
+    assert pick8(L + 1) == "dl8_256x256x128_masked"
+
+
 def _pick_ex(M, N, K, layout, dtype=3, alpha=1.0, beta=0.0, bias=None, relu=0):
     ldb = K if layout == G.GEMM_B_COL_MAJOR else N
     return G.gemm_instance_name(G.gemm_select_instance_ex(
@@ -183,10 +208,6 @@ def test_instance_choice_8bit_inputs(lib):
     assert _pick(100, 7, 33, 7) == "dl8_128x128x128_masked"
     assert _pick(256, 256, 256, 4) == "dl8_64x64x128"
     assert _pick(2048, 2048, 2048, 4, pa=PA + 1) == "dl8_128x128x128"
-    # column-major B never lands on a masked 8-bit kernel (it has no column-major form)
-    st = G.gemm_run_instance_ex(ids["dl8_256x256x128_masked"], 256, 256, 128, 4, col, PA, 128, PB, 128, PC, 256,
-                                1.0, 0.0, None, 0, None)
-    assert st == G.GEMM_ERR_INSTANCE
     # extents count 1-byte elements: C starting right after an 8-bit A is no alias
     a_end = PA + 4 * 128
     assert ex(4, 4, 128, 4, col, PA, 128, PB, 128, a_end, 4, 1.0, 0.0, None, 0) >= 0

@@ -127,8 +127,8 @@ def test_odd_leading_dimensions_and_offsets(G, code, lay):
 
 def test_instances_agree_bitwise(G):
     """Tile size, edge handling and the B layout move data only: every 8-bit
-    instance, with B row-major and (all but the masked ones) column-major,
-    gives identical bits on a shape they all run."""
+    instance, with B row-major and column-major, gives identical bits on a
+    shape they all run."""
     M, N, K = 512, 512, 1024
     ids = [i for i in range(G.gemm_num_instances()) if G.gemm_instance_name(i).startswith("dl8_")]
     assert len(ids) == 8
@@ -140,11 +140,8 @@ def test_instances_agree_bitwise(G):
         for i in ids:
             name = G.gemm_instance_name(i)
             for lay in ("row", "col"):
-                masked_col = lay == "col" and name.endswith("_masked")
                 print("8-bit instance", name, code, lay, flush=True)
-                y = _run_lay(G, A, B, code, lay, instance=i, expect=G.GEMM_ERR_INSTANCE if masked_col else 0)
-                if not masked_col:
-                    ys.append((name + " " + lay, y))
+                ys.append((name + " " + lay, _run_lay(G, A, B, code, lay, instance=i)))
         for name, y in ys[1:]:
             assert np.array_equal(y, ys[0][1], equal_nan=True), name
         assert_bound(ys[0][1], _oracle(A, B, fmt), K, out, extra=_extra(A, B, fmt))
@@ -176,7 +173,7 @@ def test_general_form_every_instance(G):
     """alpha, beta, bias and ReLU on every 8-bit instance and both B layouts
     (0.25-grid inputs: the result is exact), on whole tiles and on a ragged
     shape (N % 16 != 0: the row-major clamped kernels refuse it, the masked
-    ones take it)."""
+    ones take it in both layouts)."""
     from tests.gpu_helpers import encode_out
     ids = [i for i in range(G.gemm_num_instances()) if G.gemm_instance_name(i).startswith("dl8_")]
     for (M, N, K) in ((512, 512, 1024), (300, 264, 700)):
@@ -190,7 +187,7 @@ def test_general_form_every_instance(G):
             tile = int(name.split("_")[1].split("x")[0])
             for lay in ("row", "col"):
                 if name.endswith("_masked"):
-                    ok = lay == "row"
+                    ok = True
                 elif name.endswith("_clamp"):
                     ok = lay == "col" or N % 16 == 0
                 else:

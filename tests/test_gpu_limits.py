@@ -6,6 +6,11 @@
   are written (device-side copies; nothing that size crosses from the host).
 * Two streams: the library keeps no state and allocates nothing, so two
   different products enqueued on two streams at once both come out right.
+* The copy-offset limit: the whole-tile kernels address their copies as byte
+  offsets below 2^31 from a per-tile base.  At the largest leading dimension
+  that fits, a full tile reaches offsets just under 2^31; the result must
+  equal, bit for bit, the masked kernel's (same family, same k order), which
+  the next leading dimension up is sent to.
 """
 import numpy as np
 import pytest
@@ -16,7 +21,7 @@ from dense_half_precision_tiled_amd import inputs
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-from tests.gpu_helpers import assert_bound, decode_out  # noqa: E402
+from tests.gpu_helpers import DTYPES, assert_bound, decode_out  # noqa: E402
 
 BIG = (1 << 31) + 64        # elements: row 1 starts past 2^31
 
@@ -96,3 +101,52 @@ def test_two_streams_at_once(G):
         y = decode_out(tC.cpu().numpy().view(np.uint32 if out == "f32" else np.uint16), out)
         extra = oracle.align_bound8(A, B, fmt) if fmt == "e4m3" else None
         assert_bound(y, oracle.gemm_f64(A, B, fmt), K, out, "stream %s" % fmt, extra=extra)
+
+
+def _instance(G, name):
+    ids = {G.gemm_instance_name(i): i for i in range(G.gemm_num_instances())}
+    return ids[name]
+
+
+@pytest.mark.parametrize("code,fmt,col,fast,masked", [
+    (3, "bf16", False, "dl_256x256x64_fd2", "dl_256x256x64_masked"),
+    (6, "e4m3", True, "dl8_256x256x128", "dl8_256x256x128_masked")])
+def test_copy_offsets_at_the_31_bit_limit(G, code, fmt, col, fast, masked):
+    M = N = 256
+    K = 128
+    in8 = fmt == "e4m3"
+    esz = 1 if in8 else 2
+    ld = (2 ** 31 - 1 - 128) // (255 * esz)     # the largest that keeps a full tile under 2^31
+    idt = torch.int8 if in8 else torch.int16
+    A = inputs.normal((M, K), 1401, fmt)
+    B = inputs.normal((K, N), 1402, fmt)
+    lay = G.GEMM_B_COL_MAJOR if col else G.GEMM_B_ROW_MAJOR
+    out = DTYPES[code][1]
+    res = {}
+    for name, lda in ((fast, ld), (masked, ld + 1)):
+        if col:
+            tA = _rows_at(A, K, idt)
+            tB = _rows_at(np.ascontiguousarray(B.T), lda, idt)
+            a_ld, b_ld = K, lda
+        else:
+            tA = _rows_at(A, lda, idt)
+            tB = torch.from_numpy(B.view(np.int8 if in8 else np.int16)).cuda()
+            a_ld, b_ld = lda, N
+        tC = torch.empty((M, N), dtype=torch.int16, device="cuda")
+        print("offset limit", name, lda, flush=True)
+        st = G.gemm_run_instance_ex(_instance(G, name), M, N, K, code, lay, tA.data_ptr(), a_ld, tB.data_ptr(),
+                                    b_ld, tC.data_ptr(), N, 1.0, 0.0, None, 0,
+                                    torch.cuda.current_stream().cuda_stream)
+        assert st == 0, G.gemm_strerror(st)
+        if name == masked:          # one element more: the fast kernel declines
+            st = G.gemm_run_instance_ex(_instance(G, fast), M, N, K, code, lay, tA.data_ptr(), a_ld,
+                                        tB.data_ptr(), b_ld, tC.data_ptr(), N, 1.0, 0.0, None, 0,
+                                        torch.cuda.current_stream().cuda_stream)
+            assert st == G.GEMM_ERR_INSTANCE
+        torch.cuda.synchronize()
+        res[name] = decode_out(tC.cpu().numpy().view(np.uint16), out)
+        del tA, tB, tC
+        torch.cuda.empty_cache()
+    assert np.array_equal(res[fast], res[masked])
+    extra = oracle.align_bound8(A, B, fmt) if in8 else None
+    assert_bound(res[fast], oracle.gemm_f64(A, B, fmt), K, out, "offset limit", extra=extra)
