@@ -6,7 +6,9 @@
 // the 8-bit form below).  K is streamed in 64-deep slices through two LDS
 // stages:
 //   * global -> LDS with global_load_lds_dwordx4 (16 bytes per lane, 1 KiB
-//     per wave instruction, no VGPR staging), issued while the previous
+//     per wave instruction, no VGPR staging; a uniform scalar base per
+//     operand plus a fixed 32-bit per-lane offset below 2^31, so larger
+//     problems go to EDGE_MASKED), issued while the previous
 //     slice is multiplied -- the multi-stage copy pipeline of the Ada
 //     tensor-core GEMM write-up ("stages" section) and the acquire / copy /
 //     wait / release loop of "GEMM From Naive CUDA to Tensor Cores" ("Where
@@ -58,8 +60,10 @@
 //     never stored.  A partial last slice (K % BK != 0) is filled through
 //     VGPRs with element-exact zero fill.
 //   EDGE_MASKED: any shape.  Every slice is filled through VGPRs with
-//     element-exact zero fill (no asynchronous copies, one stage); the
-//     fallback for row-major B with N % 8 != 0 (N % 16 != 0 for 8-bit inputs).
+//     element-exact zero fill (no asynchronous copies, one stage, 64-bit
+//     addresses); the fallback for row-major B with N % 8 != 0 (N % 16 != 0
+//     for 8-bit inputs) and for leading dimensions whose copy offsets would
+//     reach 2^31 bytes.
 // 16-byte loads from any byte address return the exact bytes on gfx950
 // (pinned by a probe test), so misaligned rows and leading dimensions stay on
 // the vector paths.
