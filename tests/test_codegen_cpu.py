@@ -8,7 +8,8 @@ it is checked for properties the design relies on:
   configurations of the large workloads);
 * M0 is written only by the asynchronous-copy helper (its s_mov_b32 m0 is
   followed by s_nop 0 and the global_load_lds it addresses), so no other code
-  can move a copy's LDS destination;
+  can move a copy's LDS destination, and every copy uses the scalar-base
+  address form;
 * every kernel uses at most 512 VGPR+AGPR registers (one wave per SIMD) and the
   MFMA instructions the design names (32x32x16 for 16-bit inputs, the unscaled
   32x32x64 8-bit form for 8-bit inputs).
@@ -112,6 +113,20 @@ def test_m0_is_written_only_by_the_copy_helper(kernels):
                 assert s.startswith("s_mov_b32 m0,"), "%s: %s" % (_short(name), s)
                 assert ins[i + 1] == "s_nop 0", "%s: %s then %s" % (_short(name), s, ins[i + 1])
                 assert ins[i + 2].startswith("global_load_lds_dwordx4"), "%s: %s" % (_short(name), ins[i + 2])
+
+
+def test_copies_use_a_scalar_base(kernels):
+    """Every global -> LDS copy takes a uniform base in a scalar register pair
+    and one 32-bit offset VGPR (global_load_lds_dwordx4 vN, s[a:b]): the
+    form that halves the address registers a copy reads and lets a slice
+    advance two scalar bases instead of every lane's 64-bit pointers."""
+    checked = 0
+    for name, (unit, ins, meta) in kernels.items():
+        for s in ins:
+            if s.startswith("global_load_lds"):
+                assert re.match(r"global_load_lds_dwordx4 v\d+, s\[\d+:\d+\]", s), "%s: %s" % (_short(name), s)
+                checked += 1
+    assert checked > 1000
 
 
 def test_register_budget_and_mfma_shape(kernels):
