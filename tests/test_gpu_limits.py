@@ -108,18 +108,24 @@ def _instance(G, name):
     return ids[name]
 
 
-@pytest.mark.parametrize("code,fmt,col,fast,masked", [
-    (3, "bf16", False, "dl_256x256x64_fd2", "dl_256x256x64_masked"),
-    (6, "e4m3", True, "dl8_256x256x128", "dl8_256x256x128_masked")])
-def test_copy_offsets_at_the_31_bit_limit(G, code, fmt, col, fast, masked):
-    M = N = 256
-    K = 128
+@pytest.mark.parametrize("code,fmt,col,shape,tile,fast,masked,same_family", [
+    (3, "bf16", False, (256, 256, 128), 256, "dl_256x256x64_fd2", "dl_256x256x64_masked", True),
+    (6, "e4m3", True, (256, 256, 128), 256, "dl8_256x256x128", "dl8_256x256x128_masked", True),
+    (1, "f16", False, (300, 264, 200), 256, "dl_256x256x64_fd2_clamp", "dl_256x256x64_masked", True),
+    (0, "f16", False, (128, 128, 256), 128, "ks_128x128x64", "dl_128x128x64_masked", False)])
+def test_copy_offsets_at_the_31_bit_limit(G, code, fmt, col, shape, tile, fast, masked, same_family):
+    """A full tile at the largest leading dimension that keeps its copy
+    offsets under 2^31 bytes (A rows, or column-major B rows), then one
+    element more on the masked kernel, which the fast one declines.  Within
+    one family (dl, dl8) the two give identical bits; the k-split kernel sums
+    in another order and is held to the bound."""
+    M, N, K = shape
     in8 = fmt == "e4m3"
     esz = 1 if in8 else 2
-    ld = (2 ** 31 - 1 - 128) // (255 * esz)     # the largest that keeps a full tile under 2^31
+    ld = (2 ** 31 - 1 - 128) // ((tile - 1) * esz)
     idt = torch.int8 if in8 else torch.int16
-    A = inputs.normal((M, K), 1401, fmt)
-    B = inputs.normal((K, N), 1402, fmt)
+    A = (inputs.uniform if fmt == "f16" else inputs.normal)((M, K), 1401, fmt)
+    B = (inputs.uniform if fmt == "f16" else inputs.normal)((K, N), 1402, fmt)
     lay = G.GEMM_B_COL_MAJOR if col else G.GEMM_B_ROW_MAJOR
     out = DTYPES[code][1]
     res = {}
@@ -132,21 +138,21 @@ def test_copy_offsets_at_the_31_bit_limit(G, code, fmt, col, fast, masked):
             tA = _rows_at(A, lda, idt)
             tB = torch.from_numpy(B.view(np.int8 if in8 else np.int16)).cuda()
             a_ld, b_ld = lda, N
-        tC = torch.empty((M, N), dtype=torch.int16, device="cuda")
+        tC = torch.empty((M, N), dtype=torch.int32 if out == "f32" else torch.int16, device="cuda")
         print("offset limit", name, lda, flush=True)
-        st = G.gemm_run_instance_ex(_instance(G, name), M, N, K, code, lay, tA.data_ptr(), a_ld, tB.data_ptr(),
-                                    b_ld, tC.data_ptr(), N, 1.0, 0.0, None, 0,
-                                    torch.cuda.current_stream().cuda_stream)
+        args = (M, N, K, code, lay, tA.data_ptr(), a_ld, tB.data_ptr(), b_ld, tC.data_ptr(), N, 1.0, 0.0, None, 0,
+                torch.cuda.current_stream().cuda_stream)
+        st = G.gemm_run_instance_ex(_instance(G, name), *args)
         assert st == 0, G.gemm_strerror(st)
         if name == masked:          # one element more: the fast kernel declines
-            st = G.gemm_run_instance_ex(_instance(G, fast), M, N, K, code, lay, tA.data_ptr(), a_ld,
-                                        tB.data_ptr(), b_ld, tC.data_ptr(), N, 1.0, 0.0, None, 0,
-                                        torch.cuda.current_stream().cuda_stream)
-            assert st == G.GEMM_ERR_INSTANCE
+            assert G.gemm_run_instance_ex(_instance(G, fast), *args) == G.GEMM_ERR_INSTANCE
         torch.cuda.synchronize()
-        res[name] = decode_out(tC.cpu().numpy().view(np.uint16), out)
+        res[name] = decode_out(tC.cpu().numpy().view(np.uint32 if out == "f32" else np.uint16), out)
         del tA, tB, tC
         torch.cuda.empty_cache()
-    assert np.array_equal(res[fast], res[masked])
+    if same_family:
+        assert np.array_equal(res[fast], res[masked])
     extra = oracle.align_bound8(A, B, fmt) if in8 else None
-    assert_bound(res[fast], oracle.gemm_f64(A, B, fmt), K, out, "offset limit", extra=extra)
+    ref = oracle.gemm_f64(A, B, fmt)
+    for name in (fast, masked):
+        assert_bound(res[name], ref, K, out, "offset limit " + name, extra=extra)
