@@ -18,6 +18,14 @@ Printed: one JSON line with the contract fields plus
   cpu_baseline  the CPU fp64 oracle timed on a bounded sample of output rows
                 of the same workload on this host (and those rows checked
                 against the GPU result);
+  observed      the three denominators of the measurement: a window of
+                back-to-back launches during which amd-smi samples the eight
+                XCD shader clocks and socket power, giving FLOP/clk/CU at the
+                clock the chip held (against 4096 nominal) and the fraction
+                of the spec peak at that clock; and the same window for the
+                MFMA-only loop of bench_probe.hip on the same kind of operand
+                data (the practical MFMA ceiling), giving the fraction of the
+                probe-measured peak;
   secondary     the same measurement on bf16 4096^3;
   other_configs the same on the other workloads (fp16 2048^3, the ragged
                 fp16 3000x5000x4099 shape, fp16 256^3, and the 8-bit float
@@ -27,7 +35,8 @@ Before the warmups of each workload, untimed launches run for about
 --settle-ms so that the timed launches see a settled shader clock.
 
 Other modes: --copy-calibration (the plain copy that scales the HBM byte
-counters), --loop-seconds (one workload back to back, or an MFMA-only probe)
+counters), --loop-seconds (one workload back to back, or the MFMA-only loop of
+bench_probe.hip: mfma_probe_bf16_data, mfma_probe_f16_data, mfma_probe_e4m3_data)
 and --power-sample (that loop in a child process, with amd-smi power and clock
 samples taken by this process, which never touches the GPU).
 """
@@ -52,6 +61,12 @@ CODES = {("f16", "f32"): 0, ("f16", "f16"): 1, ("bf16", "f32"): 2, ("bf16", "bf1
          ("e5m2", "f32"): 7, ("e5m2", "f16"): 8, ("e5m2", "bf16"): 9}
 EIGHT_BIT = ("e4m3", "e5m2")
 PEAK8_TFLOPS = 5000.0       # MI355X published dense fp8 MFMA peak
+N_CU = 256                  # MI355X compute units (8 XCDs x 32)
+FLOP_PER_CLK_CU = 4096      # dense fp16/bf16 MFMA FLOP per clock per CU (nominal)
+FLOP_PER_CLK_CU8 = 8192     # dense fp8
+PROBE_LIB = os.path.join(ROOT, "libdhpt_bench_probe.so")
+TRAFFIC_SOURCE = ("profiles/hbm_traffic.json: rocprofv3 FETCH_SIZE x2.0 + WRITE_SIZE x1.0 per launch, "
+                  "looked up by workload, instance and a hash of the kernel sources; not measured in this run")
 # The sources each kernel family is compiled from, with the instance table
 # (which holds the tile visit order): a counter summary stays valid for a
 # workload while these are unchanged.
@@ -302,6 +317,131 @@ def single_thread_oracle():
             "seconds": round(best, 4)}
 
 
+def smi_sample():
+    """(socket power W, [gfx clock MHz per XCD]) from amd-smi, or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True,
+                           timeout=30)
+        d = json.loads(r.stdout)
+        d = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+        clks = [float(d["clock"][k]["clk"]["value"]) for k in d["clock"] if k.startswith("gfx_")]
+        return float(d["power"]["socket_power"]["value"]), clks
+    except Exception:          # no amd-smi, a changed JSON layout: report no clock
+        return None
+
+
+def clock_window(torch, launch, flops_per_launch: float, seconds: float) -> dict:
+    """Launch back to back for about `seconds` (batches of 8 on the current
+    stream, timed with events over the whole window) while a thread samples
+    the XCD clocks and socket power.  Returns the rate and the samples'
+    statistics (clock None when amd-smi gave nothing)."""
+    import statistics
+    import threading
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            x = smi_sample()
+            if x is None:
+                return
+            samples.append(x)
+            stop.wait(0.05)
+
+    stream = torch.cuda.current_stream()
+    launch()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n, t0 = 0, time.perf_counter()
+    e0.record(stream)
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            launch()
+        n += 8
+        torch.cuda.synchronize()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=60)
+    ms = e0.elapsed_time(e1)
+    out = {"seconds": round(ms * 1e-3, 3), "launches": n,
+           "tflops": round(n * flops_per_launch / (ms * 1e-3) / 1e12, 2), "smi_samples": len(samples)}
+    busy = [x for x in samples if statistics.mean(x[1]) > 500]      # skip samples taken while idle
+    if busy:
+        out.update({"sclk_mhz_mean": round(statistics.mean(statistics.mean(x[1]) for x in busy), 1),
+                    "sclk_mhz_xcd_min": min(min(x[1]) for x in busy),
+                    "sclk_mhz_xcd_max": max(max(x[1]) for x in busy),
+                    "power_w_mean": round(statistics.mean(x[0] for x in busy), 1)})
+    else:
+        out["sclk_mhz_mean"] = None
+    return out
+
+
+def load_probe():
+    import ctypes
+    if not os.path.exists(PROBE_LIB):
+        raise RuntimeError("%s is missing: run __graft_entry__.build()" % PROBE_LIB)
+    P = ctypes.CDLL(PROBE_LIB)
+    P.bench_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    P.bench_probe_mfma.restype = ctypes.c_int
+    P.bench_probe_flops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    P.bench_probe_flops.restype = ctypes.c_double
+    return P
+
+
+PROBE_FMT = {"f16": 0, "bf16": 1, "e4m3": 2}
+
+
+def probe_launcher(torch, fmt: str, iters: int):
+    """A launch function for the MFMA-only loop on `fmt` operand data (drawn
+    like the workloads' inputs: fp16 U[-1,1), bf16 and E4M3 N(0,1)), one
+    workgroup per CU, and its FLOPs per launch."""
+    from dense_half_precision_tiled_amd import inputs
+    P = load_probe()
+    code = PROBE_FMT[fmt]
+    n = 32 * 64 * 16 if fmt == "e4m3" else 16 * 64 * 8
+    bits = {"f16": lambda: inputs.uniform((n,), 7, inputs.F16), "bf16": lambda: inputs.normal((n,), 7, inputs.BF16),
+            "e4m3": lambda: inputs.normal((n,), 7, inputs.E4M3)}[fmt]()
+    ops = upload(bits, torch)
+    sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    nbytes = ops.numel() * ops.element_size()
+
+    def launch(_keep=(ops, sink)):
+        st = P.bench_probe_mfma(code, N_CU, iters, ops.data_ptr(), nbytes, sink.data_ptr(),
+                                torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError("probe launch failed (%d)" % st)
+    return launch, P.bench_probe_flops(code, N_CU, iters)
+
+
+def observed(torch, res, seconds: float) -> dict:
+    """The clock-based denominators for one measured workload: FLOP/clk/CU at
+    the clock held during a window of back-to-back launches, the fraction of
+    the spec peak at that clock, and the fraction of the MFMA-only loop's rate
+    on the same kind of data (measured in its own window)."""
+    w = res["w"]
+    flops = 2.0 * w["M"] * w["N"] * w["K"]
+    g = clock_window(torch, res["launch"], flops, seconds)
+    fmt = "e4m3" if w["fmt"] in EIGHT_BIT else w["fmt"]
+    plaunch, pflops = probe_launcher(torch, fmt, 4000 if fmt == "e4m3" else 8000)
+    p = clock_window(torch, plaunch, pflops, seconds)
+    nominal = FLOP_PER_CLK_CU8 if fmt == "e4m3" else FLOP_PER_CLK_CU
+    out = {"gemm_window": g, "probe_window": p,
+           "probe": "bench_probe.hip MFMA-only loop, %s operand data, one workgroup per CU" % fmt,
+           "frac_of_probe_peak": round(res["tflops"] / p["tflops"], 4),
+           "flop_per_clk_per_cu_nominal": nominal}
+    if g.get("sclk_mhz_mean"):
+        fpc = g["tflops"] * 1e12 / (N_CU * g["sclk_mhz_mean"] * 1e6)
+        out["flop_per_clk_per_cu"] = round(fpc, 1)
+        out["frac_of_peak_at_observed_clock"] = round(fpc / nominal, 4)
+    if p.get("sclk_mhz_mean"):
+        out["probe_flop_per_clk_per_cu"] = round(p["tflops"] * 1e12 / (N_CU * p["sclk_mhz_mean"] * 1e6), 1)
+    return out
+
+
 def copy_calibration(torch, nbytes: int, steps: int, warmup: int) -> int:
     """Plain device-to-device copy of nbytes: reads nbytes and writes nbytes
     per launch.  Its FETCH_SIZE / WRITE_SIZE readings calibrate the counters."""
@@ -324,71 +464,25 @@ def copy_calibration(torch, nbytes: int, steps: int, warmup: int) -> int:
 
 def loop_for(G, torch, name, seconds: float) -> int:
     """Run one workload back to back for `seconds` and print the achieved rate.
-    Besides the GEMM workloads, MFMA-only probes (eight independent
-    accumulators per wave, one wave per SIMD on every CU): "mfma_probe"
-    (32x32x16, constant operands), "mfma_probe_bf16_data" /
-    "mfma_probe_f16_data" (32x32x16, operands drawn like the bf16 N(0,1) and
-    fp16 U[-1,1) workloads' inputs, rotating so that consecutive MFMAs see new
-    values as in a GEMM) and "mfma_probe_e4m3_data" (the 8-bit 32x32x64 MFMA
-    on rotating N(0,1) E4M3 operands)."""
-    if name == "mfma_probe_e4m3_data":
-        import ctypes
-        from dense_half_precision_tiled_amd import inputs
-        P = ctypes.CDLL(os.path.join(ROOT, "tests", "probes", "libdhpt_probes.so"))
-        P.probe_mfma_data_f8.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-        ops = upload(inputs.normal((32 * 64 * 16,), 7, inputs.E4M3), torch)
-        blocks, iters = 256, 25000
-        sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    Besides the GEMM workloads, the MFMA-only loop of bench_probe.hip (eight
+    independent accumulators per wave, one wave per SIMD on every CU):
+    "mfma_probe_bf16_data" / "mfma_probe_f16_data" (32x32x16, operands drawn
+    like the bf16 N(0,1) and fp16 U[-1,1) workloads' inputs, rotating so that
+    consecutive MFMAs see new values as in a GEMM) and "mfma_probe_e4m3_data"
+    (the 8-bit 32x32x64 MFMA on rotating N(0,1) E4M3 operands)."""
+    if name in ("mfma_probe_bf16_data", "mfma_probe_f16_data", "mfma_probe_e4m3_data"):
+        fmt = name.split("_")[2]
+        launch, per = probe_launcher(torch, fmt, 25000 if fmt == "e4m3" else 50000)
         n, ms, t0 = 0, 0.0, time.perf_counter()
         while time.perf_counter() - t0 < seconds:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            if P.probe_mfma_data_f8(blocks, iters, ops.data_ptr(), sink.data_ptr()) != 0:
-                raise RuntimeError("probe launch failed")
+            launch()
             e1.record()
             torch.cuda.synchronize()
             ms += e0.elapsed_time(e1)
             n += 1
-        flops = n * blocks * 4 * iters * 32 * 131072.0
-    elif name in ("mfma_probe_bf16_data", "mfma_probe_f16_data"):
-        import ctypes
-        from dense_half_precision_tiled_amd import inputs
-        P = ctypes.CDLL(os.path.join(ROOT, "tests", "probes", "libdhpt_probes.so"))
-        P.probe_mfma_data.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-        bf16 = int(name == "mfma_probe_bf16_data")
-        bits = inputs.normal((16 * 64 * 8,), 7, inputs.BF16) if bf16 else inputs.uniform((16 * 64 * 8,), 7, inputs.F16)
-        ops = upload(bits, torch)
-        blocks, iters = 256, 50000
-        sink = torch.zeros(4, dtype=torch.float32, device="cuda")
-        n, ms, t0 = 0, 0.0, time.perf_counter()
-        while time.perf_counter() - t0 < seconds:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            if P.probe_mfma_data(bf16, blocks, iters, ops.data_ptr(), sink.data_ptr()) != 0:
-                raise RuntimeError("probe launch failed")
-            e1.record()
-            torch.cuda.synchronize()
-            ms += e0.elapsed_time(e1)
-            n += 1
-        flops = n * blocks * 4 * iters * 32 * 32768.0
-    elif name == "mfma_probe":
-        import ctypes
-        P = ctypes.CDLL(os.path.join(ROOT, "tests", "probes", "libdhpt_probes.so"))
-        P.probe_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-        blocks, iters = 256, 200000
-        cyc = torch.zeros(blocks * 4, dtype=torch.int64, device="cuda")
-        sink = torch.zeros(4, dtype=torch.float32, device="cuda")
-        n, ms, t0 = 0, 0.0, time.perf_counter()
-        while time.perf_counter() - t0 < seconds:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            if P.probe_mfma_rate(1, blocks, iters, cyc.data_ptr(), sink.data_ptr()) != 0:
-                raise RuntimeError("probe launch failed")
-            e1.record()
-            torch.cuda.synchronize()
-            ms += e0.elapsed_time(e1)
-            n += 1
-        flops = n * blocks * 4 * iters * 8 * 32768.0
+        flops = n * per
     else:
         import numpy as np
         from dense_half_precision_tiled_amd import inputs
@@ -479,8 +573,11 @@ def main(argv=None):
     ap.add_argument("--cold", type=int, default=5, metavar="LAUNCHES",
                     help="also time this many single launches of the main workload with cold caches "
                          "(a 512 MiB buffer read before each; 0 to skip)")
+    ap.add_argument("--clock-seconds", type=float, default=1.5,
+                    help="length of each clock-sampling window (main and secondary workload, and the "
+                         "MFMA-only probe beside each); 0 to skip")
     ap.add_argument("--loop-seconds", type=float, default=0.0,
-                    help="instead of the timed bench, run --workload (or one of the MFMA-only probes 'mfma_probe', "
+                    help="instead of the timed bench, run --workload (or one of the MFMA-only probes "
                          "'mfma_probe_bf16_data', 'mfma_probe_f16_data', 'mfma_probe_e4m3_data') back to back this long")
     ap.add_argument("--power-sample", type=float, default=0.0, metavar="SECONDS",
                     help="run --workload in a child process for SECONDS and sample power and clocks with amd-smi")
@@ -521,11 +618,14 @@ def main(argv=None):
                 "traffic": traffic_from_profiles(
                     r["name"] + ("" if r["layout"] == w2.get("layout", "row") else "_" + r["layout"]), r["instance"])}
 
+    main_obs = observed(torch, main_res, args.clock_seconds) if args.clock_seconds > 0 else None
     sec = None
     if args.secondary and args.secondary != "none":
         r2 = measure(G, torch, args.secondary, max(args.steps, 50), args.warmup, args.instance,
                      args.layout, args.settle_ms)
         sec = summary(r2)
+        if args.clock_seconds > 0:
+            sec["observed"] = observed(torch, r2, args.clock_seconds)
         del r2
     others = []
     if args.also and args.also != "none" and args.instance is None:
@@ -559,9 +659,15 @@ def main(argv=None):
         "roofline": {"bound": "mfma", "achieved": round(main_res["tflops"], 2), "peak": peak_for(w),
                      "unit": "TFLOP/s", "frac": round(main_res["tflops"] / peak_for(w), 4),
                      "traffic": traffic,
+                     "traffic_source": TRAFFIC_SOURCE if traffic is not None else
+                     "none: no committed counter summary matches this kernel and its sources",
                      "algorithmic_bytes": main_res["alg_bytes"],
+                     "intensity_flop_per_byte": round(2.0 * w["M"] * w["N"] * w["K"] / main_res["alg_bytes"], 1),
+                     "ridge_flop_per_byte": round(peak_for(w) * 1e12 / (HBM_GBPS * 1e9), 1),
                      "hbm_gbps_algorithmic": round(main_res["alg_bytes"] / (main_res["ms"] * 1e-3) / 1e9, 1)},
     }
+    if main_obs is not None:
+        line["roofline"]["observed"] = main_obs
     line["repeats"] = repeats(main_res)
     if args.cold > 0:
         line["cold_l2"] = measure_cold(torch, main_res, args.cold)

@@ -200,6 +200,16 @@ double oracle_ulp(int out_fmt, double r) {
     return ldexp(1.0, e - p + 1);
 }
 
+/* Element-wise forms of the two functions above over n doubles, so that a
+ * whole output matrix is rounded or measured in one call. */
+void oracle_round_to_array(int out_fmt, const double* x, double* dst, int64_t n) {
+    for (int64_t t = 0; t < n; ++t) dst[t] = oracle_round_to(out_fmt, x[t]);
+}
+
+void oracle_ulp_array(int out_fmt, const double* r, double* dst, int64_t n) {
+    for (int64_t t = 0; t < n; ++t) dst[t] = oracle_ulp(out_fmt, r[t]);
+}
+
 void oracle_decode_array(int in_fmt, const void* src, double* dst, int64_t n) {
     for (int64_t t = 0; t < n; ++t) dst[t] = load_in(in_fmt, src, t);
 }

@@ -162,9 +162,10 @@ def test_rows_mode_matches_full_general_form():
 def test_bound_ex_reduces_to_plain_bound_terms():
     r = np.array([[1.0, -3.0]])
     # alpha = 1, beta = 0, no bias: K*2^-20 plus the epilogue rounding allowance
+    acc = 64 * 2.0 ** -20
     b = oracle.bound_ex(64, "f32", r)
-    assert np.allclose(b, 64 * 2.0 ** -20 + 2.0 ** -22 * np.abs(r))
+    assert np.array_equal(b, acc + 2.0 ** -22 * (np.abs(r) + acc))
     b16 = oracle.bound_ex(64, "f16", r)
-    assert np.allclose(b16 - b, oracle.ulp(r, "f16"))
+    assert np.array_equal(b16 - b, oracle.ulp(np.abs(r) + b, "f16"))
     assert np.allclose(oracle.bound_ex(64, "f32", r, alpha=-4.0, dot=r / -4.0),
-                       4 * 64 * 2.0 ** -20 + 2.0 ** -22 * np.abs(r))
+                       4 * acc + 2.0 ** -22 * (np.abs(r) + 4 * acc), rtol=0, atol=1e-18)
