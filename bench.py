@@ -43,6 +43,7 @@ samples taken by this process, which never touches the GPU).
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -121,13 +122,15 @@ def upload(bits, torch):
     return torch.from_numpy(bits.view(np.int16) if bits.dtype.itemsize == 2 else bits.view(np.int8)).cuda()
 
 
-def measure(G, torch, name, steps, warmup, instance=None, layout=None, settle_ms=200.0):
+def measure(G, torch, name, steps, warmup, instance=None, layout=None, settle_ms=200.0, entry="run"):
     """Upload a workload, run one correctness launch into a poisoned C, let
     the clock settle (untimed launches for about settle_ms), run `warmup`
     untimed launches, then time `steps` launches.  Returns a dict with the
     timing and the buffers.
     layout "col" stores B column-major (its transpose row-major) and calls
-    gemm_run_ex; "row" calls gemm_run; None takes the workload's own."""
+    gemm_run_ex; "row" calls gemm_run; None takes the workload's own.
+    entry "ws" calls gemm_run_ws instead, with a zeroed workspace of
+    gemm_workspace_size() bytes allocated here (before timing)."""
     import numpy as np
     from dense_half_precision_tiled_amd import inputs
     A, B, w = inputs.workload_inputs(name)
@@ -144,11 +147,17 @@ def measure(G, torch, name, steps, warmup, instance=None, layout=None, settle_ms
     ldb = K if col else N
     args = (M, N, K, code, tA.data_ptr(), K, tB.data_ptr(), ldb, tC.data_ptr(), N, s)
     ex_tail = (1.0, 0.0, None, 0, s)
+    ws = torch.zeros(G.gemm_workspace_size() // 4, dtype=torch.int32, device="cuda") if entry == "ws" else None
+    lay_code = G.GEMM_B_COL_MAJOR if col else G.GEMM_B_ROW_MAJOR
+    ws_args = (args[:4] + (lay_code,) + args[4:-1] + (1.0, 0.0, None, 0) +
+               ((ws.data_ptr(), G.gemm_workspace_size(), s) if ws is not None else ()))
 
-    def launch(_keep=(tA, tB, tC)):
+    def launch(_keep=(tA, tB, tC, ws)):
         # the closure owns the buffers whose addresses `args` holds, so they
         # stay allocated for as long as it can be called
-        if col:
+        if ws is not None:
+            st = G.gemm_run_ws(*ws_args) if instance is None else G.gemm_run_instance_ws(instance, *ws_args)
+        elif col:
             a = args[:4] + (G.GEMM_B_COL_MAJOR,) + args[4:-1] + ex_tail
             st = G.gemm_run_ex(*a) if instance is None else G.gemm_run_instance_ex(instance, *a)
         else:
@@ -190,13 +199,17 @@ def measure(G, torch, name, steps, warmup, instance=None, layout=None, settle_ms
     flops = 2.0 * M * N * K
     if instance is not None:
         inst = instance
+    elif ws is not None:
+        inst = G.gemm_select_instance_ws(*ws_args[:-1])
     elif col:
         inst = G.gemm_select_instance_ex(M, N, K, code, G.GEMM_B_COL_MAJOR, tA.data_ptr(), K,
                                          tB.data_ptr(), ldb, tC.data_ptr(), N, 1.0, 0.0, None, 0)
     else:
         inst = G.gemm_select_instance(M, N, K, code, tA.data_ptr(), K, tB.data_ptr(), N,
                                       tC.data_ptr(), N)
-    return {"name": name, "w": w, "layout": layout, "A": A, "B": B, "C": tC, "ms": ms, "rep_ms": rep_ms,
+    return {"name": name, "w": w, "layout": layout, "entry": "gemm_run_ws" if ws is not None else
+            ("gemm_run_ex" if col else "gemm_run"),
+            "A": A, "B": B, "C": tC, "ms": ms, "rep_ms": rep_ms,
             "launch": launch,
             "wall_s": wall, "settle_launches": n_settle,
             "tflops": flops / (ms * 1e-3) / 1e12, "instance": G.gemm_instance_name(inst),
@@ -385,7 +398,7 @@ def load_probe():
         raise RuntimeError("%s is missing: run __graft_entry__.build()" % PROBE_LIB)
     P = ctypes.CDLL(PROBE_LIB)
     P.bench_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
-                                   ctypes.c_void_p, ctypes.c_void_p]
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     P.bench_probe_mfma.restype = ctypes.c_int
     P.bench_probe_flops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
     P.bench_probe_flops.restype = ctypes.c_double
@@ -407,39 +420,152 @@ def probe_launcher(torch, fmt: str, iters: int):
             "e4m3": lambda: inputs.normal((n,), 7, inputs.E4M3)}[fmt]()
     ops = upload(bits, torch)
     sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    clocks = torch.zeros(2 * 4 * N_CU, dtype=torch.int64, device="cuda")
     nbytes = ops.numel() * ops.element_size()
 
-    def launch(_keep=(ops, sink)):
-        st = P.bench_probe_mfma(code, N_CU, iters, ops.data_ptr(), nbytes, sink.data_ptr(),
+    def launch(_keep=(ops, sink, clocks)):
+        st = P.bench_probe_mfma(code, N_CU, iters, ops.data_ptr(), nbytes, sink.data_ptr(), clocks.data_ptr(),
                                 torch.cuda.current_stream().cuda_stream)
         if st != 0:
             raise RuntimeError("probe launch failed (%d)" % st)
+
+    def kernel_mhz():
+        """Median over the waves of the last launch of shader clocks per microsecond."""
+        import numpy as np
+        c = clocks.cpu().numpy().reshape(-1, 2).astype(np.float64)
+        c = c[c[:, 0] > 0]
+        return float(np.median(c[:, 1] / (c[:, 0] * 0.01))) if c.size else None
+    launch.kernel_mhz = kernel_mhz
     return launch, P.bench_probe_flops(code, N_CU, iters)
+
+
+def kernel_clock(name: str, entry: str):
+    """The shader clock the GEMM kernel itself runs at: a child process runs
+    `bench.py --timeline 2` on the same workload with the profiling build of
+    the library, whose waves record s_memtime and s_memrealtime; returns the
+    median over workgroups of the last launch, or None (no profiling build,
+    or the child failed).  amd-smi's clock samples are not used for this:
+    they read well above the in-kernel clock on short kernels."""
+    import subprocess
+    from dense_half_precision_tiled_amd import build as B
+    if not os.path.exists(B.TIMELINE_LIB):
+        return None
+    try:
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--timeline", "2", "--workload", name,
+                            "--entry", entry, "--warmup", "3"], capture_output=True, text=True, timeout=180)
+        d = json.loads([ln for ln in r.stdout.splitlines() if ln.startswith("{")][-1])
+        last = d["launches"][-1]
+        return {"mhz_median": last["wg_mhz_median"],
+                "xcd_mhz": [v["median_mhz"] for v in last["per_xcd"].values()]}
+    except Exception:
+        return None
 
 
 def observed(torch, res, seconds: float) -> dict:
     """The clock-based denominators for one measured workload: FLOP/clk/CU at
-    the clock held during a window of back-to-back launches, the fraction of
-    the spec peak at that clock, and the fraction of the MFMA-only loop's rate
-    on the same kind of data (measured in its own window)."""
+    the shader clock the kernel runs at (in-kernel counters of the profiling
+    build), the fraction of the spec peak at that clock, and the fraction of
+    the MFMA-only loop's rate on the same kind of data (its own window, its
+    own in-kernel clock); plus socket power and amd-smi's clock readings
+    during both windows."""
     w = res["w"]
     flops = 2.0 * w["M"] * w["N"] * w["K"]
     g = clock_window(torch, res["launch"], flops, seconds)
     fmt = "e4m3" if w["fmt"] in EIGHT_BIT else w["fmt"]
     plaunch, pflops = probe_launcher(torch, fmt, 4000 if fmt == "e4m3" else 8000)
     p = clock_window(torch, plaunch, pflops, seconds)
+    p["kernel_mhz"] = plaunch.kernel_mhz()
     nominal = FLOP_PER_CLK_CU8 if fmt == "e4m3" else FLOP_PER_CLK_CU
-    out = {"gemm_window": g, "probe_window": p,
+    kc = kernel_clock(res["name"], "ws" if res["entry"] == "gemm_run_ws" else "run")
+    out = {"gemm_window": g, "probe_window": p, "gemm_kernel_clock": kc,
            "probe": "bench_probe.hip MFMA-only loop, %s operand data, one workgroup per CU" % fmt,
            "frac_of_probe_peak": round(res["tflops"] / p["tflops"], 4),
-           "flop_per_clk_per_cu_nominal": nominal}
-    if g.get("sclk_mhz_mean"):
-        fpc = g["tflops"] * 1e12 / (N_CU * g["sclk_mhz_mean"] * 1e6)
+           "flop_per_clk_per_cu_nominal": nominal,
+           "ridge_at_kernel_clock_flop_per_byte": None}
+    if kc is not None and kc.get("mhz_median"):
+        fpc = res["tflops"] * 1e12 / (N_CU * kc["mhz_median"] * 1e6)
         out["flop_per_clk_per_cu"] = round(fpc, 1)
-        out["frac_of_peak_at_observed_clock"] = round(fpc / nominal, 4)
-    if p.get("sclk_mhz_mean"):
-        out["probe_flop_per_clk_per_cu"] = round(p["tflops"] * 1e12 / (N_CU * p["sclk_mhz_mean"] * 1e6), 1)
+        out["frac_of_peak_at_kernel_clock"] = round(fpc / nominal, 4)
+        out["ridge_at_kernel_clock_flop_per_byte"] = round(
+            N_CU * nominal * kc["mhz_median"] * 1e6 / (HBM_GBPS * 1e9), 1)
+    if p.get("kernel_mhz"):
+        out["probe_flop_per_clk_per_cu"] = round(p["tflops"] * 1e12 / (N_CU * p["kernel_mhz"] * 1e6), 1)
     return out
+
+
+TIMELINE_WAVES = 65536      # room for 8192 workgroups of 8 waves
+
+
+def timeline_summary(rec):
+    """Summary of one launch's timeline records (rows of 8 int64 words:
+    start and end on the 100 MHz real-time counter, start and end on the
+    shader-clock counter, XCC id << 32 | HW_ID, workgroup id; unused rows are
+    zero)."""
+    import statistics
+    import numpy as np
+    rec = np.asarray(rec, dtype=np.int64).reshape(-1, 8)
+    rec = rec[rec[:, 1] > 0]
+    base = int(rec[:, 0].min())
+    tick_us = 0.01                                         # s_memrealtime: 100 MHz
+    xcc = (rec[:, 4] >> 32) & 0xF
+    hw = rec[:, 4] & 0xFFFFFFFF
+    # a CU: XCC, shader engine, shader array and CU index of HW_ID
+    cu_key = xcc * 4096 + (((hw >> 13) & 7) << 8) + (((hw >> 12) & 1) << 4) + ((hw >> 8) & 0xF)
+    wgs = {}                                               # workgroup: (start, end, xcc, cu, MHz)
+    tiles = {}                                             # workgroup: output tiles it computed
+    for i in range(rec.shape[0]):
+        g = int(rec[i, 5])
+        real = int(rec[i, 1] - rec[i, 0])
+        mhz = (rec[i, 3] - rec[i, 2]) / (real * tick_us) if real > 0 else 0.0
+        a, b, _, _, f = wgs.get(g, (1 << 62, 0, 0, 0, 0.0))
+        wgs[g] = (min(a, int(rec[i, 0])), max(b, int(rec[i, 1])), int(xcc[i]), int(cu_key[i]), max(f, mhz))
+        tiles[g] = int(rec[i, 6])
+    span = (max(v[1] for v in wgs.values()) - base) * tick_us
+    per_xcd, cu_busy = {}, {}
+    for (a, b, x, c, f) in wgs.values():
+        per_xcd.setdefault(x, []).append(((a - base) * tick_us, (b - base) * tick_us, f))
+        cu_busy[c] = cu_busy.get(c, 0.0) + (b - a) * tick_us
+    durs = [(b - a) * tick_us for (a, b, _, _, _) in wgs.values()]
+    return {"span_us": round(span, 2), "workgroups": len(wgs), "cus": len(cu_busy),
+            "wg_us_min": round(min(durs), 2), "wg_us_median": round(statistics.median(durs), 2),
+            "wg_us_max": round(max(durs), 2),
+            "wg_mhz_median": round(statistics.median(v[4] for v in wgs.values()), 1),
+            "last_start_us": round(max((a - base) * tick_us for (a, _, _, _, _) in wgs.values()), 2),
+            "cu_idle_frac": round(1.0 - sum(cu_busy.values()) / (len(cu_busy) * span), 4),
+            "per_xcd": {str(x): {"wgs": len(v), "first_end_us": round(min(e for _, e, _ in v), 2),
+                                 "median_end_us": round(statistics.median(e for _, e, _ in v), 2),
+                                 "last_end_us": round(max(e for _, e, _ in v), 2),
+                                 "median_wg_us": round(statistics.median(e - s0 for s0, e, _ in v), 2),
+                                 "median_mhz": round(statistics.median(f for _, _, f in v), 1),
+                                 "tiles": sum(tiles[g] for g, w in wgs.items() if w[2] == x)}
+                        for x, v in sorted(per_xcd.items())}}
+
+
+def timeline(G, torch, name: str, launches: int, warmup: int, settle_ms: float, entry: str = "run") -> int:
+    """Per-workgroup timeline of `launches` launches of one workload, from the
+    profiling build of the library (libdhpt_gemm_timeline.so, which records
+    for every wave its start and end on the 100 MHz real-time counter and on
+    the shader clock, and the XCC and CU it ran on).  Prints, per launch, the kernel span, the end times
+    of each XCD's first and last workgroups, workgroup durations, and the
+    share of CU time spent outside workgroups."""
+    res = measure(G, torch, name, 1, warmup, None, None, settle_ms, entry)
+    buf = torch.zeros(TIMELINE_WAVES * 8, dtype=torch.int64, device="cuda")
+    lib = G.load()
+    lib.gemm_timeline_set(ctypes.c_void_p(buf.data_ptr()), TIMELINE_WAVES)
+    out = []
+    for it in range(launches):
+        buf.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        res["launch"]()
+        e1.record()
+        torch.cuda.synchronize()
+        summ = timeline_summary(buf.cpu().numpy())
+        summ.update({"launch": it, "event_ms": round(e0.elapsed_time(e1), 4)})
+        out.append(summ)
+    lib.gemm_timeline_set(None, 0)
+    print(json.dumps({"timeline": name, "kernel": res["instance"], "launches": out}), flush=True)
+    return 0
 
 
 def copy_calibration(torch, nbytes: int, steps: int, warmup: int) -> int:
@@ -565,6 +691,8 @@ def main(argv=None):
     ap.add_argument("--settle-ms", type=float, default=200.0,
                     help="untimed launches for about this long before the warmups (clock ramp-up)")
     ap.add_argument("--instance", type=int, default=None, help="force a kernel instance id")
+    ap.add_argument("--entry", choices=("run", "ws"), default="run",
+                    help="call gemm_run / gemm_run_ex (run) or gemm_run_ws with a caller-owned workspace (ws)")
     ap.add_argument("--layout", choices=("row", "col"), default=None,
                     help="storage order of B: row-major (gemm_run) or column-major (gemm_run_ex); "
                          "default: the workload's own (row-major for the 16-bit ones, column-major for 8-bit)")
@@ -581,6 +709,9 @@ def main(argv=None):
                          "'mfma_probe_bf16_data', 'mfma_probe_f16_data', 'mfma_probe_e4m3_data') back to back this long")
     ap.add_argument("--power-sample", type=float, default=0.0, metavar="SECONDS",
                     help="run --workload in a child process for SECONDS and sample power and clocks with amd-smi")
+    ap.add_argument("--timeline", type=int, default=0, metavar="LAUNCHES",
+                    help="instead of the timed bench, record the per-workgroup timeline of this many launches of "
+                         "--workload with the profiling build (libdhpt_gemm_timeline.so)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the GEMM, time a plain device copy of BYTES bytes "
                          "(the reference kernel for scaling HBM byte counters)")
@@ -601,12 +732,17 @@ def main(argv=None):
         return copy_calibration(torch, args.copy_calibration, args.steps, args.warmup)
 
     from dense_half_precision_tiled_amd import gemm as G
+    if args.timeline > 0:
+        from dense_half_precision_tiled_amd import build as B
+        lib = G.load(B.TIMELINE_LIB)
+        lib.gemm_timeline_set.argtypes = [ctypes.c_void_p, ctypes.c_int64]
+        return timeline(G, torch, args.workload, args.timeline, args.warmup, args.settle_ms, args.entry)
     G.load()
     if args.loop_seconds > 0:
         return loop_for(G, torch, args.workload, args.loop_seconds)
 
     main_res = measure(G, torch, args.workload, args.steps, args.warmup, args.instance, args.layout,
-                       args.settle_ms)
+                       args.settle_ms, args.entry)
 
     def summary(r):
         w2 = r["w"]
@@ -614,7 +750,7 @@ def main(argv=None):
                 "ms_per_step": round(r["ms"], 5), "frac_of_peak": round(r["tflops"] / peak_for(w2), 4),
                 "peak": peak_for(w2),
                 "hbm_gbps_algorithmic": round(r["alg_bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
-                "kernel": r["instance"], "repeats": repeats(r),
+                "kernel": r["instance"], "entry_point": r["entry"], "repeats": repeats(r),
                 "traffic": traffic_from_profiles(
                     r["name"] + ("" if r["layout"] == w2.get("layout", "row") else "_" + r["layout"]), r["instance"])}
 
@@ -622,7 +758,7 @@ def main(argv=None):
     sec = None
     if args.secondary and args.secondary != "none":
         r2 = measure(G, torch, args.secondary, max(args.steps, 50), args.warmup, args.instance,
-                     args.layout, args.settle_ms)
+                     args.layout, args.settle_ms, args.entry)
         sec = summary(r2)
         if args.clock_seconds > 0:
             sec["observed"] = observed(torch, r2, args.clock_seconds)
@@ -631,7 +767,7 @@ def main(argv=None):
     if args.also and args.also != "none" and args.instance is None:
         for name in args.also.split(","):
             r3 = measure(G, torch, name, max(args.steps, 200), args.warmup, None, args.layout,
-                         args.settle_ms)
+                         args.settle_ms, args.entry)
             others.append(summary(r3))
             del r3
 
@@ -655,6 +791,7 @@ def main(argv=None):
         "config": {"workload": describe(w, lay),
                    "M": w["M"], "N": w["N"], "K": w["K"], "b_layout": lay,
                    "in": w["fmt"], "out": w["out"], "kernel": main_res["instance"],
+                   "entry_point": main_res["entry"],
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(main_res["tflops"], 2), "peak": peak_for(w),
                      "unit": "TFLOP/s", "frac": round(main_res["tflops"] / peak_for(w), 4),

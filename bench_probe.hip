@@ -31,7 +31,8 @@ enum { FMT_F16 = 0, FMT_BF16 = 1, FMT_E4M3 = 2 };
 // 32-byte fragment).  Each iteration issues 32 MFMAs per wave.
 template <int FMT>
 __global__ __launch_bounds__(256, 1) void mfma_loop_kernel(const u32x4* __restrict__ ops, int iters,
-                                                           float* __restrict__ sink) {
+                                                           float* __restrict__ sink, uint64_t* __restrict__ clocks) {
+    const uint64_t real0 = __builtin_amdgcn_s_memrealtime(), clk0 = __builtin_amdgcn_s_memtime();
     const int l = threadIdx.x & 63;
     f32x16 acc[8];
 #pragma unroll
@@ -84,6 +85,14 @@ __global__ __launch_bounds__(256, 1) void mfma_loop_kernel(const u32x4* __restri
 #pragma unroll
         for (int e = 0; e < 16; ++e) s += acc[i][e];
     if (s == 12345.0f) sink[0] = s;
+    // the wave's run time on the 100 MHz real-time counter and on the shader
+    // clock (s_memtime), for the clock the loop ran at
+    if (clocks != nullptr && l == 0) {
+        const uint64_t real1 = __builtin_amdgcn_s_memrealtime(), clk1 = __builtin_amdgcn_s_memtime();
+        const uint64_t i = 2 * ((uint64_t)blockIdx.x * 4 + (threadIdx.x >> 6));
+        clocks[i] = real1 - real0;
+        clocks[i + 1] = clk1 - clk0;
+    }
 }
 
 }  // namespace
@@ -95,10 +104,12 @@ extern "C" {
 // 1 bf16 (v_mfma_f32_32x32x16, 32768 FLOP each), 2 E4M3
 // (v_mfma_f32_32x32x64_f8f6f4, 131072 FLOP each).  ops: device buffer of
 // ops_bytes bytes, at least 16 KiB (16-bit formats) or 32 KiB (E4M3), 16-byte
-// aligned; sink: one device float.  Returns 0, or -1 for bad arguments (an
-// undersized buffer included), or the HIP error of the launch.
+// aligned; sink: one device float; clocks: null, or 2 x 4 x blocks uint64
+// that receive per wave the run time in 10 ns ticks and in shader clocks.
+// Returns 0, or -1 for bad arguments (an undersized buffer included), or the
+// HIP error of the launch.
 int bench_probe_mfma(int fmt, int blocks, int iters, const void* ops, int64_t ops_bytes, float* sink,
-                     void* stream) {
+                     uint64_t* clocks, void* stream) {
     const int64_t need = fmt == FMT_E4M3 ? 32 * 64 * 16 : 16 * 64 * 16;
     if (blocks <= 0 || iters <= 0 || ops == nullptr || sink == nullptr || ops_bytes < need ||
         reinterpret_cast<uintptr_t>(ops) % 16 != 0)
@@ -106,9 +117,9 @@ int bench_probe_mfma(int fmt, int blocks, int iters, const void* ops, int64_t op
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const u32x4* o = static_cast<const u32x4*>(ops);
     switch (fmt) {
-    case FMT_F16: hipLaunchKernelGGL(mfma_loop_kernel<FMT_F16>, dim3(blocks), dim3(256), 0, s, o, iters, sink); break;
-    case FMT_BF16: hipLaunchKernelGGL(mfma_loop_kernel<FMT_BF16>, dim3(blocks), dim3(256), 0, s, o, iters, sink); break;
-    case FMT_E4M3: hipLaunchKernelGGL(mfma_loop_kernel<FMT_E4M3>, dim3(blocks), dim3(256), 0, s, o, iters, sink); break;
+    case FMT_F16: hipLaunchKernelGGL(mfma_loop_kernel<FMT_F16>, dim3(blocks), dim3(256), 0, s, o, iters, sink, clocks); break;
+    case FMT_BF16: hipLaunchKernelGGL(mfma_loop_kernel<FMT_BF16>, dim3(blocks), dim3(256), 0, s, o, iters, sink, clocks); break;
+    case FMT_E4M3: hipLaunchKernelGGL(mfma_loop_kernel<FMT_E4M3>, dim3(blocks), dim3(256), 0, s, o, iters, sink, clocks); break;
     default: return -1;
     }
     return (int)hipGetLastError();

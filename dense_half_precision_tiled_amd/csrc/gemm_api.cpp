@@ -27,13 +27,30 @@ void extent(const void* p, int64_t rows, int64_t cols, int64_t ld, int esz, uint
     *e = *b + (uintptr_t)(((rows - 1) * ld + cols) * esz);
 }
 
-// The epilogue and layout arguments of gemm_run_ex (gemm_run: the defaults).
+// The epilogue and layout arguments of gemm_run_ex (gemm_run: the defaults),
+// and the workspace of gemm_run_ws.
 struct Extra {
     int b_layout = GEMM_B_ROW_MAJOR;
     float alpha = 1.0f, beta = 0.0f;
     const float* bias = nullptr;
     int relu = 0;
+    void* ws = nullptr;
+    int64_t ws_bytes = 0;
 };
+
+// Compute units of the current device (the persistent kernels launch one
+// workgroup per CU), queried once per device and kept: a property of the
+// device, not of any call.
+int device_cus() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (dev < 64) cached[dev] = n;
+    return n;
+}
 
 // Validate; on success fill `p` and return GEMM_OK (and *noop for empty output).
 int validate(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t lda,
@@ -74,6 +91,22 @@ int validate(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t 
         const uintptr_t z0 = reinterpret_cast<uintptr_t>(x.bias), z1 = z0 + (uintptr_t)(4 * N);
         if (overlaps(c0, c1, z0, z1)) return GEMM_ERR_ALIAS;
     }
+    if (x.ws != nullptr) {
+        if (x.ws_bytes < dhpt::kWorkspaceBytes || reinterpret_cast<uintptr_t>(x.ws) % 256 != 0)
+            return GEMM_ERR_WORKSPACE;
+        const uintptr_t w0 = reinterpret_cast<uintptr_t>(x.ws), w1 = w0 + (uintptr_t)dhpt::kWorkspaceBytes;
+        if (overlaps(c0, c1, w0, w1)) return GEMM_ERR_ALIAS;
+        if (K > 0) {
+            uintptr_t a0, a1, b0, b1;
+            extent(A, M, K, lda, isz, &a0, &a1);
+            extent(B, b_rows, b_cols, ldb, isz, &b0, &b1);
+            if (overlaps(w0, w1, a0, a1) || overlaps(w0, w1, b0, b1)) return GEMM_ERR_ALIAS;
+        }
+        if (x.bias != nullptr) {
+            const uintptr_t z0 = reinterpret_cast<uintptr_t>(x.bias), z1 = z0 + (uintptr_t)(4 * N);
+            if (overlaps(w0, w1, z0, z1)) return GEMM_ERR_ALIAS;
+        }
+    }
     p->M = (int)M; p->N = (int)N; p->K = (int)K; p->dtype = dtype;
     p->A = static_cast<const uint16_t*>(A); p->lda = lda;
     p->B = static_cast<const uint16_t*>(B); p->ldb = ldb;
@@ -81,6 +114,8 @@ int validate(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_t 
     p->transB = tb;
     p->alpha = x.alpha; p->beta = x.beta; p->bias = x.bias; p->relu = x.relu != 0;
     p->epi = !(x.alpha == 1.0f && x.beta == 0.0f && x.bias == nullptr && x.relu == 0);
+    p->sched = static_cast<uint32_t*>(x.ws);
+    p->workers = 0;
     return GEMM_OK;
 }
 
@@ -102,7 +137,18 @@ int64_t tiles_for(int tile, int64_t M, int64_t N) { return ((M + tile - 1) / til
 // 128x128 tiles when those give at least half a wave, else 64x64; whole
 // tiles, then clamped edges (every shape with column-major B, N % 16 == 0
 // with row-major B), then the masked fallback (row-major B, any N).
+//
+// With a workspace (gemm_run_ws), 16-bit inputs with at least two 256x256
+// tiles per compute unit run on the persistent kernel: the tail of the
+// launch is then balanced across XCDs that hold different clocks (with one
+// tile per CU or fewer there is nothing to rebalance).
 int choose_instance(const Problem& p) {
+    if (p.sched != nullptr && p.workers > 0 && !dhpt::dtype_in8(p.dtype) &&
+        tiles_for(256, p.M, p.N) >= 2 * (int64_t)p.workers) {
+        static const int pk_order[] = {22, 23};
+        for (int k = 0; k < 2; ++k)
+            if (dhpt::instance_supports(pk_order[k], p)) return pk_order[k];
+    }
     if (dhpt::dtype_in8(p.dtype)) {
         static const int big8[] = {14, 15, 20}, mid8[] = {16, 17, 21}, small8[] = {18, 19, 21};
         const int* o = tiles_for(256, p.M, p.N) >= 128 ? big8 : tiles_for(128, p.M, p.N) >= 128 ? mid8 : small8;
@@ -150,6 +196,7 @@ int run_any(int instance, int64_t M, int64_t N, int64_t K, int dtype, const void
     bool noop;
     int st = validate(M, N, K, dtype, A, lda, B, ldb, C, ldc, x, &p, &noop);
     if (st != GEMM_OK || noop) return st;
+    if (p.sched != nullptr) p.workers = device_cus();
     return run_validated(instance, p, static_cast<hipStream_t>(stream));
 }
 
@@ -159,13 +206,16 @@ int select_any(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int64_
     bool noop;
     int st = validate(M, N, K, dtype, A, lda, B, ldb, C, ldc, x, &p, &noop);
     if (st != GEMM_OK) return st;
+    if (p.sched != nullptr) p.workers = device_cus();
     if (noop || (K == 0 && !p.epi)) return GEMM_OK;
     return choose_instance(p);
 }
 
-Extra extra(int b_layout, float alpha, float beta, const float* bias, int relu) {
+Extra extra(int b_layout, float alpha, float beta, const float* bias, int relu, void* ws = nullptr,
+            int64_t ws_bytes = 0) {
     Extra x;
     x.b_layout = b_layout; x.alpha = alpha; x.beta = beta; x.bias = bias; x.relu = relu;
+    x.ws = ws; x.ws_bytes = ws_bytes;
     return x;
 }
 
@@ -210,6 +260,35 @@ int gemm_select_instance_ex(int64_t M, int64_t N, int64_t K, int dtype, int b_la
     return select_any(M, N, K, dtype, A, lda, B, ldb, C, ldc, extra(b_layout, alpha, beta, bias, relu));
 }
 
+int64_t gemm_workspace_size(void) { return dhpt::kWorkspaceBytes; }
+
+int gemm_run_ws(int64_t M, int64_t N, int64_t K, int dtype, int b_layout, const void* A, int64_t lda,
+                const void* B, int64_t ldb, void* C, int64_t ldc, float alpha, float beta,
+                const float* bias, int relu, void* workspace, int64_t workspace_bytes, void* stream) {
+    if (workspace == nullptr) return GEMM_ERR_WORKSPACE;
+    return run_any(-1, M, N, K, dtype, A, lda, B, ldb, C, ldc,
+                   extra(b_layout, alpha, beta, bias, relu, workspace, workspace_bytes), stream);
+}
+
+int gemm_run_instance_ws(int instance, int64_t M, int64_t N, int64_t K, int dtype, int b_layout,
+                         const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                         float alpha, float beta, const float* bias, int relu, void* workspace,
+                         int64_t workspace_bytes, void* stream) {
+    if (instance < 0 || instance >= dhpt::kNumInstances) return GEMM_ERR_INSTANCE;
+    if (workspace == nullptr) return GEMM_ERR_WORKSPACE;
+    return run_any(instance, M, N, K, dtype, A, lda, B, ldb, C, ldc,
+                   extra(b_layout, alpha, beta, bias, relu, workspace, workspace_bytes), stream);
+}
+
+int gemm_select_instance_ws(int64_t M, int64_t N, int64_t K, int dtype, int b_layout, const void* A,
+                            int64_t lda, const void* B, int64_t ldb, const void* C, int64_t ldc,
+                            float alpha, float beta, const float* bias, int relu, const void* workspace,
+                            int64_t workspace_bytes) {
+    if (workspace == nullptr) return GEMM_ERR_WORKSPACE;
+    return select_any(M, N, K, dtype, A, lda, B, ldb, C, ldc,
+                      extra(b_layout, alpha, beta, bias, relu, const_cast<void*>(workspace), workspace_bytes));
+}
+
 int gemm_num_instances(void) { return dhpt::kNumInstances; }
 
 const char* gemm_instance_name(int instance) {
@@ -251,6 +330,7 @@ const char* gemm_strerror(int status) {
     case GEMM_ERR_ALIGN: return "pointer not aligned to its element size";
     case GEMM_ERR_INSTANCE: return "unknown instance, or instance cannot run this shape";
     case GEMM_ERR_LAYOUT: return "unknown B layout";
+    case GEMM_ERR_WORKSPACE: return "workspace missing, smaller than gemm_workspace_size() or not 256-byte aligned";
     default: return "unknown status";
     }
 }

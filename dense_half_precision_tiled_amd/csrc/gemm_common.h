@@ -152,11 +152,49 @@ __device__ __forceinline__ u32x4 shift_chunk(u32x4 v, int sh) {
 }
 
 // The epilogue operands of the general form (unused by the plain kernels).
+// Profiling builds (-DDHPT_TIMELINE, a separate library) also carry the
+// timeline buffer through it.
 struct EpiArgs {
     float alpha, beta;
     const float* bias;         // N values, or null
     int relu;
+#ifdef DHPT_TIMELINE
+    uint64_t* timeline;        // 8 words per wave, or null
+#endif
 };
+
+#ifdef DHPT_TIMELINE
+// Profiling builds only.  A timestamp: the constant-rate real-time counter
+// (s_memrealtime, 100 MHz) and the shader-clock counter (s_memtime).
+struct TlStamp {
+    uint64_t real, clk;
+};
+__device__ __forceinline__ TlStamp tl_now() {
+    return TlStamp{__builtin_amdgcn_s_memrealtime(), __builtin_amdgcn_s_memtime()};
+}
+// Called last by every wave: once the wave's stores have completed, lane 0
+// writes {start, end (real time), start, end (shader clock), XCC id << 32 |
+// HW_ID, workgroup id, tiles, 0} to record blockIdx.x * waves + wave of
+// `buf` (8 words per record; `tiles`: output tiles the workgroup computed).
+__device__ __forceinline__ void tl_record(uint64_t* buf, TlStamp t0, uint32_t tiles = 1) {
+    if (buf == nullptr) return;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const TlStamp t1 = tl_now();
+    uint32_t hw, xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    if ((threadIdx.x & 63) == 0) {
+        uint64_t* r = buf + 8 * ((uint64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
+        r[0] = t0.real;
+        r[1] = t1.real;
+        r[2] = t0.clk;
+        r[3] = t1.clk;
+        r[4] = ((uint64_t)xcc << 32) | hw;
+        r[5] = blockIdx.x;
+        r[6] = tiles;
+    }
+}
+#endif
 
 // The general epilogue's fp32 value, in one fixed order: alpha * acc
 // (rounded), plus beta * C_old in one fused step when C_old is read, plus the

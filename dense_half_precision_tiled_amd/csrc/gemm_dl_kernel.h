@@ -79,11 +79,27 @@
 namespace dhpt {
 namespace dl {
 
+// LDS bytes of one workgroup: NSTAGE stages of an A slice (BM rows x 128
+// bytes) and a B slice (column-major: BN rows x 128 bytes; row-major: 128 /
+// element-size rows of BN elements), one stage for EDGE_MASKED.
+template <int IN, int BM, int BN, int EDGE, bool BT>
+constexpr int dl_lds_bytes() {
+    constexpr int ESZ = kIn8<IN> ? 1 : 2;
+    return (EDGE == EDGE_MASKED ? 1 : 2) * (BM * 128 + (BT ? BN * 128 : (128 / ESZ) * ESZ * BN));
+}
+
+// One output tile, rows m0 .. m0+BM-1 and columns n0 .. n0+BN-1, by the 256
+// lanes of the calling workgroup, with `smem` (dl_lds_bytes bytes, 1 KiB
+// aligned) as its LDS stages.  `tid` is threadIdx.x (the persistent kernel
+// passes a value the compiler cannot move out of its tile loop, so that the
+// lane offsets derived from it are recomputed per tile instead of being
+// kept live across the accumulator-heavy main loop).  On return every wave
+// has issued its stores and no wave reads `smem` any more once all have
+// returned.
 template <int IN, int OUT, int BM, int BN, int FD, int EDGE, bool BT, bool EPI>
-__global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
-    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
-    void* __restrict__ C, int64_t ldc, int M, int N, int K, int tilesM, int tilesN, int group_m,
-    EpiArgs ep) {
+__device__ __forceinline__ void dl_tile(
+    char* smem, const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
+    void* __restrict__ C, int64_t ldc, int M, int N, int K, int m0, int n0, const EpiArgs& ep, int tid) {
     static_assert((BM == 256 && BN == 256) || (BM == 128 && BN == 128) || (BM == 64 && BN == 64), "tile");
     static_assert(FD == 1 || FD == 2, "fragment prefetch distance");
     constexpr bool F8 = kIn8<IN>;
@@ -107,17 +123,13 @@ __global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
     constexpr int B_CHUNKS = BROW / 16;                   // row-major B: 16-byte chunks per row
     constexpr int B_ROWS_PER_WAVE = (128 / ESZ) / 4;      // row-major B: k rows each wave copies
     constexpr int NB = (FD == 1) ? 2 : 4;                 // fragment buffers
-    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
+    static_assert(NSTAGE * STAGE == dl_lds_bytes<IN, BM, BN, EDGE, BT>(), "LDS size");
     const uint32_t smem_base = (uint32_t)(size_t)(lds_char*)smem;
 
-    const int t = threadIdx.x;
+    const int t = tid;
     const int l = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = w >> 1, wn = w & 1;
-
-    int tm, tn;
-    tile_coords(blockIdx.x, tilesM, tilesN, group_m, &tm, &tn);
-    const int m0 = tm * BM, n0 = tn * BN;
 
     // Copy sources.  A copy i of wave w fills stage rows (BM/4)w + 8i + l/8,
     // physical chunk l%8; column-major B the same over its BN rows.
@@ -450,10 +462,156 @@ __global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
         store_edge(no{});
 }
 
+// One workgroup per output tile, tiles in the tile_coords order.
+template <int IN, int OUT, int BM, int BN, int FD, int EDGE, bool BT, bool EPI>
+__global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
+    void* __restrict__ C, int64_t ldc, int M, int N, int K, int tilesM, int tilesN, int group_m,
+    EpiArgs ep) {
+#ifdef DHPT_TIMELINE
+    const TlStamp tl0 = tl_now();
+#endif
+    __shared__ __attribute__((aligned(1024))) char smem[dl_lds_bytes<IN, BM, BN, EDGE, BT>()];
+    int tm, tn;
+    tile_coords(blockIdx.x, tilesM, tilesN, group_m, &tm, &tn);
+    dl_tile<IN, OUT, BM, BN, FD, EDGE, BT, EPI>(smem, A, lda, B, ldb, C, ldc, M, N, K, tm * BM, tn * BN, ep,
+                                                (int)threadIdx.x);
+#ifdef DHPT_TIMELINE
+    tl_record(ep.timeline, tl0);
+#endif
+}
+
+// The persistent form: a grid of at most one workgroup per CU, each taking
+// tiles from shared counters until none is left -- the persistent kernel of
+// "The Asynchronous Kernel: Tensor Cores & TMA" (section "Keeping the line
+// busy"), with one queue per XCD.  Queue x holds the logical ids
+// [xcd_first(x), xcd_first(x + 1)) that the one-workgroup-per-tile launch
+// deals to XCD x, in the same order, so each XCD's L2 sees the same compact
+// block of the grouped order; a workgroup takes from the queue of the XCD it
+// runs on (read from the hardware register) and, once that is empty, from the
+// other queues in turn, so the XCDs that run ahead (they hold different
+// clocks) take over the last tiles of the slow ones.  A tile index comes from
+// a vector-memory atomic add at device scope on the queue's head; the index
+// of the next tile is fetched while the current one is computed.  There are
+// no waits between workgroups: a workgroup that finds every queue drained
+// exits, and the last one to exit (counted by a second atomic) resets the
+// heads to zero for the next launch.
+//
+// Scheduler words (uint32) in the caller's workspace: the head of XCD x's
+// queue at kSchedStride * x (one 256-byte line each), the count of finished
+// workgroups at kSchedDone.  They must be zero when the kernel starts; the
+// kernel leaves them zero when it ends.
+constexpr int kSchedStride = 64;
+constexpr int kSchedDone = 8 * kSchedStride;
+constexpr int kSchedBytes = 4 * (kSchedDone + kSchedStride);
+
+__device__ __forceinline__ int sched_pull(uint32_t* sched, int xcd, int T) {
+    for (int d = 0; d < 8; ++d) {
+        const int x = (xcd + d) & 7;
+        const int first = xcd_first(x, T), cnt = xcd_first(x + 1, T) - first;
+        if (cnt == 0) continue;
+        const uint32_t h =
+            __hip_atomic_fetch_add(sched + kSchedStride * x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (h < (uint32_t)cnt) return first + (int)h;
+    }
+    return -1;
+}
+
+template <int IN, int OUT, int BM, int BN, int FD, int EDGE, bool BT, bool EPI>
+__global__ __launch_bounds__(256, 1) void gemm_dl_persist_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
+    void* __restrict__ C, int64_t ldc, int M, int N, int K, int tilesM, int tilesN, int group_m,
+    EpiArgs ep, uint32_t* __restrict__ sched) {
+#ifdef DHPT_TIMELINE
+    const TlStamp tl0 = tl_now();
+#endif
+    __shared__ __attribute__((aligned(1024))) char smem[dl_lds_bytes<IN, BM, BN, EDGE, BT>()];
+    __shared__ int next_tile;
+    const int T = tilesM * tilesN;
+    uint32_t xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    const int xcd = (int)(xcc & 7);
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);     // kept in a scalar register
+    if (threadIdx.x == 0) next_tile = sched_pull(sched, xcd, T);
+    __syncthreads();
+    int L = __builtin_amdgcn_readfirstlane(next_tile);
+#ifdef DHPT_TIMELINE
+    uint32_t tiles_done = 0;
+#endif
+    while (L >= 0) {
+#ifdef DHPT_TIMELINE
+        ++tiles_done;
+#endif
+        __syncthreads();                    // every lane has read next_tile
+        if (threadIdx.x == 0) next_tile = sched_pull(sched, xcd, T);
+        int tm, tn;
+        grouped_tile(L, tilesM, tilesN, group_m, &tm, &tn);
+        // threadIdx.x rebuilt per tile from the wave index and the lane
+        // index (v_mbcnt in a volatile asm): nothing per lane stays live
+        // across the tile loop
+        int lane;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+        const int tid = 64 * wave + lane;
+        dl_tile<IN, OUT, BM, BN, FD, EDGE, BT, EPI>(smem, A, lda, B, ldb, C, ldc, M, N, K, tm * BM, tn * BN, ep,
+                                                    tid);
+        __syncthreads();                    // the stages are free; next_tile is published
+        L = __builtin_amdgcn_readfirstlane(next_tile);
+    }
+    if (threadIdx.x == 0) {
+        // Every pull of this workgroup has returned; the last workgroup to get
+        // here knows that every pull of the launch has, and resets the heads.
+        const uint32_t done =
+            __hip_atomic_fetch_add(sched + kSchedDone, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == gridDim.x - 1) {
+            for (int x = 0; x < 8; ++x)
+                __hip_atomic_store(sched + kSchedStride * x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(sched + kSchedDone, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+#ifdef DHPT_TIMELINE
+    tl_record(ep.timeline, tl0, tiles_done);
+#endif
+}
+
+template <int IN, int OUT, int BM, int BN, int FD, int EDGE, bool BT, bool EPI>
+static void launch_persist_typed(const Problem& p, int group_m, hipStream_t s) {
+    const int tilesM = (p.M + BM - 1) / BM, tilesN = (p.N + BN - 1) / BN;
+    const int T = tilesM * tilesN;
+    const int grid = T < p.workers ? T : p.workers;
+    EpiArgs ep{p.alpha, p.beta, p.bias, p.relu};
+#ifdef DHPT_TIMELINE
+    ep.timeline = timeline_for((int64_t)grid * 4);
+#endif
+    hipLaunchKernelGGL((gemm_dl_persist_kernel<IN, OUT, BM, BN, FD, EDGE, BT, EPI>), dim3((unsigned)grid), dim3(256), 0,
+                       s, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, p.M, p.N, p.K, tilesM, tilesN, group_m, ep, p.sched);
+}
+
+// The persistent 256x256 kernels for 16-bit inputs (EDGE_NONE, EDGE_CLAMP).
+template <bool BT, bool EPI>
+static hipError_t launch_persist_family(int edge, const Problem& p, int group_m, hipStream_t s) {
+    if (edge != EDGE_NONE && edge != EDGE_CLAMP) return hipErrorInvalidValue;
+    auto go = [&](auto edge_c) {
+        constexpr int E = decltype(edge_c)::value;
+        switch (p.dtype) {
+        case 0: launch_persist_typed<IN_F16, OUT_F32, 256, 256, 2, E, BT, EPI>(p, group_m, s); break;
+        case 1: launch_persist_typed<IN_F16, OUT_F16, 256, 256, 2, E, BT, EPI>(p, group_m, s); break;
+        case 2: launch_persist_typed<IN_BF16, OUT_F32, 256, 256, 2, E, BT, EPI>(p, group_m, s); break;
+        case 3: launch_persist_typed<IN_BF16, OUT_BF16, 256, 256, 2, E, BT, EPI>(p, group_m, s); break;
+        default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    };
+    return edge == EDGE_NONE ? go(std::integral_constant<int, EDGE_NONE>{})
+                             : go(std::integral_constant<int, EDGE_CLAMP>{});
+}
+
 template <int IN, int OUT, int BM, int BN, int FD, int EDGE, bool BT, bool EPI>
 static void launch_typed(const Problem& p, int group_m, hipStream_t s) {
     const int tilesM = (p.M + BM - 1) / BM, tilesN = (p.N + BN - 1) / BN;
-    const EpiArgs ep{p.alpha, p.beta, p.bias, p.relu};
+    EpiArgs ep{p.alpha, p.beta, p.bias, p.relu};
+#ifdef DHPT_TIMELINE
+    ep.timeline = timeline_for((int64_t)tilesM * tilesN * 4);
+#endif
     hipLaunchKernelGGL((gemm_dl_kernel<IN, OUT, BM, BN, FD, EDGE, BT, EPI>), dim3((unsigned)(tilesM * tilesN)),
                        dim3(256), 0, s, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, p.M, p.N, p.K, tilesM, tilesN,
                        group_m, ep);

@@ -39,6 +39,10 @@ const InstanceInfo kInstances[] = {
     {"dl8_64x64x128_clamp", 64, 1, EDGE_CLAMP, 4, KIND_DL, 1},
     {"dl8_256x256x128_masked", 256, 1, EDGE_MASKED, 4, KIND_DL, 1},
     {"dl8_128x128x128_masked", 128, 1, EDGE_MASKED, 4, KIND_DL, 1},
+    // persistent 256x256 kernels: tiles from per-XCD atomic queues in the
+    // caller's workspace (gemm_run_ws)
+    {"pk_256x256x64", 256, 2, EDGE_NONE, 4, KIND_PK},
+    {"pk_256x256x64_clamp", 256, 2, EDGE_CLAMP, 4, KIND_PK},
 };
 const int kNumInstances = sizeof(kInstances) / sizeof(kInstances[0]);
 
@@ -64,6 +68,7 @@ bool instance_supports(int id, const Problem& p) {
     const int64_t tiles = ((int64_t)(p.M + in.tile - 1) / in.tile) * ((p.N + in.tile - 1) / in.tile);
     if (tiles > (int64_t(1) << 24)) return false;
     if ((in.in8 != 0) != dtype_in8(p.dtype)) return false;                       // input width
+    if (in.kind == KIND_PK && (p.sched == nullptr || p.workers <= 0)) return false;  // needs a workspace
     if (!in.in8 && in.kind == KIND_DL && in.fd == 1 && (p.transB || p.epi)) return false;   // plain row-major B only
     if (in.edge != EDGE_MASKED && !copy_offsets_fit(p, in.tile, in.in8 ? 1 : 2)) return false;
     switch (in.edge) {
@@ -88,6 +93,11 @@ hipError_t launch_instance(int id, const Problem& p, hipStream_t s) {
     }
     if (in.kind == KIND_KS)
         return p.epi ? launch_ks_epi(in.edge, p, in.group_m, s) : launch_ks(in.edge, p, in.group_m, s);
+    if (in.kind == KIND_PK) {
+        if (p.transB)
+            return p.epi ? launch_pk_tn_epi(in.edge, p, in.group_m, s) : launch_pk_tn(in.edge, p, in.group_m, s);
+        return p.epi ? launch_pk_nn_epi(in.edge, p, in.group_m, s) : launch_pk_nn(in.edge, p, in.group_m, s);
+    }
     if (p.transB)
         return p.epi ? launch_dl_tn_epi(in.tile, in.fd, in.edge, p, in.group_m, s)
                      : launch_dl_tn(in.tile, in.fd, in.edge, p, in.group_m, s);
@@ -106,6 +116,13 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(T* C, int64_t ldc, int M
     }
 }
 
+#ifdef DHPT_TIMELINE
+static uint64_t* g_timeline = nullptr;
+static int64_t g_timeline_waves = 0;
+
+uint64_t* timeline_for(int64_t waves) { return waves <= g_timeline_waves ? g_timeline : nullptr; }
+#endif
+
 hipError_t launch_zero_fill(const Problem& p, hipStream_t s) {
     const int64_t total = (int64_t)p.M * p.N;
     int64_t blocks = (total + 255) / 256;
@@ -120,3 +137,14 @@ hipError_t launch_zero_fill(const Problem& p, hipStream_t s) {
 }
 
 }  // namespace dhpt
+
+#ifdef DHPT_TIMELINE
+// Profiling builds only: register a device buffer of `waves` x 8 uint64
+// words; every later launch whose waves fit records its per-wave timeline
+// there (see tl_record).  A null buffer or waves <= 0 stops recording.
+extern "C" int gemm_timeline_set(void* buf, int64_t waves) {
+    dhpt::g_timeline = waves > 0 ? static_cast<uint64_t*>(buf) : nullptr;
+    dhpt::g_timeline_waves = buf != nullptr && waves > 0 ? waves : 0;
+    return 0;
+}
+#endif

@@ -22,6 +22,11 @@ struct Problem {
     float alpha, beta;
     const float* bias;         // N fp32 values or null
     int relu;
+    // Persistent kernels only: the zeroed scheduler words of the caller's
+    // workspace (null without a workspace) and the number of workgroups to
+    // launch (the device's compute units).
+    uint32_t* sched;
+    int workers;
 };
 
 // dtype facts shared by the API and the instance table.
@@ -39,7 +44,12 @@ enum EdgeMode {
 enum KernelKind {
     KIND_DL = 0,               // gemm_dl_kernel.h: waves split the output tile
     KIND_KS = 1,               // gemm_ks_kernel.h: waves split K, 128x128 tile, LDS reduction
+    KIND_PK = 2,               // gemm_dl_kernel.h, persistent: one workgroup per CU, tiles from
+                               // per-XCD atomic queues (needs the workspace of gemm_run_ws)
 };
+
+// Bytes of workspace the persistent kernels use (their scheduler words).
+constexpr int64_t kWorkspaceBytes = 4096;
 
 // One compiled kernel configuration.  The instances of one kind compute the
 // same function with the same per-element operation order; the two kinds
@@ -61,6 +71,12 @@ extern const int kNumInstances;
 bool instance_supports(int id, const Problem& p);
 
 hipError_t launch_instance(int id, const Problem& p, hipStream_t stream);
+
+#ifdef DHPT_TIMELINE
+// Profiling builds: the buffer registered by gemm_timeline_set when it holds
+// `waves` records of 8 words, else null (no recording).
+uint64_t* timeline_for(int64_t waves);
+#endif
 hipError_t launch_zero_fill(const Problem& p, hipStream_t stream);
 
 // The instantiation units of gemm_dl_kernel.h: row-major / column-major B,
@@ -78,28 +94,37 @@ hipError_t launch_dl_f8_nn_epi(int tile, int edge, const Problem& p, int group_m
 // The instantiation units of gemm_ks_kernel.h: plain / general epilogue (both B layouts).
 hipError_t launch_ks(int edge, const Problem& p, int group_m, hipStream_t stream);
 hipError_t launch_ks_epi(int edge, const Problem& p, int group_m, hipStream_t stream);
+// The persistent 256x256 kernels (16-bit inputs): row-major / column-major B,
+// plain / general epilogue.
+hipError_t launch_pk_nn(int edge, const Problem& p, int group_m, hipStream_t stream);
+hipError_t launch_pk_nn_epi(int edge, const Problem& p, int group_m, hipStream_t stream);
+hipError_t launch_pk_tn(int edge, const Problem& p, int group_m, hipStream_t stream);
+hipError_t launch_pk_tn_epi(int edge, const Problem& p, int group_m, hipStream_t stream);
 
-// Workgroup id -> output tile (tm, tn).
+// Workgroup id -> output tile (tm, tn), in two steps, both bijections of
+// [0, tilesM*tilesN).
 //
-// Step 1, XCD-aware remap: MI355X deals consecutive workgroup ids round-robin
-// over its 8 XCDs, each with its own L2.  Workgroup w (on XCD w % 8) is given
-// logical id L so that XCD x owns one contiguous range of logical ids; tiles
-// that share an L2 are then neighbours in the visit order below.
+// Step 1, XCD-aware remap (xcd_logical): MI355X deals consecutive workgroup
+// ids round-robin over its 8 XCDs, each with its own L2.  Workgroup w (on
+// XCD w % 8) is given logical id L so that XCD x owns one contiguous range of
+// logical ids, [xcd_first(x), xcd_first(x + 1)); tiles that share an L2 are
+// then neighbours in the visit order below.
 //
-// Step 2, grouped order: logical ids walk `group_m` tile-rows at a time, down
-// the column of a group before moving right, so the tiles in flight share a
-// few A row-panels and B column-panels (the grouped CTA rasterization of the
-// Ada tensor-core GEMM write-up, section "This one wasn't in the plan" on the
-// 8192^3 slowdown; and the 4x2-block example of "The Asynchronous Kernel:
-// Tensor Cores & TMA", section "Scheduling is geometry").
-//
-// Both steps are bijections of [0, tilesM*tilesN).
-__host__ __device__ inline void tile_coords(int w, int tilesM, int tilesN, int group_m,
-                                            int* tm, int* tn) {
-    const int T = tilesM * tilesN;
+// Step 2, grouped order (grouped_tile): logical ids walk `group_m` tile-rows
+// at a time, down the column of a group before moving right, so the tiles in
+// flight share a few A row-panels and B column-panels (the grouped CTA
+// rasterization of the Ada tensor-core GEMM write-up, its section on the
+// 8192^3 slowdown and the DRAM bytes each CTA order reads; and the
+// 4x2-block example of "The Asynchronous Kernel: Tensor Cores & TMA",
+// section "Scheduling is geometry").
+__host__ __device__ inline int xcd_first(int x, int T) {
     const int q = T / 8, r = T % 8;
-    const int x = w % 8, i = w / 8;
-    const int L = x * q + (x < r ? x : r) + i;
+    return x * q + (x < r ? x : r);
+}
+
+__host__ __device__ inline int xcd_logical(int w, int T) { return xcd_first(w % 8, T) + w / 8; }
+
+__host__ __device__ inline void grouped_tile(int L, int tilesM, int tilesN, int group_m, int* tm, int* tn) {
     const int per_group = group_m * tilesN;
     const int g = L / per_group;
     const int first_m = g * group_m;
@@ -108,6 +133,10 @@ __host__ __device__ inline void tile_coords(int w, int tilesM, int tilesN, int g
     const int within = L - g * per_group;
     *tm = first_m + within % gsz;
     *tn = within / gsz;
+}
+
+__host__ __device__ inline void tile_coords(int w, int tilesM, int tilesN, int group_m, int* tm, int* tn) {
+    grouped_tile(xcd_logical(w, tilesM * tilesN), tilesM, tilesN, group_m, tm, tn);
 }
 
 }  // namespace dhpt

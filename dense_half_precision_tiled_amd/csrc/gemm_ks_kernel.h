@@ -56,6 +56,9 @@ __global__ __launch_bounds__(256, 1) void gemm_ks_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
     void* __restrict__ C, int64_t ldc, int M, int N, int K, int tilesM, int tilesN, int group_m,
     EpiArgs ep) {
+#ifdef DHPT_TIMELINE
+    const TlStamp tl0 = tl_now();
+#endif
     static_assert(EDGE == dl::EDGE_NONE || EDGE == dl::EDGE_CLAMP, "edge mode");
     constexpr int BM = 128, BN = 128, BK = 64;
     constexpr int TM = 4, TN = 4;                          // 32x32 MFMA blocks: the whole tile
@@ -347,12 +350,18 @@ __global__ __launch_bounds__(256, 1) void gemm_ks_kernel(
         }
         if (r == 0) __syncthreads();                   // the slots are rewritten in round 1
     }
+#ifdef DHPT_TIMELINE
+    tl_record(ep.timeline, tl0);
+#endif
 }
 
 template <int IN, int OUT, int EDGE, bool BT, bool EPI>
 static void launch_typed(const Problem& p, int group_m, hipStream_t s) {
     const int tilesM = (p.M + 127) / 128, tilesN = (p.N + 127) / 128;
-    const EpiArgs ep{p.alpha, p.beta, p.bias, p.relu};
+    EpiArgs ep{p.alpha, p.beta, p.bias, p.relu};
+#ifdef DHPT_TIMELINE
+    ep.timeline = timeline_for((int64_t)tilesM * tilesN * 4);
+#endif
     hipLaunchKernelGGL((gemm_ks_kernel<IN, OUT, EDGE, BT, EPI>), dim3((unsigned)(tilesM * tilesN)), dim3(256), 0,
                        s, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, p.M, p.N, p.K, tilesM, tilesN, group_m, ep);
 }

@@ -1,10 +1,11 @@
 """Python binding of libdhpt_gemm.so (argument marshalling only).
 
 The functions mirror include/gemm.h one to one (``gemm_run``, ``gemm_run_ex``,
-``gemm_strerror``, ``gemm_select_instance``, ``gemm_select_instance_ex``,
-``gemm_num_instances``, ``gemm_instance_name``, ``gemm_run_instance``,
-``gemm_run_instance_ex``, ``gemm_tile_order``) and take raw device pointers as
-Python ints.  ``gemm(A, B, out_dtype)`` is the
+``gemm_run_ws``, ``gemm_workspace_size``, ``gemm_strerror``,
+``gemm_select_instance``, ``gemm_select_instance_ex``,
+``gemm_select_instance_ws``, ``gemm_num_instances``, ``gemm_instance_name``,
+``gemm_run_instance``, ``gemm_run_instance_ex``, ``gemm_run_instance_ws``,
+``gemm_tile_order``) and take raw device pointers as Python ints.  ``gemm(A, B, out_dtype)`` is the
 convenience form on torch tensors: it allocates C with ``torch.empty`` and
 passes ``data_ptr()``, the strides and the current HIP stream (gemm_run for a
 row-major B, gemm_run_ex with GEMM_B_COL_MAJOR for a column-major B).
@@ -27,12 +28,13 @@ GEMM_E5M2_F32, GEMM_E5M2_F16, GEMM_E5M2_BF16 = 7, 8, 9
 GEMM_OK = 0
 GEMM_ERR_DIM, GEMM_ERR_LD, GEMM_ERR_NULL, GEMM_ERR_DTYPE = -1, -2, -3, -4
 GEMM_ERR_ALIAS, GEMM_ERR_RANGE, GEMM_ERR_LAUNCH, GEMM_ERR_ALIGN = -5, -6, -7, -8
-GEMM_ERR_INSTANCE, GEMM_ERR_LAYOUT = -9, -10
+GEMM_ERR_INSTANCE, GEMM_ERR_LAYOUT, GEMM_ERR_WORKSPACE = -9, -10, -11
 GEMM_B_ROW_MAJOR, GEMM_B_COL_MAJOR = 0, 1
 
 EXPORTED = ["gemm_run", "gemm_run_ex", "gemm_strerror", "gemm_select_instance",
             "gemm_select_instance_ex", "gemm_num_instances", "gemm_instance_name",
-            "gemm_run_instance", "gemm_run_instance_ex", "gemm_tile_order"]
+            "gemm_run_instance", "gemm_run_instance_ex", "gemm_tile_order",
+            "gemm_workspace_size", "gemm_run_ws", "gemm_run_instance_ws", "gemm_select_instance_ws"]
 
 _lib = None
 
@@ -43,13 +45,16 @@ class GemmError(RuntimeError):
         self.status = status
 
 
-def load() -> ctypes.CDLL:
+def load(lib_path: str | None = None) -> ctypes.CDLL:
+    """Load the library once (``lib_path``: another build of it, e.g. the
+    timeline-recording profiling variant; only the first call's path counts)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError("libdhpt_gemm.so is not built (run __graft_entry__.build() or "
-                               "python -m dense_half_precision_tiled_amd.build)")
-        lib = ctypes.CDLL(LIB_PATH)
+        path = lib_path or LIB_PATH
+        if not os.path.exists(path):
+            raise RuntimeError("%s is not built (run __graft_entry__.build() or "
+                               "python -m dense_half_precision_tiled_amd.build)" % os.path.basename(path))
+        lib = ctypes.CDLL(path)
         i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         lib.gemm_run.argtypes = [i64, i64, i64, i32, vp, i64, vp, i64, vp, i64, vp]
         lib.gemm_run.restype = i32
@@ -75,6 +80,14 @@ def load() -> ctypes.CDLL:
         lib.gemm_tile_order.argtypes = [i32, i64, i64, ctypes.POINTER(ctypes.c_int32),
                                         ctypes.POINTER(ctypes.c_int32), i64]
         lib.gemm_tile_order.restype = i64
+        lib.gemm_workspace_size.argtypes = []
+        lib.gemm_workspace_size.restype = i64
+        lib.gemm_run_ws.argtypes = lib.gemm_run_ex.argtypes[:-1] + [vp, i64, vp]
+        lib.gemm_run_ws.restype = i32
+        lib.gemm_run_instance_ws.argtypes = [i32] + lib.gemm_run_ws.argtypes
+        lib.gemm_run_instance_ws.restype = i32
+        lib.gemm_select_instance_ws.argtypes = lib.gemm_select_instance_ex.argtypes + [vp, i64]
+        lib.gemm_select_instance_ws.restype = i32
         _lib = lib
     return _lib
 
@@ -107,6 +120,28 @@ def gemm_select_instance_ex(M, N, K, dtype, b_layout, A, lda, B, ldb, C, ldc, al
                             bias=None, relu=0) -> int:
     return load().gemm_select_instance_ex(M, N, K, dtype, b_layout, A, lda, B, ldb, C, ldc, alpha,
                                           beta, bias, relu)
+
+
+def gemm_workspace_size() -> int:
+    return load().gemm_workspace_size()
+
+
+def gemm_run_ws(M, N, K, dtype, b_layout, A, lda, B, ldb, C, ldc, alpha, beta, bias, relu, workspace,
+                workspace_bytes, stream=None) -> int:
+    return load().gemm_run_ws(M, N, K, dtype, b_layout, A, lda, B, ldb, C, ldc, alpha, beta, bias, relu,
+                              workspace, workspace_bytes, stream)
+
+
+def gemm_run_instance_ws(instance, M, N, K, dtype, b_layout, A, lda, B, ldb, C, ldc, alpha, beta, bias,
+                         relu, workspace, workspace_bytes, stream=None) -> int:
+    return load().gemm_run_instance_ws(instance, M, N, K, dtype, b_layout, A, lda, B, ldb, C, ldc, alpha,
+                                       beta, bias, relu, workspace, workspace_bytes, stream)
+
+
+def gemm_select_instance_ws(M, N, K, dtype, b_layout, A, lda, B, ldb, C, ldc, alpha, beta, bias, relu,
+                            workspace, workspace_bytes) -> int:
+    return load().gemm_select_instance_ws(M, N, K, dtype, b_layout, A, lda, B, ldb, C, ldc, alpha, beta,
+                                          bias, relu, workspace, workspace_bytes)
 
 
 def gemm_strerror(status: int) -> str:

@@ -63,7 +63,9 @@ enum {
     GEMM_ERR_ALIGN = -8,    /* a pointer not aligned to its element size */
     GEMM_ERR_INSTANCE = -9, /* gemm_run_instance: unknown id, or the instance
                                cannot handle this shape/alignment */
-    GEMM_ERR_LAYOUT = -10   /* gemm_run_ex: b_layout not one of gemm_layout_t */
+    GEMM_ERR_LAYOUT = -10,  /* gemm_run_ex: b_layout not one of gemm_layout_t */
+    GEMM_ERR_WORKSPACE = -11 /* gemm_run_ws: workspace null, smaller than
+                                gemm_workspace_size() or not 256-byte aligned */
 };
 
 /* Storage order of B for gemm_run_ex (A and C are always row-major). */
@@ -150,14 +152,57 @@ int gemm_run_ex(int64_t M, int64_t N, int64_t K, int dtype, int b_layout,
                 void* C, int64_t ldc, float alpha, float beta,
                 const float* bias, int relu, void* stream);
 
+/*
+ * gemm_workspace_size -- bytes of device workspace gemm_run_ws uses (a
+ * constant of the library, 4096).
+ *
+ * gemm_run_ws -- gemm_run_ex with a caller-owned workspace, which lets the
+ * library schedule the output tiles dynamically: with at least two 256x256
+ * tiles per compute unit (16-bit inputs), it launches one workgroup per CU
+ * and each takes tiles from shared counters until none is left, first from
+ * the queue of the XCD it runs on (the tiles the one-workgroup-per-tile
+ * launch deals to that XCD, in the same L2-friendly order), then from the
+ * other XCDs' queues -- the persistent kernel of "The Asynchronous Kernel:
+ * Tensor Cores & TMA", section "Keeping the line busy", which removes the
+ * tail left by XCDs running at different clocks.  Other shapes run exactly
+ * as gemm_run_ex would.  The result is bit for bit that of gemm_run_ex (the
+ * same per-tile arithmetic; only the order in which tiles are visited
+ * changes).
+ *
+ *   workspace        device pointer, 256-byte aligned, at least
+ *                    gemm_workspace_size() bytes, on the current device.  It
+ *                    must hold zeros before its first use (e.g. hipMemset
+ *                    once after allocation); every call leaves it zeroed when
+ *                    its kernel has finished.  The caller owns it.  Calls
+ *                    that may run at the same time (different streams, or a
+ *                    graph replayed concurrently) must use different
+ *                    workspaces; calls ordered on one stream may share one.
+ *                    It must not overlap A, B, C or the bias (GEMM_ERR_ALIAS).
+ *   workspace_bytes  its size in bytes.
+ *
+ * Other arguments, ownership and status codes as gemm_run_ex, plus
+ * GEMM_ERR_WORKSPACE.  No allocation, no host synchronisation; the first call
+ * on a device queries that device's compute-unit count (kept for later
+ * calls).
+ */
+int64_t gemm_workspace_size(void);
+
+int gemm_run_ws(int64_t M, int64_t N, int64_t K, int dtype, int b_layout,
+                const void* A, int64_t lda, const void* B, int64_t ldb,
+                void* C, int64_t ldc, float alpha, float beta,
+                const float* bias, int relu, void* workspace,
+                int64_t workspace_bytes, void* stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* gemm_strerror(int status);
 
 /*
  * Kernel instances.  Each instance is one compiled kernel configuration; all
- * compute the same function.  Three families: "dl_*" (the waves of a
+ * compute the same function.  Four families: "dl_*" (the waves of a
  * workgroup split its output tile; instances of this family give identical
- * bits), "ks_*" (the four waves split K over a 128x128 tile and their partial
+ * bits), "pk_*" (the dl kernel's tiles taken from per-XCD queues by one
+ * persistent workgroup per CU; gemm_run_ws only; bits identical to "dl_*"),
+ * "ks_*" (the four waves split K over a 128x128 tile and their partial
  * sums are added in a fixed order, so repeated calls give identical bits; the
  * rounding differs from the dl family within the accuracy bound), and
  * "dl8_*" (the dl kernel for 8-bit inputs, which run only there; identical
@@ -181,6 +226,15 @@ int gemm_select_instance_ex(int64_t M, int64_t N, int64_t K, int dtype, int b_la
                             const void* C, int64_t ldc, float alpha, float beta,
                             const float* bias, int relu);
 
+/* gemm_select_instance_ex for the arguments of gemm_run_ws (the workspace
+ * is inspected for size, alignment and overlap only; the current device's
+ * compute-unit count is queried). */
+int gemm_select_instance_ws(int64_t M, int64_t N, int64_t K, int dtype, int b_layout,
+                            const void* A, int64_t lda, const void* B, int64_t ldb,
+                            const void* C, int64_t ldc, float alpha, float beta,
+                            const float* bias, int relu, const void* workspace,
+                            int64_t workspace_bytes);
+
 /* Number of instance ids (0 .. gemm_num_instances()-1). */
 int gemm_num_instances(void);
 
@@ -197,6 +251,14 @@ const char* gemm_instance_name(int instance);
 int gemm_run_instance(int instance, int64_t M, int64_t N, int64_t K, int dtype,
                       const void* A, int64_t lda, const void* B, int64_t ldb,
                       void* C, int64_t ldc, void* stream);
+
+/* gemm_run_ws with the instance forced; the persistent "pk_*" instances run
+ * only here (they need the workspace), on any shape their edge mode takes. */
+int gemm_run_instance_ws(int instance, int64_t M, int64_t N, int64_t K, int dtype,
+                         int b_layout, const void* A, int64_t lda, const void* B,
+                         int64_t ldb, void* C, int64_t ldc, float alpha, float beta,
+                         const float* bias, int relu, void* workspace,
+                         int64_t workspace_bytes, void* stream);
 
 /* gemm_run_ex with the instance forced; GEMM_ERR_INSTANCE as gemm_run_instance
  * (the prefetch-distance-1 instances run only the plain row-major form). */

@@ -50,7 +50,7 @@ def encode_out(values, out_fmt):
 
 
 def run(G, A, B, code, lda=None, ldb=None, ldc=None, a_off=0, instance=None, stream=None,
-        expect=0, layout=None, alpha=1.0, beta=0.0, bias=None, relu=0, c_init=None, c_off=0):
+        expect=0, layout=None, alpha=1.0, beta=0.0, bias=None, relu=0, c_init=None, c_off=0, ws=None):
     """C = A.B (or the general form) on the GPU; returns the decoded M x N result.
 
     B is the operand as stored: K x N for row-major, N x K for column-major
@@ -59,6 +59,8 @@ def run(G, A, B, code, lda=None, ldb=None, ldc=None, a_off=0, instance=None, str
     c_init: M x N output-format bit patterns written into C before the call
     (default: poison).  bias: N float64 values or None.  c_off: C starts that
     many elements past the guard band (an odd c_off leaves a 2-byte-aligned C).
+    ws: a device tensor used as the workspace of gemm_run_ws /
+    gemm_run_instance_ws (the call then goes through those).
     Checks that the row padding of C and guard bands around it keep their
     poison."""
     M, K = A.shape
@@ -83,7 +85,15 @@ def run(G, A, B, code, lda=None, ldb=None, ldc=None, a_off=0, instance=None, str
         tbias = torch.tensor(np.asarray(bias, dtype=np.float32), device="cuda")
         pbias = tbias.data_ptr()
     s = stream.cuda_stream if stream is not None else torch.cuda.current_stream().cuda_stream
-    if layout is None:
+    if ws is not None:
+        lay = G.GEMM_B_ROW_MAJOR if layout is None else layout
+        wsa = (ws.data_ptr(), ws.numel() * ws.element_size(), s)
+        ex = (alpha, beta, pbias, relu)
+        if instance is None:
+            st = G.gemm_run_ws(M, N, K, code, lay, pA, lda, pB, ldb, pC, ldc, *ex, *wsa)
+        else:
+            st = G.gemm_run_instance_ws(instance, M, N, K, code, lay, pA, lda, pB, ldb, pC, ldc, *ex, *wsa)
+    elif layout is None:
         if instance is None:
             st = G.gemm_run(M, N, K, code, pA, lda, pB, ldb, pC, ldc, s)
         else:

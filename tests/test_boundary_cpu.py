@@ -95,7 +95,7 @@ def test_unknown_instance(lib):
     assert G.gemm_run_instance(n, 4, 4, 4, 0, PA, 4, PB, 4, PC, 4, None) == G.GEMM_ERR_INSTANCE
     assert G.gemm_instance_name(n) == "?"
     for i in range(n):
-        assert G.gemm_instance_name(i).startswith(("dl_", "ks_", "dl8_"))
+        assert G.gemm_instance_name(i).startswith(("dl_", "ks_", "dl8_", "pk_"))
 
 
 def _pick(M, N, K, dtype=3, lda=None, ldb=None, ldc=None, pa=PA, pb=PB):
@@ -299,3 +299,48 @@ def test_tile_order_keeps_each_xcd_compact(lib, n):
         panels = _panels(tm[sel], tn[sel])
         row_major = np.unique(sel // tiles_n).size + np.unique(sel % tiles_n).size
         assert panels <= 12 and panels <= row_major, (x, panels, row_major)
+
+
+# ------------------------------------------------------------ workspace entry points
+WS = 0x5000000000          # a fake, 256-byte-aligned device address (never touched)
+
+
+def ws_call(*args, ws=WS, nbytes=None):
+    nb = G.gemm_workspace_size() if nbytes is None else nbytes
+    return G.gemm_run_ws(*args, ws, nb, None)
+
+
+def test_workspace_size_is_a_small_constant(lib):
+    assert G.gemm_workspace_size() == 4096
+
+
+@pytest.mark.parametrize("ws,nbytes", [(0, 4096), (WS, 4095), (WS, 0), (WS + 4, 4096), (WS + 128, 8192)])
+def test_bad_workspace_rejected_before_launch(lib, ws, nbytes):
+    args = (512, 512, 512, 3, 0, PA, 512, PB, 512, PC, 512, 1.0, 0.0, None, 0)
+    assert ws_call(*args, ws=ws, nbytes=nbytes) == G.GEMM_ERR_WORKSPACE
+    assert G.gemm_run_instance_ws(22, *args, ws, nbytes, None) == G.GEMM_ERR_WORKSPACE
+    assert G.gemm_select_instance_ws(*args, ws, nbytes) == G.GEMM_ERR_WORKSPACE
+
+
+def test_workspace_must_not_overlap_the_operands(lib):
+    M, N, K = 64, 64, 64
+    base = (M, N, K, 2, 0)
+    # inside C, inside A, inside B, inside the bias
+    assert ws_call(*base, PA, K, PB, N, PC, N, 1.0, 0.0, None, 0, ws=PC + 256) == G.GEMM_ERR_ALIAS
+    assert ws_call(*base, PA, K, PB, N, PC, N, 1.0, 0.0, None, 0, ws=PA) == G.GEMM_ERR_ALIAS
+    assert ws_call(*base, PA, K, PB, N, PC, N, 1.0, 0.0, None, 0, ws=PB + 1024) == G.GEMM_ERR_ALIAS
+    bias = WS + 1024
+    assert ws_call(*base, PA, K, PB, N, PC, N, 1.0, 0.0, bias, 0, ws=WS) == G.GEMM_ERR_ALIAS
+    # the other argument checks still come first
+    assert ws_call(-1, N, K, 2, 0, PA, K, PB, N, PC, N, 1.0, 0.0, None, 0) == G.GEMM_ERR_DIM
+    assert ws_call(M, N, K, 2, 5, PA, K, PB, N, PC, N, 1.0, 0.0, None, 0) == G.GEMM_ERR_LAYOUT
+
+
+def test_persistent_instances_need_a_workspace(lib):
+    ids = {G.gemm_instance_name(i): i for i in range(G.gemm_num_instances())}
+    for name in ("pk_256x256x64", "pk_256x256x64_clamp"):
+        st = G.gemm_run_instance(ids[name], 512, 512, 512, 3, PA, 512, PB, 512, PC, 512, None)
+        assert st == G.GEMM_ERR_INSTANCE
+        st = G.gemm_run_instance_ex(ids[name], 512, 512, 512, 3, 1, PA, 512, PB, 512, PC, 512,
+                                    1.0, 0.0, None, 0, None)
+        assert st == G.GEMM_ERR_INSTANCE

@@ -27,7 +27,8 @@ from dense_half_precision_tiled_amd import build as B
 
 UNITS = ["gemm_dl_nn.hip", "gemm_dl_nn_epi.hip", "gemm_dl_tn.hip", "gemm_dl_tn_epi.hip",
          "gemm_ks.hip", "gemm_ks_epi.hip", "gemm_dl_f8_tn.hip", "gemm_dl_f8_tn_epi.hip",
-         "gemm_dl_f8_nn.hip", "gemm_dl_f8_nn_epi.hip"]
+         "gemm_dl_f8_nn.hip", "gemm_dl_f8_nn_epi.hip",
+         "gemm_pk_nn.hip", "gemm_pk_nn_epi.hip", "gemm_pk_tn.hip", "gemm_pk_tn_epi.hip"]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(B.hipcc()), reason="hipcc not available")
 
@@ -52,7 +53,7 @@ def kernels():
             text = open(path).read().split("\n")
             cur = None
             for ln in text:
-                m = re.match(r"^(_ZN4dhpt\S*gemm_\w\w_kernel\S*):", ln)
+                m = re.match(r"^(_ZN4dhpt\S*gemm_\w\w(?:_persist)?_kernel\S*):", ln)
                 if m:
                     cur = m.group(1)
                     res[cur] = (unit, [], {})
@@ -63,7 +64,7 @@ def kernels():
                     s = ln.split(";")[0].strip()
                     if s:
                         res[cur][1].append(s)
-                m = re.match(r"^\s*\.set\s+(_ZN4dhpt\S*gemm_\w\w_kernel\S*)\.(\w+),\s*(\d+)", ln)
+                m = re.match(r"^\s*\.set\s+(_ZN4dhpt\S*gemm_\w\w(?:_persist)?_kernel\S*)\.(\w+),\s*(\d+)", ln)
                 if m and m.group(1) in res:
                     res[m.group(1)][2][m.group(2)] = int(m.group(3))
         return res
@@ -81,23 +82,51 @@ def test_every_unit_has_kernels(kernels):
     assert len(kernels) >= 100
 
 
+def _slice_loop(ins):
+    """The K loop of a persistent kernel: the shortest backward branch whose
+    body holds MFMAs and exactly one barrier (the per-slice barrier)."""
+    labels = {s[:-1]: i for i, s in enumerate(ins) if s.endswith(":")}
+    best = None
+    for j, s in enumerate(ins):
+        m = re.match(r"s_(?:cbranch_\w+|branch) (\.LBB\S+)", s)
+        i = labels.get(m.group(1)) if m else None
+        if i is not None and i < j:
+            body = ins[i:j]
+            if any(x.startswith("v_mfma") for x in body) and sum(x.startswith("s_barrier") for x in body) == 1:
+                if best is None or j - i < best[1] - best[0]:
+                    best = (i, j)
+    return best
+
+
 def test_no_scratch_inside_the_mfma_loop(kernels):
+    """One-tile kernels: no scratch access between the first and the last
+    MFMA.  Persistent kernels run many tiles, so there the slice loop itself
+    must be free of scratch, and what they spill (once per tile, in the tile's
+    set-up and epilogue) stays below 96 bytes."""
     for name, (unit, ins, meta) in kernels.items():
         mf = [i for i, s in enumerate(ins) if s.startswith("v_mfma_f32_")]
         assert mf, name
-        inside = [ins[i] for i in range(mf[0], mf[-1]) if ins[i].startswith("scratch_")]
+        if "persist" in name:
+            a, b = _slice_loop(ins)
+            assert sum(ins[i].startswith("v_mfma") for i in range(a, b)) == 64, _short(name)
+            lo, hi = a, b
+            assert meta.get("private_seg_size", 0) <= 96, "%s spills %d bytes" % (
+                _short(name), meta["private_seg_size"])
+        else:
+            lo, hi = mf[0], mf[-1]
+        inside = [ins[i] for i in range(lo, hi) if ins[i].startswith("scratch_")]
         assert not inside, "%s (%s): %d scratch accesses between MFMAs, e.g. %s" % (
             _short(name), unit, len(inside), inside[0])
 
 
 def test_whole_tile_plain_kernels_use_no_scratch(kernels):
-    # template arguments <IN, OUT, BM, BN, FD, EDGE=0, BT, EPI=false> (dl) and
-    # <IN, OUT, EDGE=0, BT, EPI=false> (ks)
+    # template arguments <IN, OUT, BM, BN, FD, EDGE=0, BT, EPI=false> (dl and
+    # its persistent form) and <IN, OUT, EDGE=0, BT, EPI=false> (ks)
     checked = 0
     for name, (unit, ins, meta) in kernels.items():
         args = re.findall(r"Li(\d+)E|Lb(\d)E", _short(name))
         vals = [int(a or b) for a, b in args]
-        edge, epi = (vals[5], vals[7]) if "gemm_dl_kernel" in name else (vals[2], vals[4])
+        edge, epi = (vals[5], vals[7]) if "gemm_dl" in name else (vals[2], vals[4])
         if edge == 0 and epi == 0:
             assert meta.get("private_seg_size", 0) == 0, "%s uses %d bytes of scratch" % (
                 _short(name), meta["private_seg_size"])
@@ -137,3 +166,21 @@ def test_register_budget_and_mfma_shape(kernels):
             assert ops == {"v_mfma_f32_32x32x64_f8f6f4"}, (_short(name), ops)
         else:
             assert ops <= {"v_mfma_f32_32x32x16_f16", "v_mfma_f32_32x32x16_bf16"}, (_short(name), ops)
+
+
+def test_no_scalar_memory_writes(kernels):
+    """No kernel writes memory through the scalar data cache (scalar stores,
+    scalar atomics, its write-back): counters and outputs go through vector
+    memory instructions only."""
+    for name, (unit, ins, meta) in kernels.items():
+        bad = [s for s in ins if re.match(r"s_(store|buffer_store|atomic|buffer_atomic|dcache_wb)", s)]
+        assert not bad, "%s: %s" % (_short(name), bad[0])
+
+
+def test_persistent_kernels_pull_tiles_with_vector_atomics(kernels):
+    pk = [n for n in kernels if "persist" in n]
+    assert len(pk) == 32
+    for name in pk:
+        ins = kernels[name][1]
+        assert any(s.startswith("global_atomic_add") for s in ins), _short(name)
+        assert any(s.startswith("s_getreg_b32") and "HW_REG_XCC_ID" in s for s in ins), _short(name)
