@@ -132,8 +132,10 @@ def assert_exact(y, r, out_fmt, what=""):
 
 
 def instances16(G):
-    """Ids of the instances that run 16-bit inputs (all but the dl8_* ones)."""
-    return [i for i in range(G.gemm_num_instances()) if not G.gemm_instance_name(i).startswith("dl8_")]
+    """Ids of the instances that run 16-bit inputs without a workspace (all but
+    the dl8_* ones and the persistent pk_* ones, which need gemm_run_ws)."""
+    return [i for i in range(G.gemm_num_instances())
+            if not G.gemm_instance_name(i).startswith(("dl8_", "pk_"))]
 
 
 def law_for(fmt):

@@ -81,10 +81,14 @@ def test_random_sweep(G):
                                          1 << 40, c["ldc"], c["alpha"], c["beta"], None, c["relu"]) >= 0
         desc = "case %d %s" % (case, c)
         print(desc, flush=True)
+        # a persistent instance runs through gemm_run_instance_ws with a fresh workspace
+        ws = None
+        if c["inst"] is not None and G.gemm_instance_name(c["inst"]).startswith("pk_"):
+            ws = torch.zeros(G.gemm_workspace_size() // 4, dtype=torch.int32, device="cuda")
         try:
             y = run(G, A, Bs, code, lda=c["lda"], ldb=c["ldb"], ldc=c["ldc"], a_off=c["a_off"],
                     instance=c["inst"], layout=layout, alpha=c["alpha"], beta=c["beta"], bias=bias,
-                    relu=c["relu"], c_init=cbits, expect=expect)
+                    relu=c["relu"], c_init=cbits, expect=expect, ws=ws)
         except AssertionError as e:
             # a forced instance that cannot run the shape refuses it before any launch
             if c["inst"] is not None and "cannot run this shape" in str(e):
