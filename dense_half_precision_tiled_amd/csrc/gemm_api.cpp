@@ -219,6 +219,45 @@ Extra extra(int b_layout, float alpha, float beta, const float* bias, int relu, 
     return x;
 }
 
+// ---------------------------------------------------------------------------
+// The allocation-free entry point's scratch (gemm_run_noalloc): the
+// persistent kernels' scheduler words in a file-scope device array instead of
+// a caller's workspace.  Each device that runs the library holds its own copy
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not the device address: the address is taken once per device with
+// hipGetSymbolAddress, with that device current, and only that address is
+// passed to kernels.
+constexpr int64_t kScratchBytes = 4096;
+static_assert(dhpt::kWorkspaceBytes <= kScratchBytes, "the static scratch holds the persistent kernels' words");
+__device__ __attribute__((aligned(256))) static uint32_t scratch[kScratchBytes / 4];
+
+// Zero n words of the scratch (a kernel rather than hipMemsetAsync, so that
+// the call can be captured in a HIP graph and replayed).
+__global__ void scratch_clear_kernel(uint32_t* p, int n) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+
+// The device address of this device's scratch, looked up on the first call
+// on the device and kept (each device has its own copy of the array at its
+// own address).
+int device_scratch(void** out) {
+    static void* ptrs[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GEMM_ERR_LAUNCH;
+    if (ptrs[dev] == nullptr) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+            (void)hipGetLastError();
+            return GEMM_ERR_LAUNCH;
+        }
+        ptrs[dev] = ptr;
+    }
+    *out = ptrs[dev];
+    return GEMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -287,6 +326,40 @@ int gemm_select_instance_ws(int64_t M, int64_t N, int64_t K, int dtype, int b_la
     if (workspace == nullptr) return GEMM_ERR_WORKSPACE;
     return select_any(M, N, K, dtype, A, lda, B, ldb, C, ldc,
                       extra(b_layout, alpha, beta, bias, relu, const_cast<void*>(workspace), workspace_bytes));
+}
+
+int gemm_run_noalloc(int64_t M, int64_t N, int64_t K, int dtype, int b_layout, const void* A, int64_t lda,
+                     const void* B, int64_t ldb, void* C, int64_t ldc, float alpha, float beta,
+                     const float* bias, int relu, void* stream) {
+    Problem p;
+    bool noop;
+    // validate first against a stand-in workspace address: the arguments,
+    // not the scratch, decide whether the call is valid
+    Extra x = extra(b_layout, alpha, beta, bias, relu);
+    int st = validate(M, N, K, dtype, A, lda, B, ldb, C, ldc, x, &p, &noop);
+    if (st != GEMM_OK || noop) return st;
+    void* scratch_ptr = nullptr;
+    st = device_scratch(&scratch_ptr);
+    if (st != GEMM_OK) return st;
+    x.ws = scratch_ptr;
+    x.ws_bytes = kScratchBytes;
+    st = validate(M, N, K, dtype, A, lda, B, ldb, C, ldc, x, &p, &noop);
+    if (st != GEMM_OK) return st;
+    p.workers = device_cus();
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p.K == 0 && !p.epi) return run_validated(-1, p, s);
+    const int inst = choose_instance(p);
+    if (dhpt::kInstances[inst].kind == dhpt::KIND_PK) {
+        if (dhpt::kWorkspaceBytes > kScratchBytes) return GEMM_ERR_WORKSPACE;
+        // every call on this device shares the array: clear the scheduler
+        // words (a fill kernel, not a memset, so that a captured graph
+        // replays it correctly)
+        (void)hipGetLastError();
+        hipLaunchKernelGGL(scratch_clear_kernel, dim3(1), dim3(256), 0, s, static_cast<uint32_t*>(scratch_ptr),
+                           (int)(dhpt::kWorkspaceBytes / 4));
+        if (hipGetLastError() != hipSuccess) return GEMM_ERR_LAUNCH;
+    }
+    return run_validated(inst, p, s);
 }
 
 int gemm_num_instances(void) { return dhpt::kNumInstances; }

@@ -1,7 +1,7 @@
 """Python binding of libdhpt_gemm.so (argument marshalling only).
 
 The functions mirror include/gemm.h one to one (``gemm_run``, ``gemm_run_ex``,
-``gemm_run_ws``, ``gemm_workspace_size``, ``gemm_strerror``,
+``gemm_run_ws``, ``gemm_run_noalloc``, ``gemm_workspace_size``, ``gemm_strerror``,
 ``gemm_select_instance``, ``gemm_select_instance_ex``,
 ``gemm_select_instance_ws``, ``gemm_num_instances``, ``gemm_instance_name``,
 ``gemm_run_instance``, ``gemm_run_instance_ex``, ``gemm_run_instance_ws``,
@@ -34,7 +34,8 @@ GEMM_B_ROW_MAJOR, GEMM_B_COL_MAJOR = 0, 1
 EXPORTED = ["gemm_run", "gemm_run_ex", "gemm_strerror", "gemm_select_instance",
             "gemm_select_instance_ex", "gemm_num_instances", "gemm_instance_name",
             "gemm_run_instance", "gemm_run_instance_ex", "gemm_tile_order",
-            "gemm_workspace_size", "gemm_run_ws", "gemm_run_instance_ws", "gemm_select_instance_ws"]
+            "gemm_workspace_size", "gemm_run_ws", "gemm_run_instance_ws", "gemm_select_instance_ws",
+            "gemm_run_noalloc"]
 
 _lib = None
 
@@ -88,6 +89,8 @@ def load(lib_path: str | None = None) -> ctypes.CDLL:
         lib.gemm_run_instance_ws.restype = i32
         lib.gemm_select_instance_ws.argtypes = lib.gemm_select_instance_ex.argtypes + [vp, i64]
         lib.gemm_select_instance_ws.restype = i32
+        lib.gemm_run_noalloc.argtypes = lib.gemm_run_ex.argtypes
+        lib.gemm_run_noalloc.restype = i32
         _lib = lib
     return _lib
 
@@ -142,6 +145,12 @@ def gemm_select_instance_ws(M, N, K, dtype, b_layout, A, lda, B, ldb, C, ldc, al
                             workspace, workspace_bytes) -> int:
     return load().gemm_select_instance_ws(M, N, K, dtype, b_layout, A, lda, B, ldb, C, ldc, alpha, beta,
                                           bias, relu, workspace, workspace_bytes)
+
+
+def gemm_run_noalloc(M, N, K, dtype, b_layout, A, lda, B, ldb, C, ldc, alpha=1.0, beta=0.0, bias=None,
+                     relu=0, stream=None) -> int:
+    return load().gemm_run_noalloc(M, N, K, dtype, b_layout, A, lda, B, ldb, C, ldc, alpha, beta, bias, relu,
+                                   stream)
 
 
 def gemm_strerror(status: int) -> str:

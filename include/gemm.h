@@ -193,6 +193,30 @@ int gemm_run_ws(int64_t M, int64_t N, int64_t K, int dtype, int b_layout,
                 const float* bias, int relu, void* workspace,
                 int64_t workspace_bytes, void* stream);
 
+/*
+ * gemm_run_noalloc -- gemm_run_ws for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation, bit for bit, with the persistent
+ * kernels' scheduler words kept in a 4 KiB array of the library's own device
+ * memory instead of a caller's workspace.  It calls no hipMalloc, hipFree or
+ * other allocating routine.
+ *
+ * Limit and sharing: the array (4096 bytes, the most the scheduler uses; a
+ * call needing more would be refused with GEMM_ERR_WORKSPACE) exists once
+ * per device, for the life of the process, and every call on that device
+ * uses it.  Calls that overlap in time on one device (different streams,
+ * concurrent graph replays) race on it and must not be issued; calls ordered
+ * on one stream are safe.  When the persistent kernel is selected, a small
+ * kernel first clears the array on `stream`.
+ *
+ * Arguments, ownership and status codes as gemm_run_ex; GEMM_ERR_LAUNCH also
+ * when the array's device address cannot be obtained.
+ */
+int gemm_run_noalloc(int64_t M, int64_t N, int64_t K, int dtype, int b_layout,
+                     const void* A, int64_t lda, const void* B, int64_t ldb,
+                     void* C, int64_t ldc, float alpha, float beta,
+                     const float* bias, int relu, void* stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* gemm_strerror(int status);
 
