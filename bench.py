@@ -541,14 +541,15 @@ def timeline_summary(rec):
                         for x, v in sorted(per_xcd.items())}}
 
 
-def timeline(G, torch, name: str, launches: int, warmup: int, settle_ms: float, entry: str = "run") -> int:
+def timeline(G, torch, name: str, launches: int, warmup: int, settle_ms: float, entry: str = "run",
+             instance=None) -> int:
     """Per-workgroup timeline of `launches` launches of one workload, from the
     profiling build of the library (libdhpt_gemm_timeline.so, which records
     for every wave its start and end on the 100 MHz real-time counter and on
     the shader clock, and the XCC and CU it ran on).  Prints, per launch, the kernel span, the end times
     of each XCD's first and last workgroups, workgroup durations, and the
     share of CU time spent outside workgroups."""
-    res = measure(G, torch, name, 1, warmup, None, None, settle_ms, entry)
+    res = measure(G, torch, name, 1, warmup, instance, None, settle_ms, entry)
     buf = torch.zeros(TIMELINE_WAVES * 8, dtype=torch.int64, device="cuda")
     lib = G.load()
     lib.gemm_timeline_set(ctypes.c_void_p(buf.data_ptr()), TIMELINE_WAVES)
@@ -736,7 +737,8 @@ def main(argv=None):
         from dense_half_precision_tiled_amd import build as B
         lib = G.load(B.TIMELINE_LIB)
         lib.gemm_timeline_set.argtypes = [ctypes.c_void_p, ctypes.c_int64]
-        return timeline(G, torch, args.workload, args.timeline, args.warmup, args.settle_ms, args.entry)
+        return timeline(G, torch, args.workload, args.timeline, args.warmup, args.settle_ms, args.entry,
+                        args.instance)
     G.load()
     if args.loop_seconds > 0:
         return loop_for(G, torch, args.workload, args.loop_seconds)

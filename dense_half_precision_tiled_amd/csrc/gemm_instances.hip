@@ -43,6 +43,11 @@ const InstanceInfo kInstances[] = {
     // caller's workspace (gemm_run_ws)
     {"pk_256x256x64", 256, 2, EDGE_NONE, 4, KIND_PK},
     {"pk_256x256x64_clamp", 256, 2, EDGE_CLAMP, 4, KIND_PK},
+    // ping-pong: two groups of four waves alternating multiplies and data
+    // movement (whole 256x256 tiles); `fd` holds the k-steps per phase
+    // (half a slice, or a whole slice)
+    {"pp_256x256x64", 256, 2, EDGE_NONE, 4, KIND_PP},
+    {"pp_256x256x64_ph4", 256, 4, EDGE_NONE, 4, KIND_PP},
 };
 const int kNumInstances = sizeof(kInstances) / sizeof(kInstances[0]);
 
@@ -93,6 +98,7 @@ hipError_t launch_instance(int id, const Problem& p, hipStream_t s) {
     }
     if (in.kind == KIND_KS)
         return p.epi ? launch_ks_epi(in.edge, p, in.group_m, s) : launch_ks(in.edge, p, in.group_m, s);
+    if (in.kind == KIND_PP) return launch_pp(in.fd, p, in.group_m, s);
     if (in.kind == KIND_PK) {
         if (p.transB)
             return p.epi ? launch_pk_tn_epi(in.edge, p, in.group_m, s) : launch_pk_tn(in.edge, p, in.group_m, s);

@@ -46,6 +46,7 @@ enum KernelKind {
     KIND_KS = 1,               // gemm_ks_kernel.h: waves split K, 128x128 tile, LDS reduction
     KIND_PK = 2,               // gemm_dl_kernel.h, persistent: one workgroup per CU, tiles from
                                // per-XCD atomic queues (needs the workspace of gemm_run_ws)
+    KIND_PP = 3,               // gemm_pp_kernel.h: 8 waves in two groups taking turns (ping-pong)
 };
 
 // Bytes of workspace the persistent kernels use (their scheduler words).
@@ -57,7 +58,8 @@ constexpr int64_t kWorkspaceBytes = 4096;
 struct InstanceInfo {
     const char* name;
     int tile;                  // square workgroup tile: 256 or 128 (k-slice 64)
-    int fd;                    // fragment prefetch distance in k-steps (KIND_DL): 1 or 2
+    int fd;                    // fragment prefetch distance in k-steps (KIND_DL): 1 or 2;
+                               // KIND_PP: k-steps per phase (2 or 4)
     int edge;                  // EdgeMode
     int group_m;               // tile-rows per group of the visit order
     int kind;                  // KernelKind
@@ -100,6 +102,9 @@ hipError_t launch_pk_nn(int edge, const Problem& p, int group_m, hipStream_t str
 hipError_t launch_pk_nn_epi(int edge, const Problem& p, int group_m, hipStream_t stream);
 hipError_t launch_pk_tn(int edge, const Problem& p, int group_m, hipStream_t stream);
 hipError_t launch_pk_tn_epi(int edge, const Problem& p, int group_m, hipStream_t stream);
+// The ping-pong 256x256 kernel (16-bit inputs, whole tiles, both B layouts),
+// `ph` k-steps per phase (2 or 4).
+hipError_t launch_pp(int ph, const Problem& p, int group_m, hipStream_t stream);
 
 // Workgroup id -> output tile (tm, tn), in two steps, both bijections of
 // [0, tilesM*tilesN).

@@ -138,5 +138,14 @@ def instances16(G):
             if not G.gemm_instance_name(i).startswith(("dl8_", "pk_"))]
 
 
+def family(name):
+    """Kernel family of an instance name: instances of one family do the same
+    per-element arithmetic in the same order (dl and its persistent form pk
+    are one family; pp splits the 256x256 tile among 8 waves but keeps the
+    per-element k order of dl)."""
+    f = name.split("_")[0]
+    return "dl" if f in ("pk", "pp") else f
+
+
 def law_for(fmt):
     return inputs.uniform if fmt == "f16" else inputs.normal

@@ -95,7 +95,7 @@ def test_unknown_instance(lib):
     assert G.gemm_run_instance(n, 4, 4, 4, 0, PA, 4, PB, 4, PC, 4, None) == G.GEMM_ERR_INSTANCE
     assert G.gemm_instance_name(n) == "?"
     for i in range(n):
-        assert G.gemm_instance_name(i).startswith(("dl_", "ks_", "dl8_", "pk_"))
+        assert G.gemm_instance_name(i).startswith(("dl_", "ks_", "dl8_", "pk_", "pp_"))
 
 
 def _pick(M, N, K, dtype=3, lda=None, ldb=None, ldc=None, pa=PA, pb=PB):

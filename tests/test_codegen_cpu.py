@@ -28,7 +28,7 @@ from dense_half_precision_tiled_amd import build as B
 UNITS = ["gemm_dl_nn.hip", "gemm_dl_nn_epi.hip", "gemm_dl_tn.hip", "gemm_dl_tn_epi.hip",
          "gemm_ks.hip", "gemm_ks_epi.hip", "gemm_dl_f8_tn.hip", "gemm_dl_f8_tn_epi.hip",
          "gemm_dl_f8_nn.hip", "gemm_dl_f8_nn_epi.hip",
-         "gemm_pk_nn.hip", "gemm_pk_nn_epi.hip", "gemm_pk_tn.hip", "gemm_pk_tn_epi.hip"]
+         "gemm_pk_nn.hip", "gemm_pk_nn_epi.hip", "gemm_pk_tn.hip", "gemm_pk_tn_epi.hip", "gemm_pp.hip"]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(B.hipcc()), reason="hipcc not available")
 
@@ -121,12 +121,18 @@ def test_no_scratch_inside_the_mfma_loop(kernels):
 
 def test_whole_tile_plain_kernels_use_no_scratch(kernels):
     # template arguments <IN, OUT, BM, BN, FD, EDGE=0, BT, EPI=false> (dl and
-    # its persistent form) and <IN, OUT, EDGE=0, BT, EPI=false> (ks)
+    # its persistent form), <IN, OUT, EDGE=0, BT, EPI=false> (ks) and
+    # <IN, OUT, BT, EPI=false> (pp)
     checked = 0
     for name, (unit, ins, meta) in kernels.items():
         args = re.findall(r"Li(\d+)E|Lb(\d)E", _short(name))
         vals = [int(a or b) for a, b in args]
-        edge, epi = (vals[5], vals[7]) if "gemm_dl" in name else (vals[2], vals[4])
+        if "gemm_dl" in name:
+            edge, epi = vals[5], vals[7]
+        elif "gemm_pp" in name:                 # <IN, OUT, BT, EPI>: whole tiles only
+            edge, epi = 0, vals[3]
+        else:
+            edge, epi = vals[2], vals[4]
         if edge == 0 and epi == 0:
             assert meta.get("private_seg_size", 0) == 0, "%s uses %d bytes of scratch" % (
                 _short(name), meta["private_seg_size"])
@@ -160,7 +166,9 @@ def test_copies_use_a_scalar_base(kernels):
 
 def test_register_budget_and_mfma_shape(kernels):
     for name, (unit, ins, meta) in kernels.items():
-        assert meta["num_vgpr"] + meta["num_agpr"] <= 512, _short(name)
+        # one wave per SIMD (512 registers), or two for the 8-wave ping-pong kernel
+        budget = 256 if "gemm_pp" in name else 512
+        assert meta["num_vgpr"] + meta["num_agpr"] <= budget, _short(name)
         ops = {s.split()[0] for s in ins if s.startswith("v_mfma")}
         if unit.startswith("gemm_dl_f8"):
             assert ops == {"v_mfma_f32_32x32x64_f8f6f4"}, (_short(name), ops)

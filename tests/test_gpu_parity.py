@@ -23,7 +23,7 @@ from dense_half_precision_tiled_amd import inputs
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-from tests.gpu_helpers import DTYPES, assert_bound, assert_exact, instances16, law_for, run  # noqa: E402
+from tests.gpu_helpers import DTYPES, assert_bound, assert_exact, family, instances16, law_for, run  # noqa: E402
 
 
 @pytest.fixture(scope="module")
@@ -163,7 +163,7 @@ def test_instances_agree_bitwise(G):
             name = G.gemm_instance_name(i)
             print("instance", name, code, flush=True)
             y = run(G, A, B, code, instance=i)
-            fam = name.split("_")[0]
+            fam = family(name)
             if fam in first:
                 assert np.array_equal(first[fam], y), name
             else:
