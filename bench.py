@@ -122,7 +122,7 @@ def upload(bits, torch):
     return torch.from_numpy(bits.view(np.int16) if bits.dtype.itemsize == 2 else bits.view(np.int8)).cuda()
 
 
-def measure(G, torch, name, steps, warmup, instance=None, layout=None, settle_ms=200.0, entry="run"):
+def measure(G, torch, name, steps, warmup, instance=None, layout=None, settle_ms=200.0, entry="run", relu=0):
     """Upload a workload, run one correctness launch into a poisoned C, let
     the clock settle (untimed launches for about settle_ms), run `warmup`
     untimed launches, then time `steps` launches.  Returns a dict with the
@@ -130,7 +130,8 @@ def measure(G, torch, name, steps, warmup, instance=None, layout=None, settle_ms
     layout "col" stores B column-major (its transpose row-major) and calls
     gemm_run_ex; "row" calls gemm_run; None takes the workload's own.
     entry "ws" calls gemm_run_ws instead, with a zeroed workspace of
-    gemm_workspace_size() bytes allocated here (before timing)."""
+    gemm_workspace_size() bytes allocated here (before timing).  relu = 1
+    applies ReLU through gemm_run_ex (the general-epilogue kernels)."""
     import numpy as np
     from dense_half_precision_tiled_amd import inputs
     A, B, w = inputs.workload_inputs(name)
@@ -146,10 +147,11 @@ def measure(G, torch, name, steps, warmup, instance=None, layout=None, settle_ms
     s = stream.cuda_stream
     ldb = K if col else N
     args = (M, N, K, code, tA.data_ptr(), K, tB.data_ptr(), ldb, tC.data_ptr(), N, s)
-    ex_tail = (1.0, 0.0, None, 0, s)
+    ex_tail = (1.0, 0.0, None, relu, s)
+    force_ex = bool(relu)                    # ReLU: through gemm_run_ex, whatever the B layout
     ws = torch.zeros(G.gemm_workspace_size() // 4, dtype=torch.int32, device="cuda") if entry == "ws" else None
     lay_code = G.GEMM_B_COL_MAJOR if col else G.GEMM_B_ROW_MAJOR
-    ws_args = (args[:4] + (lay_code,) + args[4:-1] + (1.0, 0.0, None, 0) +
+    ws_args = (args[:4] + (lay_code,) + args[4:-1] + (1.0, 0.0, None, relu) +
                ((ws.data_ptr(), G.gemm_workspace_size(), s) if ws is not None else ()))
 
     def launch(_keep=(tA, tB, tC, ws)):
@@ -157,8 +159,8 @@ def measure(G, torch, name, steps, warmup, instance=None, layout=None, settle_ms
         # stay allocated for as long as it can be called
         if ws is not None:
             st = G.gemm_run_ws(*ws_args) if instance is None else G.gemm_run_instance_ws(instance, *ws_args)
-        elif col:
-            a = args[:4] + (G.GEMM_B_COL_MAJOR,) + args[4:-1] + ex_tail
+        elif col or force_ex:
+            a = args[:4] + (lay_code,) + args[4:-1] + ex_tail
             st = G.gemm_run_ex(*a) if instance is None else G.gemm_run_instance_ex(instance, *a)
         else:
             st = G.gemm_run(*args) if instance is None else G.gemm_run_instance(instance, *args)
@@ -201,14 +203,14 @@ def measure(G, torch, name, steps, warmup, instance=None, layout=None, settle_ms
         inst = instance
     elif ws is not None:
         inst = G.gemm_select_instance_ws(*ws_args[:-1])
-    elif col:
-        inst = G.gemm_select_instance_ex(M, N, K, code, G.GEMM_B_COL_MAJOR, tA.data_ptr(), K,
-                                         tB.data_ptr(), ldb, tC.data_ptr(), N, 1.0, 0.0, None, 0)
+    elif col or force_ex:
+        inst = G.gemm_select_instance_ex(M, N, K, code, lay_code, tA.data_ptr(), K,
+                                         tB.data_ptr(), ldb, tC.data_ptr(), N, 1.0, 0.0, None, relu)
     else:
         inst = G.gemm_select_instance(M, N, K, code, tA.data_ptr(), K, tB.data_ptr(), N,
                                       tC.data_ptr(), N)
     return {"name": name, "w": w, "layout": layout, "entry": "gemm_run_ws" if ws is not None else
-            ("gemm_run_ex" if col else "gemm_run"),
+            ("gemm_run_ex" if col or force_ex else "gemm_run"), "relu": relu,
             "A": A, "B": B, "C": tC, "ms": ms, "rep_ms": rep_ms,
             "launch": launch,
             "wall_s": wall, "settle_launches": n_settle,
@@ -496,7 +498,7 @@ def observed(torch, res, seconds: float) -> dict:
 TIMELINE_WAVES = 65536      # room for 8192 workgroups of 8 waves
 
 
-def timeline_summary(rec):
+def timeline_summary(rec, tiles_of=None):
     """Summary of one launch's timeline records (rows of 8 int64 words:
     start and end on the 100 MHz real-time counter, start and end on the
     shader-clock counter, XCC id << 32 | HW_ID, workgroup id; unused rows are
@@ -526,7 +528,13 @@ def timeline_summary(rec):
         per_xcd.setdefault(x, []).append(((a - base) * tick_us, (b - base) * tick_us, f))
         cu_busy[c] = cu_busy.get(c, 0.0) + (b - a) * tick_us
     durs = [(b - a) * tick_us for (a, b, _, _, _) in wgs.values()]
-    return {"span_us": round(span, 2), "workgroups": len(wgs), "cus": len(cu_busy),
+    # the slowest workgroups, with the output tile each computed (one-tile
+    # launches: workgroup id -> (tile row, tile column) from the visit order)
+    slow = sorted(wgs.items(), key=lambda kv: kv[1][0] - kv[1][1])[:12]
+    slowest = [{"wg": g, "us": round((b - a) * tick_us, 2), "xcd": x,
+                "tile": (list(tiles_of[g]) if tiles_of is not None and g < len(tiles_of) else None)}
+               for g, (a, b, x, _, _) in slow]
+    return {"span_us": round(span, 2), "workgroups": len(wgs), "cus": len(cu_busy), "slowest": slowest,
             "wg_us_min": round(min(durs), 2), "wg_us_median": round(statistics.median(durs), 2),
             "wg_us_max": round(max(durs), 2),
             "wg_mhz_median": round(statistics.median(v[4] for v in wgs.values()), 1),
@@ -542,14 +550,18 @@ def timeline_summary(rec):
 
 
 def timeline(G, torch, name: str, launches: int, warmup: int, settle_ms: float, entry: str = "run",
-             instance=None) -> int:
+             instance=None, relu: int = 0) -> int:
     """Per-workgroup timeline of `launches` launches of one workload, from the
     profiling build of the library (libdhpt_gemm_timeline.so, which records
     for every wave its start and end on the 100 MHz real-time counter and on
     the shader clock, and the XCC and CU it ran on).  Prints, per launch, the kernel span, the end times
     of each XCD's first and last workgroups, workgroup durations, and the
     share of CU time spent outside workgroups."""
-    res = measure(G, torch, name, 1, warmup, instance, None, settle_ms, entry)
+    res = measure(G, torch, name, 1, warmup, instance, None, settle_ms, entry, relu)
+    w = res["w"]
+    inst_id = [i for i in range(G.gemm_num_instances()) if G.gemm_instance_name(i) == res["instance"]][0]
+    tm, tn = G.gemm_tile_order(inst_id, w["M"], w["N"])
+    tiles_of = list(zip(tm.tolist(), tn.tolist()))
     buf = torch.zeros(TIMELINE_WAVES * 8, dtype=torch.int64, device="cuda")
     lib = G.load()
     lib.gemm_timeline_set(ctypes.c_void_p(buf.data_ptr()), TIMELINE_WAVES)
@@ -561,11 +573,83 @@ def timeline(G, torch, name: str, launches: int, warmup: int, settle_ms: float, 
         res["launch"]()
         e1.record()
         torch.cuda.synchronize()
-        summ = timeline_summary(buf.cpu().numpy())
+        summ = timeline_summary(buf.cpu().numpy(), tiles_of)
         summ.update({"launch": it, "event_ms": round(e0.elapsed_time(e1), 4)})
         out.append(summ)
     lib.gemm_timeline_set(None, 0)
     print(json.dumps({"timeline": name, "kernel": res["instance"], "launches": out}), flush=True)
+    return 0
+
+
+def _counter_rows(path: str, counter: str):
+    """(kernel name, grid size, value) per dispatch of one rocprofv3 counter
+    CSV (p_counter_collection.csv), in dispatch order."""
+    import csv
+    rows = []
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"].startswith(counter):
+            rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"].split("(")[0].replace("void ", ""),
+                         int(r["Grid_Size"]), float(r["Counter_Value"])))
+    rows.sort()
+    return [(k, g, v) for _, k, g, v in rows]
+
+
+def traffic_summary(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv: str,
+                    workloads, instances, copy_bytes: int) -> int:
+    """Write profiles/hbm_traffic.json from two rocprofv3 --pmc runs of
+    `bench.py --steps 3 --warmup 1 --settle-ms 0 ...` (FETCH_SIZE, then
+    WRITE_SIZE) and two of `--copy-calibration` (the plain copy that scales
+    the counters).  The library's dispatches of each run come in the bench's
+    workload order, one run of identical dispatches (kernel, grid) per
+    workload; each workload's figures are the mean over its dispatches."""
+    import statistics
+
+    def runs(path, counter):
+        out = []
+        for k, g, v in _counter_rows(path, counter):
+            if "dhpt::" not in k:
+                continue
+            if out and out[-1][0] == (k, g):
+                out[-1][1].append(v)
+            else:
+                out.append(((k, g), [v]))
+        return out
+
+    def copy_kib(path, counter):
+        vals = [v for k, g, v in _counter_rows(path, counter) if "copyBuffer" in k or "Copy" in k]
+        return statistics.mean(vals[1:] if len(vals) > 1 else vals)
+
+    fetch_scale = copy_bytes / 1024.0 / copy_kib(copy_fetch_csv, "FETCH_SIZE")
+    write_scale = copy_bytes / 1024.0 / copy_kib(copy_write_csv, "WRITE_SIZE")
+    fr, wr = runs(fetch_csv, "FETCH_SIZE"), runs(write_csv, "WRITE_SIZE")
+    if len(fr) != len(workloads) or len(wr) != len(workloads):
+        raise RuntimeError("expected %d workloads, found %d / %d kernel runs" % (len(workloads), len(fr), len(wr)))
+    from dense_half_precision_tiled_amd import inputs
+    out = {"note": "rocprofv3 FETCH_SIZE / WRITE_SIZE per dispatch (KiB), scaled by a %d MiB device copy; "
+                   "source_hash: the sources of the kernel's family when the counters were taken" % (copy_bytes >> 20),
+           "fetch_scale": fetch_scale, "write_scale": write_scale, "workloads": {}}
+    for name, inst, (fk, fv), (wk, wv) in zip(workloads, instances, fr, wr):
+        if fk != wk:
+            raise RuntimeError("fetch and write runs differ for %s: %s / %s" % (name, fk, wk))
+        w = inputs.WORKLOADS[name]
+        esz = 1 if w["fmt"] in EIGHT_BIT else 2
+        alg = esz * (w["M"] * w["K"] + w["K"] * w["N"]) + (4 if w["out"] == "f32" else 2) * w["M"] * w["N"]
+        f, wv_ = statistics.mean(fv), statistics.mean(wv)
+        family = inst.split("_")[0]
+        out["workloads"][name] = {
+            "kernel": fk[0], "instance": inst,
+            "source_hash": kernel_source_hash(family) if family in FAMILY_SOURCES else None,
+            "fetch_kib_raw": round(f, 2), "write_kib_raw": round(wv_, 2), "dispatches": [len(fv), len(wv)],
+            "hbm_bytes_per_launch": int(round((f * fetch_scale + wv_ * write_scale) * 1024)),
+            "algorithmic_bytes": alg}
+    with open(os.path.join(ROOT, "profiles", "hbm_traffic.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    for name, e in out["workloads"].items():
+        print("| %s | `%s` | %d | %.1f | %.1f | %.1f | %.2fx |" % (
+            name, e["kernel"], e["dispatches"][0], e["fetch_kib_raw"], e["fetch_kib_raw"] * fetch_scale / 1024,
+            e["write_kib_raw"] * write_scale / 1024, e["hbm_bytes_per_launch"] / e["algorithmic_bytes"]))
+    print("fetch_scale %.4f write_scale %.4f" % (fetch_scale, write_scale))
     return 0
 
 
@@ -692,6 +776,9 @@ def main(argv=None):
     ap.add_argument("--settle-ms", type=float, default=200.0,
                     help="untimed launches for about this long before the warmups (clock ramp-up)")
     ap.add_argument("--instance", type=int, default=None, help="force a kernel instance id")
+    ap.add_argument("--relu", action="store_true",
+                    help="apply ReLU in the epilogue (gemm_run_ex: the general-epilogue kernels), e.g. to price "
+                         "their cost against the plain ones")
     ap.add_argument("--entry", choices=("run", "ws"), default="run",
                     help="call gemm_run / gemm_run_ex (run) or gemm_run_ws with a caller-owned workspace (ws)")
     ap.add_argument("--layout", choices=("row", "col"), default=None,
@@ -716,6 +803,11 @@ def main(argv=None):
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the GEMM, time a plain device copy of BYTES bytes "
                          "(the reference kernel for scaling HBM byte counters)")
+    ap.add_argument("--traffic-summary", nargs=4, default=None,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="instead of running, write profiles/hbm_traffic.json from rocprofv3 counter CSVs of this "
+                         "bench (FETCH_SIZE run, WRITE_SIZE run) and of --copy-calibration (same two counters); "
+                         "the workload list is --workload, --secondary, --also")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -725,6 +817,20 @@ def main(argv=None):
 
     if args.power_sample > 0:
         return power_sample(args.workload, args.power_sample)
+    if args.traffic_summary:
+        names = [args.workload] + ([args.secondary] if args.secondary and args.secondary != "none" else []) + \
+            ([x for x in args.also.split(",")] if args.also and args.also != "none" else [])
+        from dense_half_precision_tiled_amd import gemm as G0
+        insts = []
+        for name in names:
+            from dense_half_precision_tiled_amd import inputs
+            w = inputs.WORKLOADS[name]
+            col = w.get("layout", "row") == "col"
+            code = CODES[(w["fmt"], w["out"])]
+            i = G0.gemm_select_instance_ex(w["M"], w["N"], w["K"], code, 1 if col else 0, 1 << 32, w["K"], 1 << 36,
+                                           w["K"] if col else w["N"], 1 << 40, w["N"], 1.0, 0.0, None, 0)
+            insts.append(G0.gemm_instance_name(i))
+        return traffic_summary(*args.traffic_summary, names, insts, args.copy_calibration or (256 << 20))
     import torch
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
@@ -738,13 +844,13 @@ def main(argv=None):
         lib = G.load(B.TIMELINE_LIB)
         lib.gemm_timeline_set.argtypes = [ctypes.c_void_p, ctypes.c_int64]
         return timeline(G, torch, args.workload, args.timeline, args.warmup, args.settle_ms, args.entry,
-                        args.instance)
+                        args.instance, int(args.relu))
     G.load()
     if args.loop_seconds > 0:
         return loop_for(G, torch, args.workload, args.loop_seconds)
 
     main_res = measure(G, torch, args.workload, args.steps, args.warmup, args.instance, args.layout,
-                       args.settle_ms, args.entry)
+                       args.settle_ms, args.entry, int(args.relu))
 
     def summary(r):
         w2 = r["w"]
@@ -760,7 +866,7 @@ def main(argv=None):
     sec = None
     if args.secondary and args.secondary != "none":
         r2 = measure(G, torch, args.secondary, max(args.steps, 50), args.warmup, args.instance,
-                     args.layout, args.settle_ms, args.entry)
+                     args.layout, args.settle_ms, args.entry, int(args.relu))
         sec = summary(r2)
         if args.clock_seconds > 0:
             sec["observed"] = observed(torch, r2, args.clock_seconds)
@@ -769,7 +875,7 @@ def main(argv=None):
     if args.also and args.also != "none" and args.instance is None:
         for name in args.also.split(","):
             r3 = measure(G, torch, name, max(args.steps, 200), args.warmup, None, args.layout,
-                         args.settle_ms, args.entry)
+                         args.settle_ms, args.entry, int(args.relu))
             others.append(summary(r3))
             del r3
 
@@ -793,7 +899,7 @@ def main(argv=None):
         "config": {"workload": describe(w, lay),
                    "M": w["M"], "N": w["N"], "K": w["K"], "b_layout": lay,
                    "in": w["fmt"], "out": w["out"], "kernel": main_res["instance"],
-                   "entry_point": main_res["entry"],
+                   "entry_point": main_res["entry"], "relu": bool(main_res["relu"]),
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(main_res["tflops"], 2), "peak": peak_for(w),
                      "unit": "TFLOP/s", "frac": round(main_res["tflops"] / peak_for(w), 4),

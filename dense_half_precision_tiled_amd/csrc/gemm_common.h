@@ -151,6 +151,37 @@ __device__ __forceinline__ u32x4 shift_chunk(u32x4 v, int sh) {
     return __builtin_bit_cast(u32x4, x);
 }
 
+// Raw buffer access to C for edge tiles: a descriptor over the tile's first
+// element with 2^31 bytes of range, so that a lane whose element lies outside
+// M x N passes the offset kOutOfRange instead of branching around its access:
+// the hardware drops such a store and returns zero for such a load.  The
+// host keeps every in-range offset below 2^31 (c_offsets_fit).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOutOfRange = 0x80000000u;
+__device__ __forceinline__ rsrc_t c_rsrc(void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)kOutOfRange, 0x00020000);
+}
+
+template <int OUT>
+__device__ __forceinline__ void store_out_buf(rsrc_t r, uint32_t off, float v) {
+    if constexpr (OUT == OUT_F32)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+    else if constexpr (OUT == OUT_F16)
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (_Float16)v), r, off, 0, 0);
+    else
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)v), r, off, 0, 0);
+}
+
+template <int OUT>
+__device__ __forceinline__ float load_out_buf(rsrc_t r, uint32_t off) {
+    if constexpr (OUT == OUT_F32)
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+    else if constexpr (OUT == OUT_F16)
+        return (float)__builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+    else
+        return (float)__builtin_bit_cast(__bf16, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+}
+
 // The epilogue operands of the general form (unused by the plain kernels).
 // Profiling builds (-DDHPT_TIMELINE, a separate library) also carry the
 // timeline buffer through it.

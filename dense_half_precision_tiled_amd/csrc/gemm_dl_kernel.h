@@ -56,8 +56,11 @@
 //   EDGE_CLAMP: any M, K; any N for column-major B, N % 8 == 0 (N % 16 == 0
 //     for 8-bit inputs) for row-major B.  Rows of A (and of column-major B)
 //     past the edge and 16-byte column chunks of row-major B past N are read
-//     from a clamped, valid address: those values only reach outputs that are
-//     never stored.  A partial last slice (K % BK != 0) is filled through
+//     from valid ones of the same tile, wrapped around (m0 + (r - m0) mod
+//     (M - m0)): those values only reach outputs that are never stored, and
+//     wrapping keeps the lanes of a copy on distinct addresses (clamping
+//     them all to the last row made the edge tiles of a one-wave launch its
+//     slowest).  A partial last slice (K % BK != 0) is filled through
 //     VGPRs with element-exact zero fill.
 //   EDGE_MASKED: any shape.  Every slice is filled through VGPRs with
 //     element-exact zero fill (no asynchronous copies, one stage, 64-bit
@@ -155,7 +158,7 @@ __device__ __forceinline__ void dl_tile(
         for (int i = 0; i < CA; ++i) {
             const int r = (BM / 4) * w + 8 * i + (l >> 3);
             int grow = m0 + r;
-            if constexpr (EDGE == EDGE_CLAMP) grow = grow < M ? grow : M - 1;
+            if constexpr (EDGE == EDGE_CLAMP) grow = grow < M ? grow : m0 + (grow - m0) % (M - m0);
             a_vo[i] = (uint32_t)(((int64_t)(grow - m0) * lda + (16 / ESZ) * ((l & 7) ^ swz_a(r))) * ESZ);
         }
 #pragma unroll
@@ -163,13 +166,13 @@ __device__ __forceinline__ void dl_tile(
             if constexpr (BT) {
                 const int r = (BN / 4) * w + 8 * i + (l >> 3);
                 int gcol = n0 + r;
-                if constexpr (EDGE == EDGE_CLAMP) gcol = gcol < N ? gcol : N - 1;
+                if constexpr (EDGE == EDGE_CLAMP) gcol = gcol < N ? gcol : n0 + (gcol - n0) % (N - n0);
                 b_vo[i] = (uint32_t)(((int64_t)(gcol - n0) * ldb + (16 / ESZ) * ((l & 7) ^ swz_a(r))) * ESZ);
             } else {
                 const int kr = B_ROWS_PER_WAVE * w + B_ROWS_PER_COPY * i + l / B_CHUNKS;
                 const int sw = F8 ? swz_b8<B_CHUNKS>(kr) : swz_b(kr);
                 int col = n0 + (16 / ESZ) * ((l % B_CHUNKS) ^ sw);
-                if constexpr (EDGE == EDGE_CLAMP) col = col + 16 / ESZ <= N ? col : N - 16 / ESZ;
+                if constexpr (EDGE == EDGE_CLAMP) col = col + 16 / ESZ <= N ? col : n0 + (col - n0) % ((N - n0) / (16 / ESZ) * (16 / ESZ));
                 b_vo[i] = (uint32_t)(((int64_t)kr * ldb + (col - n0)) * ESZ);
             }
         }
@@ -422,7 +425,39 @@ __device__ __forceinline__ void dl_tile(
     // The beta test and the interior test are uniform: take them once,
     // outside the element loops.  A tile wholly inside M x N stores without
     // per-element masks (a branch per element costs more than the store).
+    // Edge tiles of the clamped kernels store through a buffer descriptor
+    // over the tile's first element: a lane whose element lies outside M x N
+    // passes an out-of-range offset, so no element needs a branch (an edge
+    // tile finishes last in a one-wave launch, and per-element branches made
+    // its epilogue the critical path).  The fully masked kernels, which take
+    // any leading dimension, keep the branches.
     auto store_tile = [&](auto read_old, auto masked) {
+        if constexpr (decltype(masked)::value && EDGE == EDGE_CLAMP) {
+            constexpr int OSZ = OUT == OUT_F32 ? 4 : 2;
+            const rsrc_t crs = c_rsrc(static_cast<char*>(C) + ((int64_t)m0 * ldc + n0) * OSZ);
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int cl = wn * WN + 32 * j + (le & 31);            // column within the tile
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int rl = wm * WM + 32 * i + 8 * (e >> 2) + 4 * gl + (e & 3);
+                        const bool ok = m0 + rl < M && n0 + cl < N;
+                        const uint32_t off = ok ? ((uint32_t)rl * (uint32_t)ldc + (uint32_t)cl) * OSZ : kOutOfRange;
+                        float v = acc[i][j][e];
+                        if constexpr (EPI) {
+                            constexpr bool ro = decltype(read_old)::value;
+                            float old = 0.0f;
+                            if constexpr (ro) old = load_out_buf<OUT>(crs, off);
+                            v = epi_value(v, ep, ro, old, bias_v[j]);
+                        }
+                        store_out_buf<OUT>(crs, off, v);
+                    }
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
 #pragma unroll

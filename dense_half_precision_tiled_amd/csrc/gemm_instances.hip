@@ -66,6 +66,15 @@ static bool copy_offsets_fit(const Problem& p, int tile, int esz) {
     return a <= lim && b <= lim;
 }
 
+// The clamped-edge kernels store edge tiles through a buffer descriptor over
+// the tile's first element of C, with 32-bit byte offsets below 2^31: at most
+// tile - 1 rows of ldc plus a tile width.  Larger leading dimensions of C take
+// the masked kernels.
+static bool c_offsets_fit(const Problem& p, int tile) {
+    const uint64_t osz = dtype_out_f32(p.dtype) ? 4 : 2;
+    return ((uint64_t)(tile - 1) * (uint64_t)p.ldc + (uint64_t)tile) * osz <= 0x7FFFFFFFull;
+}
+
 bool instance_supports(int id, const Problem& p) {
     if (id < 0 || id >= kNumInstances) return false;
     const InstanceInfo& in = kInstances[id];
@@ -80,6 +89,7 @@ bool instance_supports(int id, const Problem& p) {
     case EDGE_NONE: return p.M % in.tile == 0 && p.N % in.tile == 0 && p.K % (in.in8 ? 128 : 64) == 0;
     case EDGE_CLAMP: {
         const int chunk = in.in8 ? 16 : 8;                 // row-major B: whole 16-byte column chunks
+        if (!c_offsets_fit(p, in.tile)) return false;
         return p.transB || (p.N % chunk == 0 && p.N >= chunk);
     }
     case EDGE_MASKED: return true;                       // any shape, any leading dimension

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256, 1) void gemm_ks_kernel(
     for (int i = 0; i < CA; ++i) {
         const int r = (BM / 4) * w + 8 * i + (l >> 3);
         int grow = m0 + r;
-        if constexpr (EDGE == dl::EDGE_CLAMP) grow = grow < M ? grow : M - 1;
+        if constexpr (EDGE == dl::EDGE_CLAMP) grow = grow < M ? grow : m0 + (grow - m0) % (M - m0);
         a_vo[i] = (uint32_t)(((int64_t)(grow - m0) * lda + 8 * ((l & 7) ^ swz_a(r))) * 2);
     }
 #pragma unroll
@@ -105,12 +105,12 @@ __global__ __launch_bounds__(256, 1) void gemm_ks_kernel(
         if constexpr (BT) {
             const int r = (BN / 4) * w + 8 * i + (l >> 3);
             int gcol = n0 + r;
-            if constexpr (EDGE == dl::EDGE_CLAMP) gcol = gcol < N ? gcol : N - 1;
+            if constexpr (EDGE == dl::EDGE_CLAMP) gcol = gcol < N ? gcol : n0 + (gcol - n0) % (N - n0);
             b_vo[i] = (uint32_t)(((int64_t)(gcol - n0) * ldb + 8 * ((l & 7) ^ swz_a(r))) * 2);
         } else {
             const int kr = 16 * w + B_ROWS_PER_COPY * i + l / B_CHUNKS;
             int col = n0 + 8 * ((l % B_CHUNKS) ^ swz_b(kr));
-            if constexpr (EDGE == dl::EDGE_CLAMP) col = col + 8 <= N ? col : N - 8;
+            if constexpr (EDGE == dl::EDGE_CLAMP) col = col + 8 <= N ? col : n0 + (col - n0) % ((N - n0) / 8 * 8);
             b_vo[i] = (uint32_t)(((int64_t)kr * ldb + (col - n0)) * 2);
         }
     }
@@ -324,10 +324,29 @@ __global__ __launch_bounds__(256, 1) void gemm_ks_kernel(
             if constexpr (EPI) {
                 if (ep.bias != nullptr && (EDGE == dl::EDGE_NONE || col < N)) bias_v = ep.bias[col];
             }
+            if constexpr (EDGE == dl::EDGE_CLAMP) {
+                // clamped edges: through a buffer descriptor over the tile's
+                // first element, elements outside M x N at an out-of-range
+                // offset (dropped), so no element branches
+                constexpr int OSZ = OUT == OUT_F32 ? 4 : 2;
+                const rsrc_t crs = c_rsrc(static_cast<char*>(C) + ((int64_t)m0 * ldc + n0) * OSZ);
+                const int cl = col - n0;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int row = row_base + 8 * (e >> 2) + (e & 3);
-                if (EDGE == dl::EDGE_NONE || (row < M && col < N)) {
+                for (int e = 0; e < 16; ++e) {
+                    const int rl = row_base - m0 + 8 * (e >> 2) + (e & 3);
+                    const bool ok = m0 + rl < M && col < N;
+                    const uint32_t off = ok ? ((uint32_t)rl * (uint32_t)ldc + (uint32_t)cl) * OSZ : kOutOfRange;
+                    float y = x[e];
+                    if constexpr (EPI) {
+                        const float old = read_old ? load_out_buf<OUT>(crs, off) : 0.0f;
+                        y = epi_value(y, ep, read_old, old, bias_v);
+                    }
+                    store_out_buf<OUT>(crs, off, y);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int row = row_base + 8 * (e >> 2) + (e & 3);
                     const int64_t idx = (int64_t)row * ldc + col;
                     float y = x[e];
                     if constexpr (EPI) {
