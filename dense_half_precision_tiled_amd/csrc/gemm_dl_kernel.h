@@ -10,7 +10,7 @@
 //     operand plus a fixed 32-bit per-lane offset below 2^31, so larger
 //     problems go to EDGE_MASKED), issued while the previous
 //     slice is multiplied -- the multi-stage copy pipeline of the Ada
-//     tensor-core GEMM write-up ("stages" section) and the acquire / copy /
+//     tensor-core GEMM write-up (its pipeline-stage table) and the acquire / copy /
 //     wait / release loop of "GEMM From Naive CUDA to Tensor Cores" ("Where
 //     asynchronous copies and TMA take over"), with vmcnt as the wait and one
 //     workgroup barrier per slice as both the publish and the release;
@@ -24,7 +24,7 @@
 //     for column l % 32 straight from the row-major tile (the transposing
 //     load of "mma.sync and ldmatrix", gfx950 form);
 //   * B stage, column-major B (BT, N x K in memory, the "TN" layout of the Ada
-//     write-up, section "A row-major (MxK), B column-major"): BN rows x 128
+//     write-up's operand-layout choice, A row-major and B column-major): BN rows x 128
 //     bytes, copied and swizzled exactly like A; B fragments are then plain
 //     ds_read_b128 like A's;
 //   * A fragments: ds_read_b128 (8 consecutive k of one row);

@@ -24,7 +24,7 @@
 // so the copies of slice t+4 go there and have three slices to land; the
 // fragments of slice t+1 are read during slice t.  One workgroup barrier per
 // slice publishes slice t+1 and releases stage t.  This is the multi-stage
-// copy pipeline of the Ada tensor-core GEMM write-up ("stages" section), with
+// copy pipeline of the Ada tensor-core GEMM write-up (its pipeline-stage table), with
 // the slice split across waves instead of across output sub-tiles.
 //
 // EDGE modes as in gemm_dl_kernel.h: dl::EDGE_NONE (M % 128 == N % 128 == 0,

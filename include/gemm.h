@@ -13,9 +13,9 @@
  *     C[i*ldc + j] = sum_{k=0}^{K-1} A[i*lda + k] * B[k*ldb + j]
  *                    for 0 <= i < M, 0 <= j < N.
  *
- * The products of the half-precision inputs are accumulated in fp32 (the FP16
- * input, FP32 accumulate contract of the Ada tensor-core GEMM write-up, section
- * "D = A . B"), then converted once to the output type (fp32 as is; fp16 and
+ * The products of the half-precision inputs are accumulated in fp32 (the
+ * FP16-in, FP32-accumulate contract the Ada tensor-core GEMM write-up states
+ * at its start), then converted once to the output type (fp32 as is; fp16 and
  * bf16 by IEEE round-to-nearest-even).
  *
  * 8-bit float inputs (the GEMM_E4M3_* and GEMM_E5M2_* dtypes) extend the same
@@ -73,8 +73,8 @@ typedef enum {
     GEMM_B_ROW_MAJOR = 0,   /* B(k,j) at B[k*ldb + j], ldb >= N (gemm_run's layout) */
     GEMM_B_COL_MAJOR = 1    /* B(k,j) at B[j*ldb + k], ldb >= K: B stored column-major,
                                i.e. its N x K transpose row-major -- the "TN" layout the
-                               Ada tensor-core GEMM write-up builds on (section "A
-                               row-major (MxK), B column-major") */
+                               Ada tensor-core GEMM write-up builds on (its operand-
+                               layout choice: A row-major, B column-major) */
 } gemm_layout_t;
 
 /*
@@ -126,8 +126,8 @@ int gemm_run(int64_t M, int64_t N, int64_t K, int dtype,
  *
  * for 0 <= i < M, 0 <= j < N: the general C <- alpha*A*B + beta*C that "GEMM
  * From Naive CUDA to Tensor Cores" opens with, plus the per-column bias and
- * ReLU that the Ada tensor-core GEMM write-up folds into the epilogue (section
- * on the fused bias + ReLU epilogue).  The dot product is accumulated in fp32;
+ * ReLU that the Ada tensor-core GEMM write-up folds into the epilogue (its
+ * remark on the fused bias + ReLU epilogue).  The dot product is accumulated in fp32;
  * the epilogue runs in fp32 on that accumulator (alpha * acc, then
  * + beta * C_old as a fused multiply-add, then + bias[j], then ReLU) and the
  * result is rounded once to the output type.
@@ -293,8 +293,8 @@ int gemm_run_instance_ex(int instance, int64_t M, int64_t N, int64_t K, int dtyp
 
 /*
  * gemm_tile_order -- host evaluation of an instance's workgroup-to-tile map
- * (the L2-aware visit order of the Ada write-up, section "grouped CTA
- * rasterization", applied per XCD).  For workgroup ids 0 .. count-1 of a launch
+ * (the grouped CTA order of the Ada write-up, its table of DRAM bytes read per
+ * CTA order at 4096^3 and 8192^3, applied per XCD).  For workgroup ids 0 .. count-1 of a launch
  * on an M x N output it writes the output tile row tm[w] and column tn[w].
  * Returns the number of workgroups of that launch, or a negative GEMM_ERR_*
  * code.  With tm == NULL or tn == NULL nothing is written.  No GPU call is

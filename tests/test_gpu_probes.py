@@ -1,8 +1,8 @@
 """Lane-layout pins for the gfx950 instructions the GEMM kernels rely on, and
 the MFMA issue-rate measurement (the register-resident rate probe of the Ada
-tensor-core GEMM write-up, "If you benchmark Tensor Cores on a GeForce part":
-FLOP per clock per compute unit from an in-kernel clock, independent of the
-clock frequency).
+tensor-core GEMM write-up, its table of measured mma rates per clock and its
+warning about measuring against the clock actually held: FLOP per clock per
+compute unit from an in-kernel clock, independent of the clock frequency).
 
 Every probe runs one wave on buffers it owns; addresses are checked here and
 masked in the kernel."""
