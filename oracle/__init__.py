@@ -222,19 +222,21 @@ def decode(bits, in_fmt) -> np.ndarray:
 def round_to(x, out_fmt) -> np.ndarray:
     """IEEE round-to-nearest-even of float64 values to fp32/fp16/bf16 (as float64)."""
     f = _fmt_out(out_fmt)
-    xs = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    shape = np.shape(x)
+    xs = np.ascontiguousarray(np.asarray(x, dtype=np.float64)).reshape(-1)
     out = np.empty(xs.shape, dtype=np.float64)
     _load().oracle_round_to_array(f, _ptr(xs, ctypes.c_double), _ptr(out, ctypes.c_double), xs.size)
-    return out
+    return out.reshape(shape)
 
 
 def ulp(r, out_fmt) -> np.ndarray:
     """Spacing of the output format at r (smallest subnormal at r == 0)."""
     f = _fmt_out(out_fmt)
-    rs = np.ascontiguousarray(np.asarray(r, dtype=np.float64))
+    shape = np.shape(r)
+    rs = np.ascontiguousarray(np.asarray(r, dtype=np.float64)).reshape(-1)
     out = np.empty(rs.shape, dtype=np.float64)
     _load().oracle_ulp_array(f, _ptr(rs, ctypes.c_double), _ptr(out, ctypes.c_double), rs.size)
-    return out
+    return out.reshape(shape)
 
 
 def flops(M: int, N: int, K: int) -> int:

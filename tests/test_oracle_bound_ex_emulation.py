@@ -8,8 +8,9 @@ v1 = fl(alpha * acc), v2 = fl(beta * C_old + v1) as one fused step when
 beta != 0, v3 = fl(v2 + bias), ReLU, then one rounding to the output format.
 The acceptance bound ``bound_ex`` claims that
 
-    |y - r| <= |alpha|*K*2^-20 + 2^-22*(|alpha*d| + |beta*C_old| + |bias|)
-               (+ one ulp of a half-precision output at r)
+    |y - r| <= e32 = |alpha|*K*2^-20
+                     + 2^-22*(|alpha|*(|d| + K*2^-20) + |beta*C_old| + |bias|)
+               (+ one ulp of a half-precision output at |r| + e32)
 
 for r = act(alpha*d + beta*C_old + bias), the oracle's exact value.  This
 test does not restate that formula as its evidence: it runs the steps above
