@@ -1,10 +1,13 @@
 // gemm_api.cpp -- the C ABI declared in include/gemm.h: argument validation,
 // instance selection and the launch on the caller's stream.  No allocation,
-// no host synchronisation, no state.
+// no host synchronisation, no per-call state (only per-device caches of the
+// compute-unit count and of the static scratch's address).
 #include "gemm.h"
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <atomic>
 
 #include "gemm_internal.h"
 
@@ -42,13 +45,16 @@ struct Extra {
 // workgroup per CU), queried once per device and kept: a property of the
 // device, not of any call.
 int device_cus() {
-    static int cached[64];
+    static std::atomic<int> cached[64];        // zero until the first call on a device (any thread)
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    if (dev < 64) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (dev < 64) cached[dev] = n;
+    if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
     return n;
 }
 
@@ -243,18 +249,18 @@ constexpr int kMaxDevices = 64;
 // on the device and kept (each device has its own copy of the array at its
 // own address).
 int device_scratch(void** out) {
-    static void* ptrs[kMaxDevices];
+    static std::atomic<void*> ptrs[kMaxDevices];   // threads racing on a first call store the same address
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GEMM_ERR_LAUNCH;
-    if (ptrs[dev] == nullptr) {
-        void* ptr = nullptr;
+    void* ptr = ptrs[dev].load(std::memory_order_relaxed);
+    if (ptr == nullptr) {
         if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
             (void)hipGetLastError();
             return GEMM_ERR_LAUNCH;
         }
-        ptrs[dev] = ptr;
+        ptrs[dev].store(ptr, std::memory_order_relaxed);
     }
-    *out = ptrs[dev];
+    *out = ptr;
     return GEMM_OK;
 }
 
