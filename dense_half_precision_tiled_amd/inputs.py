@@ -60,6 +60,15 @@ def normal(shape, seed: int, fmt: str = BF16) -> np.ndarray:
     return _to_bits(x, fmt)
 
 
+def signed_magnitude(shape, seed: int, fmt: str, lo: float = 0.5, hi: float = 2.0) -> np.ndarray:
+    """Random signs times magnitudes uniform in [lo, hi), rounded to the format
+    (round to nearest even; hi itself can be reached)."""
+    g = _rng(seed)
+    mag = g.uniform(lo, hi, size=shape)
+    sign = np.where(g.random(size=shape) < 0.5, -1.0, 1.0)
+    return _to_bits(sign * mag, fmt)
+
+
 def ints(shape, seed: int, fmt: str = F16, lo: int = -2, hi: int = 2) -> np.ndarray:
     return _to_bits(_rng(seed).integers(lo, hi + 1, size=shape).astype(np.float64), fmt)
 
