@@ -811,7 +811,7 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         return 2
 

@@ -367,7 +367,7 @@ __global__ __launch_bounds__(256, 1) void gemm_ks_kernel(
             default: finish(acc[3][2 * r + jj], jj); break;
             }
         }
-        if (r == 0) __syncthreads();                   // the slots are rewritten in round 1
+        if (r == 0) __syncthreads();                   // the second pass (r = 1) rewrites the slots
     }
 #ifdef DHPT_TIMELINE
     tl_record(ep.timeline, tl0);

@@ -298,6 +298,22 @@ def test_quarter_grid_full_size_bit_exact(G):
     assert np.array_equal(y @ x, Ad @ (Bd @ x))
 
 
+@pytest.mark.parametrize("code", [0, 1])
+def test_quarter_grid_ragged_bit_exact(G, code):
+    """The ragged workload's shape and layout (3000 x 5000 x 4099, fp16 A with
+    2-byte-aligned rows of 4099 elements, a partial last tile-row, tile-column
+    and k-slice) on 0.25-grid inputs: every partial sum is a multiple of 1/16
+    below 2^15, exact in fp32, so the fp32 output is the oracle's bit for bit
+    and the fp16 output its correct rounding."""
+    M, N, K = 3000, 5000, 4099
+    fmt, out = DTYPES[code]
+    A = inputs.quarter((M, K), 221, fmt)
+    B = inputs.quarter((K, N), 222, fmt)
+    print("quarter-grid ragged", code, flush=True)
+    y = run(G, A, B, code)
+    assert_exact(y, oracle.gemm_f64(A, B, fmt), out, "quarter ragged")
+
+
 def test_quarter_grid_k_split_bit_exact(G):
     """2048^3 fp16 -> fp32 on 0.25-grid inputs through gemm_run (the k-split
     kernel: four partial tiles summed through LDS): every partial sum is a
