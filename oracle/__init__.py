@@ -39,7 +39,9 @@ the comparison rule that decides parity:
   random data and nothing more; the sharp 8-bit checks are the exact
   0.25-grid fixtures (every product a multiple of 1/16 no larger than 4, so
   the 13-binade cut drops no bit and every partial sum is exact in fp32),
-  compared bit for bit up to 8192^3.
+  compared bit for bit up to 8192^3, and random data with magnitudes in
+  [0.5, 2] (every product in [2^-2, 2^2] with its lowest bit at 2^-8 or
+  above, inside any 13-binade window), held to bound() alone.
 * ``gemm_ex_f64`` / ``bound_ex`` / ``compare_ex``: the general form
   act(alpha*A.B + beta*C_old + bias) with B row-major or column-major, for the
   fused-epilogue entry point (alpha/beta: the general GEMM the same page opens
