@@ -84,7 +84,7 @@ __device__ __forceinline__ int swz_b(int k) { return 2 * (k & 3); }
 // different groups of 4 banks for every row length used (256, 128, 64 bytes).
 template <int CPR>
 __device__ __forceinline__ int swz_b8(int k) {
-    constexpr int R = 16 / CPR;                 // rows per 64-bank cycle
+    constexpr int R = CPR < 16 ? 16 / CPR : 1;  // rows per 64-bank cycle
     return 2 * ((k / R) & (CPR / 2 - 1));
 }
 

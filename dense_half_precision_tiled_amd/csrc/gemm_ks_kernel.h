@@ -191,9 +191,6 @@ __global__ __launch_bounds__(256, 1) void gemm_ks_kernel(
         }
     };
 
-    using yes = std::integral_constant<bool, true>;
-    using no = std::integral_constant<bool, false>;
-
     // One slice: MFMAs of buffer MB, interleaved one per slot with this
     // slot's share of the R reads of the next slice (stage rstage, buffer
     // MB ^ 1) and of the COPIES copies into cstage.  MB is a compile-time
