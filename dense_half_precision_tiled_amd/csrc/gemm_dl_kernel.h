@@ -275,8 +275,16 @@ __device__ __forceinline__ void dl_tile(
             if (i == COPIES - 1) b_base += b_step;
         }
     };
-    auto mfma1 = [&](int buf, int q) {                 // MFMA q of a k-step: A block q/TN, B block q%TN
-        const int i = q / TN, j = q % TN;
+    // MFMA q of a k-step: A block q / TN, and B block q % TN walked
+    // serpentine in the prefetch-distance-2 16-bit kernels (reversed on odd A
+    // blocks), so consecutive MFMAs share an operand at every A-block change
+    // too.  Each accumulator still takes its k-steps in the same order (the
+    // same bits); measured +0.8% at bf16 4096^3, unchanged at 8192^3.  The
+    // other kernels read their fragments in this consumption order and keep
+    // the plain walk.
+    auto mfma1 = [&](int buf, int q) {
+        const int i = q / TN, jj = q % TN;
+        const int j = (FD == 2 && !F8 && (i & 1)) ? TN - 1 - jj : jj;
         if constexpr (F8) {
             acc[i][j] = mfma8<IN>(fa8[buf][i], fb8[buf][j], acc[i][j]);
         } else if constexpr (BT) {
