@@ -8,7 +8,7 @@ with eager work between the replays (new A written into the captured buffer,
 C poisoned), and the eager results against the oracle.  Cases cover every
 kernel geometry the selection uses (64x64, 128x128 split over waves or over
 K, 256x256), the general epilogue with column-major B, and 8-bit inputs in
-both B layouts.
+both B layouts; and the allocation-free entry point on the persistent kernel.
 """
 import numpy as np
 import pytest
@@ -112,3 +112,64 @@ def test_graph_replay_matches_eager(G, case):
             assert res["ok"], res
         else:
             assert_bound(y, oracle.gemm_f64(A, B, fmt), K, out, "eager %s" % name, extra=extra)
+
+
+def test_noalloc_graph_replay_matches_gemm_run(G):
+    """gemm_run_noalloc is for callers that cannot allocate, code under graph
+    capture among them: on a shape that selects the persistent kernel (two
+    256x256 tiles per compute unit), the captured call (the fill kernel that
+    clears the library's scheduler array, then the persistent kernel) replays
+    six times, with eager calls of the same entry point between the replays,
+    each replay bit for bit equal to gemm_run's result on the same inputs."""
+    M, N, K, code = 8192, 4096, 256, 3
+    fmt, out = DTYPES[code]
+    As = [law_for(fmt)((M, K), 330 + i, fmt) for i in range(2)]
+    B = law_for(fmt)((K, N), 340, fmt)
+    tA, tB = _dev(As[0]), _dev(B)
+    tC = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    ws = torch.zeros(G.gemm_workspace_size() // 4, dtype=torch.int32, device="cuda")
+    inst = G.gemm_select_instance_ws(M, N, K, code, G.GEMM_B_ROW_MAJOR, tA.data_ptr(), K, tB.data_ptr(), N,
+                                     tC.data_ptr(), N, 1.0, 0.0, None, 0, ws.data_ptr(), ws.numel() * 4)
+    assert G.gemm_instance_name(inst).startswith("pk_"), G.gemm_instance_name(inst)
+
+    def noalloc(stream_handle):
+        return G.gemm_run_noalloc(M, N, K, code, G.GEMM_B_ROW_MAJOR, tA.data_ptr(), K, tB.data_ptr(), N,
+                                  tC.data_ptr(), N, 1.0, 0.0, None, 0, stream_handle)
+
+    plain = []
+    for A in As:
+        tA.copy_(_dev(A))
+        tC.fill_(-1)
+        assert G.gemm_run(M, N, K, code, tA.data_ptr(), K, tB.data_ptr(), N, tC.data_ptr(), N,
+                          torch.cuda.current_stream().cuda_stream) == 0
+        torch.cuda.synchronize()
+        plain.append(tC.cpu().numpy().view(np.uint16).copy())
+        # an eager call first (as a caller would warm up): the library looks up
+        # the array's device address once, outside any capture
+        tC.fill_(-1)
+        assert noalloc(torch.cuda.current_stream().cuda_stream) == 0
+        torch.cuda.synchronize()
+        assert np.array_equal(tC.cpu().numpy().view(np.uint16), plain[-1])
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        st = noalloc(torch.cuda.current_stream().cuda_stream)
+    assert st == 0, G.gemm_strerror(st)
+    torch.cuda.synchronize()
+
+    for it in range(6):
+        i = it % 2
+        tA.copy_(_dev(As[1 - i]))
+        tC.fill_(-1)
+        assert noalloc(torch.cuda.current_stream().cuda_stream) == 0       # eager use of the same array
+        torch.cuda.synchronize()
+        assert np.array_equal(tC.cpu().numpy().view(np.uint16), plain[1 - i]), "eager call %d" % it
+        tA.copy_(_dev(As[i]))
+        tC.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(tC.cpu().numpy().view(np.uint16), plain[i]), "replay %d differs from gemm_run" % it
+    assert_bound(decode_out(plain[0], out), oracle.gemm_f64(As[0], B, fmt), K, out, "persistent 8192x4096x256")
