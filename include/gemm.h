@@ -207,7 +207,10 @@ int gemm_run_ws(int64_t M, int64_t N, int64_t K, int dtype, int b_layout,
  * uses it.  Calls that overlap in time on one device (different streams,
  * concurrent graph replays) race on it and must not be issued; calls ordered
  * on one stream are safe.  When the persistent kernel is selected, a small
- * kernel first clears the array on `stream`.
+ * kernel first clears the array on `stream`.  The first call on a device
+ * looks the array's device address up (hipGetSymbolAddress) and keeps it:
+ * make that first call outside any stream capture; later calls can be
+ * captured into a HIP graph and replayed.
  *
  * Arguments, ownership and status codes as gemm_run_ex; GEMM_ERR_LAUNCH also
  * when the array's device address cannot be obtained.
