@@ -122,7 +122,8 @@ def upload(bits, torch):
     return torch.from_numpy(bits.view(np.int16) if bits.dtype.itemsize == 2 else bits.view(np.int8)).cuda()
 
 
-def measure(G, torch, name, steps, warmup, instance=None, layout=None, settle_ms=200.0, entry="run", relu=0):
+def measure(G, torch, name, steps, warmup, instance=None, layout=None, settle_ms=200.0, entry="run", relu=0,
+            splits=4):
     """Upload a workload, run one correctness launch into a poisoned C, let
     the clock settle (untimed launches for about settle_ms), run `warmup`
     untimed launches, then time `steps` launches.  Returns a dict with the
@@ -130,8 +131,10 @@ def measure(G, torch, name, steps, warmup, instance=None, layout=None, settle_ms
     layout "col" stores B column-major (its transpose row-major) and calls
     gemm_run_ex; "row" calls gemm_run; None takes the workload's own.
     entry "ws" calls gemm_run_ws instead, with a zeroed workspace of
-    gemm_workspace_size() bytes allocated here (before timing).  relu = 1
-    applies ReLU through gemm_run_ex (the general-epilogue kernels)."""
+    gemm_workspace_size() bytes allocated here (before timing); entry
+    "splitk" calls gemm_run_splitk with `splits` pieces of K and its
+    workspace, allocated here too.  relu = 1 applies ReLU through gemm_run_ex
+    (the general-epilogue kernels)."""
     import numpy as np
     from dense_half_precision_tiled_amd import inputs
     A, B, w = inputs.workload_inputs(name)
@@ -153,11 +156,21 @@ def measure(G, torch, name, steps, warmup, instance=None, layout=None, settle_ms
     lay_code = G.GEMM_B_COL_MAJOR if col else G.GEMM_B_ROW_MAJOR
     ws_args = (args[:4] + (lay_code,) + args[4:-1] + (1.0, 0.0, None, relu) +
                ((ws.data_ptr(), G.gemm_workspace_size(), s) if ws is not None else ()))
+    sk_ws, sk_args = None, None
+    if entry == "splitk":
+        need = G.gemm_splitk_workspace_size(M, N, K, splits)
+        if need < 0:
+            raise RuntimeError("gemm_splitk_workspace_size: %s" % G.gemm_strerror(need))
+        sk_ws = torch.empty(need // 4 + 64, dtype=torch.float32, device="cuda")
+        sk_args = (args[:4] + (lay_code,) + args[4:-1] + (1.0, 0.0, None, relu, splits, sk_ws.data_ptr(),
+                                                          sk_ws.numel() * 4, s))
 
-    def launch(_keep=(tA, tB, tC, ws)):
+    def launch(_keep=(tA, tB, tC, ws, sk_ws)):
         # the closure owns the buffers whose addresses `args` holds, so they
         # stay allocated for as long as it can be called
-        if ws is not None:
+        if sk_args is not None:
+            st = G.gemm_run_splitk(*sk_args)
+        elif ws is not None:
             st = G.gemm_run_ws(*ws_args) if instance is None else G.gemm_run_instance_ws(instance, *ws_args)
         elif col or force_ex:
             a = args[:4] + (lay_code,) + args[4:-1] + ex_tail
@@ -199,7 +212,9 @@ def measure(G, torch, name, steps, warmup, instance=None, layout=None, settle_ms
     rep_ms = [evs[i].elapsed_time(evs[i + 1]) / (bounds[i + 1] - bounds[i])
               for i in range(nrep) if bounds[i + 1] > bounds[i]]
     flops = 2.0 * M * N * K
-    if instance is not None:
+    if sk_args is not None:
+        inst = None
+    elif instance is not None:
         inst = instance
     elif ws is not None:
         inst = G.gemm_select_instance_ws(*ws_args[:-1])
@@ -209,12 +224,14 @@ def measure(G, torch, name, steps, warmup, instance=None, layout=None, settle_ms
     else:
         inst = G.gemm_select_instance(M, N, K, code, tA.data_ptr(), K, tB.data_ptr(), N,
                                       tC.data_ptr(), N)
-    return {"name": name, "w": w, "layout": layout, "entry": "gemm_run_ws" if ws is not None else
-            ("gemm_run_ex" if col or force_ex else "gemm_run"), "relu": relu,
+    return {"name": name, "w": w, "layout": layout, "entry": "gemm_run_splitk" if sk_args is not None else
+            "gemm_run_ws" if ws is not None else ("gemm_run_ex" if col or force_ex else "gemm_run"), "relu": relu,
             "A": A, "B": B, "C": tC, "ms": ms, "rep_ms": rep_ms,
             "launch": launch,
             "wall_s": wall, "settle_launches": n_settle,
-            "tflops": flops / (ms * 1e-3) / 1e12, "instance": G.gemm_instance_name(inst),
+            "tflops": flops / (ms * 1e-3) / 1e12,
+            "instance": ("splitk_%d" % splits if splits else "splitk_auto") if inst is None else
+            G.gemm_instance_name(inst),
             "alg_bytes": (1 if w["fmt"] in EIGHT_BIT else 2) * (M * K + K * N) + (4 if w["out"] == "f32" else 2) * M * N}
 
 
@@ -478,7 +495,8 @@ def observed(torch, res, seconds: float) -> dict:
     p = clock_window(torch, plaunch, pflops, seconds)
     p["kernel_mhz"] = plaunch.kernel_mhz()
     nominal = FLOP_PER_CLK_CU8 if fmt == "e4m3" else FLOP_PER_CLK_CU
-    kc = kernel_clock(res["name"], "ws" if res["entry"] == "gemm_run_ws" else "run")
+    kc = None if res["entry"] == "gemm_run_splitk" else kernel_clock(
+        res["name"], "ws" if res["entry"] == "gemm_run_ws" else "run")
     out = {"gemm_window": g, "probe_window": p, "gemm_kernel_clock": kc,
            "probe": "bench_probe.hip MFMA-only loop, %s operand data, one workgroup per CU" % fmt,
            "frac_of_probe_peak": round(res["tflops"] / p["tflops"], 4),
@@ -779,8 +797,11 @@ def main(argv=None):
     ap.add_argument("--relu", action="store_true",
                     help="apply ReLU in the epilogue (gemm_run_ex: the general-epilogue kernels), e.g. to price "
                          "their cost against the plain ones")
-    ap.add_argument("--entry", choices=("run", "ws"), default="run",
-                    help="call gemm_run / gemm_run_ex (run) or gemm_run_ws with a caller-owned workspace (ws)")
+    ap.add_argument("--entry", choices=("run", "ws", "splitk"), default="run",
+                    help="call gemm_run / gemm_run_ex (run), gemm_run_ws with a caller-owned workspace (ws), or "
+                         "gemm_run_splitk with --splits pieces of K (splitk; 16-bit workloads only)")
+    ap.add_argument("--splits", type=int, default=4,
+                    help="pieces of K for --entry splitk (0: the library's choice)")
     ap.add_argument("--layout", choices=("row", "col"), default=None,
                     help="storage order of B: row-major (gemm_run) or column-major (gemm_run_ex); "
                          "default: the workload's own (row-major for the 16-bit ones, column-major for 8-bit)")
@@ -840,6 +861,9 @@ def main(argv=None):
 
     from dense_half_precision_tiled_amd import gemm as G
     if args.timeline > 0:
+        if args.entry == "splitk":
+            print("--timeline records the one-kernel entry points (run, ws)", file=sys.stderr)
+            return 2
         from dense_half_precision_tiled_amd import build as B
         lib = G.load(B.TIMELINE_LIB)
         lib.gemm_timeline_set.argtypes = [ctypes.c_void_p, ctypes.c_int64]
@@ -850,7 +874,7 @@ def main(argv=None):
         return loop_for(G, torch, args.workload, args.loop_seconds)
 
     main_res = measure(G, torch, args.workload, args.steps, args.warmup, args.instance, args.layout,
-                       args.settle_ms, args.entry, int(args.relu))
+                       args.settle_ms, args.entry, int(args.relu), args.splits)
 
     def summary(r):
         w2 = r["w"]
@@ -866,16 +890,19 @@ def main(argv=None):
     sec = None
     if args.secondary and args.secondary != "none":
         r2 = measure(G, torch, args.secondary, max(args.steps, 50), args.warmup, args.instance,
-                     args.layout, args.settle_ms, args.entry, int(args.relu))
+                     args.layout, args.settle_ms, args.entry, int(args.relu), args.splits)
         sec = summary(r2)
         if args.clock_seconds > 0:
             sec["observed"] = observed(torch, r2, args.clock_seconds)
         del r2
     others = []
     if args.also and args.also != "none" and args.instance is None:
+        from dense_half_precision_tiled_amd import inputs as I3
         for name in args.also.split(","):
+            if args.entry == "splitk" and I3.WORKLOADS[name]["fmt"] in EIGHT_BIT:
+                continue                     # gemm_run_splitk takes 16-bit inputs only
             r3 = measure(G, torch, name, max(args.steps, 200), args.warmup, None, args.layout,
-                         args.settle_ms, args.entry, int(args.relu))
+                         args.settle_ms, args.entry, int(args.relu), args.splits)
             others.append(summary(r3))
             del r3
 

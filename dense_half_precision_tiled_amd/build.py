@@ -19,7 +19,8 @@ ARCH = "gfx950"
 SOURCES = ["gemm_api.cpp", "gemm_instances.hip", "gemm_dl_nn.hip", "gemm_dl_nn_epi.hip",
            "gemm_dl_tn.hip", "gemm_dl_tn_epi.hip", "gemm_ks.hip", "gemm_ks_epi.hip",
            "gemm_dl_f8_tn.hip", "gemm_dl_f8_tn_epi.hip", "gemm_dl_f8_nn.hip", "gemm_dl_f8_nn_epi.hip",
-           "gemm_pk_nn.hip", "gemm_pk_nn_epi.hip", "gemm_pk_tn.hip", "gemm_pk_tn_epi.hip", "gemm_pp.hip"]
+           "gemm_pk_nn.hip", "gemm_pk_nn_epi.hip", "gemm_pk_tn.hip", "gemm_pk_tn_epi.hip", "gemm_pp.hip",
+           "gemm_sk.hip"]
 
 # Packed-fp32 VALU ops stay disabled in every HIP translation unit.
 HIP_FLAGS = ["-x", "hip", "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",

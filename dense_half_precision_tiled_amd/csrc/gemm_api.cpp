@@ -18,6 +18,7 @@ using dhpt::Problem;
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxLd = int64_t(1) << 40;
 constexpr int64_t kMaxExtent = int64_t(1) << 47;   // elements spanned by one operand
+constexpr int kMaxSplits = 64;                        // gemm_run_splitk: pieces of K
 
 int out_elem_size(int dtype) { return dhpt::dtype_out_f32(dtype) ? 4 : 2; }
 int in_elem_size(int dtype) { return dhpt::dtype_in8(dtype) ? 1 : 2; }
@@ -366,6 +367,86 @@ int gemm_run_noalloc(int64_t M, int64_t N, int64_t K, int dtype, int b_layout, c
         if (hipGetLastError() != hipSuccess) return GEMM_ERR_LAUNCH;
     }
     return run_validated(inst, p, s);
+}
+
+// splits == 0 for gemm_run_splitk: split only where even 128x128 tiles leave
+// more than half the compute units idle (fewer than 128 of them) and K is
+// long (>= 4096): enough pieces to give the 256 CUs a workgroup each, but no
+// piece shorter than 2048 (measured on one box, bf16/fp16 TFLOP/s:
+// 1024 x 1024 x 16384 390 unsplit, 699 in 8 pieces, 654 in 16;
+// 512 x 512 x 32768 57 unsplit, 375 in 16; 2048 x 2048 x 8192 934 unsplit
+// on the k-split kernel, 794 in 4 pieces).  1 means no split.
+int splitk_auto(int64_t M, int64_t N, int64_t K) {
+    if (tiles_for(128, M, N) >= 128 || K < 4096) return 1;
+    const int64_t t256 = tiles_for(256, M, N);
+    int64_t s = (256 + t256 - 1) / t256;
+    if (s > K / 2048) s = K / 2048;
+    if (s > kMaxSplits) s = kMaxSplits;
+    return s < 1 ? 1 : (int)s;
+}
+
+int64_t gemm_splitk_workspace_size(int64_t M, int64_t N, int64_t K, int splits) {
+    if (M < 0 || N < 0 || K < 0) return GEMM_ERR_DIM;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim || splits < 0 || splits > kMaxSplits) return GEMM_ERR_RANGE;
+    if (M == 0 || N == 0 || K == 0) return 0;
+    if (splits == 0) {
+        splits = splitk_auto(M, N, K);
+        if (splits == 1) return 0;                      // runs unsplit: no workspace
+    }
+    int Kc = 0;
+    const int64_t pieces = dhpt::splitk_pieces((int)K, splits, &Kc);
+    return tiles_for(256, M, N) * pieces * 256 * 256 * 4;
+}
+
+int gemm_run_splitk(int64_t M, int64_t N, int64_t K, int dtype, int b_layout, const void* A, int64_t lda,
+                    const void* B, int64_t ldb, void* C, int64_t ldc, float alpha, float beta,
+                    const float* bias, int relu, int splits, void* workspace, int64_t workspace_bytes,
+                    void* stream) {
+    Problem p;
+    bool noop;
+    int st = validate(M, N, K, dtype, A, lda, B, ldb, C, ldc, extra(b_layout, alpha, beta, bias, relu), &p, &noop);
+    if (st != GEMM_OK) return st;
+    if (dhpt::dtype_in8(dtype)) return GEMM_ERR_DTYPE;
+    if (splits < 0 || splits > kMaxSplits) return GEMM_ERR_RANGE;
+    if (noop) return GEMM_OK;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p.K == 0) return run_validated(-1, p, s);          // no product to split: act(beta*C + bias) or zeros
+    if (splits == 0) {
+        splits = splitk_auto(M, N, K);
+        if (splits == 1) return run_validated(-1, p, s);  // not worth splitting: gemm_run_ex's kernels
+    }
+    const int64_t need = gemm_splitk_workspace_size(M, N, K, splits);
+    if (workspace == nullptr || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+        return GEMM_ERR_WORKSPACE;
+    int Kc = 0;
+    const int64_t pieces = dhpt::splitk_pieces(p.K, splits, &Kc);
+    if (tiles_for(256, M, N) * pieces > (int64_t(1) << 24)) return GEMM_ERR_RANGE;
+    {
+        const bool tb = b_layout == GEMM_B_COL_MAJOR;
+        const int osz = out_elem_size(dtype), isz = in_elem_size(dtype);
+        uintptr_t c0, c1, a0, a1, b0, b1;
+        extent(C, M, N, ldc, osz, &c0, &c1);
+        extent(A, M, K, lda, isz, &a0, &a1);
+        extent(B, tb ? N : K, tb ? K : N, ldb, isz, &b0, &b1);
+        const uintptr_t w0 = reinterpret_cast<uintptr_t>(workspace), w1 = w0 + (uintptr_t)need;
+        if (overlaps(w0, w1, c0, c1) || overlaps(w0, w1, a0, a1) || overlaps(w0, w1, b0, b1)) return GEMM_ERR_ALIAS;
+        if (bias != nullptr) {
+            const uintptr_t z0 = reinterpret_cast<uintptr_t>(bias), z1 = z0 + (uintptr_t)(4 * N);
+            if (overlaps(w0, w1, z0, z1)) return GEMM_ERR_ALIAS;
+        }
+    }
+    // The pieces run the 256x256 tile of instance 0 (whole tiles) or 1
+    // (clamped edges) on sub-problems with the same leading dimensions, so
+    // those instances' limits apply.
+    const bool whole = M % 256 == 0 && N % 256 == 0 && K % 64 == 0;
+    int edge;
+    if (whole && dhpt::instance_supports(0, p)) edge = dhpt::EDGE_NONE;
+    else if (dhpt::instance_supports(1, p)) edge = dhpt::EDGE_CLAMP;
+    else return GEMM_ERR_INSTANCE;
+    (void)hipGetLastError();
+    const hipError_t err = dhpt::launch_splitk(p, splits, edge, static_cast<float*>(workspace),
+                                               dhpt::kInstances[0].group_m, s);
+    return err == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
 int gemm_num_instances(void) { return dhpt::kNumInstances; }

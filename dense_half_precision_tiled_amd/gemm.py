@@ -1,7 +1,8 @@
 """Python binding of libdhpt_gemm.so (argument marshalling only).
 
 The functions mirror include/gemm.h one to one (``gemm_run``, ``gemm_run_ex``,
-``gemm_run_ws``, ``gemm_run_noalloc``, ``gemm_workspace_size``, ``gemm_strerror``,
+``gemm_run_ws``, ``gemm_run_noalloc``, ``gemm_run_splitk``, ``gemm_workspace_size``,
+``gemm_splitk_workspace_size``, ``gemm_strerror``,
 ``gemm_select_instance``, ``gemm_select_instance_ex``,
 ``gemm_select_instance_ws``, ``gemm_num_instances``, ``gemm_instance_name``,
 ``gemm_run_instance``, ``gemm_run_instance_ex``, ``gemm_run_instance_ws``,
@@ -35,7 +36,7 @@ EXPORTED = ["gemm_run", "gemm_run_ex", "gemm_strerror", "gemm_select_instance",
             "gemm_select_instance_ex", "gemm_num_instances", "gemm_instance_name",
             "gemm_run_instance", "gemm_run_instance_ex", "gemm_tile_order",
             "gemm_workspace_size", "gemm_run_ws", "gemm_run_instance_ws", "gemm_select_instance_ws",
-            "gemm_run_noalloc"]
+            "gemm_run_noalloc", "gemm_splitk_workspace_size", "gemm_run_splitk"]
 
 _lib = None
 
@@ -91,6 +92,10 @@ def load(lib_path: str | None = None) -> ctypes.CDLL:
         lib.gemm_select_instance_ws.restype = i32
         lib.gemm_run_noalloc.argtypes = lib.gemm_run_ex.argtypes
         lib.gemm_run_noalloc.restype = i32
+        lib.gemm_splitk_workspace_size.argtypes = [i64, i64, i64, i32]
+        lib.gemm_splitk_workspace_size.restype = i64
+        lib.gemm_run_splitk.argtypes = lib.gemm_run_ex.argtypes[:-1] + [i32, vp, i64, vp]
+        lib.gemm_run_splitk.restype = i32
         _lib = lib
     return _lib
 
@@ -151,6 +156,16 @@ def gemm_run_noalloc(M, N, K, dtype, b_layout, A, lda, B, ldb, C, ldc, alpha=1.0
                      relu=0, stream=None) -> int:
     return load().gemm_run_noalloc(M, N, K, dtype, b_layout, A, lda, B, ldb, C, ldc, alpha, beta, bias, relu,
                                    stream)
+
+
+def gemm_splitk_workspace_size(M, N, K, splits) -> int:
+    return load().gemm_splitk_workspace_size(M, N, K, splits)
+
+
+def gemm_run_splitk(M, N, K, dtype, b_layout, A, lda, B, ldb, C, ldc, alpha, beta, bias, relu, splits,
+                    workspace, workspace_bytes, stream=None) -> int:
+    return load().gemm_run_splitk(M, N, K, dtype, b_layout, A, lda, B, ldb, C, ldc, alpha, beta, bias, relu,
+                                  splits, workspace, workspace_bytes, stream)
 
 
 def gemm_strerror(status: int) -> str:

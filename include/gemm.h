@@ -220,6 +220,61 @@ int gemm_run_noalloc(int64_t M, int64_t N, int64_t K, int dtype, int b_layout,
                      void* C, int64_t ldc, float alpha, float beta,
                      const float* bias, int relu, void* stream);
 
+/*
+ * gemm_splitk_workspace_size -- bytes of workspace gemm_run_splitk needs for
+ * an M x N x K problem cut into `splits` pieces of K: one fp32 256 x 256
+ * partial tile per output tile of 256 x 256 and per piece,
+ * ceil(M/256) * ceil(N/256) * pieces * 262144 bytes, where pieces =
+ * ceil(K / Kc) with Kc = ceil(K / splits) rounded up to a multiple of 64
+ * (so pieces <= splits).  0 when M, N or K is 0.  splits = 0 asks for the
+ * library's choice (below) and gives 0 where that choice is not to split.
+ * GEMM_ERR_DIM for a negative size, GEMM_ERR_RANGE for a size >= 2^31 or
+ * splits outside 0 .. 64.  No GPU call.
+ *
+ * gemm_run_splitk -- gemm_run_ex with K cut into pieces computed by different
+ * workgroups (the work-splitting half of the stream-K scheduling in "The
+ * Asynchronous Kernel: Tensor Cores & TMA", section "Keeping the line busy"),
+ * for outputs with too few 256 x 256 tiles to occupy the GPU when K is long.
+ * A first kernel computes, for every (output tile, piece), that piece's fp32
+ * partial product into the workspace; a second kernel on the same stream adds
+ * each element's partials in piece order (the result does not depend on
+ * which workgroup finished first: repeated calls give the same bits),
+ * applies act(alpha * sum + beta * C + bias[j]) in fp32 as gemm_run_ex does
+ * and rounds once to the output type.  The k order differs from gemm_run's,
+ * so results agree with it within the accumulation bound, not bit for bit
+ * (with splits = 1 they are gemm_run_instance_ex's on the 256 x 256 instance,
+ * bit for bit).
+ *
+ *   splits           requested pieces of K, 1 .. 64, or 0 for the library's
+ *                    choice: split only when fewer than 128 tiles of 128 x 128
+ *                    cover the output (more than half the GPU idle even on
+ *                    the k-split kernel) and K >= 4096, into
+ *                    min(ceil(256 / tiles of 256 x 256), K / 2048, 64) pieces;
+ *                    otherwise run unsplit, exactly as gemm_run_ex (no
+ *                    workspace used).  GEMM_ERR_RANGE outside 0 .. 64.
+ *   workspace        device pointer, 256-byte aligned, at least
+ *                    gemm_splitk_workspace_size(M, N, K, splits) bytes, on
+ *                    the current device, owned by the caller; no initial
+ *                    contents are needed.  It must not overlap A, B, C or the
+ *                    bias (GEMM_ERR_ALIAS).  Calls that may run at the same
+ *                    time need different workspaces.
+ *   workspace_bytes  its size in bytes.
+ *
+ * 16-bit input dtypes only (GEMM_ERR_DTYPE for the 8-bit ones).  Other
+ * arguments, ownership and status codes as gemm_run_ex, plus
+ * GEMM_ERR_WORKSPACE; GEMM_ERR_INSTANCE when the 256 x 256 kernels cannot run
+ * the shape (row-major B with N % 8 != 0 and a partial tile, or leading
+ * dimensions too large for their 32-bit offsets).  K == 0 needs no workspace
+ * and runs as gemm_run_ex.  No allocation, no host synchronisation.
+ */
+int64_t gemm_splitk_workspace_size(int64_t M, int64_t N, int64_t K, int splits);
+
+int gemm_run_splitk(int64_t M, int64_t N, int64_t K, int dtype, int b_layout,
+                    const void* A, int64_t lda, const void* B, int64_t ldb,
+                    void* C, int64_t ldc, float alpha, float beta,
+                    const float* bias, int relu, int splits, void* workspace,
+                    int64_t workspace_bytes, void* stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* gemm_strerror(int status);
 

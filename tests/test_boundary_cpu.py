@@ -344,3 +344,40 @@ def test_persistent_instances_need_a_workspace(lib):
         st = G.gemm_run_instance_ex(ids[name], 512, 512, 512, 3, 1, PA, 512, PB, 512, PC, 512,
                                     1.0, 0.0, None, 0, None)
         assert st == G.GEMM_ERR_INSTANCE
+
+
+def test_splitk_workspace_size(lib):
+    """One fp32 256 x 256 partial tile per output tile and per piece of K;
+    pieces of ceil(K / splits) rounded up to 64, so fewer pieces than asked
+    for when K is short."""
+    tile = 256 * 256 * 4
+    assert G.gemm_splitk_workspace_size(2048, 2048, 2048, 4) == 64 * 4 * tile
+    assert G.gemm_splitk_workspace_size(1000, 1000, 100, 4) == 16 * 2 * tile      # Kc = 64: two pieces
+    assert G.gemm_splitk_workspace_size(1024, 1024, 16384, 16) == 16 * 16 * tile
+    assert G.gemm_splitk_workspace_size(300, 5000, 4099, 3) == 2 * 20 * 3 * tile  # Kc = 1408
+    assert G.gemm_splitk_workspace_size(256, 256, 0, 4) == 0
+    # splits = 0: the library's choice
+    assert G.gemm_splitk_workspace_size(1024, 1024, 16384, 0) == 16 * 8 * tile       # 8 pieces of 2048
+    assert G.gemm_splitk_workspace_size(512, 512, 32768, 0) == 4 * 16 * tile         # 16 pieces
+    assert G.gemm_splitk_workspace_size(2048, 2048, 8192, 0) == 0                    # 256 tiles of 128^2: unsplit
+    assert G.gemm_splitk_workspace_size(512, 512, 2048, 0) == 0                      # K too short
+    assert G.gemm_splitk_workspace_size(256, 256, 256, -1) == G.GEMM_ERR_RANGE
+    assert G.gemm_splitk_workspace_size(-1, 256, 256, 4) == G.GEMM_ERR_DIM
+    assert G.gemm_splitk_workspace_size(256, 256, 256, 65) == G.GEMM_ERR_RANGE
+
+
+def test_splitk_arguments_rejected_before_launch(lib):
+    M = N = K = 512
+    need = G.gemm_splitk_workspace_size(M, N, K, 4)
+    args = (M, N, K, 3, 0, PA, K, PB, N, PC, N, 1.0, 0.0, None, 0)
+    assert G.gemm_run_splitk(*args, 4, 0, need, None) == G.GEMM_ERR_WORKSPACE             # no workspace
+    assert G.gemm_run_splitk(*args, 4, WS, need - 1, None) == G.GEMM_ERR_WORKSPACE        # too small
+    assert G.gemm_run_splitk(*args, 4, WS + 4, need, None) == G.GEMM_ERR_WORKSPACE        # misaligned
+    assert G.gemm_run_splitk(*args, -1, WS, need, None) == G.GEMM_ERR_RANGE
+    assert G.gemm_run_splitk(*args, 65, WS, need, None) == G.GEMM_ERR_RANGE
+    assert G.gemm_run_splitk(*args, 4, PC, need, None) == G.GEMM_ERR_ALIAS                # inside C
+    assert G.gemm_run_splitk(M, N, K, 6, 0, PA, K, PB, N, PC, N, 1.0, 0.0, None, 0, 4, WS, need,
+                             None) == G.GEMM_ERR_DTYPE                                      # 8-bit inputs
+    assert G.gemm_run_splitk(-1, N, K, 3, 0, PA, K, PB, N, PC, N, 1.0, 0.0, None, 0, 4, WS, need,
+                             None) == G.GEMM_ERR_DIM
+    assert G.gemm_run_splitk(0, N, K, 3, 0, PA, K, PB, N, PC, N, 1.0, 0.0, None, 0, 4, 0, 0, None) == G.GEMM_OK

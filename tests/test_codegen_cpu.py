@@ -28,7 +28,8 @@ from dense_half_precision_tiled_amd import build as B
 UNITS = ["gemm_dl_nn.hip", "gemm_dl_nn_epi.hip", "gemm_dl_tn.hip", "gemm_dl_tn_epi.hip",
          "gemm_ks.hip", "gemm_ks_epi.hip", "gemm_dl_f8_tn.hip", "gemm_dl_f8_tn_epi.hip",
          "gemm_dl_f8_nn.hip", "gemm_dl_f8_nn_epi.hip",
-         "gemm_pk_nn.hip", "gemm_pk_nn_epi.hip", "gemm_pk_tn.hip", "gemm_pk_tn_epi.hip", "gemm_pp.hip"]
+         "gemm_pk_nn.hip", "gemm_pk_nn_epi.hip", "gemm_pk_tn.hip", "gemm_pk_tn_epi.hip", "gemm_pp.hip",
+         "gemm_sk.hip"]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(B.hipcc()), reason="hipcc not available")
 
@@ -121,8 +122,9 @@ def test_no_scratch_inside_the_mfma_loop(kernels):
 
 def test_whole_tile_plain_kernels_use_no_scratch(kernels):
     # template arguments <IN, OUT, BM, BN, FD, EDGE=0, BT, EPI=false> (dl and
-    # its persistent form), <IN, OUT, EDGE=0, BT, EPI=false> (ks) and
-    # <IN, OUT, BT, EPI=false> (pp)
+    # its persistent form), <IN, OUT, EDGE=0, BT, EPI=false> (ks),
+    # <IN, OUT, BT, EPI=false> (pp) and <IN, EDGE=0, BT> (sk: fp32 partial
+    # tiles, no epilogue)
     checked = 0
     for name, (unit, ins, meta) in kernels.items():
         args = re.findall(r"Li(\d+)E|Lb(\d)E", _short(name))
@@ -131,6 +133,8 @@ def test_whole_tile_plain_kernels_use_no_scratch(kernels):
             edge, epi = vals[5], vals[7]
         elif "gemm_pp" in name:                 # <IN, OUT, BT, EPI>: whole tiles only
             edge, epi = 0, vals[3]
+        elif "gemm_sk" in name:                 # <IN, EDGE, BT>
+            edge, epi = vals[1], 0
         else:
             edge, epi = vals[2], vals[4]
         if edge == 0 and epi == 0:
