@@ -371,16 +371,20 @@ int gemm_run_noalloc(int64_t M, int64_t N, int64_t K, int dtype, int b_layout, c
 
 // splits == 0 for gemm_run_splitk: split only where even 128x128 tiles leave
 // more than half the compute units idle (fewer than 128 of them) and K is
-// long (>= 4096): enough pieces to give the 256 CUs a workgroup each, but no
-// piece shorter than 2048 (measured on one box, bf16/fp16 TFLOP/s:
-// 1024 x 1024 x 16384 390 unsplit, 699 in 8 pieces, 654 in 16;
-// 512 x 512 x 32768 57 unsplit, 375 in 16; 2048 x 2048 x 8192 934 unsplit
-// on the k-split kernel, 794 in 4 pieces).  1 means no split.
+// long (>= 4096), into enough pieces for about 192 workgroups (three
+// quarters of the CUs: more pieces add partial-tile traffic faster than they
+// add compute), but none shorter than 1024.  Fitted on a sweep of 2 .. 64
+// pieces (one box, bf16 TFLOP/s, unsplit -> this rule -> best): 512^2 x 32768
+// 57 -> 446 (32 pieces, the best); 1024^2 x 16384 390 -> 719 (12, the best);
+// 768^2 x 16384 129 -> 512 (16, the best); 1024^2 x 8192 364 -> 516 (8, the
+// best); 512^2 x 8192 58 -> 156 (8; 183 at 16); 256^2 x 65536 15 -> 201 (64,
+// the best); and 1024 x 2048 x 8192, 128 tiles of 128^2, stays unsplit (699
+// on the k-split kernel, 675 in 4 pieces).  1 means no split.
 int splitk_auto(int64_t M, int64_t N, int64_t K) {
     if (tiles_for(128, M, N) >= 128 || K < 4096) return 1;
     const int64_t t256 = tiles_for(256, M, N);
-    int64_t s = (256 + t256 - 1) / t256;
-    if (s > K / 2048) s = K / 2048;
+    int64_t s = (192 + t256 - 1) / t256;
+    if (s > K / 1024) s = K / 1024;
     if (s > kMaxSplits) s = kMaxSplits;
     return s < 1 ? 1 : (int)s;
 }

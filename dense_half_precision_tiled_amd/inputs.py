@@ -112,6 +112,9 @@ WORKLOADS = {
     "e4m3_4096": dict(M=4096, N=4096, K=4096, fmt=E4M3, out="bf16", law="normal", c=7, layout="col"),
     "e5m2_8192": dict(M=8192, N=8192, K=8192, fmt=E5M2, out="bf16", law="normal", c=8, layout="col"),
     "e4m3_2048": dict(M=2048, N=2048, K=2048, fmt=E4M3, out="f32", law="normal", c=9, layout="col"),
+    # long K with few output tiles (the case for splitting K across workgroups)
+    "bf16_longk_1024": dict(M=1024, N=1024, K=16384, fmt=BF16, out="bf16", law="normal", c=10),
+    "bf16_longk_512": dict(M=512, N=512, K=32768, fmt=BF16, out="bf16", law="normal", c=11),
 }
 
 

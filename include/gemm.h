@@ -249,7 +249,7 @@ int gemm_run_noalloc(int64_t M, int64_t N, int64_t K, int dtype, int b_layout,
  *                    choice: split only when fewer than 128 tiles of 128 x 128
  *                    cover the output (more than half the GPU idle even on
  *                    the k-split kernel) and K >= 4096, into
- *                    min(ceil(256 / tiles of 256 x 256), K / 2048, 64) pieces;
+ *                    min(ceil(192 / tiles of 256 x 256), K / 1024, 64) pieces;
  *                    otherwise run unsplit, exactly as gemm_run_ex (no
  *                    workspace used).  GEMM_ERR_RANGE outside 0 .. 64.
  *   workspace        device pointer, 256-byte aligned, at least

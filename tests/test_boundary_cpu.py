@@ -357,8 +357,9 @@ def test_splitk_workspace_size(lib):
     assert G.gemm_splitk_workspace_size(300, 5000, 4099, 3) == 2 * 20 * 3 * tile  # Kc = 1408
     assert G.gemm_splitk_workspace_size(256, 256, 0, 4) == 0
     # splits = 0: the library's choice
-    assert G.gemm_splitk_workspace_size(1024, 1024, 16384, 0) == 16 * 8 * tile       # 8 pieces of 2048
-    assert G.gemm_splitk_workspace_size(512, 512, 32768, 0) == 4 * 16 * tile         # 16 pieces
+    assert G.gemm_splitk_workspace_size(1024, 1024, 16384, 0) == 16 * 12 * tile      # 12 pieces of 1408
+    assert G.gemm_splitk_workspace_size(512, 512, 32768, 0) == 4 * 32 * tile         # 32 pieces of 1024
+    assert G.gemm_splitk_workspace_size(256, 256, 65536, 0) == 1 * 64 * tile         # capped at 64
     assert G.gemm_splitk_workspace_size(2048, 2048, 8192, 0) == 0                    # 256 tiles of 128^2: unsplit
     assert G.gemm_splitk_workspace_size(512, 512, 2048, 0) == 0                      # K too short
     assert G.gemm_splitk_workspace_size(256, 256, 256, -1) == G.GEMM_ERR_RANGE
