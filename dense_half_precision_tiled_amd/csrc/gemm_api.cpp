@@ -398,7 +398,9 @@ int64_t gemm_splitk_workspace_size(int64_t M, int64_t N, int64_t K, int splits) 
         if (splits == 1) return 0;                      // runs unsplit: no workspace
     }
     int Kc = 0;
-    const int64_t pieces = dhpt::splitk_pieces((int)K, splits, &Kc);
+    // pieces of 64-multiple length: the 16-bit count, which bounds the 8-bit
+    // one (pieces of 128-multiple length, never more of them)
+    const int64_t pieces = dhpt::splitk_pieces((int)K, splits, 64, &Kc);
     return tiles_for(256, M, N) * pieces * 256 * 256 * 4;
 }
 
@@ -410,7 +412,6 @@ int gemm_run_splitk(int64_t M, int64_t N, int64_t K, int dtype, int b_layout, co
     bool noop;
     int st = validate(M, N, K, dtype, A, lda, B, ldb, C, ldc, extra(b_layout, alpha, beta, bias, relu), &p, &noop);
     if (st != GEMM_OK) return st;
-    if (dhpt::dtype_in8(dtype)) return GEMM_ERR_DTYPE;
     if (splits < 0 || splits > kMaxSplits) return GEMM_ERR_RANGE;
     if (noop) return GEMM_OK;
     const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -422,8 +423,9 @@ int gemm_run_splitk(int64_t M, int64_t N, int64_t K, int dtype, int b_layout, co
     const int64_t need = gemm_splitk_workspace_size(M, N, K, splits);
     if (workspace == nullptr || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
         return GEMM_ERR_WORKSPACE;
+    const bool in8 = dhpt::dtype_in8(dtype);
     int Kc = 0;
-    const int64_t pieces = dhpt::splitk_pieces(p.K, splits, &Kc);
+    const int64_t pieces = dhpt::splitk_pieces(p.K, splits, in8 ? 128 : 64, &Kc);
     if (tiles_for(256, M, N) * pieces > (int64_t(1) << 24)) return GEMM_ERR_RANGE;
     {
         const bool tb = b_layout == GEMM_B_COL_MAJOR;
@@ -439,13 +441,14 @@ int gemm_run_splitk(int64_t M, int64_t N, int64_t K, int dtype, int b_layout, co
             if (overlaps(w0, w1, z0, z1)) return GEMM_ERR_ALIAS;
         }
     }
-    // The pieces run the 256x256 tile of instance 0 (whole tiles) or 1
-    // (clamped edges) on sub-problems with the same leading dimensions, so
-    // those instances' limits apply.
-    const bool whole = M % 256 == 0 && N % 256 == 0 && K % 64 == 0;
+    // The pieces run the 256x256 tile of instance 0 / 14 (whole tiles) or
+    // 1 / 15 (clamped edges; 16-bit / 8-bit inputs) on sub-problems with the
+    // same leading dimensions, so those instances' limits apply.
+    const int whole_id = in8 ? 14 : 0, clamp_id = in8 ? 15 : 1;
+    const bool whole = M % 256 == 0 && N % 256 == 0 && K % (in8 ? 128 : 64) == 0;
     int edge;
-    if (whole && dhpt::instance_supports(0, p)) edge = dhpt::EDGE_NONE;
-    else if (dhpt::instance_supports(1, p)) edge = dhpt::EDGE_CLAMP;
+    if (whole && dhpt::instance_supports(whole_id, p)) edge = dhpt::EDGE_NONE;
+    else if (dhpt::instance_supports(clamp_id, p)) edge = dhpt::EDGE_CLAMP;
     else return GEMM_ERR_INSTANCE;
     (void)hipGetLastError();
     const hipError_t err = dhpt::launch_splitk(p, splits, edge, static_cast<float*>(workspace),

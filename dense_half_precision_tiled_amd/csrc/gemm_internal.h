@@ -105,11 +105,12 @@ hipError_t launch_pk_tn_epi(int edge, const Problem& p, int group_m, hipStream_t
 // The ping-pong 256x256 kernel (16-bit inputs, whole tiles, both B layouts),
 // `ph` k-steps per phase (2 or 4).
 hipError_t launch_pp(int ph, const Problem& p, int group_m, hipStream_t stream);
-// Split-K across workgroups (gemm_sk.hip, 16-bit inputs, 256x256 tiles): the
-// pieces launched for `splits` requested and their length Kc (a multiple of
-// 64), and the two launches (partial tiles into `ws`, then their sum and the
-// epilogue into C); `edge` is EDGE_NONE or EDGE_CLAMP.
-int splitk_pieces(int K, int splits, int* Kc);
+// Split-K across workgroups (gemm_sk.hip, 256x256 tiles): the pieces
+// launched for `splits` requested and their length Kc (a multiple of `gran`,
+// the slice depth: 64 for 16-bit inputs, 128 for 8-bit ones), and the two
+// launches (partial tiles into `ws`, then their sum and the epilogue into C);
+// `edge` is EDGE_NONE or EDGE_CLAMP.
+int splitk_pieces(int K, int splits, int gran, int* Kc);
 hipError_t launch_splitk(const Problem& p, int splits, int edge, float* ws, int group_m, hipStream_t stream);
 
 // Workgroup id -> output tile (tm, tn), in two steps, both bijections of

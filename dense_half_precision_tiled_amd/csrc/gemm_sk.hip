@@ -3,8 +3,9 @@
 // "Keeping the line busy"), for outputs with too few 256x256 tiles to occupy
 // the 256 CUs when K is long.
 //
-// The K range is cut into S pieces of Kc = ceil(K / S / 64) * 64 (the last
-// one shorter), and the launch runs one workgroup per (tile, piece): each
+// The K range is cut into S pieces of Kc = ceil(K / S) rounded up to the
+// slice depth (64 for 16-bit inputs, 128 for 8-bit ones; the last piece
+// shorter), and the launch runs one workgroup per (tile, piece): each
 // computes its tile's product over its piece of K with the 256x256
 // direct-to-LDS tile of gemm_dl_kernel.h (dl_tile, unchanged: the piece is a
 // smaller GEMM with the same leading dimensions, A offset by k0 columns and B
@@ -36,6 +37,8 @@ template <int IN, int EDGE, bool BT>
 __global__ __launch_bounds__(256, 1) void gemm_sk_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
     float* __restrict__ ws, int M, int N, int K, int Kc, int tilesM, int tilesN, int group_m) {
+    constexpr int ESZ = kIn8<IN> ? 1 : 2;                // bytes per input element
+    constexpr int FD = kIn8<IN> ? 1 : 2;                 // the 256x256 instance's fragment prefetch
     __shared__ __attribute__((aligned(1024))) char smem[dl_lds_bytes<IN, kTile, kTile, EDGE, BT>()];
     const int T = tilesM * tilesN;
     const int s = blockIdx.x / T;
@@ -46,15 +49,19 @@ __global__ __launch_bounds__(256, 1) void gemm_sk_kernel(
     const int Mt = M - m0 < kTile ? M - m0 : kTile;
     const int Nt = N - n0 < kTile ? N - n0 : kTile;
     const int Kt = K - k0 < Kc ? K - k0 : Kc;           // >= 1: the host launches only pieces inside K
-    const uint16_t* As = A + (int64_t)m0 * lda + k0;
-    const uint16_t* Bs = BT ? B + (int64_t)n0 * ldb + k0 : B + (int64_t)k0 * ldb + n0;
+    // element offsets, applied in bytes (the operands are byte streams of ESZ-byte elements)
+    const char* Ab = reinterpret_cast<const char*>(A);
+    const char* Bb = reinterpret_cast<const char*>(B);
+    const uint16_t* As = reinterpret_cast<const uint16_t*>(Ab + ((int64_t)m0 * lda + k0) * ESZ);
+    const uint16_t* Bs = reinterpret_cast<const uint16_t*>(
+        Bb + (BT ? (int64_t)n0 * ldb + k0 : (int64_t)k0 * ldb + n0) * ESZ);
     float* P = ws + (((int64_t)s * tilesM + tm) * tilesN + tn) * kTileFloats;
     EpiArgs ep{1.0f, 0.0f, nullptr, 0};
 #ifdef DHPT_TIMELINE
     ep.timeline = nullptr;
 #endif
-    dl_tile<IN, OUT_F32, kTile, kTile, 2, EDGE, BT, false>(smem, As, lda, Bs, ldb, P, kTile, Mt, Nt, Kt, 0, 0, ep,
-                                                          (int)threadIdx.x);
+    dl_tile<IN, OUT_F32, kTile, kTile, FD, EDGE, BT, false>(smem, As, lda, Bs, ldb, P, kTile, Mt, Nt, Kt, 0, 0, ep,
+                                                           (int)threadIdx.x);
 }
 
 // One thread per 4 consecutive columns of a row: the S partials of those 4
@@ -120,10 +127,11 @@ static void launch_reduce(const Problem& p, int pieces, const float* ws, hipStre
 
 }  // namespace sk
 
-// Pieces actually launched for `splits` requested: ceil(K / Kc).
-int splitk_pieces(int K, int splits, int* Kc_out) {
+// Pieces actually launched for `splits` requested: ceil(K / Kc), Kc a
+// multiple of the slice depth `gran` (64 for 16-bit inputs, 128 for 8-bit).
+int splitk_pieces(int K, int splits, int gran, int* Kc_out) {
     int64_t per = ((int64_t)K + splits - 1) / splits;
-    const int Kc = (int)(((per + 63) / 64) * 64);
+    const int Kc = (int)(((per + gran - 1) / gran) * gran);
     *Kc_out = Kc;
     return (int)(((int64_t)K + Kc - 1) / Kc);
 }
@@ -134,24 +142,32 @@ hipError_t launch_splitk(const Problem& p, int splits, int edge, float* ws, int 
     using dl::OUT_F32;
     using dl::OUT_F16;
     using dl::OUT_BF16;
+    const bool in8 = dtype_in8(p.dtype);
     int Kc = 0;
-    const int pieces = splitk_pieces(p.K, splits, &Kc);
-    const bool in_bf16 = p.dtype == 2 || p.dtype == 3;
-    auto partial = [&](auto edge_c) {
+    const int pieces = splitk_pieces(p.K, splits, in8 ? 128 : 64, &Kc);
+    // input kind of each dtype (gemm_dtype_t order: f16, f16, bf16, bf16, then E4M3 x 3, E5M2 x 3)
+    const int in = p.dtype <= 1 ? 0 : p.dtype <= 3 ? 1 : p.dtype <= 6 ? 2 : 3;
+    auto by_input = [&](auto edge_c, auto bt_c) {
         constexpr int E = decltype(edge_c)::value;
-        if (p.transB) {
-            if (in_bf16) sk::launch_partial<IN_BF16, E, true>(p, pieces, Kc, ws, group_m, s);
-            else sk::launch_partial<IN_F16, E, true>(p, pieces, Kc, ws, group_m, s);
-        } else {
-            if (in_bf16) sk::launch_partial<IN_BF16, E, false>(p, pieces, Kc, ws, group_m, s);
-            else sk::launch_partial<IN_F16, E, false>(p, pieces, Kc, ws, group_m, s);
+        constexpr bool BT = decltype(bt_c)::value;
+        switch (in) {
+        case 0: sk::launch_partial<IN_F16, E, BT>(p, pieces, Kc, ws, group_m, s); break;
+        case 1: sk::launch_partial<IN_BF16, E, BT>(p, pieces, Kc, ws, group_m, s); break;
+        case 2: sk::launch_partial<dl::IN_E4M3, E, BT>(p, pieces, Kc, ws, group_m, s); break;
+        default: sk::launch_partial<dl::IN_E5M2, E, BT>(p, pieces, Kc, ws, group_m, s); break;
         }
+    };
+    auto partial = [&](auto edge_c) {
+        if (p.transB) by_input(edge_c, std::true_type{});
+        else by_input(edge_c, std::false_type{});
     };
     if (edge == dl::EDGE_NONE) partial(std::integral_constant<int, dl::EDGE_NONE>{});
     else partial(std::integral_constant<int, dl::EDGE_CLAMP>{});
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const int out = dtype_out_f32(p.dtype) ? OUT_F32 : (p.dtype == 1 ? OUT_F16 : OUT_BF16);
+    // output kind of each dtype: f32, f16, f32, bf16, then (f32, f16, bf16) twice
+    const int out = dtype_out_f32(p.dtype) ? OUT_F32 : (p.dtype == 1 || p.dtype == 5 || p.dtype == 8) ? OUT_F16
+                                                                                                        : OUT_BF16;
     if (p.epi) {
         if (out == OUT_F32) sk::launch_reduce<OUT_F32, true>(p, pieces, ws, s);
         else if (out == OUT_F16) sk::launch_reduce<OUT_F16, true>(p, pieces, ws, s);

@@ -226,7 +226,8 @@ int gemm_run_noalloc(int64_t M, int64_t N, int64_t K, int dtype, int b_layout,
  * partial tile per output tile of 256 x 256 and per piece,
  * ceil(M/256) * ceil(N/256) * pieces * 262144 bytes, where pieces =
  * ceil(K / Kc) with Kc = ceil(K / splits) rounded up to a multiple of 64
- * (so pieces <= splits).  0 when M, N or K is 0.  splits = 0 asks for the
+ * (so pieces <= splits; 8-bit inputs cut pieces of a multiple of 128, never
+ * more of them, so the same size covers them).  0 when M, N or K is 0.  splits = 0 asks for the
  * library's choice (below) and gives 0 where that choice is not to split.
  * GEMM_ERR_DIM for a negative size, GEMM_ERR_RANGE for a size >= 2^31 or
  * splits outside 0 .. 64.  No GPU call.
@@ -260,11 +261,11 @@ int gemm_run_noalloc(int64_t M, int64_t N, int64_t K, int dtype, int b_layout,
  *                    time need different workspaces.
  *   workspace_bytes  its size in bytes.
  *
- * 16-bit input dtypes only (GEMM_ERR_DTYPE for the 8-bit ones).  Other
- * arguments, ownership and status codes as gemm_run_ex, plus
+ * Every dtype (the 8-bit inputs on their 256 x 256 tile with 128-deep
+ * slices).  Other arguments, ownership and status codes as gemm_run_ex, plus
  * GEMM_ERR_WORKSPACE; GEMM_ERR_INSTANCE when the 256 x 256 kernels cannot run
- * the shape (row-major B with N % 8 != 0 and a partial tile, or leading
- * dimensions too large for their 32-bit offsets).  K == 0 needs no workspace
+ * the shape (row-major B with N % 8 != 0 -- N % 16 for 8-bit inputs -- and a
+ * partial tile, or leading dimensions too large for their 32-bit offsets).  K == 0 needs no workspace
  * and runs as gemm_run_ex.  No allocation, no host synchronisation.
  */
 int64_t gemm_splitk_workspace_size(int64_t M, int64_t N, int64_t K, int splits);

@@ -377,8 +377,8 @@ def test_splitk_arguments_rejected_before_launch(lib):
     assert G.gemm_run_splitk(*args, -1, WS, need, None) == G.GEMM_ERR_RANGE
     assert G.gemm_run_splitk(*args, 65, WS, need, None) == G.GEMM_ERR_RANGE
     assert G.gemm_run_splitk(*args, 4, PC, need, None) == G.GEMM_ERR_ALIAS                # inside C
-    assert G.gemm_run_splitk(M, N, K, 6, 0, PA, K, PB, N, PC, N, 1.0, 0.0, None, 0, 4, WS, need,
-                             None) == G.GEMM_ERR_DTYPE                                      # 8-bit inputs
+    assert G.gemm_run_splitk(M, N, K, 10, 0, PA, K, PB, N, PC, N, 1.0, 0.0, None, 0, 4, WS, need,
+                             None) == G.GEMM_ERR_DTYPE                                      # no such dtype
     assert G.gemm_run_splitk(-1, N, K, 3, 0, PA, K, PB, N, PC, N, 1.0, 0.0, None, 0, 4, WS, need,
                              None) == G.GEMM_ERR_DIM
     assert G.gemm_run_splitk(0, N, K, 3, 0, PA, K, PB, N, PC, N, 1.0, 0.0, None, 0, 4, 0, 0, None) == G.GEMM_OK

@@ -174,7 +174,9 @@ def test_register_budget_and_mfma_shape(kernels):
         budget = 256 if "gemm_pp" in name else 512
         assert meta["num_vgpr"] + meta["num_agpr"] <= budget, _short(name)
         ops = {s.split()[0] for s in ins if s.startswith("v_mfma")}
-        if unit.startswith("gemm_dl_f8"):
+        in8 = unit.startswith("gemm_dl_f8") or ("gemm_sk" in name and
+                                                int(re.findall(r"Li(\d+)E", _short(name))[0]) >= 2)
+        if in8:
             assert ops == {"v_mfma_f32_32x32x64_f8f6f4"}, (_short(name), ops)
         else:
             assert ops <= {"v_mfma_f32_32x32x16_f16", "v_mfma_f32_32x32x16_bf16"}, (_short(name), ops)

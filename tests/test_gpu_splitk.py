@@ -12,6 +12,8 @@ the C ABI, against the oracle.
 * repeated calls give identical bits (the pieces are added in a fixed order);
 * splits = 0 follows the library's rule: split where it pays, else exactly
   gemm_run_ex;
+* 8-bit inputs split on their own 256x256 tile (one piece: that instance's
+  bits; 0.25-grid inputs: exact; random data: within the bound);
 * nothing outside the M x N region of C is written (checked by run()).
 """
 import numpy as np
@@ -135,21 +137,62 @@ def test_repeated_calls_identical_and_long_k(G):
     assert res["ok"], res
 
 
-def test_zero_k_and_errors(G):
+def test_zero_k(G):
     M, N = 64, 48
     A = inputs.normal((M, 0), 540, "bf16")
     B = inputs.normal((0, N), 541, "bf16")
     cold = np.ones((M, N))
     y = _splitk(G, A, B, 2, 4, alpha=1.0, beta=2.0, c_init=encode_out(cold, "f32"))
     assert np.all(y == 2.0)
-    # 8-bit inputs are not split
-    A8 = inputs.normal((64, 64), 542, "e4m3")
-    tA = torch.from_numpy(A8).cuda()
-    tC = torch.zeros((64, 64), dtype=torch.float32, device="cuda")
-    ws = torch.zeros(G.gemm_splitk_workspace_size(64, 64, 64, 2) // 4, dtype=torch.float32, device="cuda")
-    st = G.gemm_run_splitk(64, 64, 64, 4, 0, tA.data_ptr(), 64, tA.data_ptr(), 64, tC.data_ptr(), 64, 1.0, 0.0,
-                           None, 0, 2, ws.data_ptr(), ws.numel() * 4, None)
-    assert st == G.GEMM_ERR_DTYPE
+
+
+@pytest.mark.parametrize("col", [False, True])
+@pytest.mark.parametrize("code", [4, 6, 8])
+def test_8bit_inputs(G, code, col):
+    """8-bit inputs on their 256x256 tile (128-deep slices, pieces of a
+    multiple of 128): one piece equals the 8-bit 256x256 instance bit for bit;
+    0.25-grid inputs give the oracle's value exactly (fp32 output) in any
+    number of pieces; random data stays within the bound plus the 8-bit
+    alignment envelope."""
+    fmt, out = DTYPES[code]
+    for (M, N, K), inst in (((512, 768, 1024), "dl8_256x256x128"), ((300, 528, 1100), "dl8_256x256x128_clamp")):
+        A = inputs.normal((M, K), 560 + code, fmt)
+        B = inputs.normal((K, N), 561 + code, fmt)
+        Bs = np.ascontiguousarray(B.T) if col else B
+        print("split-K 8-bit", code, col, (M, N, K), flush=True)
+        y1 = _splitk8(G, A, Bs, code, 1, col)
+        ref = run(G, A, Bs, code, instance=_instance(G, inst),
+                  layout=G.GEMM_B_COL_MAJOR if col else G.GEMM_B_ROW_MAJOR)
+        assert np.array_equal(y1, ref)
+        y4 = _splitk8(G, A, Bs, code, 4, col)
+        res = oracle.compare(y4, oracle.gemm_f64(A, B, fmt), K, out, extra=oracle.align_bound8(A, B, fmt))
+        assert res["ok"], res
+    M, N, K = 512, 528, 4096
+    fq = "e4m3" if code <= 6 else "e5m2"
+    A = inputs.quarter((M, K), 565, fq)
+    B = inputs.quarter((K, N), 566, fq)
+    Bs = np.ascontiguousarray(B.T) if col else B
+    code32 = 4 if fq == "e4m3" else 7
+    y = _splitk8(G, A, Bs, code32, 8, col)
+    assert_exact(y, oracle.gemm_f64(A, B, fq), "f32", "split-K 8-bit quarter grid")
+
+
+def _splitk8(G, A, Bs, code, splits, col):
+    """gemm_run_splitk on 1-byte inputs (A M x K, B as stored)."""
+    M, K = A.shape
+    N = Bs.shape[0] if col else Bs.shape[1]
+    out = DTYPES[code][1]
+    tA = torch.from_numpy(np.ascontiguousarray(A)).cuda()
+    tB = torch.from_numpy(np.ascontiguousarray(Bs)).cuda()
+    tC = torch.full((M, N), -1, dtype=torch.int32 if out == "f32" else torch.int16, device="cuda")
+    need = G.gemm_splitk_workspace_size(M, N, K, splits)
+    ws = torch.full((max(need // 4, 1),), float("nan"), dtype=torch.float32, device="cuda")
+    st = G.gemm_run_splitk(M, N, K, code, 1 if col else 0, tA.data_ptr(), K, tB.data_ptr(), K if col else N,
+                           tC.data_ptr(), N, 1.0, 0.0, None, 0, splits, ws.data_ptr(), ws.numel() * 4,
+                           torch.cuda.current_stream().cuda_stream)
+    assert st == 0, G.gemm_strerror(st)
+    torch.cuda.synchronize()
+    return decode_out(tC.cpu().numpy().view(np.uint32 if out == "f32" else np.uint16), out)
 
 
 def test_library_choice(G):
