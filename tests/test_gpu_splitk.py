@@ -218,3 +218,67 @@ def test_library_choice(G):
     torch.cuda.synchronize()
     y = decode_out(tC.cpu().numpy().view(np.uint16), "bf16")
     assert np.array_equal(y, run(G, A, B, 3, layout=G.GEMM_B_ROW_MAJOR))
+
+
+def test_random_sweep(G):
+    """Seeded random cases: ragged shapes, every dtype, both B layouts, the
+    general epilogue, 0 (the library's choice) to 9 pieces; every element
+    against the oracle (plus the 8-bit alignment envelope for 8-bit inputs)."""
+    rng = np.random.Generator(np.random.PCG64(20261203))
+    dims = [1, 17, 64, 200, 256, 257, 300, 511, 520, 528]
+    ran = 0
+    for case in range(80):
+        M, N = int(rng.choice(dims)), int(rng.choice(dims))
+        K = int(rng.choice([1, 63, 64, 130, 700, 1100, 2048, 4099, 5000]))
+        code = int(rng.integers(0, 10))
+        col = bool(rng.random() < 0.5)
+        splits = int(rng.integers(0, 10))
+        fmt, out = DTYPES[code]
+        if not col and N % (16 if fmt in ("e4m3", "e5m2") else 8) != 0 and (M % 256 or N % 256):
+            N = N + (-N) % 16                    # row-major B with a partial tile: whole 16-byte column chunks
+        epi = rng.random() < 0.5
+        alpha = float(rng.choice([1.0, -0.5, 2.0])) if epi else 1.0
+        beta = float(rng.choice([0.0, 1.0])) if epi else 0.0
+        bias = rng.uniform(-1, 1, N) if epi and rng.random() < 0.5 else None
+        relu = int(epi and rng.random() < 0.5)
+        A = law_for(fmt)((M, K), 7000 + 2 * case, fmt) if fmt not in ("e4m3", "e5m2") else \
+            inputs.normal((M, K), 7000 + 2 * case, fmt)
+        B = law_for(fmt)((K, N), 7001 + 2 * case, fmt) if fmt not in ("e4m3", "e5m2") else \
+            inputs.normal((K, N), 7001 + 2 * case, fmt)
+        Bs = np.ascontiguousarray(B.T) if col else B
+        cold = decode_out(encode_out(rng.uniform(-2, 2, (M, N)), out), out)
+        print("split-K sweep", case, (M, N, K), code, col, splits, epi, flush=True)
+        if fmt in ("e4m3", "e5m2"):
+            y = _splitk8_ex(G, A, Bs, code, splits, col, alpha, beta, bias, relu, encode_out(cold, out))
+        else:
+            y = _splitk(G, A, Bs, code, splits, col=col, alpha=alpha, beta=beta, bias=bias, relu=relu,
+                        c_init=encode_out(cold, out))
+        lay = "col" if col else "row"
+        bias32 = None if bias is None else bias.astype(np.float32).astype(np.float64)
+        r = oracle.gemm_ex_f64(A, Bs, fmt, b_layout=lay, alpha=alpha, beta=beta, C_old=cold, bias=bias32,
+                               relu=bool(relu))
+        dot = oracle.gemm_ex_f64(A, Bs, fmt, b_layout=lay)
+        extra = oracle.align_bound8(A, B, fmt) if fmt in ("e4m3", "e5m2") else None
+        res = oracle.compare_ex(y, r, K, out, alpha=alpha, beta=beta, C_old=cold, bias=bias32, dot=dot,
+                                extra=extra)
+        assert res["ok"], (case, res)
+        ran += 1
+    assert ran == 80
+
+
+def _splitk8_ex(G, A, Bs, code, splits, col, alpha, beta, bias, relu, cbits):
+    M, K = A.shape
+    N = Bs.shape[0] if col else Bs.shape[1]
+    out = DTYPES[code][1]
+    tA = torch.from_numpy(np.ascontiguousarray(A)).cuda()
+    tB = torch.from_numpy(np.ascontiguousarray(Bs)).cuda()
+    tC = torch.from_numpy(np.ascontiguousarray(cbits).view(np.int32 if out == "f32" else np.int16).copy()).cuda()
+    need = G.gemm_splitk_workspace_size(M, N, K, splits)
+    ws = torch.full((max(need // 4, 1),), float("nan"), dtype=torch.float32, device="cuda")
+    tb = torch.tensor(np.asarray(bias, dtype=np.float32), device="cuda") if bias is not None else None
+    st = G.gemm_run_splitk(M, N, K, code, 1 if col else 0, tA.data_ptr(), K, tB.data_ptr(), K if col else N,
+                           tC.data_ptr(), N, alpha, beta, tb.data_ptr() if tb is not None else None, relu, splits,
+                           ws.data_ptr(), ws.numel() * 4, torch.cuda.current_stream().cuda_stream)
+    assert st == 0, G.gemm_strerror(st)
+    torch.cuda.synchronize()
+    return decode_out(tC.cpu().numpy().view(np.uint32 if out == "f32" else np.uint16), out)
