@@ -82,8 +82,17 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(
         const int64_t in_tile = (int64_t)(i - tm * kTile) * kTile + (j - tn * kTile);
         const float4* p = reinterpret_cast<const float4*>(ws + ((int64_t)tm * tilesN + tn) * kTileFloats + in_tile);
         const int64_t piece = (int64_t)tilesM * tilesN * kTileFloats / 4;     // float4 stride between pieces
+        // four pieces' loads in flight at a time, added strictly in piece order
         float4 acc = p[0];
-        for (int s = 1; s < S; ++s) {
+        int s = 1;
+        for (; s + 4 <= S; s += 4) {
+            const float4 q0 = p[s * piece], q1 = p[(s + 1) * piece], q2 = p[(s + 2) * piece], q3 = p[(s + 3) * piece];
+            acc.x += q0.x; acc.y += q0.y; acc.z += q0.z; acc.w += q0.w;
+            acc.x += q1.x; acc.y += q1.y; acc.z += q1.z; acc.w += q1.w;
+            acc.x += q2.x; acc.y += q2.y; acc.z += q2.z; acc.w += q2.w;
+            acc.x += q3.x; acc.y += q3.y; acc.z += q3.z; acc.w += q3.w;
+        }
+        for (; s < S; ++s) {
             const float4 q = p[s * piece];
             acc.x += q.x; acc.y += q.y; acc.z += q.z; acc.w += q.w;
         }
