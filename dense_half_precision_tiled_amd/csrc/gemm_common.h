@@ -56,14 +56,27 @@ __device__ __forceinline__ f32x16 mfma8(u32x8 a, u32x8 b, f32x16 c) {
                                                             0, 0, 0, 0);
 }
 
-template <int OUT>
+// NT: a non-temporal store (the `nt` cache policy), for output that no later
+// step of the same kernel reads: it does not take L2 lines from the operand
+// panels still being streamed, and the end of the kernel has fewer dirty
+// lines to write back.  The value stored is the same either way.
+template <int OUT, bool NT = false>
 __device__ __forceinline__ void store_out(void* C, int64_t idx, float v) {
-    if constexpr (OUT == OUT_F32)
+    if constexpr (NT) {
+        if constexpr (OUT == OUT_F32)
+            __builtin_nontemporal_store(v, static_cast<float*>(C) + idx);
+        else if constexpr (OUT == OUT_F16)
+            __builtin_nontemporal_store((_Float16)v, static_cast<_Float16*>(C) + idx);
+        else
+            __builtin_nontemporal_store(__builtin_bit_cast(unsigned short, (__bf16)v),
+                                        static_cast<unsigned short*>(C) + idx);
+    } else if constexpr (OUT == OUT_F32) {
         static_cast<float*>(C)[idx] = v;
-    else if constexpr (OUT == OUT_F16)
+    } else if constexpr (OUT == OUT_F16) {
         static_cast<_Float16*>(C)[idx] = (_Float16)v;     // v_cvt_f16_f32: round to nearest even
-    else
+    } else {
         static_cast<__bf16*>(C)[idx] = (__bf16)v;         // round to nearest even
+    }
 }
 
 template <int OUT>

@@ -98,8 +98,13 @@ constexpr int dl_lds_bytes() {
 // lane offsets derived from it are recomputed per tile instead of being
 // kept live across the accumulator-heavy main loop).  On return every wave
 // has issued its stores and no wave reads `smem` any more once all have
-// returned.
-template <int IN, int OUT, int BM, int BN, int FD, int EDGE, bool BT, bool EPI>
+// returned.  NTC: store the tile with non-temporal stores.  The whole-tile
+// kernels do (the host gives them only C whose rows start on 64-byte
+// boundaries, so that every store instruction writes whole 64-byte
+// segments); the edge kernels, whose C rows may sit at any 2-byte offset,
+// and the split-K kernel's fp32 partial tiles, which its second kernel reads
+// back, keep the default cache policy.
+template <int IN, int OUT, int BM, int BN, int FD, int EDGE, bool BT, bool EPI, bool NTC = false>
 __device__ __forceinline__ void dl_tile(
     char* smem, const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
     void* __restrict__ C, int64_t ldc, int M, int N, int K, int m0, int n0, const EpiArgs& ep, int tid) {
@@ -483,7 +488,7 @@ __device__ __forceinline__ void dl_tile(
                             if constexpr (ro) old = load_out<OUT>(C, idx);
                             v = epi_value(v, ep, ro, old, bias_v[j]);
                         }
-                        store_out<OUT>(C, idx, v);
+                        store_out<OUT, NTC>(C, idx, v);
                     }
                 }
             }
@@ -517,8 +522,9 @@ __global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
     __shared__ __attribute__((aligned(1024))) char smem[dl_lds_bytes<IN, BM, BN, EDGE, BT>()];
     int tm, tn;
     tile_coords(blockIdx.x, tilesM, tilesN, group_m, &tm, &tn);
-    dl_tile<IN, OUT, BM, BN, FD, EDGE, BT, EPI>(smem, A, lda, B, ldb, C, ldc, M, N, K, tm * BM, tn * BN, ep,
-                                                (int)threadIdx.x);
+    constexpr bool NTC = EDGE == EDGE_NONE;          // non-temporal C stores on whole tiles
+    dl_tile<IN, OUT, BM, BN, FD, EDGE, BT, EPI, NTC>(smem, A, lda, B, ldb, C, ldc, M, N, K, tm * BM, tn * BN, ep,
+                                                     (int)threadIdx.x);
 #ifdef DHPT_TIMELINE
     tl_record(ep.timeline, tl0);
 #endif
@@ -595,8 +601,9 @@ __global__ __launch_bounds__(256, 1) void gemm_dl_persist_kernel(
         int lane;
         asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
         const int tid = 64 * wave + lane;
-        dl_tile<IN, OUT, BM, BN, FD, EDGE, BT, EPI>(smem, A, lda, B, ldb, C, ldc, M, N, K, tm * BM, tn * BN, ep,
-                                                    tid);
+        constexpr bool NTC = EDGE == EDGE_NONE;      // non-temporal C stores on whole tiles
+        dl_tile<IN, OUT, BM, BN, FD, EDGE, BT, EPI, NTC>(smem, A, lda, B, ldb, C, ldc, M, N, K, tm * BM, tn * BN, ep,
+                                                         tid);
         __syncthreads();                    // the stages are free; next_tile is published
         L = __builtin_amdgcn_readfirstlane(next_tile);
     }

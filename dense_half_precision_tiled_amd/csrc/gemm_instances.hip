@@ -86,7 +86,11 @@ bool instance_supports(int id, const Problem& p) {
     if (!in.in8 && in.kind == KIND_DL && in.fd == 1 && (p.transB || p.epi)) return false;   // plain row-major B only
     if (in.edge != EDGE_MASKED && !copy_offsets_fit(p, in.tile, in.in8 ? 1 : 2)) return false;
     switch (in.edge) {
-    case EDGE_NONE: return p.M % in.tile == 0 && p.N % in.tile == 0 && p.K % (in.in8 ? 128 : 64) == 0;
+    case EDGE_NONE:
+        // whole tiles; C rows start on 64-byte boundaries, which the
+        // non-temporal stores of these kernels need to write whole segments
+        return p.M % in.tile == 0 && p.N % in.tile == 0 && p.K % (in.in8 ? 128 : 64) == 0 &&
+               ((reinterpret_cast<uintptr_t>(p.C) | (uintptr_t)p.ldc * (dtype_out_f32(p.dtype) ? 4 : 2)) & 63) == 0;
     case EDGE_CLAMP: {
         const int chunk = in.in8 ? 16 : 8;                 // row-major B: whole 16-byte column chunks
         if (!c_offsets_fit(p, in.tile)) return false;

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256, 1) void gemm_sk_kernel(
 #ifdef DHPT_TIMELINE
     ep.timeline = nullptr;
 #endif
-    dl_tile<IN, OUT_F32, kTile, kTile, FD, EDGE, BT, false>(smem, As, lda, Bs, ldb, P, kTile, Mt, Nt, Kt, 0, 0, ep,
+    dl_tile<IN, OUT_F32, kTile, kTile, FD, EDGE, BT, false, false>(smem, As, lda, Bs, ldb, P, kTile, Mt, Nt, Kt, 0, 0, ep,
                                                            (int)threadIdx.x);
 }
 
