@@ -350,7 +350,7 @@ __global__ __launch_bounds__(256, 1) void gemm_ks_kernel(
                         const float old = read_old ? load_out<OUT>(C, idx) : 0.0f;
                         y = epi_value(y, ep, read_old, old, bias_v);
                     }
-                    store_out<OUT>(C, idx, y);
+                    store_out<OUT, EDGE == dl::EDGE_NONE>(C, idx, y);   // non-temporal on whole tiles
                 }
             }
         };
