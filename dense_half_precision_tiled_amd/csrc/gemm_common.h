@@ -118,6 +118,25 @@ __device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint
 }
 #pragma clang diagnostic pop
 
+// v_permlane32_swap_b32 on four pairs: in each, lanes 32-63 of x trade
+// places with lanes 0-31 of y (x becomes {x[0..31], y[0..31]}, y becomes
+// {x[32..63], y[32..63]}; pinned by a probe test).  The instruction needs two
+// wait states after a VALU write of its operands; assembly gets none from the
+// compiler, hence the s_nop 1 before the group (each later swap of the group
+// is further from those writes) and, conservatively, one after it.  Four to
+// a group, in assembly: the builtin, one swap at a time, pushed the 256x256
+// epilogue into scratch.
+__device__ __forceinline__ void permlane32_swap4(uint32_t& x0, uint32_t& y0, uint32_t& x1, uint32_t& y1,
+                                                 uint32_t& x2, uint32_t& y2, uint32_t& x3, uint32_t& y3) {
+    asm volatile("s_nop 1\n\t"
+                 "v_permlane32_swap_b32 %0, %1\n\t"
+                 "v_permlane32_swap_b32 %2, %3\n\t"
+                 "v_permlane32_swap_b32 %4, %5\n\t"
+                 "v_permlane32_swap_b32 %6, %7\n\t"
+                 "s_nop 1"
+                 : "+v"(x0), "+v"(y0), "+v"(x1), "+v"(y1), "+v"(x2), "+v"(y2), "+v"(x3), "+v"(y3));
+}
+
 __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 #define DL_FENCE() __builtin_amdgcn_sched_barrier(0)

@@ -103,8 +103,11 @@ constexpr int dl_lds_bytes() {
 // boundaries, so that every store instruction writes whole 64-byte
 // segments); the edge kernels, whose C rows may sit at any 2-byte offset,
 // and the split-K kernel's fp32 partial tiles, which its second kernel reads
-// back, keep the default cache policy.
-template <int IN, int OUT, int BM, int BN, int FD, int EDGE, bool BT, bool EPI, bool NTC = false>
+// back, keep the default cache policy.  ROWS: unmasked tiles store whole
+// 64-column row pieces (the lane exchange in the epilogue below); the
+// persistent kernel, whose tile loop keeps more registers live, does not
+// (with it its epilogue spilled to scratch).
+template <int IN, int OUT, int BM, int BN, int FD, int EDGE, bool BT, bool EPI, bool NTC = false, bool ROWS = false>
 __device__ __forceinline__ void dl_tile(
     char* smem, const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
     void* __restrict__ C, int64_t ldc, int M, int N, int K, int m0, int n0, const EpiArgs& ep, int tid) {
@@ -471,6 +474,52 @@ __device__ __forceinline__ void dl_tile(
             }
             return;
         }
+        if constexpr (ROWS && !decltype(masked)::value && TN % 2 == 0) {
+            // Whole rows per store: element e of blocks j and j+1 covers rows
+            // R (lanes 0-31) and R+4 (lanes 32-63) of 32 columns each; one
+            // v_permlane32_swap of the two turns them into row R and row R+4
+            // of all 64 columns 32j .. 32j+63, so every store instruction
+            // writes 64 consecutive elements of one row (128 bytes of a
+            // 16-bit output, whole cache lines when the rows are aligned)
+            // instead of two 32-element pieces.  Four elements at a time.
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+#pragma unroll
+                for (int j = 0; j < TN; j += 2) {
+                    const int col = n0 + wn * WN + 32 * j + le;
+                    const float bias_c = le < 32 ? bias_v[j] : bias_v[j + 1];
+#pragma unroll
+                    for (int e0 = 0; e0 < 16; e0 += 4) {
+                        uint32_t x[4], y[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            // through a float: a bit cast taken straight from
+                            // the vector subscript read the same register for
+                            // every subscript
+                            const float xa = acc[i][j][e0 + q], ya = acc[i][j + 1][e0 + q];
+                            x[q] = __float_as_uint(xa);
+                            y[q] = __float_as_uint(ya);
+                        }
+                        permlane32_swap4(x[0], y[0], x[1], y[1], x[2], y[2], x[3], y[3]);
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) {
+                            const int e = e0 + (q >> 1), h = q & 1;     // h: row R or R+4
+                            const int row = m0 + wm * WM + 32 * i + 8 * (e >> 2) + (e & 3) + 4 * h;
+                            const int64_t idx = (int64_t)row * ldc + col;
+                            float v = __uint_as_float(h ? y[q >> 1] : x[q >> 1]);
+                            if constexpr (EPI) {
+                                constexpr bool ro = decltype(read_old)::value;
+                                float old = 0.0f;
+                                if constexpr (ro) old = load_out<OUT>(C, idx);
+                                v = epi_value(v, ep, ro, old, bias_c);
+                            }
+                            store_out<OUT, NTC>(C, idx, v);
+                        }
+                    }
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -523,8 +572,8 @@ __global__ __launch_bounds__(256, 1) void gemm_dl_kernel(
     int tm, tn;
     tile_coords(blockIdx.x, tilesM, tilesN, group_m, &tm, &tn);
     constexpr bool NTC = EDGE == EDGE_NONE;          // non-temporal C stores on whole tiles
-    dl_tile<IN, OUT, BM, BN, FD, EDGE, BT, EPI, NTC>(smem, A, lda, B, ldb, C, ldc, M, N, K, tm * BM, tn * BN, ep,
-                                                     (int)threadIdx.x);
+    dl_tile<IN, OUT, BM, BN, FD, EDGE, BT, EPI, NTC, true>(smem, A, lda, B, ldb, C, ldc, M, N, K, tm * BM, tn * BN,
+                                                           ep, (int)threadIdx.x);
 #ifdef DHPT_TIMELINE
     tl_record(ep.timeline, tl0);
 #endif

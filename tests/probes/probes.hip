@@ -406,9 +406,24 @@ __global__ void probe_unaligned_kernel(const char* src, int offset, uint32_t* ou
     __syncthreads();
     for (int j = 0; j < 4; ++j) out_lds[4 * l + j] = lds[4 * l + j];
 }
+// The lane exchange of the whole-tile epilogues: v_permlane32_swap_b32 in
+// the kernels' form (s_nop 1 before and after) on x = 1000 + lane and
+// y = 2000 + lane; out[0..63] = x afterwards, out[64..127] = y afterwards.
+__global__ void probe_permlane32_swap_kernel(uint32_t* out) {
+    const uint32_t l = threadIdx.x;
+    uint32_t x = 1000u + l, y = 2000u + l;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+    out[l] = x;
+    out[64 + l] = y;
+}
 #pragma clang diagnostic pop
 
 extern "C" {
+
+int probe_permlane32_swap(uint32_t* out) {
+    hipLaunchKernelGGL(probe_permlane32_swap_kernel, dim3(1), dim3(64), 0, 0, out);
+    return (int)hipDeviceSynchronize();
+}
 
 int probe_unaligned(const char* src, int src_bytes, int offset, uint32_t* out_vec, uint32_t* out_lds) {
     if (offset < 0 || offset + 32 * 64 + 16 > src_bytes) return -1;

@@ -416,3 +416,19 @@ def test_unaligned_16_byte_global_loads(P, offset):
     kind = lambda got: "exact" if np.array_equal(got, exact) else ("aligned-down" if np.array_equal(got, down) else "other")
     print("offset %2d: global_load_dwordx4 -> %s, global_load_lds_dwordx4 -> %s" % (offset, kind(vec), kind(lds)))
     assert kind(vec) == "exact" and kind(lds) == "exact"
+
+
+def test_permlane32_swap_lanes(P):
+    """v_permlane32_swap_b32 x, y: lanes 32-63 of x trade with lanes 0-31 of y.
+    The whole-tile epilogues rely on it to turn two 32-column pieces of rows
+    R and R+4 into one 64-column piece of each row."""
+    P.probe_permlane32_swap.argtypes = [ctypes.c_void_p]
+    P.probe_permlane32_swap.restype = ctypes.c_int
+    out = torch.zeros(128, dtype=torch.int32, device="cuda")
+    assert P.probe_permlane32_swap(out.data_ptr()) == 0
+    got = out.cpu().numpy()
+    lane = np.arange(64)
+    want_x = np.where(lane < 32, 1000 + lane, 2000 + lane - 32)
+    want_y = np.where(lane < 32, 1000 + lane + 32, 2000 + lane)
+    assert (got[:64] == want_x).all() and (got[64:] == want_y).all(), got
+
