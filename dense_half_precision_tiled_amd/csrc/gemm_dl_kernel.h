@@ -307,14 +307,19 @@ __device__ __forceinline__ void dl_tile(
     auto fill_slice = [&](int stage, int kt) {
         fill_stage<BM, BN, BT, ESZ>(smem + stage * STAGE, A, lda, B, ldb, M, N, K, m0, n0, kt * BK, t);
     };
-    // One filled slice, unpipelined: the reads of each k-step, then its MFMAs.
-    auto compute_slice = [&](int stage) {
+    // One filled slice, unpipelined: the reads of each of its first `nks`
+    // k-steps, then that k-step's MFMAs (the k-steps past a partial slice's
+    // last valid k hold only zero fill and are skipped: adding their zero
+    // products changes no sum, at most the sign of a zero).
+    auto compute_slice = [&](int stage, int nks) {
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
+            if (s < nks) {
 #pragma unroll
-            for (int x = 0; x < R; ++x) read_piece(stage, s, 0, x);
+                for (int x = 0; x < R; ++x) read_piece(stage, s, 0, x);
 #pragma unroll
-            for (int q = 0; q < S; ++q) mfma1(0, q);
+                for (int q = 0; q < S; ++q) mfma1(0, q);
+            }
         }
     };
 
@@ -381,7 +386,7 @@ __device__ __forceinline__ void dl_tile(
             __syncthreads();            // every wave is done reading the previous slice
             fill_slice(0, kt);
             __syncthreads();
-            compute_slice(0);
+            compute_slice(0, KSTEPS);
         }
     } else {
         const int nk_full = K / BK;
@@ -414,7 +419,8 @@ __device__ __forceinline__ void dl_tile(
                 __syncthreads();        // every wave is done reading the stage being refilled
                 fill_slice(stage, nk_full);
                 __syncthreads();
-                compute_slice(stage);
+                constexpr int KK = BK / KSTEPS;                      // k per k-step
+                compute_slice(stage, (K % BK + KK - 1) / KK);
             }
         }
     }
