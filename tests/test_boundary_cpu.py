@@ -103,6 +103,21 @@ def _pick(M, N, K, dtype=3, lda=None, ldb=None, ldc=None, pa=PA, pb=PB):
         M, N, K, dtype, pa, lda or K, pb, ldb or N, 0x7000000000, ldc or N))
 
 
+def test_whole_tile_kernels_need_64_byte_aligned_c_rows(lib):
+    """The whole-tile kernels store C non-temporally in 64-column row pieces;
+    the host gives them only C whose rows start on 64-byte boundaries and
+    sends other whole-tile problems to the clamped kernel."""
+    def pick(c, ldc, dtype=3):
+        return G.gemm_instance_name(G.gemm_select_instance(8192, 8192, 8192, dtype, PA, 8192, PB, 8192, c, ldc))
+    base = 0x7000000000
+    assert pick(base, 8192) == "dl_256x256x64_fd2"
+    assert pick(base, 8192 + 32) == "dl_256x256x64_fd2"          # 16448 bytes per bf16 row
+    assert pick(base, 8192 + 8) == "dl_256x256x64_fd2_clamp"     # 16400 bytes: rows off 64-byte boundaries
+    assert pick(base + 2, 8192) == "dl_256x256x64_fd2_clamp"     # C itself one element off
+    assert pick(base + 32, 8192, dtype=2) == "dl_256x256x64_fd2_clamp"   # fp32 C, 32 bytes off
+    assert pick(base, 8192 + 16, dtype=2) == "dl_256x256x64_fd2"  # fp32 rows of 32832 bytes
+
+
 def test_instance_choice(lib):
     assert _pick(8192, 8192, 8192) == "dl_256x256x64_fd2"
     assert _pick(4096, 4096, 4096) == "dl_256x256x64_fd2"
