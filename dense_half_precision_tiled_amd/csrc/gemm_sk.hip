@@ -60,8 +60,8 @@ __global__ __launch_bounds__(256, 1) void gemm_sk_kernel(
 #ifdef DHPT_TIMELINE
     ep.timeline = nullptr;
 #endif
-    dl_tile<IN, OUT_F32, kTile, kTile, FD, EDGE, BT, false, false>(smem, As, lda, Bs, ldb, P, kTile, Mt, Nt, Kt, 0, 0, ep,
-                                                           (int)threadIdx.x);
+    dl_tile<IN, OUT_F32, kTile, kTile, FD, EDGE, BT, false, false>(smem, As, lda, Bs, ldb, P, kTile, Mt, Nt, Kt, 0,
+                                                                  0, ep, (int)threadIdx.x);
 }
 
 // One thread per 4 consecutive columns of a row: the S partials of those 4
