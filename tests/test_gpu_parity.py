@@ -172,6 +172,28 @@ def test_instances_agree_bitwise(G):
         assert set(first) == {"dl", "ks"}
 
 
+def test_c_row_alignment_picks_the_store_form_not_the_result(G):
+    """A whole-tile shape runs the whole-tile kernel (non-temporal stores of
+    64-column row pieces) when C's rows start on 64-byte boundaries and the
+    clamped kernel otherwise (a padded ldc, or C one element off): the same
+    per-element arithmetic, so the same bits, and the padding and guard
+    bands stay untouched (checked by run())."""
+    # 2048 x 2048 runs 128x128 tiles, 4096 x 4096 the 256x256 tile: both pair
+    # their 32-column blocks into row pieces
+    for (M, N, K) in ((2048, 2048, 256), (4096, 4096, 128)):
+        for code in (0, 1, 3):
+            fmt, out = DTYPES[code]
+            print("row alignment", (M, N, K), code, flush=True)
+            A = law_for(fmt)((M, K), 111, fmt)
+            B = law_for(fmt)((K, N), 112, fmt)
+            y0 = run(G, A, B, code)                      # ldc = N: aligned rows
+            y1 = run(G, A, B, code, ldc=N + 4)           # rows off 64-byte boundaries
+            y2 = run(G, A, B, code, c_off=1)             # C itself 2 or 4 bytes off
+            assert np.array_equal(y0, y1) and np.array_equal(y0, y2), (M, code)
+            if M == 2048:
+                assert_bound(y0, oracle.gemm_f64(A, B, fmt), K, out, "row alignment %d" % code)
+
+
 def test_k_split_reduction_is_deterministic(G):
     """The four partial tiles are added in a fixed order: repeated calls give
     the same bits (whole tiles with an even slice count; clamped edges with an
